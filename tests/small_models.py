@@ -1,0 +1,16 @@
+"""Small model shapes, one per family of the five workloads, for CPU pins and quick GPU
+parity cases. Shapes only; the weights come from the seeded generator."""
+from workloads import configs as C
+
+TINY = C.TINY
+
+QWEN_SMALL = C.shrink_model(C.QWEN05B, name="qwen-small", vocab=97, hidden=64, layers=2,
+                            heads=4, kv_heads=2, head_dim=16, ffn=96)
+
+LLAMA_SMALL = C.shrink_model(C.LLAMA1B, name="llama-small", vocab=101, hidden=64, layers=2,
+                             heads=8, kv_heads=2, head_dim=8, ffn=128)
+
+ENCODER_SMALL = C.shrink_model(C.ENCODER, name="encoder-small", vocab=89, hidden=64,
+                               layers=2, heads=4, kv_heads=2, head_dim=32, ffn=96)
+
+FAMILIES = [TINY, QWEN_SMALL, LLAMA_SMALL, ENCODER_SMALL]

@@ -1,0 +1,114 @@
+"""Seeded synthetic inputs: random-init weights and random prompt ids.
+
+This module is shared by the oracle and the GPU path and holds none of the forward
+pass's arithmetic: it only draws numbers and stores them in the checkpoint formats the
+pages load (bf16 bit patterns or f32, under HuggingFace tensor names).
+
+Recipe (all draws from ``numpy.random.default_rng(seed)``, PCG64):
+
+* weights: seed = the workload's ``weight_seed``; tensors are drawn in a fixed order --
+  embedding, then per layer the order in which ember's NumPy reference reads them
+  (q, q-bias, k, k-bias, v, v-bias, o, gate, up, down), then the classification head
+  weight and bias; each draw is ``standard_normal(shape, float32) * 0.02``.
+* every RMSNorm weight (input, post-attention, final, per-head q/k) is 1.0 and is not
+  drawn, as the Falcon-H1 Rust reference's ``synthetic_weights`` fills norm weights with 1.
+* bf16 models: each f32 draw is rounded once to bf16 (round to nearest, ties to even);
+  those bf16 values *are* the model.
+* prompt ids: seed = the workload's ``ids_seed``,
+  ``integers(0, vocab, size=(batch, prompt_len), dtype=int32)``.
+"""
+from __future__ import annotations
+
+from collections import OrderedDict
+from typing import Dict, Tuple
+
+import numpy as np
+
+from .configs import ModelConfig, Workload
+
+# A checkpoint: HF tensor name -> (dtype tag, array). dtype tag "bf16" means the array is
+# uint16 bit patterns; "f32" means float32 values.
+Checkpoint = "OrderedDict[str, Tuple[str, np.ndarray]]"
+
+INIT_STD = 0.02
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even) and return the bit patterns.
+
+    Used only to store the seeded draws in bf16, the checkpoint format; inputs are finite.
+    """
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def tensor_shapes(m: ModelConfig) -> "OrderedDict[str, Tuple[int, ...]]":
+    """Names and shapes of every tensor of the model, in draw order."""
+    s: "OrderedDict[str, Tuple[int, ...]]" = OrderedDict()
+    s["model.embed_tokens.weight"] = (m.vocab, m.hidden)
+    for i in range(m.layers):
+        p = f"model.layers.{i}."
+        s[p + "input_layernorm.weight"] = (m.hidden,)
+        s[p + "self_attn.q_proj.weight"] = (m.q_dim, m.hidden)
+        if m.qkv_bias:
+            s[p + "self_attn.q_proj.bias"] = (m.q_dim,)
+        s[p + "self_attn.k_proj.weight"] = (m.kv_dim, m.hidden)
+        if m.qkv_bias:
+            s[p + "self_attn.k_proj.bias"] = (m.kv_dim,)
+        s[p + "self_attn.v_proj.weight"] = (m.kv_dim, m.hidden)
+        if m.qkv_bias:
+            s[p + "self_attn.v_proj.bias"] = (m.kv_dim,)
+        s[p + "self_attn.o_proj.weight"] = (m.hidden, m.q_dim)
+        if m.qk_norm:
+            s[p + "self_attn.q_norm.weight"] = (m.head_dim,)
+            s[p + "self_attn.k_norm.weight"] = (m.head_dim,)
+        s[p + "post_attention_layernorm.weight"] = (m.hidden,)
+        s[p + "mlp.gate_proj.weight"] = (m.ffn, m.hidden)
+        s[p + "mlp.up_proj.weight"] = (m.ffn, m.hidden)
+        s[p + "mlp.down_proj.weight"] = (m.hidden, m.ffn)
+    s["model.norm.weight"] = (m.hidden,)
+    if m.head == "cls":
+        s["token_cls_head.weight"] = (m.n_classes, m.hidden)
+        s["token_cls_head.bias"] = (m.n_classes,)
+    return s
+
+
+def is_norm_weight(name: str) -> bool:
+    return name.endswith("layernorm.weight") or name.endswith("norm.weight")
+
+
+def make_weights(m: ModelConfig, seed: int) -> "OrderedDict[str, Tuple[str, np.ndarray]]":
+    rng = np.random.default_rng(seed)
+    out: "OrderedDict[str, Tuple[str, np.ndarray]]" = OrderedDict()
+    for name, shape in tensor_shapes(m).items():
+        if is_norm_weight(name):
+            a = np.ones(shape, dtype=np.float32)
+        else:
+            a = rng.standard_normal(shape, dtype=np.float32)
+            a *= np.float32(INIT_STD)
+        if m.weight_dtype == "bf16":
+            out[name] = ("bf16", f32_to_bf16_bits(a))
+        elif m.weight_dtype == "f32":
+            out[name] = ("f32", a)
+        else:
+            raise ValueError(f"unknown weight dtype {m.weight_dtype}")
+    return out
+
+
+def make_ids(w: Workload, batch: int | None = None, prompt_len: int | None = None) -> np.ndarray:
+    rng = np.random.default_rng(w.ids_seed)
+    b = w.batch if batch is None else batch
+    t = w.prompt_len if prompt_len is None else prompt_len
+    return rng.integers(0, w.model.vocab, size=(b, t), dtype=np.int32)
+
+
+_cache: Dict[Tuple, object] = {}
+
+
+def weights_for(w: Workload):
+    """Weights of a workload, memoised per process (the large shapes take seconds)."""
+    key = (w.model, w.weight_seed)
+    if key not in _cache:
+        _cache[key] = make_weights(w.model, w.weight_seed)
+    return _cache[key]
