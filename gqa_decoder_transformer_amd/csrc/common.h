@@ -1,0 +1,92 @@
+// Device helpers shared by the gfx950 kernels: bf16 conversions, wave64 reductions,
+// vector types for 16-byte loads and the MFMA operand types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define EMBER_DEV __device__ __forceinline__
+
+typedef uint16_t bf16_t;                                        // raw bf16 bits
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));     // MFMA A/B operand
+typedef float f32x4_t __attribute__((ext_vector_type(4)));       // MFMA 16x16 accumulator
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));    // 16-byte load unit
+
+constexpr int kWave = 64;
+
+// bf16 -> f32 is exact: the stored 16 bits become the high half of the f32 word
+// ("ember scripts/reference_forward.py", load_safetensors, BF16 branch).
+EMBER_DEV float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+EMBER_DEV float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+EMBER_DEV float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
+
+// f32 -> bf16, round to nearest, ties to even (finite inputs).
+EMBER_DEV uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Split x = hi + lo with hi = bf16(x), lo = bf16(x - hi); |x - hi - lo| <= 2^-17 |x|.
+EMBER_DEV void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f32_to_bf16_rne(x);
+  lo = f32_to_bf16_rne(x - bf16_to_f32(hi));
+}
+
+template <typename T>
+EMBER_DEV T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <typename T>
+EMBER_DEV T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+EMBER_DEV float group_sum(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Block-wide sum for blockDim.x <= 1024; `red` holds >= 16 floats of shared memory.
+EMBER_DEV float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  const int nw = (blockDim.x + kWave - 1) / kWave;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < nw; ++i) s += red[i];   // same order in every thread
+  return s;
+}
+
+// Order-preserving map of an f32 to u32 (larger float -> larger key); -0.0 is folded
+// onto +0.0 first so the two zeros tie.
+EMBER_DEV uint32_t ordered_key(float v) {
+  v = v + 0.0f;
+  uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Argmax key: value in the high word, complemented index in the low word, so the max
+// key is the max value with the lowest index.
+EMBER_DEV unsigned long long argmax_key(float v, uint32_t idx) {
+  return ((unsigned long long)ordered_key(v) << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
+}
+
+EMBER_DEV unsigned long long wave_max_u64(unsigned long long k) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    unsigned long long other = __shfl_xor(k, o);
+    k = other > k ? other : k;
+  }
+  return k;
+}
+
+EMBER_DEV float silu(float z) { return z / (1.0f + expf(-z)); }

@@ -1,0 +1,810 @@
+// C ABI of the GQA decoder forward pass: host validation, the workspace plan, weight
+// repacking, the prefill and decode schedules, HIP-graph replay of decode steps.
+//
+// The interface follows the "ember internals" page (ForwardModel: create_cache,
+// forward_with_cache(token_ids, cache, start_pos); explicit write positions from
+// "cursor semantics") and the checks of "Falcon-H1-0.5B-Rust src/lib.rs"
+// (Config::validate, validate_weights, Model::logits). No device memory is allocated
+// here: everything lives in the caller's workspace and KV buffer.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/ember.h"
+#include "kernels.h"
+
+using namespace ember;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ember_status fail(ember_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(EMBER_E_DEVICE, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t dtype_size(int dt) { return dt == EMBER_BF16 ? 2 : 4; }
+
+struct LayerOff {
+  size_t ln1, wqkv, bqkv, wo, qn, kn, ln2, wgu, wd;
+};
+
+struct Plan {
+  // weights
+  size_t embed, fnorm, cls_w, cls_b, cos_t, sin_t;
+  std::vector<LayerOff> layer;
+  // activations
+  size_t ids, pos, next, flags, x, xb, pa_hi, pa_lo, pb_hi, pb_lo, qkv, q, att, act, part,
+      logits, hrow, argpart;
+  size_t total;
+  int Mx, qkv_n, ka, nsplit_max, argparts;
+};
+
+// Config validation (cf. Falcon-H1 Rust reference, Config::validate: zero dimensions,
+// heads % kv_heads, odd head_dim), plus what the kernels assume.
+ember_status validate_config(const ember_config* c) {
+  if (!c) return fail(EMBER_E_ARG, "config is NULL");
+  if (c->vocab <= 0 || c->hidden <= 0 || c->layers <= 0 || c->heads <= 0 || c->kv_heads <= 0 ||
+      c->head_dim <= 0 || c->ffn <= 0)
+    return fail(EMBER_E_CONFIG, "zero dimension");
+  if (c->heads % c->kv_heads != 0 || c->head_dim % 2 != 0)
+    return fail(EMBER_E_CONFIG, "invalid GQA/RoPE shape");
+  if (c->heads / c->kv_heads > 8) return fail(EMBER_E_CONFIG, "GQA group above 8 is not supported");
+  const int hd = c->head_dim;
+  if (hd != 8 && hd != 16 && hd != 32 && hd != 64 && hd != 128)
+    return fail(EMBER_E_CONFIG, "head_dim must be one of 8, 16, 32, 64, 128");
+  if (c->weight_dtype != EMBER_F32 && c->weight_dtype != EMBER_BF16)
+    return fail(EMBER_E_DTYPE, "unsupported weight dtype %d", c->weight_dtype);
+  if (c->kv_dtype != EMBER_F32 && c->kv_dtype != EMBER_BF16)
+    return fail(EMBER_E_DTYPE, "unsupported KV dtype %d", c->kv_dtype);
+  if (c->precision != EMBER_EXACT && c->precision != EMBER_FAST)
+    return fail(EMBER_E_CONFIG, "unknown precision mode");
+  if (c->precision == EMBER_EXACT && c->kv_dtype != EMBER_F32)
+    return fail(EMBER_E_CONFIG, "EXACT precision needs an f32 KV cache");
+  if (c->head_kind != EMBER_HEAD_TIED_LM && c->head_kind != EMBER_HEAD_CLS)
+    return fail(EMBER_E_CONFIG, "unknown head kind");
+  if (c->head_kind == EMBER_HEAD_CLS && (c->n_classes <= 0 || c->n_classes > 64))
+    return fail(EMBER_E_CONFIG, "n_classes must be in 1..64");
+  if (c->head_kind == EMBER_HEAD_TIED_LM && !c->causal)
+    return fail(EMBER_E_CONFIG, "a tied LM head needs a causal model");
+  if (c->ffn % 16 != 0) return fail(EMBER_E_CONFIG, "ffn must be a multiple of 16");
+  const int K8 = c->weight_dtype == EMBER_BF16 ? 8 : 4;
+  if (c->hidden % K8 || c->ffn % K8 || (c->heads * hd) % K8)
+    return fail(EMBER_E_CONFIG, "hidden, ffn and heads*head_dim must be multiples of %d", K8);
+  if (c->hidden > 8192 || c->ffn > 32768 || c->heads * hd > 8192)
+    return fail(EMBER_E_CONFIG, "dimension above the supported maximum");
+  if (c->max_batch <= 0 || c->max_seq <= 0 || c->max_tokens <= 0)
+    return fail(EMBER_E_CONFIG, "max_batch, max_seq and max_tokens must be positive");
+  if (c->max_seq > 65536) return fail(EMBER_E_CONFIG, "max_seq above 65536");
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.0))
+    return fail(EMBER_E_CONFIG, "rms_eps must be >= 0 and rope_theta > 0");
+  if (c->rope_llama3 && (!(c->llama3_factor > 0) ||
+                         !(c->llama3_high_freq_factor > c->llama3_low_freq_factor) ||
+                         !(c->llama3_original_max_pos > 0)))
+    return fail(EMBER_E_CONFIG, "invalid llama3 RoPE scaling parameters");
+  return EMBER_OK;
+}
+
+Plan make_plan(const ember_config& c) {
+  Plan p{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  const size_t ws = dtype_size(c.weight_dtype);
+  const int H = c.hidden, HD = c.head_dim, NH = c.heads, NKV = c.kv_heads, FF = c.ffn;
+  p.qkv_n = (NH + 2 * NKV) * HD;
+  p.embed = take((size_t)c.vocab * H * ws);
+  p.layer.resize(c.layers);
+  for (int l = 0; l < c.layers; ++l) {
+    LayerOff& L = p.layer[l];
+    L.ln1 = take((size_t)H * 4);
+    L.wqkv = take((size_t)p.qkv_n * H * ws);
+    L.bqkv = c.qkv_bias ? take((size_t)p.qkv_n * 4) : 0;
+    L.wo = take((size_t)H * NH * HD * ws);
+    L.qn = c.qk_norm ? take((size_t)HD * 4) : 0;
+    L.kn = c.qk_norm ? take((size_t)HD * 4) : 0;
+    L.ln2 = take((size_t)H * 4);
+    L.wgu = take((size_t)2 * FF * H * ws);
+    L.wd = take((size_t)H * FF * ws);
+  }
+  p.fnorm = take((size_t)H * 4);
+  p.cls_w = c.head_kind == EMBER_HEAD_CLS ? take((size_t)c.n_classes * H * ws) : 0;
+  p.cls_b = c.head_kind == EMBER_HEAD_CLS ? take((size_t)c.n_classes * 4) : 0;
+  p.cos_t = take((size_t)c.max_seq * (HD / 2) * 4);
+  p.sin_t = take((size_t)c.max_seq * (HD / 2) * 4);
+
+  const int Mx = c.max_tokens > c.max_batch ? c.max_tokens : c.max_batch;
+  p.Mx = Mx;
+  p.ka = H > NH * HD ? H : NH * HD;
+  const int out_dim = c.head_kind == EMBER_HEAD_CLS ? c.n_classes : c.vocab;
+  p.nsplit_max = (c.max_seq + 63) / 64;
+  p.argparts = gemv_num_blocks(c.vocab, GEMV_LOGITS, H);
+  p.ids = take((size_t)Mx * 4);
+  p.pos = take(4);
+  p.next = take((size_t)Mx * 4);
+  p.flags = take(kNumFlags * 4);
+  p.x = take((size_t)Mx * H * 4);
+  p.xb = take((size_t)Mx * H * 4);
+  p.pa_hi = take((size_t)Mx * p.ka * 2);
+  p.pa_lo = take((size_t)Mx * p.ka * 2);
+  p.pb_hi = take((size_t)Mx * FF * 2);
+  p.pb_lo = take((size_t)Mx * FF * 2);
+  p.qkv = take((size_t)Mx * p.qkv_n * 4);
+  p.q = take((size_t)Mx * NH * HD * 4);
+  p.att = take((size_t)Mx * NH * HD * 4);
+  p.act = take((size_t)Mx * FF * 4);
+  p.part = take((size_t)c.max_batch * NH * p.nsplit_max * (HD + 2) * 4);
+  p.logits = take((size_t)c.max_batch * out_dim * 4);
+  p.hrow = take((size_t)c.max_batch * H * 4);
+  p.argpart = take((size_t)2 * p.argparts * 8);
+  p.total = off;
+  return p;
+}
+
+// RoPE frequencies: freq_i = theta^(-2i/HD) ("ember scripts/reference_forward.py",
+// inv_freq), llama3-scaled by lerp(1/factor, 1, clip(z, 0, 1)) with
+// z = (orig * freq / (2 pi) - low) / (high - low) ("LowLlamaBasic reference.py",
+// rotary_cos_sin). Angles pos * freq and their cos/sin in f64, rounded once to f32.
+void rope_host(const ember_config& c, int n_pos, float* cs, float* sn) {
+  const int half = c.head_dim / 2;
+  std::vector<double> freq(half);
+  for (int i = 0; i < half; ++i) {
+    double f = 1.0 / std::pow(c.rope_theta, 2.0 * (double)i / (double)c.head_dim);
+    if (c.rope_llama3) {
+      const double lo = c.llama3_low_freq_factor, hi = c.llama3_high_freq_factor;
+      double z = (c.llama3_original_max_pos * f / (2.0 * M_PI) - lo) / (hi - lo);
+      z = z < 0.0 ? 0.0 : (z > 1.0 ? 1.0 : z);
+      const double start = 1.0 / c.llama3_factor;
+      f *= start + z * (1.0 - start);
+    }
+    freq[i] = f;
+  }
+  for (int p = 0; p < n_pos; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)p * freq[i];
+      cs[(size_t)p * half + i] = (float)std::cos(ang);
+      sn[(size_t)p * half + i] = (float)std::sin(ang);
+    }
+}
+
+}  // namespace
+
+struct ember_model {
+  ember_config cfg;
+  Plan plan;
+  char* ws;
+  bool wbf16;
+  int has_logits_rows;      // rows in the logits buffer, 0 before any forward
+  // decode graph cache
+  hipGraphExec_t graph = nullptr;
+  const ember_cache* graph_cache = nullptr;
+  int graph_batch = -1;
+  hipStream_t graph_stream = nullptr;
+  template <typename T> T* at(size_t off) const { return (T*)(ws + off); }
+};
+
+struct ember_cache {
+  ember_model* model;
+  char* kv;
+  size_t layer_bytes;
+  int filled;               // positions 0..filled-1 hold K/V (all rows share positions)
+};
+
+namespace {
+
+struct Ctx {
+  ember_model* m;
+  ember_cache* c;
+  hipStream_t st;
+};
+
+void* k_layer(const ember_cache* c, int l) { return c->kv + (size_t)l * c->layer_bytes; }
+void* v_layer(const ember_cache* c, int l) {
+  return c->kv + (size_t)(c->model->cfg.layers + l) * c->layer_bytes;
+}
+
+enum Path { PATH_GEMV, PATH_MFMA, PATH_F32W };
+enum Attn { ATTN_FLASH, ATTN_DECODE };
+
+struct Pass {
+  int M;             // tokens in the pass = rows * tpr
+  int rows, tpr, b0, start;
+  const int* d_pos;  // decode: position from device
+  Path path;
+  Attn attn;
+};
+
+// One decoder block over the pass's tokens: x += attn(norm(x)); x += mlp(norm(x)).
+void run_layer(const Ctx& cx, int li, const Pass& ps) {
+  ember_model* md = cx.m;
+  const ember_config& c = md->cfg;
+  const Plan& p = md->plan;
+  const LayerOff& L = p.layer[li];
+  hipStream_t st = cx.st;
+  const int H = c.hidden, NH = c.heads, NKV = c.kv_heads, HD = c.head_dim, FF = c.ffn;
+  const bool exact = c.precision == EMBER_EXACT;
+  float* x = md->at<float>(p.x);
+  float* xb = md->at<float>(p.xb);
+  float* qkv = md->at<float>(p.qkv);
+  float* q = md->at<float>(p.q);
+  float* att = md->at<float>(p.att);
+  float* act = md->at<float>(p.act);
+  float* part = md->at<float>(p.part);
+  uint16_t* pa_hi = md->at<uint16_t>(p.pa_hi);
+  uint16_t* pa_lo = exact ? md->at<uint16_t>(p.pa_lo) : nullptr;
+  uint16_t* pb_hi = md->at<uint16_t>(p.pb_hi);
+  uint16_t* pb_lo = exact ? md->at<uint16_t>(p.pb_lo) : nullptr;
+  const float* ln1 = md->at<float>(L.ln1);
+  const float* ln2 = md->at<float>(L.ln2);
+  const void* wqkv = md->ws + L.wqkv;
+  const void* wo = md->ws + L.wo;
+  const void* wgu = md->ws + L.wgu;
+  const void* wd = md->ws + L.wd;
+  const float* bqkv = c.qkv_bias ? md->at<float>(L.bqkv) : nullptr;
+  const float scale = (float)(1.0 / std::sqrt((double)HD));
+  int nsplit = 1, chunk_min = 64;
+  if (ps.attn == ATTN_DECODE) decode_split_plan(ps.M, NKV, c.max_seq, &nsplit, &chunk_min);
+
+  // ---- attention block
+  if (ps.path == PATH_GEMV) {
+    GemvArgs g{};
+    g.W = wqkv; g.w_bf16 = md->wbf16; g.N = p.qkv_n; g.K = H; g.M = ps.M;
+    g.x = x; g.norm_w = ln1; g.eps = c.rms_eps; g.bias = bqkv; g.y = qkv; g.ldy = p.qkv_n;
+    launch_gemv(g, GEMV_STORE, st);
+  } else if (ps.path == PATH_MFMA) {
+    launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st);
+    GemmArgs g{};
+    g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka; g.w = (const uint16_t*)wqkv;
+    g.M = ps.M; g.N = p.qkv_n; g.K = H; g.bias = bqkv; g.c = qkv; g.ldc = p.qkv_n;
+    launch_gemm(g, GEMM_STORE, st);
+  } else {
+    launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, xb, nullptr, nullptr, 0, st);
+    GemmF32Args g{};
+    g.a = xb; g.lda = H; g.w = (const float*)wqkv; g.M = ps.M; g.N = p.qkv_n; g.K = H;
+    g.bias = bqkv; g.c = qkv; g.ldc = p.qkv_n;
+    launch_gemm_f32w(g, GEMM_STORE, st);
+  }
+
+  QkvPostArgs qa{};
+  qa.qkv = qkv; qa.M = ps.M; qa.NH = NH; qa.NKV = NKV; qa.HD = HD;
+  qa.tokens_per_row = ps.tpr; qa.b0 = ps.b0; qa.start_pos = ps.start; qa.d_pos = ps.d_pos;
+  qa.cos_t = md->at<float>(p.cos_t); qa.sin_t = md->at<float>(p.sin_t);
+  qa.q_norm = c.qk_norm ? md->at<float>(L.qn) : nullptr;
+  qa.k_norm = c.qk_norm ? md->at<float>(L.kn) : nullptr;
+  qa.eps = c.rms_eps; qa.q_out = q;
+  qa.k_cache = k_layer(cx.c, li); qa.v_cache = v_layer(cx.c, li);
+  qa.kv_bf16 = c.kv_dtype == EMBER_BF16; qa.max_seq = c.max_seq;
+  launch_qkv_post(qa, st);
+
+  const bool planes_out = ps.path == PATH_MFMA;
+  if (ps.attn == ATTN_FLASH) {
+    FlashArgs fa{};
+    fa.q = q; fa.k_cache = qa.k_cache; fa.v_cache = qa.v_cache; fa.kv_bf16 = qa.kv_bf16;
+    fa.NH = NH; fa.NKV = NKV; fa.HD = HD; fa.max_seq = c.max_seq;
+    fa.tokens_per_row = ps.tpr; fa.rows = ps.rows; fa.b0 = ps.b0; fa.start_pos = ps.start;
+    fa.causal = c.causal != 0; fa.scale = scale;
+    fa.out_f32 = planes_out ? nullptr : att;
+    fa.out_hi = planes_out ? pa_hi : nullptr;
+    fa.out_lo = planes_out ? pa_lo : nullptr;
+    launch_flash_prefill(fa, st);
+  } else {
+    DecodeAttnArgs da{};
+    da.q = q; da.k_cache = qa.k_cache; da.v_cache = qa.v_cache; da.kv_bf16 = qa.kv_bf16;
+    da.B = ps.M; da.NH = NH; da.NKV = NKV; da.HD = HD; da.max_seq = c.max_seq;
+    da.d_pos = ps.d_pos; da.nsplit = nsplit; da.chunk_min = chunk_min; da.scale = scale;
+    da.part = part;
+    launch_decode_attn(da, st);
+    if (ps.path != PATH_GEMV)
+      launch_attn_combine(part, ps.M, NH, HD, nsplit, ps.d_pos, chunk_min,
+                          planes_out ? nullptr : att, planes_out ? pa_hi : nullptr,
+                          planes_out ? pa_lo : nullptr, st);
+  }
+
+  if (ps.path == PATH_GEMV) {
+    GemvArgs g{};
+    g.W = wo; g.w_bf16 = md->wbf16; g.N = H; g.K = NH * HD; g.M = ps.M;
+    if (ps.attn == ATTN_DECODE) {
+      g.part = part; g.part_heads = NH; g.part_hd = HD; g.part_nsplit = nsplit;
+      g.d_pos = ps.d_pos; g.part_chunk_min = chunk_min;
+    } else {
+      g.x = att;
+    }
+    g.y = x; g.ldy = H;
+    launch_gemv(g, GEMV_RESID, st);
+  } else if (ps.path == PATH_MFMA) {
+    GemmArgs g{};
+    g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka; g.w = (const uint16_t*)wo;
+    g.M = ps.M; g.N = H; g.K = NH * HD; g.c = x; g.ldc = H;
+    launch_gemm(g, GEMM_RESID, st);
+  } else {
+    GemmF32Args g{};
+    g.a = att; g.lda = NH * HD; g.w = (const float*)wo; g.M = ps.M; g.N = H; g.K = NH * HD;
+    g.c = x; g.ldc = H;
+    launch_gemm_f32w(g, GEMM_RESID, st);
+  }
+
+  // ---- MLP block
+  if (ps.path == PATH_GEMV) {
+    GemvArgs g{};
+    g.W = wgu; g.w_bf16 = md->wbf16; g.N = FF; g.K = H; g.M = ps.M;
+    g.x = x; g.norm_w = ln2; g.eps = c.rms_eps; g.y = act; g.ldy = FF;
+    launch_gemv(g, GEMV_SILU, st);
+    GemvArgs d{};
+    d.W = wd; d.w_bf16 = md->wbf16; d.N = H; d.K = FF; d.M = ps.M; d.x = act; d.y = x; d.ldy = H;
+    launch_gemv(d, GEMV_RESID, st);
+  } else if (ps.path == PATH_MFMA) {
+    launch_rmsnorm(x, ln2, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st);
+    GemmArgs g{};
+    g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka; g.w = (const uint16_t*)wgu;
+    g.M = ps.M; g.N = 2 * FF; g.K = H; g.o_hi = pb_hi; g.o_lo = pb_lo; g.ldo = FF;
+    launch_gemm(g, GEMM_SILU, st);
+    GemmArgs d{};
+    d.a_hi = pb_hi; d.a_lo = pb_lo; d.lda = FF; d.w = (const uint16_t*)wd;
+    d.M = ps.M; d.N = H; d.K = FF; d.c = x; d.ldc = H;
+    launch_gemm(d, GEMM_RESID, st);
+  } else {
+    launch_rmsnorm(x, ln2, c.rms_eps, ps.M, H, 1, 0, xb, nullptr, nullptr, 0, st);
+    GemmF32Args g{};
+    g.a = xb; g.lda = H; g.w = (const float*)wgu; g.M = ps.M; g.N = 2 * FF; g.K = H;
+    g.o_f32 = act; g.ldo = FF;
+    launch_gemm_f32w(g, GEMM_SILU, st);
+    GemmF32Args d{};
+    d.a = act; d.lda = FF; d.w = (const float*)wd; d.M = ps.M; d.N = H; d.K = FF;
+    d.c = x; d.ldc = H;
+    launch_gemm_f32w(d, GEMM_RESID, st);
+  }
+}
+
+// Tied LM head over R rows of x (row r = x[r * row_step + row_off]): final RMSNorm, then
+// logits = E . h ("ember scripts/reference_forward.py", end of forward), then the greedy
+// argmax. Writes logits [R, ld] at `out` and next ids when `next` is non-null.
+void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, long long ld,
+                 int32_t* next) {
+  ember_model* md = cx.m;
+  const ember_config& c = md->cfg;
+  const Plan& p = md->plan;
+  hipStream_t st = cx.st;
+  const int H = c.hidden, V = c.vocab;
+  const float* fn = md->at<float>(p.fnorm);
+  const void* E = md->ws + p.embed;
+  float* hrow = md->at<float>(p.hrow);
+  if (R == 1 && ld == V) {
+    launch_rmsnorm(md->at<float>(p.x), fn, c.rms_eps, 1, H, row_step, row_off, hrow, nullptr,
+                   nullptr, 0, st);
+    GemvArgs g{};
+    g.W = E; g.w_bf16 = md->wbf16; g.N = V; g.K = H; g.M = 1; g.x = hrow; g.y = out; g.ldy = V;
+    g.argmax_part = md->at<unsigned long long>(p.argpart);
+    g.flags = md->at<int>(p.flags);
+    launch_gemv(g, GEMV_LOGITS, st);
+    if (next) launch_argmax_reduce(g.argmax_part, gemv_num_blocks(V, GEMV_LOGITS, H), 1, next, st);
+    return;
+  }
+  // R rows (at most the pass capacity Mx at a time: the plane / xb buffers hold Mx rows)
+  const int G = p.Mx;
+  float* xb = md->at<float>(p.xb);
+  for (int r0 = 0; r0 < R; r0 += G) {
+    const int rn = R - r0 < G ? R - r0 : G;
+    const int off = row_off + r0 * row_step;
+    if (md->wbf16) {
+      uint16_t* hi = md->at<uint16_t>(p.pa_hi);
+      uint16_t* lo = c.precision == EMBER_EXACT ? md->at<uint16_t>(p.pa_lo) : nullptr;
+      launch_rmsnorm(md->at<float>(p.x), fn, c.rms_eps, rn, H, row_step, off, nullptr, hi, lo,
+                     p.ka, st);
+      GemmArgs g{};
+      g.a_hi = hi; g.a_lo = lo; g.lda = p.ka; g.w = (const uint16_t*)E;
+      g.M = rn; g.N = V; g.K = H; g.c = out + (size_t)r0 * ld; g.ldc = ld;
+      launch_gemm(g, GEMM_STORE, st);
+    } else {
+      launch_rmsnorm(md->at<float>(p.x), fn, c.rms_eps, rn, H, row_step, off, xb, nullptr,
+                     nullptr, 0, st);
+      GemmF32Args g{};
+      g.a = xb; g.lda = H; g.w = (const float*)E; g.M = rn; g.N = V; g.K = H;
+      g.c = out + (size_t)r0 * ld; g.ldc = ld;
+      launch_gemm_f32w(g, GEMM_STORE, st);
+    }
+    if (next) launch_argmax_rows(out + (size_t)r0 * ld, rn, V, ld, next + r0,
+                                 md->at<int>(p.flags), st);
+  }
+}
+
+// Classification head over R rows of x: out[r] = Wc . rmsnorm(x_r) + bc, next[r] = argmax.
+void run_cls_head(const Ctx& cx, int R, int row_step, int row_off, float* out, int32_t* next) {
+  ember_model* md = cx.m;
+  const ember_config& c = md->cfg;
+  const Plan& p = md->plan;
+  const int H = c.hidden;
+  float* xb = md->at<float>(p.xb);
+  const int G = p.Mx;
+  for (int r0 = 0; r0 < R; r0 += G) {
+    const int rn = R - r0 < G ? R - r0 : G;
+    launch_rmsnorm(md->at<float>(p.x), md->at<float>(p.fnorm), c.rms_eps, rn, H, row_step,
+                   row_off + r0 * row_step, xb, nullptr, nullptr, 0, cx.st);
+    launch_cls_head(xb, md->ws + p.cls_w, md->wbf16, md->at<float>(p.cls_b), rn, H, c.n_classes,
+                    out ? out + (size_t)r0 * c.n_classes : nullptr, next ? next + r0 : nullptr,
+                    cx.st);
+  }
+}
+
+// One decode step's device work for B rows, ids in plan.ids, position in plan.pos.
+void decode_body(const Ctx& cx, int B) {
+  ember_model* md = cx.m;
+  const ember_config& c = md->cfg;
+  const Plan& p = md->plan;
+  launch_embed(md->at<int32_t>(p.ids), md->ws + p.embed, md->wbf16, md->at<float>(p.x), B,
+               c.hidden, c.vocab, md->at<int>(p.flags), cx.st);
+  Pass ps{};
+  ps.M = B; ps.rows = B; ps.tpr = 1; ps.b0 = 0; ps.start = 0; ps.d_pos = md->at<int>(p.pos);
+  ps.path = B == 1 ? PATH_GEMV : (md->wbf16 ? PATH_MFMA : PATH_F32W);
+  ps.attn = ATTN_DECODE;
+  for (int l = 0; l < c.layers; ++l) run_layer(cx, l, ps);
+  run_lm_head(cx, B, 1, 0, md->at<float>(p.logits), c.vocab, md->at<int32_t>(p.next));
+}
+
+bool graphs_enabled() {
+  const char* e = getenv("EMBER_NO_GRAPH");
+  return !(e && e[0] && e[0] != '0');
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+
+extern "C" {
+
+const char* ember_last_error(void) { return g_last_error.c_str(); }
+
+size_t ember_workspace_bytes(const ember_config* cfg) {
+  if (validate_config(cfg) != EMBER_OK) return 0;
+  return make_plan(*cfg).total;
+}
+
+size_t ember_kv_cache_bytes(const ember_config* cfg) {
+  if (validate_config(cfg) != EMBER_OK) return 0;
+  return (size_t)2 * cfg->layers * cfg->max_batch * cfg->kv_heads * cfg->max_seq *
+         cfg->head_dim * dtype_size(cfg->kv_dtype);
+}
+
+ember_status ember_rope_table(const ember_config* cfg, int32_t n_pos, float* h_cos,
+                              float* h_sin) {
+  ember_status s = validate_config(cfg);
+  if (s != EMBER_OK) return s;
+  if (n_pos <= 0 || !h_cos || !h_sin) return fail(EMBER_E_ARG, "bad RoPE table arguments");
+  rope_host(*cfg, n_pos, h_cos, h_sin);
+  return EMBER_OK;
+}
+
+ember_status ember_load_weights(const ember_config* cfg, const ember_tensor* tensors,
+                                int32_t n_tensors, void* d_workspace, size_t workspace_bytes,
+                                void* stream, ember_model** out) {
+  g_last_error.clear();
+  if (!out) return fail(EMBER_E_ARG, "out is NULL");
+  *out = nullptr;
+  ember_status s = validate_config(cfg);
+  if (s != EMBER_OK) return s;
+  if (!d_workspace || (n_tensors > 0 && !tensors)) return fail(EMBER_E_ARG, "NULL pointer");
+  const ember_config& c = *cfg;
+  Plan plan = make_plan(c);
+  if (workspace_bytes < plan.total)
+    return fail(EMBER_E_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes, plan.total);
+
+  // name -> tensor, with shape checks (cf. Falcon-H1 Rust reference, validate_weights)
+  std::map<std::string, const ember_tensor*> byname;
+  for (int i = 0; i < n_tensors; ++i) {
+    if (!tensors[i].name || !tensors[i].data) return fail(EMBER_E_ARG, "tensor %d has NULL name/data", i);
+    byname[tensors[i].name] = &tensors[i];
+  }
+  auto need = [&](const std::string& n, std::vector<int64_t> shape,
+                  const ember_tensor** t) -> ember_status {
+    auto it = byname.find(n);
+    if (it == byname.end()) return fail(EMBER_E_TENSOR_MISSING, "missing tensor %s", n.c_str());
+    const ember_tensor* e = it->second;
+    if (e->dtype != EMBER_F32 && e->dtype != EMBER_BF16)
+      return fail(EMBER_E_DTYPE, "unsupported dtype %d for %s", e->dtype, n.c_str());
+    if (e->dtype != c.weight_dtype)
+      return fail(EMBER_E_DTYPE, "tensor %s dtype %d differs from the config's weight dtype",
+                  n.c_str(), e->dtype);
+    bool ok = e->ndim == (int)shape.size();
+    for (size_t d = 0; ok && d < shape.size(); ++d) ok = e->shape[d] == shape[d];
+    if (!ok) return fail(EMBER_E_TENSOR_SHAPE, "bad shape for %s", n.c_str());
+    *t = e;
+    return EMBER_OK;
+  };
+  const int H = c.hidden, V = c.vocab, NH = c.heads, NKV = c.kv_heads, HD = c.head_dim, FF = c.ffn;
+  struct LT { const ember_tensor *ln1, *q, *k, *v, *qb, *kb, *vb, *o, *qn, *kn, *ln2, *g, *u, *d; };
+  std::vector<LT> lt(c.layers);
+  const ember_tensor *emb = nullptr, *fn = nullptr, *clsw = nullptr, *clsb = nullptr;
+#define NEED(n, shape, dst) do { ember_status s_ = need(n, shape, dst); if (s_ != EMBER_OK) return s_; } while (0)
+  NEED("model.embed_tokens.weight", (std::vector<int64_t>{V, H}), &emb);
+  for (int l = 0; l < c.layers; ++l) {
+    const std::string pf = "model.layers." + std::to_string(l) + ".";
+    LT& t = lt[l];
+    NEED(pf + "input_layernorm.weight", (std::vector<int64_t>{H}), &t.ln1);
+    NEED(pf + "self_attn.q_proj.weight", (std::vector<int64_t>{NH * HD, H}), &t.q);
+    NEED(pf + "self_attn.k_proj.weight", (std::vector<int64_t>{NKV * HD, H}), &t.k);
+    NEED(pf + "self_attn.v_proj.weight", (std::vector<int64_t>{NKV * HD, H}), &t.v);
+    if (c.qkv_bias) {
+      NEED(pf + "self_attn.q_proj.bias", (std::vector<int64_t>{NH * HD}), &t.qb);
+      NEED(pf + "self_attn.k_proj.bias", (std::vector<int64_t>{NKV * HD}), &t.kb);
+      NEED(pf + "self_attn.v_proj.bias", (std::vector<int64_t>{NKV * HD}), &t.vb);
+    }
+    NEED(pf + "self_attn.o_proj.weight", (std::vector<int64_t>{H, NH * HD}), &t.o);
+    if (c.qk_norm) {
+      NEED(pf + "self_attn.q_norm.weight", (std::vector<int64_t>{HD}), &t.qn);
+      NEED(pf + "self_attn.k_norm.weight", (std::vector<int64_t>{HD}), &t.kn);
+    }
+    NEED(pf + "post_attention_layernorm.weight", (std::vector<int64_t>{H}), &t.ln2);
+    NEED(pf + "mlp.gate_proj.weight", (std::vector<int64_t>{FF, H}), &t.g);
+    NEED(pf + "mlp.up_proj.weight", (std::vector<int64_t>{FF, H}), &t.u);
+    NEED(pf + "mlp.down_proj.weight", (std::vector<int64_t>{H, FF}), &t.d);
+  }
+  NEED("model.norm.weight", (std::vector<int64_t>{H}), &fn);
+  if (c.head_kind == EMBER_HEAD_CLS) {
+    NEED("token_cls_head.weight", (std::vector<int64_t>{c.n_classes, H}), &clsw);
+    NEED("token_cls_head.bias", (std::vector<int64_t>{c.n_classes}), &clsb);
+  }
+#undef NEED
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)d_workspace;
+  const size_t es = dtype_size(c.weight_dtype);
+  const bool bf = c.weight_dtype == EMBER_BF16;
+  auto copy = [&](size_t dst, const ember_tensor* t, size_t bytes) -> hipError_t {
+    return hipMemcpyAsync(ws + dst, t->data, bytes, hipMemcpyDeviceToDevice, st);
+  };
+  HIP_TRY(copy(plan.embed, emb, (size_t)V * H * es));
+  for (int l = 0; l < c.layers; ++l) {
+    const LayerOff& L = plan.layer[l];
+    const LT& t = lt[l];
+    launch_widen(t.ln1->data, bf, (float*)(ws + L.ln1), H, st);
+    launch_widen(t.ln2->data, bf, (float*)(ws + L.ln2), H, st);
+    // fused QKV rows: q, then k, then v
+    HIP_TRY(copy(L.wqkv, t.q, (size_t)NH * HD * H * es));
+    HIP_TRY(copy(L.wqkv + (size_t)NH * HD * H * es, t.k, (size_t)NKV * HD * H * es));
+    HIP_TRY(copy(L.wqkv + (size_t)(NH + NKV) * HD * H * es, t.v, (size_t)NKV * HD * H * es));
+    if (c.qkv_bias) {
+      launch_widen(t.qb->data, bf, (float*)(ws + L.bqkv), NH * HD, st);
+      launch_widen(t.kb->data, bf, (float*)(ws + L.bqkv) + NH * HD, NKV * HD, st);
+      launch_widen(t.vb->data, bf, (float*)(ws + L.bqkv) + (NH + NKV) * HD, NKV * HD, st);
+    }
+    HIP_TRY(copy(L.wo, t.o, (size_t)H * NH * HD * es));
+    if (c.qk_norm) {
+      launch_widen(t.qn->data, bf, (float*)(ws + L.qn), HD, st);
+      launch_widen(t.kn->data, bf, (float*)(ws + L.kn), HD, st);
+    }
+    // gate/up rows interleaved in blocks of 16: [g 0..15][u 0..15][g 16..31][u 16..31]...
+    const size_t blk = (size_t)16 * H * es;
+    HIP_TRY(hipMemcpy2DAsync(ws + L.wgu, 2 * blk, t.g->data, blk, blk, FF / 16,
+                             hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemcpy2DAsync(ws + L.wgu + blk, 2 * blk, t.u->data, blk, blk, FF / 16,
+                             hipMemcpyDeviceToDevice, st));
+    HIP_TRY(copy(L.wd, t.d, (size_t)H * FF * es));
+  }
+  launch_widen(fn->data, bf, (float*)(ws + plan.fnorm), H, st);
+  if (clsw) {
+    HIP_TRY(copy(plan.cls_w, clsw, (size_t)c.n_classes * H * es));
+    launch_widen(clsb->data, bf, (float*)(ws + plan.cls_b), c.n_classes, st);
+  }
+  {
+    std::vector<float> cs((size_t)c.max_seq * (HD / 2)), sn(cs.size());
+    rope_host(c, c.max_seq, cs.data(), sn.data());
+    HIP_TRY(hipMemcpyAsync(ws + plan.cos_t, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, st));
+    HIP_TRY(hipMemcpyAsync(ws + plan.sin_t, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, st));
+    HIP_TRY(hipStreamSynchronize(st));
+  }
+  launch_fill_i32((int*)(ws + plan.flags), kNumFlags, 0, st);
+  HIP_TRY(hipGetLastError());
+  HIP_TRY(hipStreamSynchronize(st));
+
+  ember_model* m = new ember_model();
+  m->cfg = c;
+  m->plan = plan;
+  m->ws = ws;
+  m->wbf16 = bf;
+  m->has_logits_rows = 0;
+  *out = m;
+  return EMBER_OK;
+}
+
+ember_status ember_cache_bind(ember_model* model, void* d_kv, size_t kv_bytes, ember_cache** out) {
+  g_last_error.clear();
+  if (!model || !d_kv || !out) return fail(EMBER_E_ARG, "NULL argument");
+  *out = nullptr;
+  const size_t need = ember_kv_cache_bytes(&model->cfg);
+  if (kv_bytes < need) return fail(EMBER_E_CAPACITY, "KV buffer too small: %zu < %zu", kv_bytes, need);
+  ember_cache* c = new ember_cache();
+  c->model = model;
+  c->kv = (char*)d_kv;
+  c->layer_bytes = need / (2 * (size_t)model->cfg.layers);
+  c->filled = 0;
+  *out = c;
+  return EMBER_OK;
+}
+
+ember_status ember_prefill(ember_model* md, ember_cache* cache, const int32_t* h_ids,
+                           int32_t batch, int32_t n_tokens, int32_t start_pos,
+                           float* d_all_logits, int32_t* d_next, void* stream) {
+  g_last_error.clear();
+  if (!md || !cache || !h_ids) return fail(EMBER_E_ARG, "NULL argument");
+  if (cache->model != md) return fail(EMBER_E_ARG, "cache bound to another model");
+  const ember_config& c = md->cfg;
+  if (n_tokens <= 0) return fail(EMBER_E_ARG, "input_ids must not be empty");
+  if (batch <= 0 || batch > c.max_batch)
+    return fail(EMBER_E_CAPACITY, "batch %d outside 1..%d", batch, c.max_batch);
+  if (start_pos < 0 || (long long)start_pos + n_tokens > c.max_seq)
+    return fail(EMBER_E_CAPACITY, "positions [%d, %d) exceed max_seq %d", start_pos,
+                start_pos + n_tokens, c.max_seq);
+  if (start_pos > cache->filled)
+    return fail(EMBER_E_STATE, "start_pos %d leaves a gap after %d cached positions", start_pos,
+                cache->filled);
+  if (!c.causal && start_pos != 0)
+    return fail(EMBER_E_ARG, "a bidirectional model takes whole sequences (start_pos 0)");
+  for (long long i = 0; i < (long long)batch * n_tokens; ++i)
+    if (h_ids[i] < 0 || h_ids[i] >= c.vocab)
+      return fail(EMBER_E_TOKEN, "token %d outside vocabulary", h_ids[i]);
+
+  hipStream_t st = (hipStream_t)stream;
+  const Plan& p = md->plan;
+  Ctx cx{md, cache, st};
+  const int out_dim = c.head_kind == EMBER_HEAD_CLS ? c.n_classes : c.vocab;
+  // passes: whole rows when a row fits max_tokens, else position chunks of one row
+  const int T = n_tokens;
+  const int rows_per_pass = T <= p.Mx ? (p.Mx / T < batch ? p.Mx / T : batch) : 1;
+  const int tok_chunk = T <= p.Mx ? T : p.Mx;
+  for (int b0 = 0; b0 < batch; b0 += rows_per_pass) {
+    const int rows = batch - b0 < rows_per_pass ? batch - b0 : rows_per_pass;
+    for (int t0 = 0; t0 < T; t0 += tok_chunk) {
+      const int tpr = T - t0 < tok_chunk ? T - t0 : tok_chunk;
+      const int M = rows * tpr;
+      // stage ids of this pass (rows x tpr)
+      std::vector<int32_t> ids((size_t)M);
+      for (int r = 0; r < rows; ++r)
+        memcpy(&ids[(size_t)r * tpr], h_ids + (size_t)(b0 + r) * T + t0, (size_t)tpr * 4);
+      HIP_TRY(hipMemcpyAsync(md->at<int32_t>(p.ids), ids.data(), (size_t)M * 4,
+                             hipMemcpyHostToDevice, st));
+      launch_embed(md->at<int32_t>(p.ids), md->ws + p.embed, md->wbf16, md->at<float>(p.x), M,
+                   c.hidden, c.vocab, md->at<int>(p.flags), st);
+      Pass ps{};
+      ps.M = M; ps.rows = rows; ps.tpr = tpr; ps.b0 = b0; ps.start = start_pos + t0;
+      ps.d_pos = nullptr;
+      ps.path = M == 1 ? PATH_GEMV : (md->wbf16 ? PATH_MFMA : PATH_F32W);
+      ps.attn = ATTN_FLASH;
+      for (int l = 0; l < c.layers; ++l) run_layer(cx, l, ps);
+      const bool last_chunk = t0 + tpr == T;
+      if (c.head_kind == EMBER_HEAD_TIED_LM) {
+        if (d_all_logits) {
+          for (int r = 0; r < rows; ++r)
+            run_lm_head(cx, tpr, 1, r * tpr,
+                        d_all_logits + ((size_t)(b0 + r) * T + t0) * out_dim, out_dim, nullptr);
+        }
+        if (last_chunk)
+          run_lm_head(cx, rows, tpr, tpr - 1, md->at<float>(p.logits) + (size_t)b0 * out_dim,
+                      out_dim, d_next ? d_next + b0 : nullptr);
+      } else {
+        for (int r = 0; r < rows; ++r)
+          if (d_all_logits || d_next)
+            run_cls_head(cx, tpr, 1, r * tpr,
+                         d_all_logits ? d_all_logits + ((size_t)(b0 + r) * T + t0) * out_dim : nullptr,
+                         d_next ? d_next + (size_t)(b0 + r) * T + t0 : nullptr);
+        if (last_chunk)
+          run_cls_head(cx, rows, tpr, tpr - 1, md->at<float>(p.logits) + (size_t)b0 * out_dim,
+                       nullptr);
+      }
+      HIP_TRY(hipGetLastError());
+    }
+  }
+  if (start_pos + T > cache->filled) cache->filled = start_pos + T;
+  md->has_logits_rows = batch;
+  return EMBER_OK;
+}
+
+ember_status ember_decode_step(ember_model* md, ember_cache* cache, const int32_t* d_ids,
+                               int32_t batch, int32_t pos, int32_t* d_next, void* stream) {
+  g_last_error.clear();
+  if (!md || !cache || !d_ids || !d_next) return fail(EMBER_E_ARG, "NULL argument");
+  if (cache->model != md) return fail(EMBER_E_ARG, "cache bound to another model");
+  const ember_config& c = md->cfg;
+  if (!c.causal) return fail(EMBER_E_STATE, "decode steps need a causal model");
+  if (batch <= 0 || batch > c.max_batch)
+    return fail(EMBER_E_CAPACITY, "batch %d outside 1..%d", batch, c.max_batch);
+  if (pos < 0 || pos >= c.max_seq) return fail(EMBER_E_CAPACITY, "position %d >= max_seq %d", pos, c.max_seq);
+  if (cache->filled == 0) return fail(EMBER_E_STATE, "decode step before any prefill");
+  if (pos > cache->filled)
+    return fail(EMBER_E_STATE, "position %d leaves a gap after %d cached positions", pos, cache->filled);
+  hipStream_t st = (hipStream_t)stream;
+  const Plan& p = md->plan;
+  Ctx cx{md, cache, st};
+  launch_stage_step(d_ids, batch, c.vocab, pos, md->at<int32_t>(p.ids), md->at<int>(p.pos),
+                    md->at<int>(p.flags), st);
+  const bool use_graph = st != nullptr && graphs_enabled();
+  if (use_graph) {
+    if (!md->graph || md->graph_cache != cache || md->graph_batch != batch || md->graph_stream != st) {
+      if (md->graph) {
+        (void)hipGraphExecDestroy(md->graph);
+        md->graph = nullptr;
+      }
+      HIP_TRY(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
+      decode_body(cx, batch);
+      hipGraph_t g = nullptr;
+      HIP_TRY(hipStreamEndCapture(st, &g));
+      hipError_t e = hipGraphInstantiate(&md->graph, g, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(g);
+      if (e != hipSuccess) return fail(EMBER_E_DEVICE, "graph instantiate: %s", hipGetErrorString(e));
+      md->graph_cache = cache;
+      md->graph_batch = batch;
+      md->graph_stream = st;
+    }
+    HIP_TRY(hipGraphLaunch(md->graph, st));
+  } else {
+    decode_body(cx, batch);
+  }
+  launch_copy_ids(md->at<int32_t>(p.next), batch, d_next, st);
+  HIP_TRY(hipGetLastError());
+  if (pos + 1 > cache->filled) cache->filled = pos + 1;
+  md->has_logits_rows = batch;
+  return EMBER_OK;
+}
+
+ember_status ember_logits(ember_model* md, void* d_out, int32_t dtype, void* stream) {
+  g_last_error.clear();
+  if (!md || !d_out) return fail(EMBER_E_ARG, "NULL argument");
+  if (dtype != EMBER_F32 && dtype != EMBER_BF16) return fail(EMBER_E_DTYPE, "unsupported dtype %d", dtype);
+  if (md->has_logits_rows <= 0) return fail(EMBER_E_STATE, "no forward has run yet");
+  const int out_dim = md->cfg.head_kind == EMBER_HEAD_CLS ? md->cfg.n_classes : md->cfg.vocab;
+  launch_convert_logits(md->at<float>(md->plan.logits), md->has_logits_rows, out_dim, out_dim,
+                        d_out, dtype == EMBER_BF16, (hipStream_t)stream);
+  HIP_TRY(hipGetLastError());
+  return EMBER_OK;
+}
+
+ember_status ember_sync(ember_model* md, void* stream) {
+  g_last_error.clear();
+  if (!md) return fail(EMBER_E_ARG, "NULL model");
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipStreamSynchronize(st));
+  int flags[kNumFlags];
+  HIP_TRY(hipMemcpy(flags, md->at<int>(md->plan.flags), sizeof flags, hipMemcpyDeviceToHost));
+  launch_fill_i32(md->at<int>(md->plan.flags), kNumFlags, 0, st);
+  HIP_TRY(hipStreamSynchronize(st));
+  if (flags[kFlagNaN]) return fail(EMBER_E_NONFINITE, "NaN in logits");
+  if (flags[kFlagBadToken]) return fail(EMBER_E_TOKEN, "decode id outside vocabulary");
+  return EMBER_OK;
+}
+
+void ember_cache_free(ember_cache* cache) {
+  if (!cache) return;
+  ember_model* m = cache->model;
+  if (m && m->graph_cache == cache && m->graph) {
+    (void)hipGraphExecDestroy(m->graph);
+    m->graph = nullptr;
+    m->graph_cache = nullptr;
+  }
+  delete cache;
+}
+
+void ember_free(ember_model* model) {
+  if (!model) return;
+  if (model->graph) (void)hipGraphExecDestroy(model->graph);
+  delete model;
+}
+
+}  // extern "C"

@@ -1,0 +1,175 @@
+// Host-side launch wrappers of the gfx950 kernels (one translation unit per kernel
+// family). Pointers are device pointers; every launch is asynchronous on `st`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ember {
+
+// Flags raised by kernels and reported by ember_sync.
+enum DeviceFlag { kFlagBadToken = 0, kFlagNaN = 1, kNumFlags = 4 };
+
+// ------------------------------------------------------------------ misc (kernels_misc.hip)
+
+// x[m, :] = widen(E[ids[m], :]) for m < M; ids outside [0, V) read row 0 and raise
+// flags[kFlagBadToken] (host-validated prefill ids never do).
+void launch_embed(const int32_t* ids, const void* E, bool e_bf16, float* x, int M, int H,
+                  int V, int* flags, hipStream_t st);
+
+// Row-wise RMSNorm of rows src_row(r) = r * row_step + row_off, r < R, of x [*, H]:
+// y = x / sqrt(mean(x^2) + eps) * w. Writes any of: out_f32 [R, H], planes hi/lo
+// [R, ld_plane] bf16 (lo may be null: single plane).
+void launch_rmsnorm(const float* x, const float* w, float eps, int R, int H, int row_step,
+                    int row_off, float* out_f32, uint16_t* hi, uint16_t* lo, int ld_plane,
+                    hipStream_t st);
+
+struct QkvPostArgs {
+  const float* qkv;        // [M, (NH + 2 NKV) HD] raw projections (bias included)
+  int M, NH, NKV, HD;
+  int tokens_per_row;      // token m belongs to row b0 + m / tpr at position start + m % tpr
+  int b0, start_pos;
+  const int* d_pos;        // if non-null, start_pos is read from *d_pos
+  const float* cos_t;      // [max_seq, HD/2]
+  const float* sin_t;
+  const float* q_norm;     // [HD] or null (per-head RMSNorm before RoPE)
+  const float* k_norm;
+  float eps;
+  float* q_out;            // [M, NH*HD] f32 (roped, normed)
+  void* k_cache;           // layer base: [B_cache][NKV][max_seq][HD]
+  void* v_cache;
+  bool kv_bf16;
+  int max_seq;
+};
+// Per-head q/k RMSNorm (optional), rotate-half RoPE from the tables, K/V store at the
+// tokens' explicit positions.
+void launch_qkv_post(const QkvPostArgs& a, hipStream_t st);
+
+// next[r] = argmax over the partial keys part[r, 0..nparts); NaN flag handled upstream.
+void launch_argmax_reduce(const unsigned long long* part, int nparts, int R, int32_t* next,
+                          hipStream_t st);
+// next[r] = argmax(logits[r, 0..n)) (lowest index on ties); raises kFlagNaN on NaN.
+void launch_argmax_rows(const float* logits, int R, int n, long long ld, int32_t* next,
+                        int* flags, hipStream_t st);
+
+// Token classification head: out[m, c] = dot(h[m], W[c]) + b[c] (h already normalised),
+// next[m] = argmax_c out[m, c].
+void launch_cls_head(const float* h, const void* W, bool w_bf16, const float* b, int M, int H,
+                     int C, float* out, int32_t* next, hipStream_t st);
+
+// Copy R rows of n logits (row stride ld) to f32 or bf16 (round to nearest even).
+void launch_convert_logits(const float* src, int R, int n, long long ld, void* dst,
+                           bool to_bf16, hipStream_t st);
+
+// Stage a decode step: ids_internal[r] = ids[r] (out-of-range ids -> 0 + flag) and
+// *d_pos = pos.
+void launch_stage_step(const int32_t* ids, int R, int V, int pos, int32_t* ids_internal,
+                       int* d_pos, int* flags, hipStream_t st);
+void launch_copy_ids(const int32_t* src, int n, int32_t* dst, hipStream_t st);
+void launch_fill_i32(int* p, int n, int v, hipStream_t st);
+// dst[i] = widen(src[i]) for i < n (bf16 or f32 source).
+void launch_widen(const void* src, bool bf16, float* dst, long long n, hipStream_t st);
+
+// ------------------------------------------------------------------ GEMV (kernels_gemv.hip)
+
+enum GemvEpi { GEMV_STORE = 0, GEMV_RESID = 1, GEMV_SILU = 2, GEMV_LOGITS = 3 };
+
+struct GemvArgs {
+  const void* W;           // [N_rows, K] row-major, bf16 or f32
+  bool w_bf16;
+  int N;                   // outputs per token (SILU: FF outputs from 2*FF packed rows)
+  int K;
+  int M;                   // tokens (1..2)
+  // input: x [M, K] f32; when norm_w != null the kernel applies RMSNorm to x first
+  const float* x;
+  const float* norm_w;
+  float eps;
+  // input alternative: attention split-K partials to combine (x == null)
+  const float* part;       // [M][NH][nsplit][HD + 2]: (m, l, acc[HD]) per split
+  int part_heads, part_hd, part_nsplit;
+  const int* d_pos;        // valid splits computed from *d_pos + 1 keys
+  int part_chunk_min;
+  // outputs
+  const float* bias;       // [N] or null (STORE)
+  float* y;                // STORE/SILU/LOGITS: [M, ldy]; RESID: x_res [M, ldy] (+=)
+  int ldy;
+  unsigned long long* argmax_part;   // LOGITS: [M][gridDim.x]
+  int* flags;
+};
+void launch_gemv(const GemvArgs& a, int epi, hipStream_t st);
+int gemv_num_blocks(int N, int epi, int K);
+
+// ------------------------------------------------------------------ GEMM (kernels_gemm.hip)
+
+enum GemmEpi { GEMM_STORE = 0, GEMM_RESID = 1, GEMM_SILU = 2 };
+
+struct GemmArgs {
+  // A: activations as bf16 planes [M, lda] (hi, and lo in EXACT mode; lo == null: one pass)
+  const uint16_t* a_hi;
+  const uint16_t* a_lo;
+  int lda;
+  // B: weights bf16 [N, K] row-major (K contiguous)
+  const uint16_t* w;
+  int M, N, K;
+  const float* bias;       // STORE: [N] or null
+  float* c;                // STORE: [M, ldc] f32; RESID: [M, ldc] +=
+  long long ldc;
+  uint16_t* o_hi;          // SILU: planes [M, ldo] of silu(g)*u (o_lo may be null)
+  uint16_t* o_lo;
+  float* o_f32;            // SILU: optional f32 [M, ldo]
+  int ldo;
+};
+void launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
+
+// f32-weight path (VALU), same epilogues; A is f32 [M, lda].
+struct GemmF32Args {
+  const float* a;
+  int lda;
+  const float* w;          // [N, K]
+  int M, N, K;
+  const float* bias;
+  float* c;
+  long long ldc;
+  float* o_f32;            // SILU output [M, ldo] f32
+  int ldo;
+};
+void launch_gemm_f32w(const GemmF32Args& a, int epi, hipStream_t st);
+
+// ------------------------------------------------------------------ attention (kernels_attn.hip)
+
+struct FlashArgs {
+  const float* q;          // [M, NH*HD] f32, roped
+  const void* k_cache;     // layer base [B_cache][NKV][max_seq][HD]
+  const void* v_cache;
+  bool kv_bf16;
+  int NH, NKV, HD, max_seq;
+  int tokens_per_row, rows, b0, start_pos;   // queries: rows x tokens_per_row
+  bool causal;             // causal: keys 0..pos; else keys 0..start+tpr-1
+  float scale;
+  float* out_f32;          // [M, NH*HD] or null
+  uint16_t* out_hi;        // planes [M, NH*HD] or null
+  uint16_t* out_lo;
+};
+void launch_flash_prefill(const FlashArgs& a, hipStream_t st);
+
+struct DecodeAttnArgs {
+  const float* q;          // [B, NH*HD] f32 roped
+  const void* k_cache;
+  const void* v_cache;
+  bool kv_bf16;
+  int B, NH, NKV, HD, max_seq;
+  const int* d_pos;        // keys 0..*d_pos
+  int nsplit, chunk_min;
+  float scale;
+  float* part;             // [B][NH][nsplit][HD + 2]
+};
+void launch_decode_attn(const DecodeAttnArgs& a, hipStream_t st);
+// att = combine(part) for B rows, written as f32 [B, NH*HD] and/or planes.
+void launch_attn_combine(const float* part, int B, int NH, int HD, int nsplit, const int* d_pos,
+                         int chunk_min, float* out_f32, uint16_t* out_hi, uint16_t* out_lo,
+                         hipStream_t st);
+
+// number of splits and minimum chunk used for decode attention
+void decode_split_plan(int B, int NKV, int max_seq, int* nsplit, int* chunk_min);
+
+}  // namespace ember

@@ -1,0 +1,324 @@
+// Small row-wise kernels of the forward pass: embedding gather, RMSNorm, the QKV
+// epilogue (per-head q/k norm, RoPE, KV-cache store), argmax, the classification head,
+// logits conversion and decode-step staging.
+#include "common.h"
+#include "kernels.h"
+
+namespace ember {
+
+// ------------------------------------------------------------------ embedding gather
+// x = E[id] widened to f32 ("ember scripts/reference_forward.py", forward: embed[tok]).
+__global__ void __launch_bounds__(256) k_embed(const int32_t* ids, const void* E, int e_bf16,
+                                               float* x, int H, int V, int* flags) {
+  const int m = blockIdx.x;
+  int id = ids[m];
+  if (id < 0 || id >= V) {
+    if (threadIdx.x == 0) atomicOr(&flags[kFlagBadToken], 1);
+    id = 0;
+  }
+  float* xr = x + (size_t)m * H;
+  if (e_bf16) {
+    const uint16_t* er = (const uint16_t*)E + (size_t)id * H;
+    for (int i = threadIdx.x; i < H; i += blockDim.x) xr[i] = bf16_to_f32(er[i]);
+  } else {
+    const float* er = (const float*)E + (size_t)id * H;
+    for (int i = threadIdx.x; i < H; i += blockDim.x) xr[i] = er[i];
+  }
+}
+
+void launch_embed(const int32_t* ids, const void* E, bool e_bf16, float* x, int M, int H, int V,
+                  int* flags, hipStream_t st) {
+  if (M <= 0) return;
+  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, ids, E, (int)e_bf16, x, H, V, flags);
+}
+
+// ------------------------------------------------------------------ RMSNorm
+// y = x / sqrt(mean(x^2) + eps) * w (operation order of "ember scripts/
+// reference_forward.py", rmsnorm). Sum of squares accumulated in f32 per thread, then a
+// fixed-order block reduction.
+__global__ void __launch_bounds__(256) k_rmsnorm(const float* x, const float* w, float eps, int H,
+                                                 int row_step, int row_off, float* out_f32,
+                                                 uint16_t* hi, uint16_t* lo, int ld_plane) {
+  __shared__ float red[16];
+  const int r = blockIdx.x;
+  const float* xr = x + ((size_t)r * row_step + row_off) * H;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) ss += xr[i] * xr[i];
+  ss = block_sum(ss, red);
+  const float rms = sqrtf(ss / (float)H + eps);
+  for (int i = threadIdx.x; i < H; i += blockDim.x) {
+    const float y = xr[i] / rms * w[i];
+    if (out_f32) out_f32[(size_t)r * H + i] = y;
+    if (hi) {
+      uint32_t h, l;
+      split_bf16(y, h, l);
+      hi[(size_t)r * ld_plane + i] = (uint16_t)h;
+      if (lo) lo[(size_t)r * ld_plane + i] = (uint16_t)l;
+    }
+  }
+}
+
+void launch_rmsnorm(const float* x, const float* w, float eps, int R, int H, int row_step,
+                    int row_off, float* out_f32, uint16_t* hi, uint16_t* lo, int ld_plane,
+                    hipStream_t st) {
+  if (R <= 0) return;
+  hipLaunchKernelGGL(k_rmsnorm, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off,
+                     out_f32, hi, lo, ld_plane);
+}
+
+// ------------------------------------------------------------------ QKV epilogue
+// One block per token, one wave per head. Lane i < HD/2 owns the rotated pair
+// (i, i + HD/2) (rotate-half RoPE: "ember scripts/reference_forward.py", rope); with
+// q/k norm the head is first RMS-normalised over HD ("PII-Tracer serving/
+// reference_forward.py", forward: q_norm / k_norm before RoPE). K and V are stored at
+// the token's explicit position (ember internals page, "cursor semantics").
+__global__ void __launch_bounds__(256) k_qkv_post(QkvPostArgs a) {
+  const int m = blockIdx.x;
+  const int HD = a.HD, half = HD / 2;
+  const int qkv_n = (a.NH + 2 * a.NKV) * HD;
+  const int start = a.d_pos ? *a.d_pos : a.start_pos;
+  const int b = a.b0 + m / a.tokens_per_row;
+  const int p = start + m % a.tokens_per_row;
+  const float* row = a.qkv + (size_t)m * qkv_n;
+  const float* cs = a.cos_t + (size_t)p * half;
+  const float* sn = a.sin_t + (size_t)p * half;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int nwaves = blockDim.x / kWave;
+  // heads 0..NH-1: q; NH..NH+NKV-1: k; then v
+  for (int h = wave; h < a.NH + 2 * a.NKV; h += nwaves) {
+    const float* src = row + (size_t)h * HD;
+    if (h >= a.NH + a.NKV) {          // value head: plain copy into the cache
+      const int kvh = h - a.NH - a.NKV;
+      size_t off = (((size_t)b * a.NKV + kvh) * a.max_seq + p) * HD;
+      for (int d = lane; d < HD; d += kWave) {
+        if (a.kv_bf16) ((uint16_t*)a.v_cache)[off + d] = (uint16_t)f32_to_bf16_rne(src[d]);
+        else ((float*)a.v_cache)[off + d] = src[d];
+      }
+      continue;
+    }
+    const bool is_q = h < a.NH;
+    const float* nw = is_q ? a.q_norm : a.k_norm;
+    // each lane holds pairs i = lane + 64 j (HD/2 <= 128)
+    float x0[2], x1[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = lane + j * kWave;
+      x0[j] = i < half ? src[i] : 0.f;
+      x1[j] = i < half ? src[i + half] : 0.f;
+    }
+    if (nw) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) ss += x0[j] * x0[j] + x1[j] * x1[j];
+      ss = wave_sum(ss);
+      const float rms = sqrtf(ss / (float)HD + a.eps);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int i = lane + j * kWave;
+        if (i < half) {
+          x0[j] = x0[j] / rms * nw[i];
+          x1[j] = x1[j] / rms * nw[i + half];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = lane + j * kWave;
+      if (i >= half) continue;
+      const float c = cs[i], s = sn[i];
+      const float y0 = x0[j] * c - x1[j] * s;
+      const float y1 = x1[j] * c + x0[j] * s;
+      if (is_q) {
+        float* dst = a.q_out + (size_t)m * a.NH * HD + (size_t)h * HD;
+        dst[i] = y0;
+        dst[i + half] = y1;
+      } else {
+        const int kvh = h - a.NH;
+        size_t off = (((size_t)b * a.NKV + kvh) * a.max_seq + p) * HD;
+        if (a.kv_bf16) {
+          ((uint16_t*)a.k_cache)[off + i] = (uint16_t)f32_to_bf16_rne(y0);
+          ((uint16_t*)a.k_cache)[off + i + half] = (uint16_t)f32_to_bf16_rne(y1);
+        } else {
+          ((float*)a.k_cache)[off + i] = y0;
+          ((float*)a.k_cache)[off + i + half] = y1;
+        }
+      }
+    }
+  }
+}
+
+void launch_qkv_post(const QkvPostArgs& a, hipStream_t st) {
+  if (a.M <= 0) return;
+  hipLaunchKernelGGL(k_qkv_post, dim3(a.M), dim3(256), 0, st, a);
+}
+
+// ------------------------------------------------------------------ argmax
+// Greedy choice: lowest index of the maximum ("ember scripts/reference_forward.py",
+// np.argmax in the decode loop). Keys order by value, then by lowest index.
+__global__ void __launch_bounds__(256) k_argmax_reduce(const unsigned long long* part,
+                                                       int nparts, int32_t* next) {
+  __shared__ unsigned long long red[4];
+  const int r = blockIdx.x;
+  unsigned long long k = 0;
+  for (int i = threadIdx.x; i < nparts; i += blockDim.x) {
+    unsigned long long v = part[(size_t)r * nparts + i];
+    k = v > k ? v : k;
+  }
+  k = wave_max_u64(k);
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = k;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    k = red[0];
+    for (int i = 1; i < (int)blockDim.x / kWave; ++i) k = red[i] > k ? red[i] : k;
+    next[r] = (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+  }
+}
+
+void launch_argmax_reduce(const unsigned long long* part, int nparts, int R, int32_t* next,
+                          hipStream_t st) {
+  if (R <= 0) return;
+  hipLaunchKernelGGL(k_argmax_reduce, dim3(R), dim3(256), 0, st, part, nparts, next);
+}
+
+__global__ void __launch_bounds__(256) k_argmax_rows(const float* logits, int n, long long ld,
+                                                     int32_t* next, int* flags) {
+  __shared__ unsigned long long red[4];
+  const int r = blockIdx.x;
+  const float* row = logits + (size_t)r * ld;
+  unsigned long long k = 0;
+  bool nan = false;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const float v = row[i];
+    nan |= (v != v);
+    unsigned long long key = argmax_key(v, (uint32_t)i);
+    k = key > k ? key : k;
+  }
+  if (nan) atomicOr(&flags[kFlagNaN], 1);
+  k = wave_max_u64(k);
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = k;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    k = red[0];
+    for (int i = 1; i < (int)blockDim.x / kWave; ++i) k = red[i] > k ? red[i] : k;
+    next[r] = (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+  }
+}
+
+void launch_argmax_rows(const float* logits, int R, int n, long long ld, int32_t* next, int* flags,
+                        hipStream_t st) {
+  if (R <= 0) return;
+  hipLaunchKernelGGL(k_argmax_rows, dim3(R), dim3(256), 0, st, logits, n, ld, next, flags);
+}
+
+// ------------------------------------------------------------------ classification head
+// logits = Wc h + bc per token ("PII-Tracer serving/reference_forward.py", token head),
+// one wave per (token, class); then the per-token argmax.
+__global__ void __launch_bounds__(256) k_cls_head(const float* h, const void* W, int w_bf16,
+                                                  const float* b, int M, int H, int C, float* out,
+                                                  int32_t* next) {
+  const int m = blockIdx.x;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  __shared__ float vals[64];
+  const float* hr = h + (size_t)m * H;
+  for (int c = wave; c < C; c += blockDim.x / kWave) {
+    float acc = 0.f;
+    for (int k = lane; k < H; k += kWave) {
+      const float wv = w_bf16 ? bf16_to_f32(((const uint16_t*)W)[(size_t)c * H + k])
+                              : ((const float*)W)[(size_t)c * H + k];
+      acc += wv * hr[k];
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      const float v = acc + (b ? b[c] : 0.f);
+      vals[c] = v;
+      if (out) out[(size_t)m * C + c] = v;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && next) {
+    int best = 0;
+    for (int c = 1; c < C; ++c) if (ordered_key(vals[c]) > ordered_key(vals[best])) best = c;
+    next[m] = best;
+  }
+}
+
+void launch_cls_head(const float* h, const void* W, bool w_bf16, const float* b, int M, int H,
+                     int C, float* out, int32_t* next, hipStream_t st) {
+  if (M <= 0) return;
+  hipLaunchKernelGGL(k_cls_head, dim3(M), dim3(256), 0, st, h, W, (int)w_bf16, b, M, H, C, out,
+                     next);
+}
+
+// ------------------------------------------------------------------ conversions, staging
+__global__ void k_convert_logits(const float* src, int n, long long ld, void* dst, int to_bf16) {
+  const int r = blockIdx.y;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const float v = src[(size_t)r * ld + i];
+    if (to_bf16) ((uint16_t*)dst)[(size_t)r * n + i] = (uint16_t)f32_to_bf16_rne(v);
+    else ((float*)dst)[(size_t)r * n + i] = v;
+  }
+}
+
+void launch_convert_logits(const float* src, int R, int n, long long ld, void* dst, bool to_bf16,
+                           hipStream_t st) {
+  if (R <= 0 || n <= 0) return;
+  int gx = (n + 255) / 256;
+  if (gx > 512) gx = 512;
+  hipLaunchKernelGGL(k_convert_logits, dim3(gx, R), dim3(256), 0, st, src, n, ld, dst,
+                     (int)to_bf16);
+}
+
+__global__ void k_stage_step(const int32_t* ids, int R, int V, int pos, int32_t* ids_internal,
+                             int* d_pos, int* flags) {
+  const int r = threadIdx.x + blockIdx.x * blockDim.x;
+  if (r == 0) *d_pos = pos;
+  if (r < R) {
+    int id = ids[r];
+    if (id < 0 || id >= V) {
+      atomicOr(&flags[kFlagBadToken], 1);
+      id = 0;
+    }
+    ids_internal[r] = id;
+  }
+}
+
+void launch_stage_step(const int32_t* ids, int R, int V, int pos, int32_t* ids_internal, int* d_pos,
+                       int* flags, hipStream_t st) {
+  hipLaunchKernelGGL(k_stage_step, dim3((R + 255) / 256), dim3(256), 0, st, ids, R, V, pos,
+                     ids_internal, d_pos, flags);
+}
+
+__global__ void k_copy_ids(const int32_t* src, int n, int32_t* dst) {
+  const int i = threadIdx.x + blockIdx.x * blockDim.x;
+  if (i < n) dst[i] = src[i];
+}
+
+void launch_copy_ids(const int32_t* src, int n, int32_t* dst, hipStream_t st) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_copy_ids, dim3((n + 255) / 256), dim3(256), 0, st, src, n, dst);
+}
+
+__global__ void k_fill_i32(int* p, int n, int v) {
+  const int i = threadIdx.x + blockIdx.x * blockDim.x;
+  if (i < n) p[i] = v;
+}
+
+void launch_fill_i32(int* p, int n, int v, hipStream_t st) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, st, p, n, v);
+}
+
+__global__ void k_widen(const void* src, int bf16, float* dst, long long n) {
+  for (long long i = threadIdx.x + (long long)blockIdx.x * blockDim.x; i < n;
+       i += (long long)gridDim.x * blockDim.x)
+    dst[i] = bf16 ? bf16_to_f32(((const uint16_t*)src)[i]) : ((const float*)src)[i];
+}
+
+void launch_widen(const void* src, bool bf16, float* dst, long long n, hipStream_t st) {
+  if (n <= 0) return;
+  long long g = (n + 255) / 256;
+  if (g > 4096) g = 4096;
+  hipLaunchKernelGGL(k_widen, dim3((unsigned)g), dim3(256), 0, st, src, (int)bf16, dst, n);
+}
+
+}  // namespace ember

@@ -1,0 +1,177 @@
+/*
+ * ember.h -- C ABI of the MI355X (gfx950) GQA decoder forward pass.
+ *
+ * The forward pass is the one the pages define: bf16 (or f32) weights widened to f32,
+ * RMSNorm, rotate-half RoPE with optional llama3 frequency scaling, grouped-query
+ * attention over a causal KV cache (prefill once, then one cached step per new token)
+ * or bidirectional attention, SwiGLU MLP, tied LM head (or a token classification head)
+ * and greedy argmax. Interface shape: "ember internals" page, section "ForwardModel
+ * trait" (create_cache, forward_with_cache(token_ids, cache, start_pos)), with the
+ * explicit write position of section "cursor semantics", and the validation and error
+ * cases of "Falcon-H1-0.5B-Rust src/lib.rs" (Config::validate, validate_weights,
+ * Model::logits).
+ *
+ * Conventions
+ *  - Every call returns ember_status (0 = EMBER_OK). When the host detects an error
+ *    nothing is enqueued; ember_last_error() returns a message (thread-local).
+ *  - Device memory is owned by the caller. The library allocates no device memory: the
+ *    weights, activations and scratch live in a caller-provided workspace, the KV cache
+ *    in a caller-provided buffer. Handles (ember_model, ember_cache) are host objects
+ *    owned by the library and released with ember_free / ember_cache_free.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
+ *    asynchronously; calls on one model must be ordered on one stream. A model handle is
+ *    not thread-safe.
+ *  - All tensors are row-major and contiguous. Batch rows share positions.
+ */
+#ifndef EMBER_H
+#define EMBER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ember_status {
+  EMBER_OK = 0,
+  EMBER_E_ARG = 1,             /* bad argument: NULL pointer, size 0, workspace too small */
+  EMBER_E_CONFIG = 2,          /* zero dimension, heads % kv_heads != 0, odd head_dim, ... */
+  EMBER_E_TENSOR_MISSING = 3,  /* a required named tensor is absent */
+  EMBER_E_TENSOR_SHAPE = 4,    /* a tensor's shape differs from the config */
+  EMBER_E_DTYPE = 5,           /* unsupported dtype, or a tensor dtype != weight_dtype */
+  EMBER_E_TOKEN = 6,           /* token id outside [0, vocab) */
+  EMBER_E_CAPACITY = 7,        /* positions or rows beyond the cache / config capacity */
+  EMBER_E_STATE = 8,           /* call out of order (e.g. decode before any prefill) */
+  EMBER_E_DEVICE = 9,          /* a HIP runtime error */
+  EMBER_E_NONFINITE = 10       /* the device saw a NaN logit */
+} ember_status;
+
+typedef enum ember_dtype { EMBER_F32 = 0, EMBER_BF16 = 1 } ember_dtype;
+
+/* EXACT: every product is an f32-accurate product of the bf16 weight and the f32
+ *        activation (decode: f32 FMA; prefill MFMA: activation split into two bf16
+ *        planes hi + lo). KV cache must be F32 (f32 logits, 1e-4 tier).
+ * FAST:  single-pass bf16 activations into the MFMA GEMMs and attention, f32
+ *        accumulation, norms, softmax and residual (bf16 logits, 2e-2 tier). */
+typedef enum ember_precision { EMBER_EXACT = 0, EMBER_FAST = 1 } ember_precision;
+
+typedef enum ember_head_kind {
+  EMBER_HEAD_TIED_LM = 0,      /* logits = E . rmsnorm(h), E = model.embed_tokens.weight */
+  EMBER_HEAD_CLS = 1           /* logits = Wc . rmsnorm(h) + bc at every token */
+} ember_head_kind;
+
+typedef struct ember_config {
+  double rope_theta;           /* RoPE base theta */
+  double llama3_factor;        /* llama3 frequency scaling (used when rope_llama3 != 0) */
+  double llama3_low_freq_factor;
+  double llama3_high_freq_factor;
+  double llama3_original_max_pos;
+  float rms_eps;               /* RMSNorm epsilon (also for per-head q/k norm) */
+  int32_t vocab, hidden, layers, heads, kv_heads, head_dim, ffn;
+  int32_t rope_llama3;         /* 0/1 */
+  int32_t qkv_bias;            /* 0/1: q/k/v projections carry a bias (Qwen2 family) */
+  int32_t qk_norm;             /* 0/1: per-head RMSNorm of q and k before RoPE (Qwen3) */
+  int32_t causal;              /* 1 = causal decoder, 0 = bidirectional encoder */
+  int32_t head_kind;           /* ember_head_kind */
+  int32_t n_classes;           /* classes of the EMBER_HEAD_CLS head */
+  int32_t weight_dtype;        /* ember_dtype of every stored tensor */
+  int32_t kv_dtype;            /* ember_dtype of the KV cache */
+  int32_t precision;           /* ember_precision */
+  int32_t max_batch;           /* rows per call */
+  int32_t max_seq;             /* positions per row: capacity of the cache and RoPE table */
+  int32_t max_tokens;          /* tokens processed per prefill pass (>= max_batch) */
+} ember_config;
+
+/* A named weight tensor, HuggingFace naming ("model.embed_tokens.weight",
+ * "model.layers.{i}.self_attn.q_proj.weight", ".bias", "...k_norm.weight",
+ * "model.norm.weight", "token_cls_head.weight", ...). `data` is a device pointer,
+ * borrowed for the duration of ember_load_weights only. */
+typedef struct ember_tensor {
+  const char* name;
+  const void* data;
+  int64_t shape[4];
+  int32_t ndim;
+  int32_t dtype;               /* ember_dtype */
+} ember_tensor;
+
+typedef struct ember_model ember_model;
+typedef struct ember_cache ember_cache;
+
+/* Bytes of workspace ember_load_weights needs for `cfg` (repacked weights, RoPE tables,
+ * activations for max_tokens tokens, split-K partials, logits [max_batch, out_dim] f32).
+ * 0 if the config is invalid. */
+size_t ember_workspace_bytes(const ember_config* cfg);
+
+/* Bytes of a KV cache for `cfg`: K and V, [layers][max_batch][kv_heads][max_seq][head_dim]
+ * of kv_dtype. 0 if the config is invalid. */
+size_t ember_kv_cache_bytes(const ember_config* cfg);
+
+/* Validate the config (zero dimensions, heads % kv_heads, even head_dim, dtypes,
+ * capacities) and every tensor (presence, shape, dtype), then repack the weights into
+ * `d_workspace` (QKV rows fused, gate/up rows interleaved, norm vectors and biases as
+ * f32) and upload the RoPE cos/sin tables (angles in f64, rounded once to f32).
+ * `d_workspace` must stay allocated and untouched while the model lives. Synchronises
+ * `stream` before returning. */
+ember_status ember_load_weights(const ember_config* cfg, const ember_tensor* tensors,
+                                int32_t n_tensors, void* d_workspace, size_t workspace_bytes,
+                                void* stream, ember_model** out);
+
+/* Bind a caller-owned KV buffer of at least ember_kv_cache_bytes(cfg) bytes
+ * ("ForwardModel::create_cache"). The buffer holds no valid positions until a prefill. */
+ember_status ember_cache_bind(ember_model* model, void* d_kv, size_t kv_bytes,
+                              ember_cache** out);
+
+/* Forward `n_tokens` tokens of each of `batch` rows at positions
+ * [start_pos, start_pos + n_tokens) ("forward_with_cache(token_ids, cache, start_pos)"),
+ * writing their K/V at those explicit positions. `h_ids` is host memory [batch, n_tokens]
+ * int32, validated (EMBER_E_TOKEN). start_pos must not leave a gap after the positions
+ * already held by the cache (EMBER_E_STATE); start_pos + n_tokens <= max_seq
+ * (EMBER_E_CAPACITY). The head output at each row's last position is kept for
+ * ember_logits. Optional outputs (NULL to skip), device memory:
+ *   d_all_logits  f32 [batch, n_tokens, out_dim]: head output at every position;
+ *   d_next        int32 [batch] (decoder: argmax of the last position, lowest index on
+ *                 ties) or [batch, n_tokens] (classification head: argmax per token).
+ * For a bidirectional config, start_pos must be 0 and every token attends to every
+ * token of its row. */
+ember_status ember_prefill(ember_model* model, ember_cache* cache, const int32_t* h_ids,
+                           int32_t batch, int32_t n_tokens, int32_t start_pos,
+                           float* d_all_logits, int32_t* d_next, void* stream);
+
+/* One cached greedy step for `batch` rows at position `pos` (causal configs only):
+ * reads the ids d_ids [batch] int32 (device), writes their K/V at `pos`, attends over
+ * positions 0..pos, and writes the argmax of the new logits to d_next [batch] int32
+ * (device; may alias d_ids). Requires pos <= the cache's filled length (EMBER_E_STATE)
+ * and pos < max_seq (EMBER_E_CAPACITY). The step is replayed from a HIP graph and does
+ * not synchronise. An id outside [0, vocab) is replaced by 0 and flagged; ember_sync
+ * reports it as EMBER_E_TOKEN. */
+ember_status ember_decode_step(ember_model* model, ember_cache* cache, const int32_t* d_ids,
+                               int32_t batch, int32_t pos, int32_t* d_next, void* stream);
+
+/* Copy the head output of the most recent prefill / decode step, [batch, out_dim], into
+ * d_out as EMBER_F32 or EMBER_BF16 (round to nearest even). EMBER_E_STATE before any
+ * forward. */
+ember_status ember_logits(ember_model* model, void* d_out, int32_t dtype, void* stream);
+
+/* Synchronise `stream` and report device-side conditions raised since the last call:
+ * an out-of-range decode id (EMBER_E_TOKEN) or a NaN logit (EMBER_E_NONFINITE); then
+ * clear them. */
+ember_status ember_sync(ember_model* model, void* stream);
+
+void ember_cache_free(ember_cache* cache);
+void ember_free(ember_model* model);
+
+/* Thread-local message describing the last error of this thread ("" if none). */
+const char* ember_last_error(void);
+
+/* Host-only: the RoPE tables the library uploads, cos/sin [n_pos, head_dim/2] f32
+ * (angles pos * freq in f64, freq = theta^(-2i/head_dim), llama3-scaled when enabled,
+ * rounded once to f32). No device call. */
+ember_status ember_rope_table(const ember_config* cfg, int32_t n_pos, float* h_cos,
+                              float* h_sin);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EMBER_H */
