@@ -26,7 +26,8 @@ HEAD_TIED_LM, HEAD_CLS = 0, 1
 EXPORTED = ["ember_workspace_bytes", "ember_kv_cache_bytes", "ember_load_weights",
             "ember_cache_bind", "ember_prefill", "ember_decode_step", "ember_logits",
             "ember_sync", "ember_cache_free", "ember_free", "ember_last_error",
-            "ember_rope_table"]
+            "ember_rope_table", "ember_time_kernel"]
+K_LM_HEAD, K_QKV, K_ATTN, K_O, K_GATE_UP, K_DOWN = range(6)
 
 
 class EmberConfig(ctypes.Structure):
@@ -82,6 +83,8 @@ def _load():
         "ember_free": (None, [P]),
         "ember_last_error": (ctypes.c_char_p, []),
         "ember_rope_table": (ctypes.c_int, [cfgp, ctypes.c_int32, P, P]),
+        "ember_time_kernel": (ctypes.c_int, [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             P, ctypes.POINTER(ctypes.c_float)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -163,6 +166,13 @@ def ember_rope_table(cfg: EmberConfig, n_pos: int) -> Tuple[np.ndarray, np.ndarr
     sin = np.zeros((n_pos, half), np.float32)
     _check(LIB.ember_rope_table(ctypes.byref(cfg), n_pos, cos.ctypes.data, sin.ctypes.data))
     return cos, sin
+
+
+def ember_time_kernel(model: int, cache: int, kernel: int, phase: int, iters: int,
+                      stream: int) -> float:
+    out = ctypes.c_float()
+    _check(LIB.ember_time_kernel(model, cache, kernel, phase, iters, stream, ctypes.byref(out)))
+    return out.value
 
 
 # ------------------------------------------------------------------ marshalling helpers
@@ -268,6 +278,9 @@ class Engine:
 
     def sync(self):
         ember_sync(self.model, self.sp)
+
+    def time_kernel(self, kernel: int, phase: int, iters: int = 20) -> float:
+        return ember_time_kernel(self.model, self.cache, kernel, phase, iters, self.sp)
 
     def close(self):
         if getattr(self, "cache", None):

@@ -195,6 +195,8 @@ struct ember_model {
   char* ws;
   bool wbf16;
   int has_logits_rows;      // rows in the logits buffer, 0 before any forward
+  int last_decode_batch = 0;
+  struct { int M, rows, tpr, b0, start; } last_pass = {0, 0, 0, 0, 0};
   // decode graph cache
   hipGraphExec_t graph = nullptr;
   const ember_cache* graph_cache = nullptr;
@@ -216,7 +218,11 @@ struct Ctx {
   ember_model* m;
   ember_cache* c;
   hipStream_t st;
+  int only = -1;     // >= 0: launch only the kernel of this ember_kernel kind (timing)
 };
+
+bool want(const Ctx& cx, int kind) { return cx.only < 0 || cx.only == kind; }
+bool want_aux(const Ctx& cx) { return cx.only < 0; }
 
 void* k_layer(const ember_cache* c, int l) { return c->kv + (size_t)l * c->layer_bytes; }
 void* v_layer(const ember_cache* c, int l) {
@@ -270,19 +276,19 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     GemvArgs g{};
     g.W = wqkv; g.w_bf16 = md->wbf16; g.N = p.qkv_n; g.K = H; g.M = ps.M;
     g.x = x; g.norm_w = ln1; g.eps = c.rms_eps; g.bias = bqkv; g.y = qkv; g.ldy = p.qkv_n;
-    launch_gemv(g, GEMV_STORE, st);
+    if (want(cx, EMBER_K_QKV)) launch_gemv(g, GEMV_STORE, st);
   } else if (ps.path == PATH_MFMA) {
-    launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st);
+    if (want_aux(cx)) launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st);
     GemmArgs g{};
     g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka; g.w = (const uint16_t*)wqkv;
     g.M = ps.M; g.N = p.qkv_n; g.K = H; g.bias = bqkv; g.c = qkv; g.ldc = p.qkv_n;
-    launch_gemm(g, GEMM_STORE, st);
+    if (want(cx, EMBER_K_QKV)) launch_gemm(g, GEMM_STORE, st);
   } else {
-    launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, xb, nullptr, nullptr, 0, st);
+    if (want_aux(cx)) launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, xb, nullptr, nullptr, 0, st);
     GemmF32Args g{};
     g.a = xb; g.lda = H; g.w = (const float*)wqkv; g.M = ps.M; g.N = p.qkv_n; g.K = H;
     g.bias = bqkv; g.c = qkv; g.ldc = p.qkv_n;
-    launch_gemm_f32w(g, GEMM_STORE, st);
+    if (want(cx, EMBER_K_QKV)) launch_gemm_f32w(g, GEMM_STORE, st);
   }
 
   QkvPostArgs qa{};
@@ -294,7 +300,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   qa.eps = c.rms_eps; qa.q_out = q;
   qa.k_cache = k_layer(cx.c, li); qa.v_cache = v_layer(cx.c, li);
   qa.kv_bf16 = c.kv_dtype == EMBER_BF16; qa.max_seq = c.max_seq;
-  launch_qkv_post(qa, st);
+  if (want_aux(cx)) launch_qkv_post(qa, st);
 
   const bool planes_out = ps.path == PATH_MFMA;
   if (ps.attn == ATTN_FLASH) {
@@ -306,15 +312,15 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     fa.out_f32 = planes_out ? nullptr : att;
     fa.out_hi = planes_out ? pa_hi : nullptr;
     fa.out_lo = planes_out ? pa_lo : nullptr;
-    launch_flash_prefill(fa, st);
+    if (want(cx, EMBER_K_ATTN)) launch_flash_prefill(fa, st);
   } else {
     DecodeAttnArgs da{};
     da.q = q; da.k_cache = qa.k_cache; da.v_cache = qa.v_cache; da.kv_bf16 = qa.kv_bf16;
     da.B = ps.M; da.NH = NH; da.NKV = NKV; da.HD = HD; da.max_seq = c.max_seq;
     da.d_pos = ps.d_pos; da.nsplit = nsplit; da.chunk_min = chunk_min; da.scale = scale;
     da.part = part;
-    launch_decode_attn(da, st);
-    if (ps.path != PATH_GEMV)
+    if (want(cx, EMBER_K_ATTN)) launch_decode_attn(da, st);
+    if (ps.path != PATH_GEMV && want_aux(cx))
       launch_attn_combine(part, ps.M, NH, HD, nsplit, ps.d_pos, chunk_min,
                           planes_out ? nullptr : att, planes_out ? pa_hi : nullptr,
                           planes_out ? pa_lo : nullptr, st);
@@ -330,17 +336,17 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
       g.x = att;
     }
     g.y = x; g.ldy = H;
-    launch_gemv(g, GEMV_RESID, st);
+    if (want(cx, EMBER_K_O)) launch_gemv(g, GEMV_RESID, st);
   } else if (ps.path == PATH_MFMA) {
     GemmArgs g{};
     g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka; g.w = (const uint16_t*)wo;
     g.M = ps.M; g.N = H; g.K = NH * HD; g.c = x; g.ldc = H;
-    launch_gemm(g, GEMM_RESID, st);
+    if (want(cx, EMBER_K_O)) launch_gemm(g, GEMM_RESID, st);
   } else {
     GemmF32Args g{};
     g.a = att; g.lda = NH * HD; g.w = (const float*)wo; g.M = ps.M; g.N = H; g.K = NH * HD;
     g.c = x; g.ldc = H;
-    launch_gemm_f32w(g, GEMM_RESID, st);
+    if (want(cx, EMBER_K_O)) launch_gemm_f32w(g, GEMM_RESID, st);
   }
 
   // ---- MLP block
@@ -348,30 +354,30 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     GemvArgs g{};
     g.W = wgu; g.w_bf16 = md->wbf16; g.N = FF; g.K = H; g.M = ps.M;
     g.x = x; g.norm_w = ln2; g.eps = c.rms_eps; g.y = act; g.ldy = FF;
-    launch_gemv(g, GEMV_SILU, st);
+    if (want(cx, EMBER_K_GATE_UP)) launch_gemv(g, GEMV_SILU, st);
     GemvArgs d{};
     d.W = wd; d.w_bf16 = md->wbf16; d.N = H; d.K = FF; d.M = ps.M; d.x = act; d.y = x; d.ldy = H;
-    launch_gemv(d, GEMV_RESID, st);
+    if (want(cx, EMBER_K_DOWN)) launch_gemv(d, GEMV_RESID, st);
   } else if (ps.path == PATH_MFMA) {
-    launch_rmsnorm(x, ln2, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st);
+    if (want_aux(cx)) launch_rmsnorm(x, ln2, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st);
     GemmArgs g{};
     g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka; g.w = (const uint16_t*)wgu;
     g.M = ps.M; g.N = 2 * FF; g.K = H; g.o_hi = pb_hi; g.o_lo = pb_lo; g.ldo = FF;
-    launch_gemm(g, GEMM_SILU, st);
+    if (want(cx, EMBER_K_GATE_UP)) launch_gemm(g, GEMM_SILU, st);
     GemmArgs d{};
     d.a_hi = pb_hi; d.a_lo = pb_lo; d.lda = FF; d.w = (const uint16_t*)wd;
     d.M = ps.M; d.N = H; d.K = FF; d.c = x; d.ldc = H;
-    launch_gemm(d, GEMM_RESID, st);
+    if (want(cx, EMBER_K_DOWN)) launch_gemm(d, GEMM_RESID, st);
   } else {
-    launch_rmsnorm(x, ln2, c.rms_eps, ps.M, H, 1, 0, xb, nullptr, nullptr, 0, st);
+    if (want_aux(cx)) launch_rmsnorm(x, ln2, c.rms_eps, ps.M, H, 1, 0, xb, nullptr, nullptr, 0, st);
     GemmF32Args g{};
     g.a = xb; g.lda = H; g.w = (const float*)wgu; g.M = ps.M; g.N = 2 * FF; g.K = H;
     g.o_f32 = act; g.ldo = FF;
-    launch_gemm_f32w(g, GEMM_SILU, st);
+    if (want(cx, EMBER_K_GATE_UP)) launch_gemm_f32w(g, GEMM_SILU, st);
     GemmF32Args d{};
     d.a = act; d.lda = FF; d.w = (const float*)wd; d.M = ps.M; d.N = H; d.K = FF;
     d.c = x; d.ldc = H;
-    launch_gemm_f32w(d, GEMM_RESID, st);
+    if (want(cx, EMBER_K_DOWN)) launch_gemm_f32w(d, GEMM_RESID, st);
   }
 }
 
@@ -389,14 +395,15 @@ void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, lo
   const void* E = md->ws + p.embed;
   float* hrow = md->at<float>(p.hrow);
   if (R == 1 && ld == V) {
-    launch_rmsnorm(md->at<float>(p.x), fn, c.rms_eps, 1, H, row_step, row_off, hrow, nullptr,
-                   nullptr, 0, st);
+    if (want_aux(cx))
+      launch_rmsnorm(md->at<float>(p.x), fn, c.rms_eps, 1, H, row_step, row_off, hrow, nullptr,
+                     nullptr, 0, st);
     GemvArgs g{};
     g.W = E; g.w_bf16 = md->wbf16; g.N = V; g.K = H; g.M = 1; g.x = hrow; g.y = out; g.ldy = V;
     g.argmax_part = md->at<unsigned long long>(p.argpart);
     g.flags = md->at<int>(p.flags);
-    launch_gemv(g, GEMV_LOGITS, st);
-    if (next) launch_argmax_reduce(g.argmax_part, gemv_num_blocks(V, GEMV_LOGITS, H), 1, next, st);
+    if (want(cx, EMBER_K_LM_HEAD)) launch_gemv(g, GEMV_LOGITS, st);
+    if (next && want_aux(cx)) launch_argmax_reduce(g.argmax_part, gemv_num_blocks(V, GEMV_LOGITS, H), 1, next, st);
     return;
   }
   // R rows (at most the pass capacity Mx at a time: the plane / xb buffers hold Mx rows)
@@ -408,21 +415,23 @@ void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, lo
     if (md->wbf16) {
       uint16_t* hi = md->at<uint16_t>(p.pa_hi);
       uint16_t* lo = c.precision == EMBER_EXACT ? md->at<uint16_t>(p.pa_lo) : nullptr;
-      launch_rmsnorm(md->at<float>(p.x), fn, c.rms_eps, rn, H, row_step, off, nullptr, hi, lo,
-                     p.ka, st);
+      if (want_aux(cx))
+        launch_rmsnorm(md->at<float>(p.x), fn, c.rms_eps, rn, H, row_step, off, nullptr, hi, lo,
+                       p.ka, st);
       GemmArgs g{};
       g.a_hi = hi; g.a_lo = lo; g.lda = p.ka; g.w = (const uint16_t*)E;
       g.M = rn; g.N = V; g.K = H; g.c = out + (size_t)r0 * ld; g.ldc = ld;
-      launch_gemm(g, GEMM_STORE, st);
+      if (want(cx, EMBER_K_LM_HEAD)) launch_gemm(g, GEMM_STORE, st);
     } else {
-      launch_rmsnorm(md->at<float>(p.x), fn, c.rms_eps, rn, H, row_step, off, xb, nullptr,
-                     nullptr, 0, st);
+      if (want_aux(cx))
+        launch_rmsnorm(md->at<float>(p.x), fn, c.rms_eps, rn, H, row_step, off, xb, nullptr,
+                       nullptr, 0, st);
       GemmF32Args g{};
       g.a = xb; g.lda = H; g.w = (const float*)E; g.M = rn; g.N = V; g.K = H;
       g.c = out + (size_t)r0 * ld; g.ldc = ld;
-      launch_gemm_f32w(g, GEMM_STORE, st);
+      if (want(cx, EMBER_K_LM_HEAD)) launch_gemm_f32w(g, GEMM_STORE, st);
     }
-    if (next) launch_argmax_rows(out + (size_t)r0 * ld, rn, V, ld, next + r0,
+    if (next && want_aux(cx)) launch_argmax_rows(out + (size_t)r0 * ld, rn, V, ld, next + r0,
                                  md->at<int>(p.flags), st);
   }
 }
@@ -446,18 +455,20 @@ void run_cls_head(const Ctx& cx, int R, int row_step, int row_off, float* out, i
 }
 
 // One decode step's device work for B rows, ids in plan.ids, position in plan.pos.
-void decode_body(const Ctx& cx, int B) {
+void decode_body(const Ctx& cx, int B, int only_layer = -1) {
   ember_model* md = cx.m;
   const ember_config& c = md->cfg;
   const Plan& p = md->plan;
-  launch_embed(md->at<int32_t>(p.ids), md->ws + p.embed, md->wbf16, md->at<float>(p.x), B,
+  if (want_aux(cx)) launch_embed(md->at<int32_t>(p.ids), md->ws + p.embed, md->wbf16, md->at<float>(p.x), B,
                c.hidden, c.vocab, md->at<int>(p.flags), cx.st);
   Pass ps{};
   ps.M = B; ps.rows = B; ps.tpr = 1; ps.b0 = 0; ps.start = 0; ps.d_pos = md->at<int>(p.pos);
   ps.path = B == 1 ? PATH_GEMV : (md->wbf16 ? PATH_MFMA : PATH_F32W);
   ps.attn = ATTN_DECODE;
-  for (int l = 0; l < c.layers; ++l) run_layer(cx, l, ps);
-  run_lm_head(cx, B, 1, 0, md->at<float>(p.logits), c.vocab, md->at<int32_t>(p.next));
+  for (int l = 0; l < c.layers; ++l)
+    if (only_layer < 0 || l == only_layer) run_layer(cx, l, ps);
+  if (want(cx, EMBER_K_LM_HEAD) && (cx.only >= 0 || only_layer < 0))
+    run_lm_head(cx, B, 1, 0, md->at<float>(p.logits), c.vocab, md->at<int32_t>(p.next));
 }
 
 bool graphs_enabled() {
@@ -689,6 +700,7 @@ ember_status ember_prefill(ember_model* md, ember_cache* cache, const int32_t* h
       ps.path = M == 1 ? PATH_GEMV : (md->wbf16 ? PATH_MFMA : PATH_F32W);
       ps.attn = ATTN_FLASH;
       for (int l = 0; l < c.layers; ++l) run_layer(cx, l, ps);
+      md->last_pass = {M, rows, tpr, b0, start_pos + t0};
       const bool last_chunk = t0 + tpr == T;
       if (c.head_kind == EMBER_HEAD_TIED_LM) {
         if (d_all_logits) {
@@ -761,6 +773,72 @@ ember_status ember_decode_step(ember_model* md, ember_cache* cache, const int32_
   HIP_TRY(hipGetLastError());
   if (pos + 1 > cache->filled) cache->filled = pos + 1;
   md->has_logits_rows = batch;
+  md->last_decode_batch = batch;
+  return EMBER_OK;
+}
+
+ember_status ember_time_kernel(ember_model* md, ember_cache* cache, int32_t kernel, int32_t phase,
+                               int32_t iters, void* stream, float* avg_us) {
+  g_last_error.clear();
+  if (!md || !cache || !avg_us || iters <= 0) return fail(EMBER_E_ARG, "bad arguments");
+  if (kernel < EMBER_K_LM_HEAD || kernel > EMBER_K_DOWN) return fail(EMBER_E_ARG, "unknown kernel");
+  hipStream_t st = (hipStream_t)stream;
+  Ctx cx{md, cache, st, kernel};
+  const ember_config& c = md->cfg;
+  const Plan& p = md->plan;
+  // the launches are captured into a graph (non-null stream) so that back-to-back
+  // execution, not the host launch rate, sets the measured time
+  auto enqueue = [&](int n) -> ember_status {
+    if (phase == 0) {
+      if (md->last_decode_batch <= 0) return fail(EMBER_E_STATE, "no decode step has run");
+      for (int i = 0; i < n; ++i) decode_body(cx, md->last_decode_batch, 0);
+    } else {
+      if (md->last_pass.M <= 0) return fail(EMBER_E_STATE, "no prefill has run");
+      Pass ps{};
+      ps.M = md->last_pass.M; ps.rows = md->last_pass.rows; ps.tpr = md->last_pass.tpr;
+      ps.b0 = md->last_pass.b0; ps.start = md->last_pass.start; ps.d_pos = nullptr;
+      ps.path = ps.M == 1 ? PATH_GEMV : (md->wbf16 ? PATH_MFMA : PATH_F32W);
+      ps.attn = ATTN_FLASH;
+      for (int i = 0; i < n; ++i) {
+        if (kernel == EMBER_K_LM_HEAD)
+          run_lm_head(cx, ps.rows, ps.tpr, ps.tpr - 1, md->at<float>(p.logits), c.vocab, nullptr);
+        else
+          run_layer(cx, 0, ps);
+      }
+    }
+    return EMBER_OK;
+  };
+  hipGraphExec_t ge = nullptr;
+  if (st != nullptr) {
+    HIP_TRY(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
+    ember_status s0 = enqueue(iters);
+    hipGraph_t g = nullptr;
+    HIP_TRY(hipStreamEndCapture(st, &g));
+    if (s0 != EMBER_OK) { (void)hipGraphDestroy(g); return s0; }
+    hipError_t e = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e != hipSuccess) return fail(EMBER_E_DEVICE, "graph instantiate: %s", hipGetErrorString(e));
+    HIP_TRY(hipGraphLaunch(ge, st));     // warm-up replay
+  }
+  hipEvent_t e0, e1;
+  HIP_TRY(hipEventCreate(&e0));
+  HIP_TRY(hipEventCreate(&e1));
+  HIP_TRY(hipEventRecord(e0, st));
+  if (ge) {
+    HIP_TRY(hipGraphLaunch(ge, st));
+  } else {
+    ember_status s1 = enqueue(iters);
+    if (s1 != EMBER_OK) return s1;
+  }
+  HIP_TRY(hipEventRecord(e1, st));
+  HIP_TRY(hipEventSynchronize(e1));
+  float ms = 0.f;
+  HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (ge) (void)hipGraphExecDestroy(ge);
+  HIP_TRY(hipGetLastError());
+  *avg_us = ms * 1000.f / (float)iters;
   return EMBER_OK;
 }
 

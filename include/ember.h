@@ -170,6 +170,27 @@ const char* ember_last_error(void);
 ember_status ember_rope_table(const ember_config* cfg, int32_t n_pos, float* h_cos,
                               float* h_sin);
 
+/* Measurement support (not part of the forward pass): the kernels of one step that
+ * ember_time_kernel can time. Layer-0 instances; the projection kinds time the GEMV of
+ * a one-row decode step or the MFMA GEMM of a multi-row pass. */
+typedef enum ember_kernel {
+  EMBER_K_LM_HEAD = 0,         /* tied LM head over the vocabulary (+ argmax partials) */
+  EMBER_K_QKV = 1,             /* fused QKV projection (+ bias; RMSNorm fused in the GEMV) */
+  EMBER_K_ATTN = 2,            /* split-K decode attention, or flash prefill attention */
+  EMBER_K_O = 3,               /* output projection + residual (GEMV: + split-K combine) */
+  EMBER_K_GATE_UP = 4,         /* gate/up projection + SiLU*up */
+  EMBER_K_DOWN = 5             /* down projection + residual */
+} ember_kernel;
+
+/* Launch kernel `kernel` of the most recent decode step (phase 0) or prefill pass
+ * (phase 1) `iters` times back to back on `stream`, with that step's launch arguments,
+ * between two HIP events recorded on `stream`, and return the mean duration per launch
+ * in microseconds. The repeated launches may leave activations and logits of the model
+ * modified (residual-add kernels accumulate); the KV cache is not touched except by
+ * re-writing the same values. EMBER_E_STATE if no such step has run. */
+ember_status ember_time_kernel(ember_model* model, ember_cache* cache, int32_t kernel,
+                               int32_t phase, int32_t iters, void* stream, float* avg_us);
+
 #ifdef __cplusplus
 }
 #endif
