@@ -47,9 +47,46 @@ EMBER_DEV T wave_max(T v) {
   return v;
 }
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
-EMBER_DEV float group_sum(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o);
+// DPP lane moves (gfx9 encodings): quad_perm [1,0,3,2] = 0xB1 (xor 1), [2,3,0,1] = 0x4E
+// (xor 2); row_ror:4 = 0x124 and row_ror:8 = 0x128 rotate within a 16-lane row.
+template <int CTRL>
+EMBER_DEV float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned 16-lane row; every lane of the row receives the row's sum.
+EMBER_DEV float row16_sum(float v) {
+  v += dpp_move<0xB1>(v);
+  v += dpp_move<0x4E>(v);
+  v += dpp_move<0x124>(v);
+  v += dpp_move<0x128>(v);
+  return v;
+}
+
+// Wave sum with a wave-uniform result: row sums by DPP, then the four rows combined
+// through v_readlane in a fixed order.
+EMBER_DEV float wave_sum_uniform(float v) {
+  v = row16_sum(v);
+  const int b = __float_as_int(v);
+  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+}
+
+// Sum over aligned groups of `WIDTH` lanes (power of two <= 64); every lane of a group
+// receives the group's sum.
+template <int WIDTH>
+EMBER_DEV float group_sum(float v) {
+  if (WIDTH >= 2) v += dpp_move<0xB1>(v);
+  if (WIDTH >= 4) v += dpp_move<0x4E>(v);
+  if (WIDTH == 8) v += __shfl_xor(v, 4);
+  if (WIDTH >= 16) {
+    v += dpp_move<0x124>(v);
+    v += dpp_move<0x128>(v);
+  }
+  if (WIDTH >= 32) v += __shfl_xor(v, 16);
+  if (WIDTH >= 64) v += __shfl_xor(v, 32);
   return v;
 }
 

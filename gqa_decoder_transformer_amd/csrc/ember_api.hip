@@ -138,7 +138,7 @@ Plan make_plan(const ember_config& c) {
   p.ka = H > NH * HD ? H : NH * HD;
   const int out_dim = c.head_kind == EMBER_HEAD_CLS ? c.n_classes : c.vocab;
   p.nsplit_max = (c.max_seq + 63) / 64;
-  p.argparts = gemv_num_blocks(c.vocab, GEMV_LOGITS, H);
+  p.argparts = gemv_num_blocks(c.vocab, GEMV_LOGITS, H, c.weight_dtype == EMBER_BF16);
   p.ids = take((size_t)Mx * 4);
   p.pos = take(4);
   p.next = take((size_t)Mx * 4);
@@ -300,7 +300,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   qa.eps = c.rms_eps; qa.q_out = q;
   qa.k_cache = k_layer(cx.c, li); qa.v_cache = v_layer(cx.c, li);
   qa.kv_bf16 = c.kv_dtype == EMBER_BF16; qa.max_seq = c.max_seq;
-  if (want_aux(cx)) launch_qkv_post(qa, st);
+  if (want_aux(cx) && ps.attn == ATTN_FLASH) launch_qkv_post(qa, st);
 
   const bool planes_out = ps.path == PATH_MFMA;
   if (ps.attn == ATTN_FLASH) {
@@ -312,10 +312,15 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     fa.out_f32 = planes_out ? nullptr : att;
     fa.out_hi = planes_out ? pa_hi : nullptr;
     fa.out_lo = planes_out ? pa_lo : nullptr;
-    if (want(cx, EMBER_K_ATTN)) launch_flash_prefill(fa, st);
+    if (want(cx, EMBER_K_ATTN)) {
+      if (planes_out && flash_mfma_supported(HD)) launch_flash_mfma(fa, exact, st);
+      else launch_flash_prefill(fa, st);
+    }
   } else {
     DecodeAttnArgs da{};
-    da.q = q; da.k_cache = qa.k_cache; da.v_cache = qa.v_cache; da.kv_bf16 = qa.kv_bf16;
+    da.qkv = qkv; da.cos_t = qa.cos_t; da.sin_t = qa.sin_t; da.q_norm = qa.q_norm;
+    da.k_norm = qa.k_norm; da.eps = c.rms_eps;
+    da.k_cache = qa.k_cache; da.v_cache = qa.v_cache; da.kv_bf16 = qa.kv_bf16;
     da.B = ps.M; da.NH = NH; da.NKV = NKV; da.HD = HD; da.max_seq = c.max_seq;
     da.d_pos = ps.d_pos; da.nsplit = nsplit; da.chunk_min = chunk_min; da.scale = scale;
     da.part = part;
@@ -403,7 +408,8 @@ void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, lo
     g.argmax_part = md->at<unsigned long long>(p.argpart);
     g.flags = md->at<int>(p.flags);
     if (want(cx, EMBER_K_LM_HEAD)) launch_gemv(g, GEMV_LOGITS, st);
-    if (next && want_aux(cx)) launch_argmax_reduce(g.argmax_part, gemv_num_blocks(V, GEMV_LOGITS, H), 1, next, st);
+    if (next && want_aux(cx))
+      launch_argmax_reduce(g.argmax_part, gemv_num_blocks(V, GEMV_LOGITS, H, md->wbf16), 1, next, st);
     return;
   }
   // R rows (at most the pass capacity Mx at a time: the plane / xb buffers hold Mx rows)

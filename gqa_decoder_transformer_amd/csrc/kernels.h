@@ -79,25 +79,25 @@ struct GemvArgs {
   bool w_bf16;
   int N;                   // outputs per token (SILU: FF outputs from 2*FF packed rows)
   int K;
-  int M;                   // tokens (1..2)
-  // input: x [M, K] f32; when norm_w != null the kernel applies RMSNorm to x first
+  int M;                   // tokens: must be 1
+  // input: x [K] f32; when norm_w != null the kernel applies RMSNorm to x first
   const float* x;
   const float* norm_w;
   float eps;
   // input alternative: attention split-K partials to combine (x == null)
-  const float* part;       // [M][NH][nsplit][HD + 2]: (m, l, acc[HD]) per split
+  const float* part;       // [NH][nsplit][HD + 2]: (m, l, acc[HD]) per split (nsplit <= 64)
   int part_heads, part_hd, part_nsplit;
   const int* d_pos;        // valid splits computed from *d_pos + 1 keys
   int part_chunk_min;
   // outputs
   const float* bias;       // [N] or null (STORE)
-  float* y;                // STORE/SILU/LOGITS: [M, ldy]; RESID: x_res [M, ldy] (+=)
+  float* y;                // STORE/SILU/LOGITS: [N]; RESID: x_res [N] (+=)
   int ldy;
-  unsigned long long* argmax_part;   // LOGITS: [M][gridDim.x]
+  unsigned long long* argmax_part;   // LOGITS: [gridDim.x]
   int* flags;
 };
 void launch_gemv(const GemvArgs& a, int epi, hipStream_t st);
-int gemv_num_blocks(int N, int epi, int K);
+int gemv_num_blocks(int N, int epi, int K, bool bf16);
 
 // ------------------------------------------------------------------ GEMM (kernels_gemm.hip)
 
@@ -151,18 +151,28 @@ struct FlashArgs {
   uint16_t* out_lo;
 };
 void launch_flash_prefill(const FlashArgs& a, hipStream_t st);
+// MFMA flash attention (kernels_flash.hip) for head_dim 64 / 128; `split`: EXACT hi+lo.
+bool flash_mfma_supported(int HD);
+void launch_flash_mfma(const FlashArgs& a, bool split, hipStream_t st);
 
 struct DecodeAttnArgs {
-  const float* q;          // [B, NH*HD] f32 roped
-  const void* k_cache;
-  const void* v_cache;
+  const float* qkv;        // [B, (NH + 2 NKV) HD] raw projections of the current token
+  const float* cos_t;      // [max_seq, HD/2]
+  const float* sin_t;
+  const float* q_norm;     // [HD] or null
+  const float* k_norm;
+  float eps;
+  void* k_cache;           // layer base [B_cache][NKV][max_seq][HD]; K/V at *d_pos written
+  void* v_cache;
   bool kv_bf16;
   int B, NH, NKV, HD, max_seq;
-  const int* d_pos;        // keys 0..*d_pos
+  const int* d_pos;        // current position; keys 0..*d_pos
   int nsplit, chunk_min;
   float scale;
   float* part;             // [B][NH][nsplit][HD + 2]
 };
+// Split-K decode attention with the QKV epilogue (q/k norm, RoPE, K/V store at the
+// current position) fused in.
 void launch_decode_attn(const DecodeAttnArgs& a, hipStream_t st);
 // att = combine(part) for B rows, written as f32 [B, NH*HD] and/or planes.
 void launch_attn_combine(const float* part, int B, int NH, int HD, int nsplit, const int* d_pos,

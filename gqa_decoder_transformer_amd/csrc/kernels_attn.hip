@@ -96,12 +96,14 @@ __global__ void __launch_bounds__(256) k_flash_prefill(FlashArgs a) {
 
 // ------------------------------------------------------------------ split-K decode
 // Block (split, kv head, row): the G query heads of the group share every K/V read.
-// A group of LPK lanes reads one key (16 bytes per lane); per head the partial dot
-// products are summed with lane shuffles, then each lane group keeps an online softmax
-// state; groups are merged through LDS in a fixed order. Output per (row, head, split):
-// (m, l, acc[HD]) with acc unnormalised.
-constexpr int kMaxG = 8;
-
+// The block first issues its K/V loads (cache positions < pos), then builds the
+// current token's roped q (G heads) and -- in the split that holds position pos -- the
+// roped k and v, which it also stores into the cache at pos (qkv epilogue fused: q/k
+// RMSNorm when configured, rotate-half RoPE from the tables, K/V store at the explicit
+// position). A group of LPK lanes reads one key (16 bytes per lane); per head the
+// partial dot products are summed with lane shuffles and each lane group keeps an online
+// softmax state; key batches are double-buffered in registers. Groups are merged through
+// LDS in a fixed order. Output per (row, head, split): (m, l, acc[HD]), acc unnormalised.
 EMBER_DEV void split_range(int S, int nsplit, int chunk_min, int split, int& s0, int& s1) {
   int chunk = (S + nsplit - 1) / nsplit;
   if (chunk < chunk_min) chunk = chunk_min;
@@ -117,24 +119,119 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
   static_assert(LPK >= 1 && LPK <= 64, "head_dim");
   constexpr int KPW = kWave / LPK;             // keys per wave pass
   constexpr int NGRP = 4 * KPW;                // lane groups per block
+  constexpr int KI = G > 4 ? 2 : 4;            // keys per group per batch
+  constexpr int HALF = HD / 2;
+  constexpr bool ONE_PASS = NGRP * G * (HD + 2) * 4 <= 48 * 1024;
+  constexpr int MG = ONE_PASS ? G : 1;
   __shared__ float qs[G * HD];
-  __shared__ float sm[NGRP], sl[NGRP];
-  __shared__ float sacc[NGRP * HD];
+  __shared__ float kc[HD], vc[HD];
+  __shared__ float cs[HALF], sn[HALF];
+  __shared__ float sm[NGRP * MG], sl[NGRP * MG];
+  __shared__ float sacc[NGRP * MG * HD];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int S = *a.d_pos + 1;
+  const int pos = *a.d_pos;
+  const int S = pos + 1;
   int s0, s1;
   split_range(S, a.nsplit, a.chunk_min, split, s0, s1);
   if (s0 >= S) return;                         // beyond the valid splits: never read
-
-  const int h0 = kvh * G;
-  for (int e = threadIdx.x; e < G * HD; e += blockDim.x)
-    qs[e] = a.q[(size_t)b * a.NH * HD + (size_t)h0 * HD + e];
-  __syncthreads();
+  const bool has_cur = s1 == S;
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int grp = wave * KPW + lane / LPK;     // 0..NGRP-1
   const int sub = lane % LPK;
+  const size_t base = ((size_t)b * a.NKV + kvh) * a.max_seq * HD;
+  const int nkeys = s1 - s0 - grp > 0 ? (s1 - s0 - grp + NGRP - 1) / NGRP : 0;
+  const int nb = (nkeys + KI - 1) / KI;
+
+  u32x4_t kb0[KI], vb0[KI], kb1[KI], vb1[KI];
+  auto load = [&](int batch, u32x4_t* kb, u32x4_t* vb) {
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int key = s0 + grp + NGRP * (batch * KI + i);
+      if (key < s1 && key != pos) {
+        const size_t off = base + (size_t)key * HD + sub * DPL;
+        if (KV_BF16) {
+          kb[i] = *(const u32x4_t*)((const uint16_t*)a.k_cache + off);
+          vb[i] = *(const u32x4_t*)((const uint16_t*)a.v_cache + off);
+        } else {
+          kb[i] = *(const u32x4_t*)((const float*)a.k_cache + off);
+          vb[i] = *(const u32x4_t*)((const float*)a.v_cache + off);
+        }
+      }
+    }
+  };
+  if (nb > 0) load(0, kb0, vb0);
+
+  // current token: raw q (G heads) and, in the last split, raw k/v of head kvh
+  const int qkv_n = (a.NH + 2 * a.NKV) * HD;
+  const float* row = a.qkv + (size_t)b * qkv_n;
+  const int h0 = kvh * G;
+  for (int e = threadIdx.x; e < G * HD; e += blockDim.x) qs[e] = row[h0 * HD + e];
+  for (int e = threadIdx.x; e < HALF; e += blockDim.x) {
+    cs[e] = a.cos_t[(size_t)pos * HALF + e];
+    sn[e] = a.sin_t[(size_t)pos * HALF + e];
+  }
+  if (has_cur)
+    for (int e = threadIdx.x; e < HD; e += blockDim.x) {
+      kc[e] = row[(a.NH + kvh) * HD + e];
+      vc[e] = row[(a.NH + a.NKV + kvh) * HD + e];
+    }
+  __syncthreads();
+  // RoPE (and q/k norm) in place: pair e (thread e + 256 j) is pair e % HALF of head
+  // e / HALF, head G being the current key
+  const int npairs = (G + (has_cur ? 1 : 0)) * HALF;
+  constexpr int PJ = ((G + 1) * HALF + 255) / 256;
+  float y0[PJ], y1[PJ];
+#pragma unroll
+  for (int j = 0; j < PJ; ++j) {
+    const int e = threadIdx.x + 256 * j;
+    if (e >= npairs) continue;
+    const int hh = e / HALF, i = e % HALF;
+    const float* src = hh < G ? qs + hh * HD : kc;
+    const float* nw = hh < G ? a.q_norm : a.k_norm;
+    float x0 = src[i], x1 = src[i + HALF];
+    if (nw) {
+      float ss = 0.f;
+      for (int d = 0; d < HD; ++d) ss += src[d] * src[d];
+      const float rms = sqrtf(ss / (float)HD + a.eps);
+      x0 = x0 / rms * nw[i];
+      x1 = x1 / rms * nw[i + HALF];
+    }
+    y0[j] = x0 * cs[i] - x1 * sn[i];
+    y1[j] = x1 * cs[i] + x0 * sn[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < PJ; ++j) {
+    const int e = threadIdx.x + 256 * j;
+    if (e >= npairs) continue;
+    const int hh = e / HALF, i = e % HALF;
+    float* dst = hh < G ? qs + hh * HD : kc;
+    float v0 = y0[j], v1 = y1[j];
+    if (hh == G && KV_BF16) {                  // the cache holds bf16: use the stored values
+      v0 = bf16_to_f32(f32_to_bf16_rne(v0));
+      v1 = bf16_to_f32(f32_to_bf16_rne(v1));
+    }
+    dst[i] = v0;
+    dst[i + HALF] = v1;
+  }
+  if (has_cur && KV_BF16)
+    for (int e = threadIdx.x; e < HD; e += blockDim.x) vc[e] = bf16_to_f32(f32_to_bf16_rne(vc[e]));
+  __syncthreads();
+  if (has_cur) {                               // store this token's K/V at position pos
+    const size_t off = base + (size_t)pos * HD;
+    for (int e = threadIdx.x; e < HD; e += blockDim.x) {
+      if (KV_BF16) {
+        ((uint16_t*)a.k_cache)[off + e] = (uint16_t)f32_to_bf16_rne(kc[e]);
+        ((uint16_t*)a.v_cache)[off + e] = (uint16_t)f32_to_bf16_rne(vc[e]);
+      } else {
+        ((float*)a.k_cache)[off + e] = kc[e];
+        ((float*)a.v_cache)[off + e] = vc[e];
+      }
+    }
+  }
+
   float qv[G][DPL];
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -149,65 +246,95 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
 #pragma unroll
     for (int d = 0; d < DPL; ++d) acc[g][d] = 0.f;
   }
-  const size_t base = ((size_t)b * a.NKV + kvh) * a.max_seq * HD;
-  for (int key = s0 + grp; key < s1; key += NGRP) {
-    const size_t off = base + (size_t)key * HD + sub * DPL;
-    u32x4_t kraw, vraw;
-    if (KV_BF16) {
-      kraw = *(const u32x4_t*)((const uint16_t*)a.k_cache + off);
-      vraw = *(const u32x4_t*)((const uint16_t*)a.v_cache + off);
-    } else {
-      kraw = *(const u32x4_t*)((const float*)a.k_cache + off);
-      vraw = *(const u32x4_t*)((const float*)a.v_cache + off);
-    }
-    float kf[DPL], vf[DPL];
+  // one batch of KI keys: scores first, then one running-max update per head
+  auto compute = [&](int batch, const u32x4_t* kb, const u32x4_t* vb) {
+    float kf[KI][DPL], vf[KI][DPL];
+    bool valid[KI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (KV_BF16) {
-        kf[2 * i] = bf16_lo(kraw[i]); kf[2 * i + 1] = bf16_hi(kraw[i]);
-        vf[2 * i] = bf16_lo(vraw[i]); vf[2 * i + 1] = bf16_hi(vraw[i]);
+    for (int i = 0; i < KI; ++i) {
+      const int key = s0 + grp + NGRP * (batch * KI + i);
+      valid[i] = key < s1;
+      if (key == pos) {
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) { kf[i][d] = kc[sub * DPL + d]; vf[i][d] = vc[sub * DPL + d]; }
       } else {
-        kf[i] = __uint_as_float(kraw[i]);
-        vf[i] = __uint_as_float(vraw[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (KV_BF16) {
+            kf[i][2 * j] = bf16_lo(kb[i][j]); kf[i][2 * j + 1] = bf16_hi(kb[i][j]);
+            vf[i][2 * j] = bf16_lo(vb[i][j]); vf[i][2 * j + 1] = bf16_hi(vb[i][j]);
+          } else {
+            kf[i][j] = __uint_as_float(kb[i][j]);
+            vf[i][j] = __uint_as_float(vb[i][j]);
+          }
+        }
       }
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float s = 0.f;
+      float sc[KI];
+      float mb = -INFINITY;
 #pragma unroll
-      for (int d = 0; d < DPL; ++d) s = fmaf(qv[g][d], kf[d], s);
-      s = group_sum(s, LPK) * a.scale;
-      const float mnew = fmaxf(mrun[g], s);
-      const float alpha = expf(mrun[g] - mnew);
-      const float p = expf(s - mnew);
-      l[g] = l[g] * alpha + p;
+      for (int i = 0; i < KI; ++i) {
+        float s = 0.f;
 #pragma unroll
-      for (int d = 0; d < DPL; ++d) acc[g][d] = fmaf(p, vf[d], acc[g][d] * alpha);
+        for (int d = 0; d < DPL; ++d) s = fmaf(qv[g][d], kf[i][d], s);
+        s = group_sum<LPK>(s) * a.scale;
+        sc[i] = valid[i] ? s : -INFINITY;
+        mb = fmaxf(mb, sc[i]);
+      }
+      if (mb == -INFINITY) continue;           // no admissible key in this batch
+      const float mnew = fmaxf(mrun[g], mb);
+      const float alpha = expf(mrun[g] - mnew); // mrun = -inf -> 0
+      l[g] *= alpha;
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) acc[g][d] *= alpha;
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        const float p = valid[i] ? expf(sc[i] - mnew) : 0.f;
+        l[g] += p;
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) acc[g][d] = fmaf(p, vf[i][d], acc[g][d]);
+      }
       mrun[g] = mnew;
     }
+  };
+  for (int bt = 0; bt < nb; bt += 2) {
+    if (bt + 1 < nb) load(bt + 1, kb1, vb1);
+    compute(bt, kb0, vb0);
+    if (bt + 1 >= nb) break;
+    if (bt + 2 < nb) load(bt + 2, kb0, vb0);
+    compute(bt + 1, kb1, vb1);
   }
-  // merge lane groups through LDS (fixed order), one head at a time
+
+  // merge lane groups through LDS (fixed order)
   const int h_base = b * a.NH + h0;
-  for (int g = 0; g < G; ++g) {
-    if (sub == 0) {
-      sm[grp] = mrun[g];
-      sl[grp] = l[g];
-    }
+  for (int g0 = 0; g0 < G; g0 += MG) {
 #pragma unroll
-    for (int d = 0; d < DPL; ++d) sacc[grp * HD + sub * DPL + d] = acc[g][d];
+    for (int gg = 0; gg < MG; ++gg) {
+      const int g = g0 + gg;
+      if (sub == 0) {
+        sm[grp * MG + gg] = mrun[g];
+        sl[grp * MG + gg] = l[g];
+      }
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) sacc[(grp * MG + gg) * HD + sub * DPL + d] = acc[g][d];
+    }
     __syncthreads();
-    for (int d = threadIdx.x; d < HD; d += blockDim.x) {
+    for (int e = threadIdx.x; e < MG * HD; e += blockDim.x) {
+      const int gg = e / HD, d = e % HD;
       float M = -INFINITY;
-      for (int i = 0; i < NGRP; ++i) M = fmaxf(M, sm[i]);
+      for (int i = 0; i < NGRP; ++i) M = fmaxf(M, sm[i * MG + gg]);
       float L = 0.f, A = 0.f;
       if (M != -INFINITY) {
         for (int i = 0; i < NGRP; ++i) {
-          const float w = (sm[i] == -INFINITY) ? 0.f : expf(sm[i] - M);
-          L += sl[i] * w;
-          A += sacc[i * HD + d] * w;
+          const float mi = sm[i * MG + gg];
+          const float w = (mi == -INFINITY) ? 0.f : expf(mi - M);
+          L += sl[i * MG + gg] * w;
+          A += sacc[(i * MG + gg) * HD + d] * w;
         }
       }
-      float* out = a.part + (((size_t)(h_base + g)) * a.nsplit + split) * (HD + 2);
+      float* out = a.part + (((size_t)(h_base + g0 + gg)) * a.nsplit + split) * (HD + 2);
       if (d == 0) { out[0] = M; out[1] = L; }
       out[2 + d] = A;
     }
@@ -299,10 +426,14 @@ void launch_attn_combine(const float* part, int B, int NH, int HD, int nsplit, c
 }
 
 void decode_split_plan(int B, int NKV, int max_seq, int* nsplit, int* chunk_min) {
+  // enough blocks to cover the CUs for one row, more for batches; chunks >= 64 keys,
+  // at most 64 splits (the one-row combine keeps per-split weights in LDS)
   const int cmin = 64;
-  int target = (2048 + NKV * B - 1) / (NKV * B);
+  const int target_blocks = B == 1 ? 256 : 2048;
+  int target = (target_blocks + NKV * B - 1) / (NKV * B);
   int maxs = (max_seq + cmin - 1) / cmin;
   int ns = target < maxs ? target : maxs;
+  if (ns > 64) ns = 64;
   if (ns < 1) ns = 1;
   *nsplit = ns;
   *chunk_min = cmin;

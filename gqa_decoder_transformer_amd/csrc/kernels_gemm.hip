@@ -63,9 +63,9 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   constexpr int TN = BN / WN / 16;
   static_assert(WM * WN == 4, "4 waves");
   static_assert(EPI != GEMM_SILU || TN % 2 == 0, "SiLU pairs 16-column fragments");
-  __shared__ uint16_t As_hi[BM * LDS_STRIDE];
-  __shared__ uint16_t As_lo[SPLIT ? BM * LDS_STRIDE : 1];
-  __shared__ uint16_t Bs[BN * LDS_STRIDE];
+  __shared__ __align__(16) uint16_t As_hi[BM * LDS_STRIDE];
+  __shared__ __align__(16) uint16_t As_lo[SPLIT ? BM * LDS_STRIDE : 8];
+  __shared__ __align__(16) uint16_t Bs[BN * LDS_STRIDE];
 
   // XCD-aware tile order: blocks are dealt round-robin to the 8 XCDs; give each XCD a
   // contiguous run of logical tiles, M-tiles fastest, so a weight column block stays

@@ -1,12 +1,19 @@
-// Decode GEMV: y[m, n] = sum_k W[n, k] x[m, k] for M <= 2 tokens, streaming W from HBM
+// Decode GEMV: y[n] = sum_k W[n, k] x[k] for one token, streaming W from HBM
 // once with 16-byte coalesced loads (bf16 weights widened to f32 in registers, f32 FMA).
 //
-// The input vector is staged in LDS once per block, either RMS-normalised on the fly
-// (RMSNorm fused into the consumer GEMV) or combined from split-K attention partials
-// (the attention combine fused into the O projection). Each wave owns RPW outputs; each
-// lane owns 16-byte chunks c = lane + 64 t of the weight rows, with U chunks per row in
-// flight before the FMAs. Epilogues: store (+bias), residual add, SiLU*up (gate/up rows
-// interleaved in blocks of 16), logits with a fused block argmax.
+// Latency is what limits these kernels at decode sizes (a dependent global round trip
+// costs ~1 us on this part), so every thread issues ALL of its weight loads first --
+// they depend on nothing the previous kernel wrote -- and only then stages the input
+// vector in LDS: RMS-normalised on the fly (RMSNorm fused into the consumer GEMV) or
+// combined from split-K attention partials (combine fused into the O projection).
+//
+// Two layouts of the work:
+//  * row per wave  (K <= 64 * U * E): a wave owns RPW outputs, lane l reads 16-byte
+//    chunks l + 64 t of each row, wave-shuffle reduction;
+//  * row per block (longer K): the whole block owns RPW outputs, thread t reads chunks
+//    t + 256 t', partial sums reduced through LDS in a fixed order.
+// Epilogues: store (+bias), residual add, SiLU*up (gate/up rows interleaved in blocks of
+// 16), logits with a fused block argmax (value, then lowest index).
 #include "common.h"
 #include "kernels.h"
 
@@ -14,7 +21,6 @@ namespace ember {
 
 namespace {
 
-constexpr int kMaxM = 2;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
@@ -38,67 +44,86 @@ template <> struct WTraits<float> {
 // then the 16 matching up rows).
 EMBER_DEV int gu_row(int n, int up) { return (n >> 4) * 32 + (up ? 16 : 0) + (n & 15); }
 
-// Stage the (normalised or combined) input rows into LDS xs[M][K].
-EMBER_DEV void stage_input(const GemvArgs& a, float* xs, float* red) {
+// Stage the (normalised or combined) input vector into LDS xs[K]. `cw` is LDS scratch
+// of 3 * NH * nsplit floats for the attention combine.
+EMBER_DEV void stage_input(const GemvArgs& a, float* xs, float* cw, float* red) {
   const int K = a.K;
   if (a.x) {
-    for (int m = 0; m < a.M; ++m) {
-      const float* xr = a.x + (size_t)m * K;
-      float inv_scale = 1.f;
-      if (a.norm_w) {
-        float ss = 0.f;
-        for (int k = threadIdx.x; k < K; k += blockDim.x) ss += xr[k] * xr[k];
-        ss = block_sum(ss, red);
-        inv_scale = sqrtf(ss / (float)K + a.eps);
-        for (int k = threadIdx.x; k < K; k += blockDim.x) xs[m * K + k] = xr[k] / inv_scale * a.norm_w[k];
-      } else {
-        for (int k = threadIdx.x; k < K; k += blockDim.x) xs[m * K + k] = xr[k];
+    if (a.norm_w) {
+      float ss = 0.f;
+      for (int k = threadIdx.x; k < K; k += blockDim.x) {
+        const float v = a.x[k];
+        xs[k] = v;
+        ss += v * v;
       }
+      ss = block_sum(ss, red);
+      const float rms = sqrtf(ss / (float)K + a.eps);
+      for (int k = threadIdx.x; k < K; k += blockDim.x) xs[k] = xs[k] / rms * a.norm_w[k];
+    } else {
+      for (int k = threadIdx.x; k < K; k += blockDim.x) xs[k] = a.x[k];
     }
   } else {
-    // split-K attention combine: out = sum_j acc_j e^{m_j - M} / sum_j l_j e^{m_j - M}
+    // split-K attention combine: att_h = sum_j acc_hj * (e^{m_hj - M_h} / L_h),
+    // M_h = max_j m_hj, L_h = sum_j l_hj e^{m_hj - M_h}
     const int HD = a.part_hd, NH = a.part_heads, ns = a.part_nsplit;
     const int S = *a.d_pos + 1;
     int chunk = (S + ns - 1) / ns;
     if (chunk < a.part_chunk_min) chunk = a.part_chunk_min;
-    const int nvalid = (S + chunk - 1) / chunk;
+    const int nv = (S + chunk - 1) / chunk;
     const int stride = HD + 2;
-    for (int m = 0; m < a.M; ++m) {
-      for (int e = threadIdx.x; e < NH * HD; e += blockDim.x) {
-        const int h = e / HD, d = e % HD;
-        const float* ph = a.part + (((size_t)m * NH + h) * ns) * stride;
-        float mx = -INFINITY;
-        for (int j = 0; j < nvalid; ++j) mx = fmaxf(mx, ph[(size_t)j * stride]);
-        float L = 0.f, acc = 0.f;
-        if (mx != -INFINITY) {
-          for (int j = 0; j < nvalid; ++j) {
-            const float mj = ph[(size_t)j * stride];
-            const float wj = (mj == -INFINITY) ? 0.f : expf(mj - mx);
-            L += ph[(size_t)j * stride + 1] * wj;
-            acc += ph[(size_t)j * stride + 2 + d] * wj;
-          }
-        }
-        xs[m * K + e] = L > 0.f ? acc / L : 0.f;
+    float* sm = cw;
+    float* sl = cw + NH * ns;
+    float* sw = cw + 2 * NH * ns;
+    for (int e = threadIdx.x; e < NH * nv; e += blockDim.x) {
+      const int h = e / nv, j = e % nv;
+      const float* ph = a.part + ((size_t)h * ns + j) * stride;
+      sm[e] = ph[0];
+      sl[e] = ph[1];
+    }
+    __syncthreads();
+    for (int h = threadIdx.x; h < NH; h += blockDim.x) {
+      float M = -INFINITY;
+      for (int j = 0; j < nv; ++j) M = fmaxf(M, sm[h * nv + j]);
+      float L = 0.f;
+      for (int j = 0; j < nv; ++j) {
+        const float mj = sm[h * nv + j];
+        const float w = (mj == -INFINITY) ? 0.f : expf(mj - M);
+        sw[h * nv + j] = w;
+        L += sl[h * nv + j] * w;
       }
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      for (int j = 0; j < nv; ++j) sw[h * nv + j] *= inv;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < NH * HD; e += blockDim.x) {
+      const int h = e / HD, d = e % HD;
+      const float* ph = a.part + (size_t)h * ns * stride + 2 + d;
+      float acc = 0.f;
+      for (int j = 0; j < nv; ++j) acc = fmaf(ph[(size_t)j * stride], sw[h * nv + j], acc);
+      xs[e] = acc;
     }
   }
   __syncthreads();
 }
 
-template <typename WT, int EPI, int RPW, int U>
+// BLOCK_ROW = false: a wave owns RPW outputs; true: the block owns RPW outputs.
+template <typename WT, int EPI, int RPW, int U, bool BLOCK_ROW>
 __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
-  extern __shared__ float xs[];                       // [M][K]
+  extern __shared__ float xs[];                       // [K] (+ combine scratch)
   __shared__ float red[16];
+  __shared__ float wred[kWaves][4];                   // BLOCK_ROW partial sums
   __shared__ unsigned long long best[kWaves];
-  stage_input(a, xs, red);
 
   constexpr int E = WTraits<WT>::E;
   constexpr int RU = (EPI == GEMV_SILU) ? 2 : 1;     // weight rows per output unit
   constexpr int NR = RPW * RU;
+  static_assert(!BLOCK_ROW || NR <= 4, "BLOCK_ROW partials");
+  constexpr int STRIDE = BLOCK_ROW ? kThreads : kWave;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int K = a.K, M = a.M;
+  const int tix = BLOCK_ROW ? (int)threadIdx.x : lane;
+  const int K = a.K;
   const int nch = K / E;
-  const int n0 = (blockIdx.x * kWaves + wave) * RPW;
+  const int n0 = BLOCK_ROW ? blockIdx.x * RPW : (blockIdx.x * kWaves + wave) * RPW;
 
   const WT* rows[NR];
 #pragma unroll
@@ -112,123 +137,165 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
     }
   }
 
-  float acc[kMaxM][NR];
+  // 1) weight loads of the first batch, before anything that depends on the input
+  u32x4_t wv[U][NR];
 #pragma unroll
-  for (int m = 0; m < kMaxM; ++m)
+  for (int t = 0; t < U; ++t) {
+    const int c = tix + t * STRIDE;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) acc[m][r] = 0.f;
+    for (int r = 0; r < NR; ++r)
+      wv[t][r] = c < nch ? *(const u32x4_t*)(rows[r] + (size_t)c * E) : u32x4_t{0, 0, 0, 0};
+  }
+  // 2) input vector -> LDS (norm or attention combine) while the loads are in flight
+  stage_input(a, xs, xs + K, red);
 
-  for (int c0 = lane; c0 < nch; c0 += kWave * U) {
-    u32x4_t wv[U][NR];
+  float acc[NR];
 #pragma unroll
-    for (int t = 0; t < U; ++t) {
-      const int c = c0 + t * kWave;
+  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+
+  for (int c0 = 0; c0 < nch; c0 += STRIDE * U) {
+    if (c0 > 0) {
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        if (c < nch) wv[t][r] = *(const u32x4_t*)(rows[r] + (size_t)c * E);
-        else wv[t][r] = u32x4_t{0, 0, 0, 0};
+      for (int t = 0; t < U; ++t) {
+        const int c = c0 + tix + t * STRIDE;
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+          wv[t][r] = c < nch ? *(const u32x4_t*)(rows[r] + (size_t)c * E) : u32x4_t{0, 0, 0, 0};
       }
     }
 #pragma unroll
     for (int t = 0; t < U; ++t) {
-      const int c = c0 + t * kWave;
+      const int c = c0 + tix + t * STRIDE;
       if (c >= nch) break;
-      float xv[kMaxM][E];
+      float xv[E];
 #pragma unroll
-      for (int m = 0; m < kMaxM; ++m) {
-        if (m < M) {
-#pragma unroll
-          for (int e = 0; e < E; ++e) xv[m][e] = xs[m * K + c * E + e];
-        }
-      }
+      for (int e = 0; e < E; ++e) xv[e] = xs[c * E + e];
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         float wf[E];
         WTraits<WT>::widen(wv[t][r], wf);
 #pragma unroll
-        for (int m = 0; m < kMaxM; ++m) {
-          if (m < M) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[m][r] = fmaf(wf[e], xv[m][e], acc[m][r]);
-          }
-        }
+        for (int e = 0; e < E; ++e) acc[r] = fmaf(wf[e], xv[e], acc[r]);
       }
     }
   }
 
 #pragma unroll
-  for (int m = 0; m < kMaxM; ++m)
-#pragma unroll
-    for (int r = 0; r < NR; ++r) acc[m][r] = wave_sum(acc[m][r]);
+  for (int r = 0; r < NR; ++r) acc[r] = wave_sum_uniform(acc[r]);
 
-  for (int m = 0; m < M; ++m) {
-    unsigned long long bk = 0;
+  if (BLOCK_ROW) {
+    // fixed-order sum of the 4 waves' partials (identical result in every thread)
+    if (lane == 0) {
 #pragma unroll
-    for (int u = 0; u < RPW; ++u) {
-      const int n = n0 + u;
-      if (n >= a.N) continue;
-      float* yp = a.y + (size_t)m * a.ldy + n;
-      if (EPI == GEMV_STORE) {
-        if (lane == 0) *yp = acc[m][u] + (a.bias ? a.bias[n] : 0.f);
-      } else if (EPI == GEMV_RESID) {
-        if (lane == 0) *yp += acc[m][u];
-      } else if (EPI == GEMV_SILU) {
-        if (lane == 0) *yp = silu(acc[m][2 * u]) * acc[m][2 * u + 1];
-      } else {
-        const float v = acc[m][u];
-        if (lane == 0) {
-          *yp = v;
-          if (v != v) atomicOr(&a.flags[kFlagNaN], 1);
-        }
-        const unsigned long long key = argmax_key(v, (uint32_t)n);
-        bk = key > bk ? key : bk;
-      }
+      for (int r = 0; r < NR; ++r) wred[wave][r] = acc[r];
     }
-    if (EPI == GEMV_LOGITS) {
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[r] = (wred[0][r] + wred[1][r]) + (wred[2][r] + wred[3][r]);
+  }
+  const bool writer = BLOCK_ROW ? threadIdx.x == 0 : lane == 0;
+
+  unsigned long long bk = 0;
+#pragma unroll
+  for (int u = 0; u < RPW; ++u) {
+    const int n = n0 + u;
+    if (n >= a.N) continue;
+    float* yp = a.y + n;
+    if (EPI == GEMV_STORE) {
+      if (writer) *yp = acc[u] + (a.bias ? a.bias[n] : 0.f);
+    } else if (EPI == GEMV_RESID) {
+      if (writer) *yp += acc[u];
+    } else if (EPI == GEMV_SILU) {
+      if (writer) *yp = silu(acc[2 * u]) * acc[2 * u + 1];
+    } else {
+      const float v = acc[u];
+      if (writer) {
+        *yp = v;
+        if (v != v) atomicOr(&a.flags[kFlagNaN], 1);
+      }
+      const unsigned long long key = argmax_key(v, (uint32_t)n);
+      bk = key > bk ? key : bk;
+    }
+  }
+  if (EPI == GEMV_LOGITS) {
+    if (BLOCK_ROW) {
+      if (threadIdx.x == 0) a.argmax_part[blockIdx.x] = bk;
+    } else {
       if (lane == 0) best[wave] = bk;
       __syncthreads();
       if (threadIdx.x == 0) {
         unsigned long long k = best[0];
         for (int w = 1; w < kWaves; ++w) k = best[w] > k ? best[w] : k;
-        a.argmax_part[(size_t)m * gridDim.x + blockIdx.x] = k;
+        a.argmax_part[blockIdx.x] = k;
       }
-      __syncthreads();
     }
   }
 }
 
-template <typename WT, int EPI>
-void launch_t(const GemvArgs& a, int rpw, hipStream_t st) {
-  const size_t shmem = (size_t)a.M * a.K * sizeof(float);
-  if (rpw == 4) {
-    const int blocks = (a.N + kWaves * 4 - 1) / (kWaves * 4);
-    hipLaunchKernelGGL((k_gemv<WT, EPI, 4, 2>), dim3(blocks), dim3(kThreads), shmem, st, a);
+struct Shape {
+  bool block_row;
+  int rpw, u;
+};
+
+// Work layout: every load of a thread issued in one round when the row fits.
+Shape pick(int N, int K, bool bf16, int epi) {
+  const int E = bf16 ? 8 : 4;
+  const int nch = K / E;
+  Shape s;
+  if (nch <= kWave * 4) {
+    s.block_row = false;
+    s.u = nch <= kWave * 2 ? 2 : 4;
+    s.rpw = (N >= 4096 && epi != GEMV_SILU) ? 4 : (N >= 4096 ? 2 : 1);
+    if (epi == GEMV_SILU && s.u == 4) s.rpw = 1;
   } else {
-    const int blocks = (a.N + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL((k_gemv<WT, EPI, 1, 4>), dim3(blocks), dim3(kThreads), shmem, st, a);
+    s.block_row = true;
+    s.u = 4;
+    s.rpw = N >= 8192 ? 2 : 1;
+    if (epi == GEMV_SILU) s.rpw = 1;
   }
+  return s;
 }
 
-int pick_rpw(int N, int epi) {
-  (void)epi;
-  return N >= 4096 ? 4 : 1;
+template <typename WT, int EPI, int RPW, int U, bool BR>
+void launch_one(const GemvArgs& a, hipStream_t st) {
+  size_t shmem = (size_t)a.K * sizeof(float);
+  if (!a.x) shmem += (size_t)3 * a.part_heads * a.part_nsplit * sizeof(float);
+  const int per_block = BR ? RPW : kWaves * RPW;
+  const int blocks = (a.N + per_block - 1) / per_block;
+  hipLaunchKernelGGL((k_gemv<WT, EPI, RPW, U, BR>), dim3(blocks), dim3(kThreads), shmem, st, a);
+}
+
+template <typename WT, int EPI>
+void launch_t(const GemvArgs& a, hipStream_t st) {
+  const Shape s = pick(a.N, a.K, sizeof(WT) == 2, EPI);
+  if (s.block_row) {
+    if (s.rpw == 2) launch_one<WT, EPI, 2, 4, true>(a, st);
+    else launch_one<WT, EPI, 1, 4, true>(a, st);
+  } else if (s.u == 2) {
+    if (s.rpw == 4) launch_one<WT, EPI, 4, 2, false>(a, st);
+    else if (s.rpw == 2) launch_one<WT, EPI, 2, 2, false>(a, st);
+    else launch_one<WT, EPI, 1, 2, false>(a, st);
+  } else {
+    if (s.rpw == 4) launch_one<WT, EPI, 4, 4, false>(a, st);
+    else if (s.rpw == 2) launch_one<WT, EPI, 2, 4, false>(a, st);
+    else launch_one<WT, EPI, 1, 4, false>(a, st);
+  }
 }
 
 }  // namespace
 
-int gemv_num_blocks(int N, int epi, int K) {
-  (void)K;
-  const int rpw = pick_rpw(N, epi);
-  return (N + kWaves * rpw - 1) / (kWaves * rpw);
+int gemv_num_blocks(int N, int epi, int K, bool bf16) {
+  const Shape s = pick(N, K, bf16, epi);
+  const int per_block = s.block_row ? s.rpw : kWaves * s.rpw;
+  return (N + per_block - 1) / per_block;
 }
 
 void launch_gemv(const GemvArgs& a, int epi, hipStream_t st) {
-  if (a.M <= 0 || a.N <= 0) return;
-  const int rpw = pick_rpw(a.N, epi);
+  if (a.M != 1 || a.N <= 0) return;     // one token per launch
 #define EMBER_GEMV_CASE(E)                                               \
   case E:                                                                \
-    if (a.w_bf16) launch_t<uint16_t, E>(a, rpw, st);                     \
-    else launch_t<float, E>(a, rpw, st);                                 \
+    if (a.w_bf16) launch_t<uint16_t, E>(a, st);                          \
+    else launch_t<float, E>(a, st);                                      \
     break;
   switch (epi) {
     EMBER_GEMV_CASE(GEMV_STORE)

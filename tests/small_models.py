@@ -14,3 +14,13 @@ ENCODER_SMALL = C.shrink_model(C.ENCODER, name="encoder-small", vocab=89, hidden
                                layers=2, heads=4, kv_heads=2, head_dim=32, ffn=96)
 
 FAMILIES = [TINY, QWEN_SMALL, LLAMA_SMALL, ENCODER_SMALL]
+
+# head_dim 64 / 128 shapes: exercise the MFMA attention kernels
+LLAMA_HD64 = C.shrink_model(C.LLAMA1B, name="llama-hd64", vocab=131, hidden=128, layers=2,
+                            heads=4, kv_heads=2, head_dim=64, ffn=192)
+
+ENCODER_HD128 = C.shrink_model(C.ENCODER, name="encoder-hd128", vocab=83, hidden=128, layers=2,
+                               heads=2, kv_heads=1, head_dim=128, ffn=160)
+
+QWEN_HD64_G7 = C.shrink_model(C.QWEN05B, name="qwen-hd64-g7", vocab=97, hidden=448, layers=2,
+                              heads=7, kv_heads=1, head_dim=64, ffn=320)
