@@ -156,7 +156,7 @@ Plan make_plan(const ember_config& c) {
   p.part = take((size_t)c.max_batch * NH * p.nsplit_max * (HD + 2) * 4);
   p.logits = take((size_t)c.max_batch * out_dim * 4);
   p.hrow = take((size_t)c.max_batch * H * 4);
-  p.argpart = take((size_t)2 * p.argparts * 8);
+  p.argpart = take((size_t)p.argparts * 8);
   p.total = off;
   return p;
 }
@@ -325,7 +325,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     da.d_pos = ps.d_pos; da.nsplit = nsplit; da.chunk_min = chunk_min; da.scale = scale;
     da.part = part;
     if (want(cx, EMBER_K_ATTN)) launch_decode_attn(da, st);
-    if (ps.path != PATH_GEMV && want_aux(cx))
+    if (want_aux(cx))
       launch_attn_combine(part, ps.M, NH, HD, nsplit, ps.d_pos, chunk_min,
                           planes_out ? nullptr : att, planes_out ? pa_hi : nullptr,
                           planes_out ? pa_lo : nullptr, st);
@@ -334,13 +334,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   if (ps.path == PATH_GEMV) {
     GemvArgs g{};
     g.W = wo; g.w_bf16 = md->wbf16; g.N = H; g.K = NH * HD; g.M = ps.M;
-    if (ps.attn == ATTN_DECODE) {
-      g.part = part; g.part_heads = NH; g.part_hd = HD; g.part_nsplit = nsplit;
-      g.d_pos = ps.d_pos; g.part_chunk_min = chunk_min;
-    } else {
-      g.x = att;
-    }
-    g.y = x; g.ldy = H;
+    g.x = att; g.y = x; g.ldy = H;
     if (want(cx, EMBER_K_O)) launch_gemv(g, GEMV_RESID, st);
   } else if (ps.path == PATH_MFMA) {
     GemmArgs g{};

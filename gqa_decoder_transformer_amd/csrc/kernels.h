@@ -84,11 +84,6 @@ struct GemvArgs {
   const float* x;
   const float* norm_w;
   float eps;
-  // input alternative: attention split-K partials to combine (x == null)
-  const float* part;       // [NH][nsplit][HD + 2]: (m, l, acc[HD]) per split (nsplit <= 64)
-  int part_heads, part_hd, part_nsplit;
-  const int* d_pos;        // valid splits computed from *d_pos + 1 keys
-  int part_chunk_min;
   // outputs
   const float* bias;       // [N] or null (STORE)
   float* y;                // STORE/SILU/LOGITS: [N]; RESID: x_res [N] (+=)
@@ -169,12 +164,12 @@ struct DecodeAttnArgs {
   const int* d_pos;        // current position; keys 0..*d_pos
   int nsplit, chunk_min;
   float scale;
-  float* part;             // [B][NH][nsplit][HD + 2]
+  float* part;             // [B][NH][nsplit][HD + 2] split partials (m, l, acc)
 };
 // Split-K decode attention with the QKV epilogue (q/k norm, RoPE, K/V store at the
 // current position) fused in.
 void launch_decode_attn(const DecodeAttnArgs& a, hipStream_t st);
-// att = combine(part) for B rows, written as f32 [B, NH*HD] and/or planes.
+// att = combine(part) for B rows (nsplit <= 64), written as f32 [B, NH*HD] and/or planes.
 void launch_attn_combine(const float* part, int B, int NH, int HD, int nsplit, const int* d_pos,
                          int chunk_min, float* out_f32, uint16_t* out_hi, uint16_t* out_lo,
                          hipStream_t st);

@@ -340,32 +340,45 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
     }
     __syncthreads();
   }
+
 }
 
+// Combine of the split partials of one (row, head):
+// att = sum_j acc_j w_j / L, w_j = e^{m_j - M}, M = max_j m_j, L = sum_j l_j w_j,
+// the per-split weights computed once per head in LDS.
 __global__ void __launch_bounds__(128) k_attn_combine(const float* part, int NH, int HD,
                                                       int nsplit, const int* d_pos, int chunk_min,
                                                       float* out_f32, uint16_t* out_hi,
                                                       uint16_t* out_lo) {
+  __shared__ float w[64], lsum[64];
+  __shared__ float inv_l;
   const int bh = blockIdx.x;                   // b * NH + h
   const int S = *d_pos + 1;
   int chunk = (S + nsplit - 1) / nsplit;
   if (chunk < chunk_min) chunk = chunk_min;
-  const int nvalid = (S + chunk - 1) / chunk;
+  const int nv = (S + chunk - 1) / chunk;
   const int stride = HD + 2;
   const float* ph = part + (size_t)bh * nsplit * stride;
-  for (int d = threadIdx.x; d < HD; d += blockDim.x) {
+  for (int j = threadIdx.x; j < nv; j += blockDim.x) {
+    w[j] = ph[(size_t)j * stride];
+    lsum[j] = ph[(size_t)j * stride + 1];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
     float M = -INFINITY;
-    for (int j = 0; j < nvalid; ++j) M = fmaxf(M, ph[(size_t)j * stride]);
-    float L = 0.f, A = 0.f;
-    if (M != -INFINITY) {
-      for (int j = 0; j < nvalid; ++j) {
-        const float mj = ph[(size_t)j * stride];
-        const float w = (mj == -INFINITY) ? 0.f : expf(mj - M);
-        L += ph[(size_t)j * stride + 1] * w;
-        A += ph[(size_t)j * stride + 2 + d] * w;
-      }
+    for (int j = 0; j < nv; ++j) M = fmaxf(M, w[j]);
+    float L = 0.f;
+    for (int j = 0; j < nv; ++j) {
+      w[j] = w[j] == -INFINITY ? 0.f : expf(w[j] - M);
+      L += lsum[j] * w[j];
     }
-    const float v = L > 0.f ? A / L : 0.f;
+    inv_l = L > 0.f ? 1.f / L : 0.f;
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < HD; d += blockDim.x) {
+    float acc = 0.f;
+    for (int j = 0; j < nv; ++j) acc = fmaf(ph[(size_t)j * stride + 2 + d], w[j], acc);
+    const float v = acc * inv_l;
     const size_t o = (size_t)bh * HD + d;
     if (out_f32) out_f32[o] = v;
     if (out_hi) {
