@@ -128,11 +128,12 @@ class OracleModel:
         return x + act @ w[p + "mlp.down_proj.weight"].T
 
     def forward_sequence(self, ids, start_pos: int = 0, cache: KVCache | None = None,
-                         all_positions: bool = False) -> np.ndarray:
+                         all_positions: bool = False, progress=None) -> np.ndarray:
         """Forward of one row of ``T`` tokens at positions ``start_pos..start_pos+T-1``.
 
         Returns the head output at the last position (``[out_dim]``) or, with
-        ``all_positions``, at every position (``[T, out_dim]``).
+        ``all_positions``, at every position (``[T, out_dim]``). ``progress(layer)`` is
+        called after each layer when given (long runs report that they are alive).
         """
         ids = self._check_ids(ids)
         T = ids.shape[0]
@@ -140,6 +141,8 @@ class OracleModel:
         x = self.w["model.embed_tokens.weight"][ids].astype(self.dtype, copy=True)
         for li in range(self.cfg.layers):
             x = self.layer_sequence(li, x, positions, cache)
+            if progress is not None:
+                progress(li)
         if cache is not None:
             cache.length = max(cache.length, start_pos + T)
         return self.head(x if all_positions else x[-1])
@@ -199,7 +202,8 @@ class OracleModel:
         return self.head(x)
 
 
-def generate(model: OracleModel, prompt, n_steps: int, max_seq: int | None = None):
+def generate(model: OracleModel, prompt, n_steps: int, max_seq: int | None = None,
+             progress=None):
     """Prefill once, then ``n_steps`` greedy steps, one cached forward each (the NumPy
     reference's generation loop; ember internals page: one prefill and one cached step per
     new token). End-of-sequence ids are not special: the step count is fixed.
@@ -211,7 +215,7 @@ def generate(model: OracleModel, prompt, n_steps: int, max_seq: int | None = Non
     prompt = np.asarray(prompt)
     T = prompt.shape[0]
     cache = KVCache(model.cfg, max_seq or (T + n_steps), model.dtype)
-    logits = [model.forward_sequence(prompt, 0, cache)]
+    logits = [model.forward_sequence(prompt, 0, cache, progress=progress)]
     ids = [int(greedy_argmax(logits[0]))]
     for k in range(n_steps):
         logits.append(model.forward_token(ids[-1], T + k, cache))

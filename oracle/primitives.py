@@ -116,7 +116,7 @@ def softmax(s: np.ndarray) -> np.ndarray:
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray,
               k_pos: np.ndarray, causal: bool, mask: np.ndarray | None = None,
-              q_block: int = 512) -> np.ndarray:
+              q_block: int = 1024) -> np.ndarray:
     """Grouped-query scaled dot-product attention.
 
     q ``[T, NH, HD]``, k/v ``[S, NKV, HD]``; query head ``h`` reads kv head
@@ -129,20 +129,28 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray,
     exists so tests can reach the fully-masked-row fallback of ``softmax``. The output is
     ``softmax(scores) @ v`` per head, ``[T, NH, HD]``.
 
-    Queries are processed in blocks of ``q_block`` rows to bound memory. In the causal case
-    without an explicit mask, every query of a block admits key position 0..its own
-    position, so keys after the block's last query position are inadmissible for all of
-    its rows and contribute exactly zero; they are dropped from that block's product.
+    The block arithmetic runs on torch CPU tensors (multithreaded elementwise ops; the
+    steps are the ones above, with the fallback of ``softmax``), the query heads that share
+    a kv head batched together, and queries in blocks of ``q_block`` rows to bound memory.
+    In the causal case without an explicit mask every query of a block admits key
+    position 0..its own position, so keys after the block's last query position are
+    inadmissible for all of its rows and contribute exactly zero; they are dropped from
+    that block's product.
     """
+    import torch
     T, NH, HD = q.shape
     S, NKV, _ = k.shape
     if NH % NKV:
         raise ValueError("query heads must be a multiple of kv heads")
     group = NH // NKV
-    scale = q.dtype.type(1.0 / np.sqrt(HD))
+    dt = torch.float64 if q.dtype == np.float64 else torch.float32
+    scale = torch.tensor(q.dtype.type(1.0 / np.sqrt(HD)), dtype=dt)
     out = np.zeros((T, NH, HD), dtype=q.dtype)
     q_pos = np.asarray(q_pos)
     k_pos = np.asarray(k_pos)
+    tq = torch.from_numpy(np.ascontiguousarray(q))
+    tk = torch.from_numpy(np.ascontiguousarray(k))
+    tv = torch.from_numpy(np.ascontiguousarray(v))
     for t0 in range(0, T, q_block):
         t1 = min(T, t0 + q_block)
         qp = q_pos[t0:t1]
@@ -154,13 +162,26 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray,
             allowed &= k_pos[None, :s_hi] <= qp[:, None]
         if mask is not None:
             allowed &= mask[t0:t1, :s_hi]
-        for h in range(NH):
-            kh = h // group
-            sc = (q[t0:t1, h, :] @ k[:s_hi, kh, :].T) * scale
-            sc = np.where(allowed, sc, q.dtype.type(NEG_INF))
-            p = softmax(sc)
-            out[t0:t1, h, :] = p @ v[:s_hi, kh, :]
+        ta = torch.from_numpy(allowed)
+        for kh in range(NKV):
+            hs = slice(kh * group, (kh + 1) * group)
+            qb = tq[t0:t1, hs, :].permute(1, 0, 2)                  # [G, tb, HD]
+            sc = torch.matmul(qb, tk[:s_hi, kh, :].T) * scale       # [G, tb, s_hi]
+            sc = torch.where(ta, sc, torch.tensor(float("-inf"), dtype=dt))
+            p = _softmax_t(sc)
+            out[t0:t1, hs, :] = torch.matmul(p, tv[:s_hi, kh, :]).permute(1, 0, 2).numpy()
     return out
+
+
+def _softmax_t(s):
+    """``softmax`` on a torch tensor (same max-subtracted form and fallback)."""
+    import torch
+    m = torch.amax(s, dim=-1, keepdim=True) if s.shape[-1] else torch.zeros(s.shape[:-1] + (1,), dtype=s.dtype)
+    dead = torch.isneginf(m)
+    e = torch.exp(s - torch.where(dead, torch.zeros_like(m), m))
+    p = e / torch.sum(e, dim=-1, keepdim=True)
+    n = s.shape[-1]
+    return torch.where(dead, torch.full_like(p, 1.0 / n if n else 0.0), p)
 
 
 # --------------------------------------------------------------------------- MLP
