@@ -240,6 +240,7 @@ def test_tiny_workload_exact():
     assert check_greedy(g_ids[:, 0], or_ids, or_logits, TOL_EXACT) is None
 
 
+@pytest.mark.timeout(600)
 def test_qwen05b_workload_exact_free_running_and_teacher_forced():
     eng, prompt, n, or_ids, or_logits = _workload_case("qwen05b")
     g_ids, g_logits = gpu_generate(eng, prompt, n)
@@ -275,6 +276,7 @@ def test_long_ragged_prefill_mfma_attention_tiles():
             assert err < tol
 
 
+@pytest.mark.timeout(600)
 def test_llama1b_workload_exact_prefill_2048_and_decode():
     eng, prompt, n, or_ids, or_logits = _workload_case("llama1b", steps=48)
     g_ids, g_logits = gpu_generate(eng, prompt, n)
@@ -285,6 +287,7 @@ def test_llama1b_workload_exact_prefill_2048_and_decode():
     assert err[:upto].max() < TOL_EXACT
 
 
+@pytest.mark.timeout(600)
 def test_llama1b_workload_fast_bf16_logits_teacher_forced():
     from gqa_decoder_transformer_amd import binding as B
     eng, prompt, n, or_ids, or_logits = _workload_case("llama1b", steps=16, precision=B.FAST)
@@ -294,6 +297,7 @@ def test_llama1b_workload_fast_bf16_logits_teacher_forced():
     assert err.max() < TOL_FAST
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("prec_name", ["exact", "fast"])
 def test_encoder_workload_sampled_rows(prec_name):
     """16 x 512 bidirectional encoder, run whole on the GPU; rows are independent, the
@@ -319,3 +323,50 @@ def test_encoder_workload_sampled_rows(prec_name):
         assert err < tol
         if prec == B.EXACT:
             assert np.array_equal(nxt[r], np.argmax(g[r], -1))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("prec_name", ["exact", "fast"])
+def test_longctx_workload_sampled_rows(prec_name):
+    """64 rows x 8192 prompt tokens prefilled, then batched greedy decode at positions
+    8192.., run whole on the GPU (the benchmark's launch configuration: one row per
+    prefill pass, the batch-64 decode path). Rows never interact, so the oracle checks
+    sampled rows exactly: rows 0 and 63 (EXACT, f32 KV) or row 0 (FAST, bf16 KV), over the
+    first 6 decode steps, teacher-forced with the oracle's ids."""
+    import torch
+    from gqa_decoder_transformer_amd import binding as B
+    w = W.get("longctx")
+    prec = B.EXACT if prec_name == "exact" else B.FAST
+    tol = TOL_EXACT if prec == B.EXACT else TOL_FAST
+    steps = 6
+    rows = (0, 63) if prec == B.EXACT else (0,)
+    ck = W.weights_for(w)
+    ids = W.make_ids(w)
+    om = O.OracleModel(w.model, ck)
+    ref = {}
+    for r in rows:
+        say(f"longctx oracle row {r}: 8192-token prefill + {steps} steps")
+        ref[r] = O.generate(om, ids[r], steps, max_seq=w.max_pos,
+                            progress=lambda li, r=r: say(f"  oracle row {r} layer {li}") if li % 4 == 3 else None)
+    del om
+    cfg = B.make_config(w.model, precision=prec, max_batch=w.batch, max_seq=w.max_pos,
+                        max_tokens=w.prompt_len)
+    eng = B.Engine(cfg, ck)
+    say(f"longctx GPU prefill 64 x 8192 precision={prec_name}")
+    eng.prefill(ids)
+    logs = [eng.logits(w.batch, B.F32 if prec == B.EXACT else B.BF16).float().cpu().numpy()]
+    feed = np.zeros((steps, w.batch), np.int32)
+    for r in rows:
+        feed[:, r] = ref[r][0][:steps]
+    for k in range(steps):
+        cur = torch.from_numpy(feed[k].copy()).to(eng.device)
+        out = torch.empty_like(cur)
+        eng.decode_step(cur, w.prompt_len + k, out)
+        logs.append(eng.logits(w.batch, B.F32 if prec == B.EXACT else B.BF16).float().cpu().numpy())
+        say(f"decode step {k} done")
+    eng.sync()
+    logs = np.stack(logs)                        # [steps + 1, 64, V]
+    for r in rows:
+        err = rel_maxabs(logs[:, r], ref[r][1])
+        say(f"row {r}: max rel err {err.max():.3g}")
+        assert err.max() < tol
