@@ -56,7 +56,8 @@ struct Plan {
   std::vector<LayerOff> layer;
   // activations
   size_t ids, pos, next, flags, x, xb, pa_hi, pa_lo, pb_hi, pb_lo, qkv, q, att, act, part,
-      logits, hrow, argpart;
+      logits, hrow, argpart, splitk;
+  size_t splitk_elems;
   size_t total;
   int Mx, qkv_n, ka, nsplit_max, argparts;
 };
@@ -157,6 +158,14 @@ Plan make_plan(const ember_config& c) {
   p.logits = take((size_t)c.max_batch * out_dim * 4);
   p.hrow = take((size_t)c.max_batch * H * 4);
   p.argpart = take((size_t)p.argparts * 8);
+  {
+    // split-K partial planes for GEMMs whose tiles cannot fill the GPU (M <= 128)
+    int maxn = 2 * FF > p.qkv_n ? 2 * FF : p.qkv_n;
+    if (H > maxn) maxn = H;
+    const int mrows = Mx < 128 ? Mx : 128;
+    p.splitk_elems = c.weight_dtype == EMBER_BF16 ? (size_t)16 * mrows * maxn : 0;
+    p.splitk = p.splitk_elems ? take(p.splitk_elems * 4) : 0;
+  }
   p.total = off;
   return p;
 }
@@ -203,6 +212,7 @@ struct ember_model {
   int graph_batch = -1;
   hipStream_t graph_stream = nullptr;
   template <typename T> T* at(size_t off) const { return (T*)(ws + off); }
+  float* splitk() const { return plan.splitk_elems ? (float*)(ws + plan.splitk) : nullptr; }
 };
 
 struct ember_cache {
@@ -280,6 +290,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   } else if (ps.path == PATH_MFMA) {
     if (want_aux(cx)) launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st);
     GemmArgs g{};
+    g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
     g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka; g.w = (const uint16_t*)wqkv;
     g.M = ps.M; g.N = p.qkv_n; g.K = H; g.bias = bqkv; g.c = qkv; g.ldc = p.qkv_n;
     if (want(cx, EMBER_K_QKV)) launch_gemm(g, GEMM_STORE, st);
@@ -338,6 +349,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     if (want(cx, EMBER_K_O)) launch_gemv(g, GEMV_RESID, st);
   } else if (ps.path == PATH_MFMA) {
     GemmArgs g{};
+    g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
     g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka; g.w = (const uint16_t*)wo;
     g.M = ps.M; g.N = H; g.K = NH * HD; g.c = x; g.ldc = H;
     if (want(cx, EMBER_K_O)) launch_gemm(g, GEMM_RESID, st);
@@ -360,10 +372,12 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   } else if (ps.path == PATH_MFMA) {
     if (want_aux(cx)) launch_rmsnorm(x, ln2, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st);
     GemmArgs g{};
+    g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
     g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka; g.w = (const uint16_t*)wgu;
     g.M = ps.M; g.N = 2 * FF; g.K = H; g.o_hi = pb_hi; g.o_lo = pb_lo; g.ldo = FF;
     if (want(cx, EMBER_K_GATE_UP)) launch_gemm(g, GEMM_SILU, st);
     GemmArgs d{};
+    d.partial = md->splitk(); d.partial_elems = p.splitk_elems;
     d.a_hi = pb_hi; d.a_lo = pb_lo; d.lda = FF; d.w = (const uint16_t*)wd;
     d.M = ps.M; d.N = H; d.K = FF; d.c = x; d.ldc = H;
     if (want(cx, EMBER_K_DOWN)) launch_gemm(d, GEMM_RESID, st);
@@ -419,6 +433,7 @@ void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, lo
         launch_rmsnorm(md->at<float>(p.x), fn, c.rms_eps, rn, H, row_step, off, nullptr, hi, lo,
                        p.ka, st);
       GemmArgs g{};
+      g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
       g.a_hi = hi; g.a_lo = lo; g.lda = p.ka; g.w = (const uint16_t*)E;
       g.M = rn; g.N = V; g.K = H; g.c = out + (size_t)r0 * ld; g.ldc = ld;
       if (want(cx, EMBER_K_LM_HEAD)) launch_gemm(g, GEMM_STORE, st);

@@ -113,6 +113,12 @@ struct GemmArgs {
   uint16_t* o_lo;
   float* o_f32;            // SILU: optional f32 [M, ldo]
   int ldo;
+  // split-K scratch (optional): when the tiles cannot fill the GPU, K is cut into slices
+  // whose f32 partial tiles land here ([slices][M][N]) and a fixed-order sum applies the
+  // epilogue. null: never split.
+  float* partial;
+  size_t partial_elems;
+  int k_chunk;             // set by launch_gemm
 };
 void launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
 

@@ -90,10 +90,13 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
 
   TileLoader<BM> la_hi, la_lo;
   TileLoader<BN> lb;
-  const int nk = (a.K + BK - 1) / BK;
-  la_hi.load(a.a_hi, a.lda, m0, a.M, 0, a.K);
-  if (SPLIT) la_lo.load(a.a_lo, a.lda, m0, a.M, 0, a.K);
-  lb.load(a.w, a.K, n0, a.N, 0, a.K);
+  // K range of this block (split-K over gridDim.y slices of k_chunk columns)
+  const int kb0 = blockIdx.y * a.k_chunk;
+  const int kend = min(a.K, kb0 + a.k_chunk);
+  const int nk = (kend - kb0 + BK - 1) / BK;
+  la_hi.load(a.a_hi, a.lda, m0, a.M, kb0, kend);
+  if (SPLIT) la_lo.load(a.a_lo, a.lda, m0, a.M, kb0, kend);
+  lb.load(a.w, a.K, n0, a.N, kb0, kend);
   la_hi.store(As_hi);
   if (SPLIT) la_lo.store(As_lo);
   lb.store(Bs);
@@ -101,9 +104,9 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
 
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) {
-      la_hi.load(a.a_hi, a.lda, m0, a.M, (kt + 1) * BK, a.K);
-      if (SPLIT) la_lo.load(a.a_lo, a.lda, m0, a.M, (kt + 1) * BK, a.K);
-      lb.load(a.w, a.K, n0, a.N, (kt + 1) * BK, a.K);
+      la_hi.load(a.a_hi, a.lda, m0, a.M, kb0 + (kt + 1) * BK, kend);
+      if (SPLIT) la_lo.load(a.a_lo, a.lda, m0, a.M, kb0 + (kt + 1) * BK, kend);
+      lb.load(a.w, a.K, n0, a.N, kb0 + (kt + 1) * BK, kend);
     }
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 32) {
@@ -135,6 +138,22 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
 
   // epilogue: lane holds C[row0 + e][col] for e < 4 of each 16x16 fragment
   const int rbase = m0 + wm0 + (lane / 16) * 4;
+  if (a.partial) {                         // split-K: raw f32 tile into this slice's plane
+    float* pp = a.partial + (size_t)blockIdx.y * a.M * a.N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wn0 + j * 16 + fr;
+        if (col >= a.N) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = rbase + i * 16 + e;
+          if (row < a.M) pp[(size_t)row * a.N + col] = acc[i][j][e];
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -174,19 +193,67 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
 }
 
 template <int BM, int BN, int WM, int WN, int EPI>
-void launch_cfg(const GemmArgs& a, hipStream_t st) {
+void launch_cfg(const GemmArgs& a, int splits, hipStream_t st) {
   const int blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   if (a.a_lo)
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, true, EPI>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, true, EPI>), dim3(blocks, splits), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, false, EPI>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, false, EPI>), dim3(blocks, splits), dim3(256), 0, st, a);
 }
 
 template <int EPI>
-void launch_epi(const GemmArgs& a, hipStream_t st) {
+void launch_epi(const GemmArgs& a, int splits, hipStream_t st) {
   // small M (decode batches, short prompts): 64-row tiles
-  if (a.M <= 64) launch_cfg<64, 128, 2, 2, EPI>(a, st);
-  else launch_cfg<128, 128, 2, 2, EPI>(a, st);
+  if (a.M <= 64) launch_cfg<64, 128, 2, 2, EPI>(a, splits, st);
+  else launch_cfg<128, 128, 2, 2, EPI>(a, splits, st);
+}
+
+// Fixed-order sum of the split-K partial planes, then the epilogue.
+template <int EPI>
+__global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs a, int splits) {
+  const int nout = EPI == GEMM_SILU ? a.N / 2 : a.N;
+  const size_t total = (size_t)a.M * nout;
+  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total;
+       e += (size_t)gridDim.x * blockDim.x) {
+    const int row = (int)(e / nout), col = (int)(e % nout);
+    if (EPI == GEMM_SILU) {
+      const int gcol = (col / 16) * 32 + (col % 16), ucol = gcol + 16;
+      float g = 0.f, u = 0.f;
+      for (int s = 0; s < splits; ++s) {
+        const float* pp = a.partial + (size_t)s * a.M * a.N + (size_t)row * a.N;
+        g += pp[gcol];
+        u += pp[ucol];
+      }
+      const float v = silu(g) * u;
+      const size_t o = (size_t)row * a.ldo + col;
+      if (a.o_f32) a.o_f32[o] = v;
+      if (a.o_hi) {
+        uint32_t h, l;
+        split_bf16(v, h, l);
+        a.o_hi[o] = (uint16_t)h;
+        if (a.o_lo) a.o_lo[o] = (uint16_t)l;
+      }
+    } else {
+      float acc = 0.f;
+      for (int s = 0; s < splits; ++s) acc += a.partial[(size_t)s * a.M * a.N + (size_t)row * a.N + col];
+      float* cp = a.c + (size_t)row * a.ldc + col;
+      if (EPI == GEMM_RESID) *cp += acc;
+      else *cp = acc + (a.bias ? a.bias[col] : 0.f);
+    }
+  }
+}
+
+// Split K when the tiles cannot fill the GPU: slices of >= 256 columns, about 512 blocks.
+int pick_splits(const GemmArgs& a) {
+  if (!a.partial) return 1;
+  const int BM = a.M <= 64 ? 64 : 128;
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + 127) / 128);
+  if (tiles >= 192) return 1;
+  int s = (512 + tiles - 1) / tiles;
+  const int max_s = a.K / 256;
+  if (s > max_s) s = max_s;
+  if ((size_t)s * a.M * a.N > a.partial_elems) s = (int)(a.partial_elems / ((size_t)a.M * a.N));
+  return s < 2 ? 1 : s;
 }
 
 // ------------------------------------------------------------------ f32-weight VALU GEMM
@@ -217,12 +284,32 @@ __global__ void __launch_bounds__(256) k_gemm_f32w(GemmF32Args a) {
 
 }  // namespace
 
-void launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
-  if (a.M <= 0 || a.N <= 0) return;
+void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
+  if (a0.M <= 0 || a0.N <= 0) return;
+  GemmArgs a = a0;
+  const int splits = pick_splits(a);
+  if (splits <= 1) {
+    a.partial = nullptr;
+    a.k_chunk = a.K;
+    switch (epi) {
+      case GEMM_STORE: launch_epi<GEMM_STORE>(a, 1, st); break;
+      case GEMM_RESID: launch_epi<GEMM_RESID>(a, 1, st); break;
+      case GEMM_SILU: launch_epi<GEMM_SILU>(a, 1, st); break;
+      default: break;
+    }
+    return;
+  }
+  // K slices are whole 64-column stages
+  a.k_chunk = ((a.K + splits - 1) / splits + 63) / 64 * 64;
+  const int used = (a.K + a.k_chunk - 1) / a.k_chunk;
+  launch_epi<GEMM_STORE>(a, used, st);            // partial planes (epilogue skipped)
+  const int nout = epi == GEMM_SILU ? a.N / 2 : a.N;
+  long long blocks = ((long long)a.M * nout + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
   switch (epi) {
-    case GEMM_STORE: launch_epi<GEMM_STORE>(a, st); break;
-    case GEMM_RESID: launch_epi<GEMM_RESID>(a, st); break;
-    case GEMM_SILU: launch_epi<GEMM_SILU>(a, st); break;
+    case GEMM_STORE: hipLaunchKernelGGL(k_splitk_reduce<GEMM_STORE>, dim3((unsigned)blocks), dim3(256), 0, st, a, used); break;
+    case GEMM_RESID: hipLaunchKernelGGL(k_splitk_reduce<GEMM_RESID>, dim3((unsigned)blocks), dim3(256), 0, st, a, used); break;
+    case GEMM_SILU: hipLaunchKernelGGL(k_splitk_reduce<GEMM_SILU>, dim3((unsigned)blocks), dim3(256), 0, st, a, used); break;
     default: break;
   }
 }

@@ -10,8 +10,8 @@ import pytest
 import oracle as O
 import workloads as W
 from tests.gpu_util import TOL_EXACT, TOL_FAST, check_greedy, gpu_generate, rel_maxabs, say
-from tests.small_models import (ENCODER_HD128, ENCODER_SMALL, LLAMA_HD64, LLAMA_SMALL, QWEN_HD64_G7,
-                                QWEN_SMALL, TINY)
+from tests.small_models import (ENCODER_HD128, ENCODER_SMALL, LLAMA_HD64, LLAMA_SMALL, LLAMA_SPLITK,
+                                QWEN_HD64_G7, QWEN_SMALL, TINY)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,8 +34,8 @@ def _sharp(ck, factor=30.0):
 
 # ----------------------------------------------------------------------------- small shapes
 
-@pytest.mark.parametrize("model", [TINY, QWEN_SMALL, LLAMA_SMALL, LLAMA_HD64, QWEN_HD64_G7],
-                         ids=lambda m: m.name)
+@pytest.mark.parametrize("model", [TINY, QWEN_SMALL, LLAMA_SMALL, LLAMA_HD64, QWEN_HD64_G7,
+                                   LLAMA_SPLITK], ids=lambda m: m.name)
 @pytest.mark.parametrize("sharp", [False, True], ids=["init", "peaked"])
 def test_small_decoder_exact_prefill_and_decode(model, sharp):
     from gqa_decoder_transformer_amd import binding as B
@@ -63,7 +63,7 @@ def test_small_decoder_exact_prefill_and_decode(model, sharp):
     assert rel_maxabs(allg[0].cpu().numpy(), full).max() < TOL_EXACT
 
 
-@pytest.mark.parametrize("model", [QWEN_SMALL, LLAMA_SMALL, LLAMA_HD64, QWEN_HD64_G7],
+@pytest.mark.parametrize("model", [QWEN_SMALL, LLAMA_SMALL, LLAMA_HD64, QWEN_HD64_G7, LLAMA_SPLITK],
                          ids=lambda m: m.name)
 @pytest.mark.parametrize("sharp", [1.0, 4.0], ids=["init", "x4"])
 def test_small_decoder_fast_bf16_logits(model, sharp):
