@@ -211,7 +211,10 @@ class Engine:
     forwards calls to the C ABI."""
 
     def __init__(self, cfg: EmberConfig, checkpoint: Dict[str, Tuple[str, np.ndarray]],
-                 device: str = "cuda", stream=None):
+                 device: str = "cuda", stream=None, poison: bool = False):
+        """poison: fill the workspace and the KV cache with 0xFF bytes (NaN as f32 and
+        bf16) before use, so that a read of memory the library has not written shows up
+        as NaN in the results."""
         import torch
         self.torch = torch
         self.cfg = cfg
@@ -224,6 +227,8 @@ class Engine:
             _check(LIB.ember_load_weights(ctypes.byref(cfg), None, 0, None, 0, None,
                                           ctypes.byref(ctypes.c_void_p())))
         self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
+        if poison:
+            self.workspace.fill_(255)
         staged = []
         tensors = []
         for name, (tag, arr) in checkpoint.items():
@@ -243,6 +248,8 @@ class Engine:
         del staged
         kv_bytes = ember_kv_cache_bytes(cfg)
         self.kv = torch.empty(kv_bytes, dtype=torch.uint8, device=self.device)
+        if poison:
+            self.kv.fill_(255)
         self.cache = ember_cache_bind(self.model, self.kv.data_ptr(), kv_bytes)
         self.out_dim = cfg.n_classes if cfg.head_kind == HEAD_CLS else cfg.vocab
 

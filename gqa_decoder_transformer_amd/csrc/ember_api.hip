@@ -55,7 +55,7 @@ struct Plan {
   size_t embed, fnorm, cls_w, cls_b, cos_t, sin_t;
   std::vector<LayerOff> layer;
   // activations
-  size_t ids, pos, next, flags, x, xb, pa_hi, pa_lo, pb_hi, pb_lo, qkv, q, att, act, part,
+  size_t ids, pos, rope_cur, next, flags, x, xb, pa_hi, pa_lo, pb_hi, pb_lo, qkv, q, att, act, part,
       logits, hrow, argpart, splitk;
   size_t splitk_elems;
   size_t total;
@@ -142,6 +142,7 @@ Plan make_plan(const ember_config& c) {
   p.argparts = gemv_num_blocks(c.vocab, GEMV_LOGITS, H, c.weight_dtype == EMBER_BF16);
   p.ids = take((size_t)Mx * 4);
   p.pos = take(4);
+  p.rope_cur = take((size_t)c.head_dim * 4);
   p.next = take((size_t)Mx * 4);
   p.flags = take(kNumFlags * 4);
   p.x = take((size_t)Mx * H * 4);
@@ -278,8 +279,8 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   const void* wd = md->ws + L.wd;
   const float* bqkv = c.qkv_bias ? md->at<float>(L.bqkv) : nullptr;
   const float scale = (float)(1.0 / std::sqrt((double)HD));
-  int nsplit = 1, chunk_min = 64;
-  if (ps.attn == ATTN_DECODE) decode_split_plan(ps.M, NKV, c.max_seq, &nsplit, &chunk_min);
+  DecodePlan dp{1, c.max_seq, NH / NKV};
+  if (ps.attn == ATTN_DECODE) dp = decode_split_plan(ps.M, NH, NKV, c.max_seq);
 
   // ---- attention block
   if (ps.path == PATH_GEMV) {
@@ -329,17 +330,19 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     }
   } else {
     DecodeAttnArgs da{};
-    da.qkv = qkv; da.cos_t = qa.cos_t; da.sin_t = qa.sin_t; da.q_norm = qa.q_norm;
+    da.qkv = qkv; da.rope_cur = md->at<float>(p.rope_cur); da.q_norm = qa.q_norm;
     da.k_norm = qa.k_norm; da.eps = c.rms_eps;
     da.k_cache = qa.k_cache; da.v_cache = qa.v_cache; da.kv_bf16 = qa.kv_bf16;
     da.B = ps.M; da.NH = NH; da.NKV = NKV; da.HD = HD; da.max_seq = c.max_seq;
-    da.d_pos = ps.d_pos; da.nsplit = nsplit; da.chunk_min = chunk_min; da.scale = scale;
-    da.part = part;
+    da.d_pos = ps.d_pos; da.nsplit = dp.nsplit; da.chunk_min = dp.chunk_min; da.scale = scale;
+    da.part = part; da.heads_per_block = dp.heads_per_block;
+    da.out_f32 = planes_out ? nullptr : att;
+    da.out_hi = planes_out ? pa_hi : nullptr;
+    da.out_lo = planes_out ? pa_lo : nullptr;
     if (want(cx, EMBER_K_ATTN)) launch_decode_attn(da, st);
-    if (want_aux(cx))
-      launch_attn_combine(part, ps.M, NH, HD, nsplit, ps.d_pos, chunk_min,
-                          planes_out ? nullptr : att, planes_out ? pa_hi : nullptr,
-                          planes_out ? pa_lo : nullptr, st);
+    if (want_aux(cx) && dp.nsplit > 1)
+      launch_attn_combine(part, ps.M, NH, HD, dp.nsplit, ps.d_pos, dp.chunk_min,
+                          da.out_f32, da.out_hi, da.out_lo, st);
   }
 
   if (ps.path == PATH_GEMV) {
@@ -761,7 +764,8 @@ ember_status ember_decode_step(ember_model* md, ember_cache* cache, const int32_
   const Plan& p = md->plan;
   Ctx cx{md, cache, st};
   launch_stage_step(d_ids, batch, c.vocab, pos, md->at<int32_t>(p.ids), md->at<int>(p.pos),
-                    md->at<int>(p.flags), st);
+                    md->at<int>(p.flags), md->at<float>(p.cos_t), md->at<float>(p.sin_t),
+                    c.head_dim / 2, md->at<float>(p.rope_cur), st);
   const bool use_graph = st != nullptr && graphs_enabled();
   if (use_graph) {
     if (!md->graph || md->graph_cache != cache || md->graph_batch != batch || md->graph_stream != st) {
@@ -806,7 +810,7 @@ ember_status ember_time_kernel(ember_model* md, ember_cache* cache, int32_t kern
   auto enqueue = [&](int n) -> ember_status {
     if (phase == 0) {
       if (md->last_decode_batch <= 0) return fail(EMBER_E_STATE, "no decode step has run");
-      for (int i = 0; i < n; ++i) decode_body(cx, md->last_decode_batch, 0);
+      for (int i = 0; i < n; ++i) decode_body(cx, md->last_decode_batch, i % c.layers);
     } else {
       if (md->last_pass.M <= 0) return fail(EMBER_E_STATE, "no prefill has run");
       Pass ps{};
@@ -818,7 +822,7 @@ ember_status ember_time_kernel(ember_model* md, ember_cache* cache, int32_t kern
         if (kernel == EMBER_K_LM_HEAD)
           run_lm_head(cx, ps.rows, ps.tpr, ps.tpr - 1, md->at<float>(p.logits), c.vocab, nullptr);
         else
-          run_layer(cx, 0, ps);
+          run_layer(cx, i % c.layers, ps);
       }
     }
     return EMBER_OK;

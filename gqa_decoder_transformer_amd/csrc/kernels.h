@@ -64,7 +64,8 @@ void launch_convert_logits(const float* src, int R, int n, long long ld, void* d
 // Stage a decode step: ids_internal[r] = ids[r] (out-of-range ids -> 0 + flag) and
 // *d_pos = pos.
 void launch_stage_step(const int32_t* ids, int R, int V, int pos, int32_t* ids_internal,
-                       int* d_pos, int* flags, hipStream_t st);
+                       int* d_pos, int* flags, const float* cos_t, const float* sin_t, int half,
+                       float* rope_cur, hipStream_t st);
 void launch_copy_ids(const int32_t* src, int n, int32_t* dst, hipStream_t st);
 void launch_fill_i32(int* p, int n, int v, hipStream_t st);
 // dst[i] = widen(src[i]) for i < n (bf16 or f32 source).
@@ -158,8 +159,7 @@ void launch_flash_mfma(const FlashArgs& a, bool split, hipStream_t st);
 
 struct DecodeAttnArgs {
   const float* qkv;        // [B, (NH + 2 NKV) HD] raw projections of the current token
-  const float* cos_t;      // [max_seq, HD/2]
-  const float* sin_t;
+  const float* rope_cur;   // cos[HD/2], sin[HD/2] of the current position
   const float* q_norm;     // [HD] or null
   const float* k_norm;
   float eps;
@@ -168,9 +168,13 @@ struct DecodeAttnArgs {
   bool kv_bf16;
   int B, NH, NKV, HD, max_seq;
   const int* d_pos;        // current position; keys 0..*d_pos
-  int nsplit, chunk_min;
+  int nsplit, chunk_min;   // nsplit == 1 or chunk_min >= ceil(max_seq / nsplit)
   float scale;
   float* part;             // [B][NH][nsplit][HD + 2] split partials (m, l, acc)
+  float* out_f32;          // nsplit == 1: the normalised output [B, NH*HD] (f32 and/or
+  uint16_t* out_hi;        // bf16 planes) is written directly and no combine follows
+  uint16_t* out_lo;
+  int heads_per_block;     // 1 or NH / NKV (a whole kv group per block)
 };
 // Split-K decode attention with the QKV epilogue (q/k norm, RoPE, K/V store at the
 // current position) fused in.
@@ -180,7 +184,9 @@ void launch_attn_combine(const float* part, int B, int NH, int HD, int nsplit, c
                          int chunk_min, float* out_f32, uint16_t* out_hi, uint16_t* out_lo,
                          hipStream_t st);
 
-// number of splits and minimum chunk used for decode attention
-void decode_split_plan(int B, int NKV, int max_seq, int* nsplit, int* chunk_min);
+// Launch plan of decode attention: number of splits (1: no combine), minimum chunk of
+// keys per split, threads per block.
+struct DecodePlan { int nsplit, chunk_min, heads_per_block; };
+DecodePlan decode_split_plan(int B, int NH, int NKV, int max_seq);
 
 }  // namespace ember

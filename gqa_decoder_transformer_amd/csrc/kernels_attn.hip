@@ -95,10 +95,13 @@ __global__ void __launch_bounds__(256) k_flash_prefill(FlashArgs a) {
 }
 
 // ------------------------------------------------------------------ split-K decode
-// Block (split, kv head, row): the G query heads of the group share every K/V read.
-// The block first issues its K/V loads (cache positions < pos), then builds the
+// Block (split, head block, row): G query heads of one kv group, either the whole group
+// (every K/V read shared by G heads: bandwidth-bound grids) or one head (short
+// per-wave instruction streams when the grid is small; the group's other heads re-read
+// the same keys through L2). The block first issues its K/V loads, then builds the
 // current token's roped q (G heads) and -- in the split that holds position pos -- the
-// roped k and v, which it also stores into the cache at pos (qkv epilogue fused: q/k
+// roped k and v, which the group's first head block also stores into the cache at pos
+// (qkv epilogue fused: q/k
 // RMSNorm when configured, rotate-half RoPE from the tables, K/V store at the explicit
 // position). A group of LPK lanes reads one key (16 bytes per lane); per head the
 // partial dot products are summed with lane shuffles and each lane group keeps an online
@@ -113,43 +116,50 @@ EMBER_DEV void split_range(int S, int nsplit, int chunk_min, int split, int& s0,
 
 template <int HD, bool KV_BF16, int G>
 __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
+  constexpr int NT = 256;
   constexpr int ES = KV_BF16 ? 2 : 4;
   constexpr int DPL = 16 / ES;                 // dims per lane
   constexpr int LPK = HD / DPL;                // lanes per key
   static_assert(LPK >= 1 && LPK <= 64, "head_dim");
   constexpr int KPW = kWave / LPK;             // keys per wave pass
-  constexpr int NGRP = 4 * KPW;                // lane groups per block
-  constexpr int KI = G > 4 ? 2 : 4;            // keys per group per batch
+  constexpr int NGRP = (NT / kWave) * KPW;     // lane groups per block
+  // keys per group per batch (fewer for wide bf16 groups: 256 VGPRs per lane)
+  constexpr int KI = (KV_BF16 && G > 4) ? 2 : 4;
   constexpr int HALF = HD / 2;
   constexpr bool ONE_PASS = NGRP * G * (HD + 2) * 4 <= 48 * 1024;
   constexpr int MG = ONE_PASS ? G : 1;
   __shared__ float qs[G * HD];
   __shared__ float kc[HD], vc[HD];
   __shared__ float cs[HALF], sn[HALF];
-  __shared__ float sm[NGRP * MG], sl[NGRP * MG];
+  __shared__ float sm[NGRP * MG], sl[NGRP * MG], smax[MG];
   __shared__ float sacc[NGRP * MG * HD];
 
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int pos = *a.d_pos;
-  const int S = pos + 1;
-  int s0, s1;
-  split_range(S, a.nsplit, a.chunk_min, split, s0, s1);
-  if (s0 >= S) return;                         // beyond the valid splits: never read
-  const bool has_cur = s1 == S;
+  const int split = blockIdx.x, b = blockIdx.z;
+  const int group = a.NH / a.NKV;
+  const int h0 = blockIdx.y * G;               // first query head of this block
+  const int kvh = h0 / group;
+  const bool kv_writer = h0 % group == 0;
+  // The key range of a split does not depend on the position (chunk_min is at least
+  // ceil(max_seq / nsplit)), so the first K/V batch is issued before the position is
+  // known; keys at or past the position are masked afterwards.
+  const int s0 = split * a.chunk_min;
+  const int s_hi = min(a.max_seq, s0 + a.chunk_min);
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int grp = wave * KPW + lane / LPK;     // 0..NGRP-1
   const int sub = lane % LPK;
   const size_t base = ((size_t)b * a.NKV + kvh) * a.max_seq * HD;
-  const int nkeys = s1 - s0 - grp > 0 ? (s1 - s0 - grp + NGRP - 1) / NGRP : 0;
-  const int nb = (nkeys + KI - 1) / KI;
+  auto batches = [&](int end) {
+    const int nkeys = end - s0 - grp > 0 ? (end - s0 - grp + NGRP - 1) / NGRP : 0;
+    return (nkeys + KI - 1) / KI;
+  };
 
   u32x4_t kb0[KI], vb0[KI], kb1[KI], vb1[KI];
   auto load = [&](int batch, u32x4_t* kb, u32x4_t* vb) {
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int key = s0 + grp + NGRP * (batch * KI + i);
-      if (key < s1 && key != pos) {
+      if (key < s_hi) {
         const size_t off = base + (size_t)key * HD + sub * DPL;
         if (KV_BF16) {
           kb[i] = *(const u32x4_t*)((const uint16_t*)a.k_cache + off);
@@ -161,17 +171,23 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
       }
     }
   };
-  if (nb > 0) load(0, kb0, vb0);
+  if (batches(s_hi) > 0) load(0, kb0, vb0);
 
-  // current token: raw q (G heads) and, in the last split, raw k/v of head kvh
+  // current token: raw q (G heads), this step's RoPE row and, in the split that holds
+  // the position, raw k/v of head kvh
   const int qkv_n = (a.NH + 2 * a.NKV) * HD;
   const float* row = a.qkv + (size_t)b * qkv_n;
-  const int h0 = kvh * G;
   for (int e = threadIdx.x; e < G * HD; e += blockDim.x) qs[e] = row[h0 * HD + e];
   for (int e = threadIdx.x; e < HALF; e += blockDim.x) {
-    cs[e] = a.cos_t[(size_t)pos * HALF + e];
-    sn[e] = a.sin_t[(size_t)pos * HALF + e];
+    cs[e] = a.rope_cur[e];
+    sn[e] = a.rope_cur[HALF + e];
   }
+  const int pos = *a.d_pos;
+  const int S = pos + 1;
+  if (s0 >= S) return;                         // beyond the valid splits: never read
+  const int s1 = min(S, s_hi);
+  const bool has_cur = s1 == S;
+  const int nb = batches(s1);
   if (has_cur)
     for (int e = threadIdx.x; e < HD; e += blockDim.x) {
       kc[e] = row[(a.NH + kvh) * HD + e];
@@ -181,11 +197,11 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
   // RoPE (and q/k norm) in place: pair e (thread e + 256 j) is pair e % HALF of head
   // e / HALF, head G being the current key
   const int npairs = (G + (has_cur ? 1 : 0)) * HALF;
-  constexpr int PJ = ((G + 1) * HALF + 255) / 256;
+  constexpr int PJ = ((G + 1) * HALF + NT - 1) / NT;
   float y0[PJ], y1[PJ];
 #pragma unroll
   for (int j = 0; j < PJ; ++j) {
-    const int e = threadIdx.x + 256 * j;
+    const int e = threadIdx.x + NT * j;
     if (e >= npairs) continue;
     const int hh = e / HALF, i = e % HALF;
     const float* src = hh < G ? qs + hh * HD : kc;
@@ -204,7 +220,7 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < PJ; ++j) {
-    const int e = threadIdx.x + 256 * j;
+    const int e = threadIdx.x + NT * j;
     if (e >= npairs) continue;
     const int hh = e / HALF, i = e % HALF;
     float* dst = hh < G ? qs + hh * HD : kc;
@@ -219,7 +235,7 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
   if (has_cur && KV_BF16)
     for (int e = threadIdx.x; e < HD; e += blockDim.x) vc[e] = bf16_to_f32(f32_to_bf16_rne(vc[e]));
   __syncthreads();
-  if (has_cur) {                               // store this token's K/V at position pos
+  if (has_cur && kv_writer) {                  // store this token's K/V at position pos
     const size_t off = base + (size_t)pos * HD;
     for (int e = threadIdx.x; e < HD; e += blockDim.x) {
       if (KV_BF16) {
@@ -257,6 +273,9 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
       if (key == pos) {
 #pragma unroll
         for (int d = 0; d < DPL; ++d) { kf[i][d] = kc[sub * DPL + d]; vf[i][d] = vc[sub * DPL + d]; }
+      } else if (!valid[i]) {                  // never-written or stale entries: zeros
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) { kf[i][d] = 0.f; vf[i][d] = 0.f; }
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -307,7 +326,8 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
     compute(bt + 1, kb1, vb1);
   }
 
-  // merge lane groups through LDS (fixed order)
+  // merge lane groups through LDS (fixed order): per head the group weights
+  // w_i = e^{m_i - M} once, then every output dimension sums acc_i w_i over the groups
   const int h_base = b * a.NH + h0;
   for (int g0 = 0; g0 < G; g0 += MG) {
 #pragma unroll
@@ -321,22 +341,41 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
       for (int d = 0; d < DPL; ++d) sacc[(grp * MG + gg) * HD + sub * DPL + d] = acc[g][d];
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < MG * HD; e += blockDim.x) {
-      const int gg = e / HD, d = e % HD;
+    if (threadIdx.x < MG) {
+      const int gg = threadIdx.x;
       float M = -INFINITY;
       for (int i = 0; i < NGRP; ++i) M = fmaxf(M, sm[i * MG + gg]);
+      smax[gg] = M;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < NGRP * MG; e += blockDim.x) {
+      const float M = smax[e % MG];
+      sm[e] = (M == -INFINITY || sm[e] == -INFINITY) ? 0.f : expf(sm[e] - M);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < MG * HD; e += blockDim.x) {
+      const int gg = e / HD, d = e % HD;
       float L = 0.f, A = 0.f;
-      if (M != -INFINITY) {
-        for (int i = 0; i < NGRP; ++i) {
-          const float mi = sm[i * MG + gg];
-          const float w = (mi == -INFINITY) ? 0.f : expf(mi - M);
-          L += sl[i * MG + gg] * w;
-          A += sacc[(i * MG + gg) * HD + d] * w;
-        }
+      for (int i = 0; i < NGRP; ++i) {
+        const float w = sm[i * MG + gg];
+        L = fmaf(sl[i * MG + gg], w, L);
+        A = fmaf(sacc[(i * MG + gg) * HD + d], w, A);
       }
-      float* out = a.part + (((size_t)(h_base + g0 + gg)) * a.nsplit + split) * (HD + 2);
-      if (d == 0) { out[0] = M; out[1] = L; }
-      out[2 + d] = A;
+      if (a.nsplit == 1) {                     // the only split: final, normalised
+        const float v = L > 0.f ? A / L : 0.f;
+        const size_t o = (size_t)(h_base + g0 + gg) * HD + d;
+        if (a.out_f32) a.out_f32[o] = v;
+        if (a.out_hi) {
+          uint32_t hi, lo;
+          split_bf16(v, hi, lo);
+          a.out_hi[o] = (uint16_t)hi;
+          if (a.out_lo) a.out_lo[o] = (uint16_t)lo;
+        }
+      } else {
+        float* out = a.part + (((size_t)(h_base + g0 + gg)) * a.nsplit + split) * (HD + 2);
+        if (d == 0) { out[0] = smax[gg]; out[1] = L; }
+        out[2 + d] = A;
+      }
     }
     __syncthreads();
   }
@@ -344,40 +383,39 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
 }
 
 // Combine of the split partials of one (row, head):
-// att = sum_j acc_j w_j / L, w_j = e^{m_j - M}, M = max_j m_j, L = sum_j l_j w_j,
-// the per-split weights computed once per head in LDS.
+// att = sum_j acc_j w_j / L, w_j = e^{m_j - M}, M = max_j m_j, L = sum_j l_j w_j.
+// Every split's partial is staged in LDS before the position is read (the loads do not
+// wait for it); only the splits that hold a key up to the position are summed.
+constexpr int kCombineMaxElems = 64 * (128 + 2);
 __global__ void __launch_bounds__(128) k_attn_combine(const float* part, int NH, int HD,
                                                       int nsplit, const int* d_pos, int chunk_min,
                                                       float* out_f32, uint16_t* out_hi,
                                                       uint16_t* out_lo) {
-  __shared__ float w[64], lsum[64];
+  __shared__ float sp[kCombineMaxElems];
+  __shared__ float w[64];
   __shared__ float inv_l;
   const int bh = blockIdx.x;                   // b * NH + h
+  const int stride = HD + 2;
+  const float* ph = part + (size_t)bh * nsplit * stride;
+  for (int e = threadIdx.x; e < nsplit * stride; e += blockDim.x) sp[e] = ph[e];
   const int S = *d_pos + 1;
   int chunk = (S + nsplit - 1) / nsplit;
   if (chunk < chunk_min) chunk = chunk_min;
   const int nv = (S + chunk - 1) / chunk;
-  const int stride = HD + 2;
-  const float* ph = part + (size_t)bh * nsplit * stride;
-  for (int j = threadIdx.x; j < nv; j += blockDim.x) {
-    w[j] = ph[(size_t)j * stride];
-    lsum[j] = ph[(size_t)j * stride + 1];
-  }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float M = -INFINITY;
-    for (int j = 0; j < nv; ++j) M = fmaxf(M, w[j]);
-    float L = 0.f;
-    for (int j = 0; j < nv; ++j) {
-      w[j] = w[j] == -INFINITY ? 0.f : expf(w[j] - M);
-      L += lsum[j] * w[j];
-    }
-    inv_l = L > 0.f ? 1.f / L : 0.f;
+  if (threadIdx.x < kWave) {                   // split j on lane j (nsplit <= 64)
+    const int j = threadIdx.x;
+    const float mj = j < nv ? sp[j * stride] : -INFINITY;
+    const float M = wave_max(mj);
+    const float wj = (mj == -INFINITY) ? 0.f : expf(mj - M);
+    const float L = wave_sum(j < nv ? sp[j * stride + 1] * wj : 0.f);
+    w[j] = wj;
+    if (j == 0) inv_l = L > 0.f ? 1.f / L : 0.f;
   }
   __syncthreads();
   for (int d = threadIdx.x; d < HD; d += blockDim.x) {
     float acc = 0.f;
-    for (int j = 0; j < nv; ++j) acc = fmaf(ph[(size_t)j * stride + 2 + d], w[j], acc);
+    for (int j = 0; j < nv; ++j) acc = fmaf(sp[j * stride + 2 + d], w[j], acc);
     const float v = acc * inv_l;
     const size_t o = (size_t)bh * HD + d;
     if (out_f32) out_f32[o] = v;
@@ -392,8 +430,8 @@ __global__ void __launch_bounds__(128) k_attn_combine(const float* part, int NH,
 
 template <int HD, bool BF>
 void launch_decode_hd(const DecodeAttnArgs& a, hipStream_t st) {
-  const int G = a.NH / a.NKV;
-  dim3 grid(a.nsplit, a.NKV, a.B);
+  const int G = a.heads_per_block;
+  dim3 grid(a.nsplit, a.NH / G, a.B);
 #define EMBER_G(GV) \
   case GV: hipLaunchKernelGGL((k_decode_attn<HD, BF, GV>), grid, dim3(256), 0, st, a); break;
   switch (G) {
@@ -438,18 +476,28 @@ void launch_attn_combine(const float* part, int B, int NH, int HD, int nsplit, c
                      chunk_min, out_f32, out_hi, out_lo);
 }
 
-void decode_split_plan(int B, int NKV, int max_seq, int* nsplit, int* chunk_min) {
-  // enough blocks to cover the CUs for one row, more for batches; chunks >= 64 keys,
-  // at most 64 splits (the one-row combine keeps per-split weights in LDS)
-  const int cmin = 64;
-  const int target_blocks = B == 1 ? 256 : 2048;
-  int target = (target_blocks + NKV * B - 1) / (NKV * B);
-  int maxs = (max_seq + cmin - 1) / cmin;
-  int ns = target < maxs ? target : maxs;
+DecodePlan decode_split_plan(int B, int NH, int NKV, int max_seq) {
+  // Keys are split so that the grid covers the CUs: chunks of >= 64 keys, at most 64
+  // splits (the combine keeps per-split weights in LDS). Few (row, head) pairs: one
+  // query head per block, about 512 blocks; otherwise a whole kv group per block
+  // (every K/V byte read once), about 256 blocks for one row and 2048 for batches.
+  DecodePlan p{1, max_seq, NH / NKV};
+  const int maxs = (max_seq + 63) / 64;
+  int ns;
+  if (B * NH <= 64) {
+    p.heads_per_block = 1;
+    ns = (512 + B * NH - 1) / (B * NH);
+  } else {
+    const int target_blocks = B == 1 ? 256 : 2048;
+    ns = (target_blocks + NKV * B - 1) / (NKV * B);
+  }
+  if (ns > maxs) ns = maxs;
   if (ns > 64) ns = 64;
-  if (ns < 1) ns = 1;
-  *nsplit = ns;
-  *chunk_min = cmin;
+  if (ns >= 2) {
+    p.nsplit = ns;
+    p.chunk_min = (max_seq + ns - 1) / ns;     // fixed ranges: split j holds [j c, j c + c)
+  }
+  return p;
 }
 
 }  // namespace ember

@@ -268,10 +268,18 @@ void launch_convert_logits(const float* src, int R, int n, long long ld, void* d
                      (int)to_bf16);
 }
 
+// Per decode step: position, validated ids, and the RoPE row of the position (cos, sin)
+// copied to a fixed place so that the step's kernels can read it without first reading
+// the position.
 __global__ void k_stage_step(const int32_t* ids, int R, int V, int pos, int32_t* ids_internal,
-                             int* d_pos, int* flags) {
+                             int* d_pos, int* flags, const float* cos_t, const float* sin_t,
+                             int half, float* rope_cur) {
   const int r = threadIdx.x + blockIdx.x * blockDim.x;
   if (r == 0) *d_pos = pos;
+  if (r < half) {
+    rope_cur[r] = cos_t[(size_t)pos * half + r];
+    rope_cur[half + r] = sin_t[(size_t)pos * half + r];
+  }
   if (r < R) {
     int id = ids[r];
     if (id < 0 || id >= V) {
@@ -283,9 +291,11 @@ __global__ void k_stage_step(const int32_t* ids, int R, int V, int pos, int32_t*
 }
 
 void launch_stage_step(const int32_t* ids, int R, int V, int pos, int32_t* ids_internal, int* d_pos,
-                       int* flags, hipStream_t st) {
-  hipLaunchKernelGGL(k_stage_step, dim3((R + 255) / 256), dim3(256), 0, st, ids, R, V, pos,
-                     ids_internal, d_pos, flags);
+                       int* flags, const float* cos_t, const float* sin_t, int half,
+                       float* rope_cur, hipStream_t st) {
+  const int n = R > half ? R : half;
+  hipLaunchKernelGGL(k_stage_step, dim3((n + 255) / 256), dim3(256), 0, st, ids, R, V, pos,
+                     ids_internal, d_pos, flags, cos_t, sin_t, half, rope_cur);
 }
 
 __global__ void k_copy_ids(const int32_t* src, int n, int32_t* dst) {

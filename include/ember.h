@@ -171,8 +171,8 @@ ember_status ember_rope_table(const ember_config* cfg, int32_t n_pos, float* h_c
                               float* h_sin);
 
 /* Measurement support (not part of the forward pass): the kernels of one step that
- * ember_time_kernel can time. Layer-0 instances; the projection kinds time the GEMV of
- * a one-row decode step or the MFMA GEMM of a multi-row pass. */
+ * ember_time_kernel can time. The projection kinds time the GEMV of a one-row decode
+ * step or the MFMA GEMM of a multi-row pass. */
 typedef enum ember_kernel {
   EMBER_K_LM_HEAD = 0,         /* tied LM head over the vocabulary (+ argmax partials) */
   EMBER_K_QKV = 1,             /* fused QKV projection (+ bias; RMSNorm fused in the GEMV) */
@@ -183,11 +183,12 @@ typedef enum ember_kernel {
 } ember_kernel;
 
 /* Launch kernel `kernel` of the most recent decode step (phase 0) or prefill pass
- * (phase 1) `iters` times back to back on `stream`, with that step's launch arguments,
+ * (phase 1) `iters` times back to back on `stream`, launch i on layer i mod layers (so
+ * the weights stream from HBM as in a real step), with that step's launch arguments,
  * between two HIP events recorded on `stream`, and return the mean duration per launch
- * in microseconds. The repeated launches may leave activations and logits of the model
- * modified (residual-add kernels accumulate); the KV cache is not touched except by
- * re-writing the same values. EMBER_E_STATE if no such step has run. */
+ * in microseconds. The launches work on the model's own buffers: afterwards the
+ * activations, logits and the cache entries of the step's positions are unspecified, so
+ * time only a finished sequence. EMBER_E_STATE if no such step has run. */
 ember_status ember_time_kernel(ember_model* model, ember_cache* cache, int32_t kernel,
                                int32_t phase, int32_t iters, void* stream, float* avg_us);
 

@@ -17,10 +17,12 @@ pytestmark = pytest.mark.gpu
 
 
 def _engine(model, ck, precision, max_batch=1, max_seq=64, max_tokens=None, kv_dtype=None):
+    # workspace and cache start as NaN bytes: a read of memory the library has not
+    # written turns into a NaN failure instead of passing on zeroed memory
     from gqa_decoder_transformer_amd import binding as B
     cfg = B.make_config(model, precision=precision, kv_dtype=kv_dtype, max_batch=max_batch,
                         max_seq=max_seq, max_tokens=max_tokens or max_batch * max_seq)
-    return B.Engine(cfg, ck)
+    return B.Engine(cfg, ck, poison=True)
 
 
 def _sharp(ck, factor=30.0):
@@ -160,7 +162,7 @@ def test_graph_replayed_decode_equals_direct_launches():
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         cfg = B.make_config(model, precision=B.EXACT, max_batch=2, max_seq=64, max_tokens=128)
-        eng = B.Engine(cfg, ck, stream=s)
+        eng = B.Engine(cfg, ck, stream=s, poison=True)
         graphed = gpu_generate(eng, prompt, 7)
     torch.cuda.synchronize()
     assert np.array_equal(direct[0], graphed[0])
@@ -168,7 +170,7 @@ def test_graph_replayed_decode_equals_direct_launches():
     one = gpu_generate(_engine(model, ck, B.EXACT, max_batch=1), prompt[:1], 7)
     with torch.cuda.stream(s):
         eng1 = B.Engine(B.make_config(model, precision=B.EXACT, max_batch=1, max_seq=64,
-                                      max_tokens=64), ck, stream=s)
+                                      max_tokens=64), ck, stream=s, poison=True)
         g1 = gpu_generate(eng1, prompt[:1], 7)
     torch.cuda.synchronize()
     assert np.array_equal(one[1].view(np.uint32), g1[1].view(np.uint32))
@@ -229,7 +231,7 @@ def _workload_case(name, steps=None, precision=None):
     say(f"oracle done for {name}")
     cfg = B.make_config(w.model, precision=prec, max_batch=w.batch, max_seq=w.max_pos,
                         max_tokens=w.batch * w.prompt_len)
-    eng = B.Engine(cfg, ck)
+    eng = B.Engine(cfg, ck, poison=True)
     return eng, prompt, n, or_ids, or_logits
 
 
@@ -310,7 +312,7 @@ def test_encoder_workload_sampled_rows(prec_name):
     ids = W.make_ids(w)
     cfg = B.make_config(w.model, precision=prec, max_batch=w.batch, max_seq=w.prompt_len,
                         max_tokens=w.batch * w.prompt_len)
-    eng = B.Engine(cfg, ck)
+    eng = B.Engine(cfg, ck, poison=True)
     say(f"encoder workload 16x512 precision={prec_name}")
     nxt, allg = eng.prefill(ids, all_logits=True)
     g = allg.cpu().numpy()
@@ -351,7 +353,7 @@ def test_longctx_workload_sampled_rows(prec_name):
     del om
     cfg = B.make_config(w.model, precision=prec, max_batch=w.batch, max_seq=w.max_pos,
                         max_tokens=w.prompt_len)
-    eng = B.Engine(cfg, ck)
+    eng = B.Engine(cfg, ck, poison=True)
     say(f"longctx GPU prefill 64 x 8192 precision={prec_name}")
     eng.prefill(ids)
     logs = [eng.logits(w.batch, B.F32 if prec == B.EXACT else B.BF16).float().cpu().numpy()]
