@@ -89,7 +89,7 @@ ember_status validate_config(const ember_config* c) {
     return fail(EMBER_E_CONFIG, "n_classes must be in 1..64");
   if (c->head_kind == EMBER_HEAD_TIED_LM && !c->causal)
     return fail(EMBER_E_CONFIG, "a tied LM head needs a causal model");
-  if (c->ffn % 16 != 0) return fail(EMBER_E_CONFIG, "ffn must be a multiple of 16");
+  if (c->ffn % kGuBlock != 0) return fail(EMBER_E_CONFIG, "ffn must be a multiple of %d", kGuBlock);
   const int K8 = c->weight_dtype == EMBER_BF16 ? 8 : 4;
   if (c->hidden % K8 || c->ffn % K8 || (c->heads * hd) % K8)
     return fail(EMBER_E_CONFIG, "hidden, ffn and heads*head_dim must be multiples of %d", K8);
@@ -533,6 +533,7 @@ ember_status ember_load_weights(const ember_config* cfg, const ember_tensor* ten
   if (!d_workspace || (n_tensors > 0 && !tensors)) return fail(EMBER_E_ARG, "NULL pointer");
   const ember_config& c = *cfg;
   Plan plan = make_plan(c);
+  gemm_init();
   if (workspace_bytes < plan.total)
     return fail(EMBER_E_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes, plan.total);
 
@@ -620,11 +621,11 @@ ember_status ember_load_weights(const ember_config* cfg, const ember_tensor* ten
       launch_widen(t.qn->data, bf, (float*)(ws + L.qn), HD, st);
       launch_widen(t.kn->data, bf, (float*)(ws + L.kn), HD, st);
     }
-    // gate/up rows interleaved in blocks of 16: [g 0..15][u 0..15][g 16..31][u 16..31]...
-    const size_t blk = (size_t)16 * H * es;
-    HIP_TRY(hipMemcpy2DAsync(ws + L.wgu, 2 * blk, t.g->data, blk, blk, FF / 16,
+    // gate/up rows interleaved in blocks of kGuBlock (see gu_row)
+    const size_t blk = (size_t)kGuBlock * H * es;
+    HIP_TRY(hipMemcpy2DAsync(ws + L.wgu, 2 * blk, t.g->data, blk, blk, FF / kGuBlock,
                              hipMemcpyDeviceToDevice, st));
-    HIP_TRY(hipMemcpy2DAsync(ws + L.wgu + blk, 2 * blk, t.u->data, blk, blk, FF / 16,
+    HIP_TRY(hipMemcpy2DAsync(ws + L.wgu + blk, 2 * blk, t.u->data, blk, blk, FF / kGuBlock,
                              hipMemcpyDeviceToDevice, st));
     HIP_TRY(copy(L.wd, t.d, (size_t)H * FF * es));
   }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#define EMBER_INLINE_HD __host__ __device__ inline
+
 namespace ember {
 
 // Flags raised by kernels and reported by ember_sync.
@@ -73,6 +75,14 @@ void launch_widen(const void* src, bool bf16, float* dst, long long n, hipStream
 
 // ------------------------------------------------------------------ GEMV (kernels_gemv.hip)
 
+// The gate and up projections are stored as one matrix of 2*FF rows, interleaved in
+// blocks of kGuBlock rows: [g 0..31][u 0..31][g 32..63][u 32..63]... (one 32-column MFMA
+// fragment of gate outputs is followed by the fragment of the matching up outputs).
+constexpr int kGuBlock = 32;
+EMBER_INLINE_HD int gu_row(int n, int up) {
+  return (n / kGuBlock) * 2 * kGuBlock + (up ? kGuBlock : 0) + n % kGuBlock;
+}
+
 enum GemvEpi { GEMV_STORE = 0, GEMV_RESID = 1, GEMV_SILU = 2, GEMV_LOGITS = 3 };
 
 struct GemvArgs {
@@ -122,6 +132,8 @@ struct GemmArgs {
   int k_chunk;             // set by launch_gemm
 };
 void launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
+// Sets the dynamic LDS limit of every GEMM kernel (call once before the first launch).
+void gemm_init();
 
 // f32-weight path (VALU), same epilogues; A is f32 [M, lda].
 struct GemmF32Args {

@@ -1,20 +1,24 @@
 // Prefill GEMM: C[M, N] = A[M, K] . W[N, K]^T with bf16 weights on gfx950 MFMA
-// (v_mfma_f32_16x16x32_bf16), f32 accumulation.
+// (v_mfma_f32_32x32x16_bf16), f32 accumulation.
 //
 // A (activations) arrives as bf16 planes written by the producing kernel: in EXACT mode
 // x = hi + lo (hi = bf16(x), lo = bf16(x - hi)) and every weight fragment is multiplied
 // by both planes, which makes each product f32-accurate to ~2^-17 relative (the weights
 // are exactly bf16, and bf16 x bf16 products are exact in f32); in FAST mode only hi.
 //
-// Tiling: 256 threads (4 waves, WM x WN), block tile BM x BN, K-stage 64. Global ->
-// registers (16-byte loads, next stage prefetched during the MFMAs of the current
-// one) -> LDS (rows padded by 16 bytes: the 16 rows a fragment read touches fall on
-// distinct banks) -> MFMA fragments. Blocks are remapped so that consecutive tiles of
-// one weight column block run on the same XCD (its L2 serves the repeated weight reads).
+// Tiling: 256 threads (4 waves, 2 x 2), block tile BM x BN, K stage 64. Global loads are
+// 16 bytes per lane, 8 lanes per 128-byte row segment, and run PF stages ahead in
+// registers; the LDS holds two stages (rows padded by 16 bytes, so the 32 rows a
+// fragment read touches fall on distinct banks). Each wave computes (BM/2) x (BN/2) with
+// 32x32x16 MFMAs and reads the fragments of k-step t + 1 while the MFMAs of step t run
+// (scheduling groups pin that interleave, and put the next stage's LDS stores under the
+// last step's MFMAs). Blocks are remapped so that consecutive tiles of one weight column
+// block run on the same XCD (its L2 serves the repeated weight reads).
 //
 // Epilogues: store (+bias), residual add (x += C), SiLU*up over the gate/up rows that
-// the weight repack interleaves in blocks of 16 (the lane holding gate column j holds
-// the matching up column in the next 16-column fragment).
+// the weight repack interleaves in blocks of 32 (the lane holding gate column j of
+// fragment 2q holds the matching up column in fragment 2q + 1), or raw f32 partial tiles
+// for split-K.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,48 +28,27 @@ namespace {
 
 constexpr int BK = 64;
 constexpr int LDS_STRIDE = BK + 8;   // bf16 elements per LDS row (128 + 16 bytes)
+constexpr int kGemmThreads = 256;
 
-template <int ROWS>
-struct TileLoader {
-  // ROWS x BK bf16 tile = ROWS * 8 chunks of 16 bytes; 256 threads.
-  static constexpr int CHUNKS = ROWS * (BK / 8) / 256;
-  u32x4_t r[CHUNKS];
-  EMBER_DEV void load(const uint16_t* base, int ld, int row0, int nrows, int k0, int K) {
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int id = threadIdx.x + 256 * i;
-      int row = row0 + id / (BK / 8);
-      row = row < nrows ? row : nrows - 1;          // clamp: rows beyond M/N never stored
-      const int col = k0 + (id % (BK / 8)) * 8;
-      // K is a multiple of 8: a chunk is either inside K or wholly past it (zeros)
-      r[i] = col < K ? *(const u32x4_t*)(base + (size_t)row * ld + col) : u32x4_t{0, 0, 0, 0};
-    }
-  }
-  EMBER_DEV void store(uint16_t* lds) const {
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int id = threadIdx.x + 256 * i;
-      const int row = id / (BK / 8);
-      const int col = (id % (BK / 8)) * 8;
-      *(u32x4_t*)(lds + row * LDS_STRIDE + col) = r[i];
-    }
-  }
-};
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-EMBER_DEV bf16x8_t lds_frag(const uint16_t* lds, int row, int k) {
-  const u32x4_t v = *(const u32x4_t*)(lds + row * LDS_STRIDE + k);
-  return __builtin_bit_cast(bf16x8_t, v);
+template <int BM, int BN, bool SPLIT>
+constexpr size_t gemm_lds_bytes() {
+  return (size_t)2 * ((SPLIT ? 2 : 1) * BM + BN) * LDS_STRIDE * 2;
 }
 
-template <int BM, int BN, int WM, int WN, bool SPLIT, int EPI>
-__global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
-  constexpr int TM = BM / WM / 16;
-  constexpr int TN = BN / WN / 16;
-  static_assert(WM * WN == 4, "4 waves");
-  static_assert(EPI != GEMM_SILU || TN % 2 == 0, "SiLU pairs 16-column fragments");
-  __shared__ __align__(16) uint16_t As_hi[BM * LDS_STRIDE];
-  __shared__ __align__(16) uint16_t As_lo[SPLIT ? BM * LDS_STRIDE : 8];
-  __shared__ __align__(16) uint16_t Bs[BN * LDS_STRIDE];
+template <int BM, int BN, int PF, bool SPLIT, int EPI, bool TAIL>
+__global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs a) {
+  constexpr int NT = kGemmThreads;
+  constexpr int TM = BM / 2 / 32, TN = BN / 2 / 32;      // 32x32 fragments per wave
+  constexpr int RS = NT / 8;                              // rows per load round
+  constexpr int CA = BM / RS, CB = BN / RS;               // 16-byte loads per plane
+  constexpr int NP = SPLIT ? 2 : 1;
+  constexpr int PLANE = BM * LDS_STRIDE;                  // A plane size in a stage
+  constexpr int STAGE = NP * PLANE + BN * LDS_STRIDE;
+  static_assert(CA * RS == BM && CB * RS == BN, "tile rows");
+  static_assert(EPI != GEMM_SILU || TN % 2 == 0, "SiLU pairs gate/up fragments");
+  extern __shared__ __align__(16) uint16_t smem[];
 
   // XCD-aware tile order: blocks are dealt round-robin to the 8 XCDs; give each XCD a
   // contiguous run of logical tiles, M-tiles fastest, so a weight column block stays
@@ -76,79 +59,145 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   if (nblk % 8 == 0) lin = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
   const int tm = lin % mt, tn = lin / mt;
   const int m0 = tm * BM, n0 = tn * BN;
-
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int wm = wave / WN, wn = wave % WN;
-  const int wm0 = wm * (BM / WM), wn0 = wn * (BN / WN);
-  const int fr = lane % 16, fk = (lane / 16) * 8;
+  const int wm0 = (wave / 2) * (BM / 2), wn0 = (wave % 2) * (BN / 2);
+  const int fr = lane % 32, fk = (lane / 32) * 8;
 
-  f32x4_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  TileLoader<BM> la_hi, la_lo;
-  TileLoader<BN> lb;
   // K range of this block (split-K over gridDim.y slices of k_chunk columns)
   const int kb0 = blockIdx.y * a.k_chunk;
   const int kend = min(a.K, kb0 + a.k_chunk);
   const int nk = (kend - kb0 + BK - 1) / BK;
-  la_hi.load(a.a_hi, a.lda, m0, a.M, kb0, kend);
-  if (SPLIT) la_lo.load(a.a_lo, a.lda, m0, a.M, kb0, kend);
-  lb.load(a.w, a.K, n0, a.N, kb0, kend);
-  la_hi.store(As_hi);
-  if (SPLIT) la_lo.store(As_lo);
-  lb.store(Bs);
-  __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) {
-      la_hi.load(a.a_hi, a.lda, m0, a.M, kb0 + (kt + 1) * BK, kend);
-      if (SPLIT) la_lo.load(a.a_lo, a.lda, m0, a.M, kb0 + (kt + 1) * BK, kend);
-      lb.load(a.w, a.K, n0, a.N, kb0 + (kt + 1) * BK, kend);
+  // this thread's load rows (clamped: rows past M/N are loaded but never stored) and
+  // its 8-element k chunk within a stage
+  const int r0 = threadIdx.x / 8, kc = (threadIdx.x % 8) * 8;
+  const uint16_t* pa_hi = a.a_hi + (size_t)min(m0 + r0, a.M - 1) * a.lda + kc;
+  const uint16_t* pa_lo = SPLIT ? a.a_lo + (size_t)min(m0 + r0, a.M - 1) * a.lda + kc : nullptr;
+  const uint16_t* pw = a.w + (size_t)min(n0 + r0, a.N - 1) * a.K + kc;
+  int oa[CA], ob[CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) oa[i] = (min(m0 + r0 + RS * i, a.M - 1) - min(m0 + r0, a.M - 1)) * a.lda;
+#pragma unroll
+  for (int i = 0; i < CB; ++i) ob[i] = (min(n0 + r0 + RS * i, a.N - 1) - min(n0 + r0, a.N - 1)) * a.K;
+  const int lofs = r0 * LDS_STRIDE + kc;
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  u32x4_t rh[PF][CA], rl[PF][SPLIT ? CA : 1], rw[PF][CB];
+  bool okb[PF];
+  // stage t of this block: k0 = kb0 + 64 t. With TAIL (K range not a multiple of 64) a
+  // chunk wholly past the range is zeroed when it is stored to LDS (K is a multiple of
+  // 8, so a chunk is either inside or past it); without it no select touches the data.
+  auto gload = [&](int b, int t) {
+    const int k0 = kb0 + t * BK;
+    const bool ok = !TAIL || k0 + kc < kend;
+    const int kk = ok ? k0 : kb0;
+    okb[b] = ok;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      rh[b][i] = *(const u32x4_t*)(pa_hi + oa[i] + kk);
+      if (SPLIT) rl[b][i] = *(const u32x4_t*)(pa_lo + oa[i] + kk);
     }
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 32) {
-      bf16x8_t bf[TN];
+    for (int i = 0; i < CB; ++i) rw[b][i] = *(const u32x4_t*)(pw + ob[i] + kk);
+  };
+  auto sstore = [&](int b, int s) {
+    uint16_t* base = smem + s * STAGE + lofs;
+    const u32x4_t z = {0, 0, 0, 0};
+    const bool ok = okb[b];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bf[j] = lds_frag(Bs, wn0 + j * 16 + fr, ks + fk);
+    for (int i = 0; i < CA; ++i) {
+      *(u32x4_t*)(base + RS * i * LDS_STRIDE) = !TAIL || ok ? rh[b][i] : z;
+      if (SPLIT) *(u32x4_t*)(base + PLANE + RS * i * LDS_STRIDE) = !TAIL || ok ? rl[b][i] : z;
+    }
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const bf16x8_t ah = lds_frag(As_hi, wm0 + i * 16 + fr, ks + fk);
+    for (int i = 0; i < CB; ++i)
+      *(u32x4_t*)(base + NP * PLANE + RS * i * LDS_STRIDE) = !TAIL || ok ? rw[b][i] : z;
+  };
+  bf16x8_t fh[2][TM], fl[2][SPLIT ? TM : 1], fw[2][TN];
+  auto rdfrag = [&](int f, int s, int ks) {
+    const uint16_t* st = smem + s * STAGE;
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bf[j], acc[i][j], 0, 0, 0);
-        if (SPLIT) {
-          const bf16x8_t al = lds_frag(As_lo, wm0 + i * 16 + fr, ks + fk);
+    for (int i = 0; i < TM; ++i) {
+      const int o = (wm0 + i * 32 + fr) * LDS_STRIDE + ks + fk;
+      fh[f][i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + o));
+      if (SPLIT) fl[f][i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + PLANE + o));
+    }
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf[j], acc[i][j], 0, 0, 0);
-        }
+    for (int j = 0; j < TN; ++j)
+      fw[f][j] = __builtin_bit_cast(bf16x8_t,
+                                    *(const u32x4_t*)(st + NP * PLANE + (wn0 + j * 32 + fr) * LDS_STRIDE + ks + fk));
+  };
+  auto mfmas = [&](int f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[f][i], fw[f][j], acc[i][j], 0, 0, 0);
+        if (SPLIT)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[f][i], fw[f][j], acc[i][j], 0, 0, 0);
       }
-    }
-    __syncthreads();
-    if (kt + 1 < nk) {
-      la_hi.store(As_hi);
-      if (SPLIT) la_lo.store(As_lo);
-      lb.store(Bs);
+  };
+  constexpr int NMF = NP * TM * TN, NRD = NP * TM + TN, NLD = NP * CA + CB;
+
+  // prologue: stages 0 .. PF-1 in flight (past the end: the last stage again), stage 0
+  // stored
+#pragma unroll
+  for (int b = 0; b < PF; ++b) gload(b, min(b, nk - 1));
+  sstore(0, 0);
+  __syncthreads();
+  for (int k0 = 0; k0 < nk; k0 += PF) {
+#pragma unroll
+    for (int ph = 0; ph < PF; ++ph) {
+      const int k = k0 + ph;                   // stage computed now, from LDS k & 1
+      const int s = k & 1;
+      gload(ph, min(k + PF, nk - 1));          // the registers of stage k are free
+      rdfrag(0, s, 0);
+#pragma unroll
+      for (int t = 0; t < BK / 16; ++t) {
+        if (t + 1 < BK / 16) rdfrag((t + 1) & 1, s, (t + 1) * 16);
+        mfmas(t & 1);
+      }
+      sstore((ph + 1) % PF, s ^ 1);            // stage k + 1 (past the end: unused)
+      __builtin_amdgcn_sched_group_barrier(0x020, NLD, 0);        // global loads
+      __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);        // step-0 fragments
+#pragma unroll
+      for (int t = 0; t < BK / 16 - 1; ++t)
+#pragma unroll
+        for (int r = 0; r < NRD; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, NMF / NRD > 0 ? NMF / NRD : 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+      for (int r = 0; r < NLD; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF / NLD > 0 ? NMF / NLD : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
       __syncthreads();
+      if (k + 1 >= nk) break;
     }
   }
 
-  // epilogue: lane holds C[row0 + e][col] for e < 4 of each 16x16 fragment
-  const int rbase = m0 + wm0 + (lane / 16) * 4;
+  // epilogue: element e of fragment (i, j) is C[row][col] with
+  // row = m0 + wm0 + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, col = n0 + wn0 + 32 j + lane % 32
+  const int rbase = m0 + wm0 + 4 * (lane / 32);
   if (a.partial) {                         // split-K: raw f32 tile into this slice's plane
     float* pp = a.partial + (size_t)blockIdx.y * a.M * a.N;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int col = n0 + wn0 + j * 16 + fr;
+        const int col = n0 + wn0 + j * 32 + fr;
         if (col >= a.N) continue;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = rbase + i * 16 + e;
+        for (int e = 0; e < 16; ++e) {
+          const int row = rbase + i * 32 + 8 * (e / 4) + e % 4;
           if (row < a.M) pp[(size_t)row * a.N + col] = acc[i][j][e];
         }
       }
@@ -158,13 +207,14 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn0 + j * 16 + fr;
+      const int col = n0 + wn0 + j * 32 + fr;
       if (EPI == GEMM_SILU) {
+        // fragment j (even) holds gate outputs, fragment j + 1 the matching up outputs
         if (j % 2) continue;
-        const int ocol = (col / 32) * 16 + (col % 16);
+        const int ocol = (col / (2 * kGuBlock)) * kGuBlock + col % kGuBlock;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = rbase + i * 16 + e;
+        for (int e = 0; e < 16; ++e) {
+          const int row = rbase + i * 32 + 8 * (e / 4) + e % 4;
           if (row >= a.M || col >= a.N) continue;
           const float v = silu(acc[i][j][e]) * acc[i][j + 1][e];
           const size_t o = (size_t)row * a.ldo + ocol;
@@ -180,8 +230,8 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
         if (col >= a.N) continue;
         const float bias = (EPI == GEMM_STORE && a.bias) ? a.bias[col] : 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = rbase + i * 16 + e;
+        for (int e = 0; e < 16; ++e) {
+          const int row = rbase + i * 32 + 8 * (e / 4) + e % 4;
           if (row >= a.M) continue;
           float* cp = a.c + (size_t)row * a.ldc + col;
           if (EPI == GEMM_RESID) *cp += acc[i][j][e];
@@ -192,20 +242,79 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+// Tile configurations (block BM x BN, register prefetch depth PF).
+enum GemmCfg { CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x128 = 3 };
+
+template <int BM, int BN, int PF, bool SPLIT, int EPI>
+void set_attr() {
+  (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, PF, SPLIT, EPI, false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)gemm_lds_bytes<BM, BN, SPLIT>());
+  (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, PF, SPLIT, EPI, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)gemm_lds_bytes<BM, BN, SPLIT>());
+}
+
+template <int BM, int BN, int PF, bool SPLIT, int EPI>
 void launch_cfg(const GemmArgs& a, int splits, hipStream_t st) {
   const int blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  if (a.a_lo)
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, true, EPI>), dim3(blocks, splits), dim3(256), 0, st, a);
+  const size_t lds = gemm_lds_bytes<BM, BN, SPLIT>();
+  // every K slice a whole number of 64-column stages: no tail handling
+  const bool tail = a.K % BK != 0 || a.k_chunk % BK != 0;
+  if (tail)
+    hipLaunchKernelGGL((k_gemm<BM, BN, PF, SPLIT, EPI, true>), dim3(blocks, splits),
+                       dim3(kGemmThreads), lds, st, a);
   else
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, false, EPI>), dim3(blocks, splits), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm<BM, BN, PF, SPLIT, EPI, false>), dim3(blocks, splits),
+                       dim3(kGemmThreads), lds, st, a);
+}
+
+int tiles_of(const GemmArgs& a, int bm, int bn) {
+  return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+}
+
+// Largest tile that still leaves about 0.7 tiles per CU (256 CUs); small M takes 64 rows.
+// (A 256 x 256 tile holds 256 accumulators per lane and spills around its epilogue.)
+int pick_cfg(const GemmArgs& a) {
+  if (a.M <= 64) return CFG_64x128;
+  if (tiles_of(a, 128, 256) >= 180) return CFG_128x256;
+  return CFG_128x128;
+}
+
+void cfg_dims(int cfg, int& bm, int& bn) {
+  switch (cfg) {
+    case CFG_128x256: bm = 128; bn = 256; break;
+    case CFG_128x128: bm = 128; bn = 128; break;
+    default: bm = 64; bn = 128; break;
+  }
+}
+
+template <bool SPLIT, int EPI>
+void launch_split(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
+  switch (cfg) {
+    case CFG_128x256: launch_cfg<128, 256, 2, SPLIT, EPI>(a, splits, st); break;
+    case CFG_128x128: launch_cfg<128, 128, 2, SPLIT, EPI>(a, splits, st); break;
+    default: launch_cfg<64, 128, 2, SPLIT, EPI>(a, splits, st); break;
+  }
 }
 
 template <int EPI>
-void launch_epi(const GemmArgs& a, int splits, hipStream_t st) {
-  // small M (decode batches, short prompts): 64-row tiles
-  if (a.M <= 64) launch_cfg<64, 128, 2, 2, EPI>(a, splits, st);
-  else launch_cfg<128, 128, 2, 2, EPI>(a, splits, st);
+void launch_epi(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
+  if (a.a_lo) launch_split<true, EPI>(a, cfg, splits, st);
+  else launch_split<false, EPI>(a, cfg, splits, st);
+}
+
+template <bool SPLIT, int EPI>
+void set_attrs_split() {
+  set_attr<128, 256, 2, SPLIT, EPI>();
+  set_attr<128, 128, 2, SPLIT, EPI>();
+  set_attr<64, 128, 2, SPLIT, EPI>();
+}
+
+template <int EPI>
+void set_attrs_epi() {
+  set_attrs_split<false, EPI>();
+  set_attrs_split<true, EPI>();
 }
 
 // Fixed-order sum of the split-K partial planes, then the epilogue.
@@ -217,7 +326,7 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs a, int splits) {
        e += (size_t)gridDim.x * blockDim.x) {
     const int row = (int)(e / nout), col = (int)(e % nout);
     if (EPI == GEMM_SILU) {
-      const int gcol = (col / 16) * 32 + (col % 16), ucol = gcol + 16;
+      const int gcol = gu_row(col, 0), ucol = gu_row(col, 1);
       float g = 0.f, u = 0.f;
       for (int s = 0; s < splits; ++s) {
         const float* pp = a.partial + (size_t)s * a.M * a.N + (size_t)row * a.N;
@@ -244,10 +353,11 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs a, int splits) {
 }
 
 // Split K when the tiles cannot fill the GPU: slices of >= 256 columns, about 512 blocks.
-int pick_splits(const GemmArgs& a) {
+int pick_splits(const GemmArgs& a, int cfg) {
   if (!a.partial) return 1;
-  const int BM = a.M <= 64 ? 64 : 128;
-  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + 127) / 128);
+  int bm, bn;
+  cfg_dims(cfg, bm, bn);
+  const int tiles = tiles_of(a, bm, bn);
   if (tiles >= 192) return 1;
   int s = (512 + tiles - 1) / tiles;
   const int max_s = a.K / 256;
@@ -266,7 +376,7 @@ __global__ void __launch_bounds__(256) k_gemm_f32w(GemmF32Args a) {
   if (n >= nout || m >= a.M) return;
   const float* x = a.a + (size_t)m * a.lda;
   if (EPI == GEMM_SILU) {
-    const int rg = (n >> 4) * 32 + (n & 15), ru = rg + 16;
+    const int rg = gu_row(n, 0), ru = gu_row(n, 1);
     float g = 0.f, u = 0.f;
     for (int k = 0; k < a.K; ++k) {
       g = fmaf(a.w[(size_t)rg * a.K + k], x[k], g);
@@ -284,17 +394,24 @@ __global__ void __launch_bounds__(256) k_gemm_f32w(GemmF32Args a) {
 
 }  // namespace
 
+void gemm_init() {
+  set_attrs_epi<GEMM_STORE>();
+  set_attrs_epi<GEMM_RESID>();
+  set_attrs_epi<GEMM_SILU>();
+}
+
 void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
   if (a0.M <= 0 || a0.N <= 0) return;
   GemmArgs a = a0;
-  const int splits = pick_splits(a);
+  const int cfg = pick_cfg(a);
+  const int splits = pick_splits(a, cfg);
   if (splits <= 1) {
     a.partial = nullptr;
     a.k_chunk = a.K;
     switch (epi) {
-      case GEMM_STORE: launch_epi<GEMM_STORE>(a, 1, st); break;
-      case GEMM_RESID: launch_epi<GEMM_RESID>(a, 1, st); break;
-      case GEMM_SILU: launch_epi<GEMM_SILU>(a, 1, st); break;
+      case GEMM_STORE: launch_epi<GEMM_STORE>(a, cfg, 1, st); break;
+      case GEMM_RESID: launch_epi<GEMM_RESID>(a, cfg, 1, st); break;
+      case GEMM_SILU: launch_epi<GEMM_SILU>(a, cfg, 1, st); break;
       default: break;
     }
     return;
@@ -302,7 +419,7 @@ void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
   // K slices are whole 64-column stages
   a.k_chunk = ((a.K + splits - 1) / splits + 63) / 64 * 64;
   const int used = (a.K + a.k_chunk - 1) / a.k_chunk;
-  launch_epi<GEMM_STORE>(a, used, st);            // partial planes (epilogue skipped)
+  launch_epi<GEMM_STORE>(a, cfg, used, st);      // partial planes (epilogue skipped)
   const int nout = epi == GEMM_SILU ? a.N / 2 : a.N;
   long long blocks = ((long long)a.M * nout + 255) / 256;
   if (blocks > 4096) blocks = 4096;

@@ -15,7 +15,7 @@
 //  * row per block (longer K): thread t owns chunks t + 256 u; one block-wide sum of
 //    squares for the norm; per row group the four waves' partials meet in LDS.
 // Epilogues: store (+bias), residual add, SiLU*up (gate/up rows interleaved in blocks of
-// 16), logits with an argmax partial (value, then lowest index) per wave or block.
+// 32, see gu_row), logits with an argmax partial (value, then lowest index) per wave or block.
 #include "common.h"
 #include "kernels.h"
 
@@ -42,9 +42,6 @@ template <> struct WTraits<float> {
   }
 };
 
-// packed row of gate/up output n: rows are interleaved in blocks of 16 (16 gate rows,
-// then the 16 matching up rows).
-EMBER_DEV int gu_row(int n, int up) { return (n >> 4) * 32 + (up ? 16 : 0) + (n & 15); }
 
 template <int EPI>
 EMBER_DEV int weight_row(int n, int r) { return EPI == GEMV_SILU ? gu_row(n, r) : n; }

@@ -68,6 +68,10 @@ typedef struct ember_config {
   double llama3_high_freq_factor;
   double llama3_original_max_pos;
   float rms_eps;               /* RMSNorm epsilon (also for per-head q/k norm) */
+  /* head_dim in {8, 16, 32, 64, 128}; heads a multiple of kv_heads with at most 8 query
+   * heads per kv head; ffn a multiple of 32; hidden, ffn and heads * head_dim multiples
+   * of 8 (bf16 weights) or 4 (f32); hidden <= 8192, ffn <= 32768, heads * head_dim <=
+   * 8192, max_seq <= 65536. Other shapes fail with EMBER_E_CONFIG. */
   int32_t vocab, hidden, layers, heads, kv_heads, head_dim, ffn;
   int32_t rope_llama3;         /* 0/1 */
   int32_t qkv_bias;            /* 0/1: q/k/v projections carry a bias (Qwen2 family) */
