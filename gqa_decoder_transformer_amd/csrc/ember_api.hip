@@ -56,8 +56,8 @@ struct Plan {
   std::vector<LayerOff> layer;
   // activations
   size_t ids, pos, rope_cur, next, flags, x, xb, pa_hi, pa_lo, pb_hi, pb_lo, qkv, q, att, act, part,
-      logits, hrow, argpart, splitk;
-  size_t splitk_elems;
+      logits, hrow, argpart, splitk, kvpack;
+  size_t splitk_elems, kvpack_elems;
   size_t total;
   int Mx, qkv_n, ka, nsplit_max, argparts;
 };
@@ -166,6 +166,14 @@ Plan make_plan(const ember_config& c) {
     const int mrows = Mx < 128 ? Mx : 128;
     p.splitk_elems = c.weight_dtype == EMBER_BF16 ? (size_t)16 * mrows * maxn : 0;
     p.splitk = p.splitk_elems ? take(p.splitk_elems * 4) : 0;
+  }
+  {
+    // packed K / V^T planes for the tiled prefill attention: one pass holds at most Mx
+    // tokens, or one row of up to max_seq keys, each row rounded up to a 64-key tile
+    const bool tiled = c.weight_dtype == EMBER_BF16 && (HD == 64 || HD == 128);
+    const int cap_keys = (Mx > c.max_seq ? Mx : c.max_seq) + 64 * c.max_batch;
+    p.kvpack_elems = tiled ? (size_t)(c.precision == EMBER_EXACT ? 2 : 1) * 2 * NKV * cap_keys * HD : 0;
+    p.kvpack = p.kvpack_elems ? take(p.kvpack_elems * 2) : 0;
   }
   p.total = off;
   return p;
@@ -325,8 +333,24 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     fa.out_hi = planes_out ? pa_hi : nullptr;
     fa.out_lo = planes_out ? pa_lo : nullptr;
     if (want(cx, EMBER_K_ATTN)) {
-      if (planes_out && flash_mfma_supported(HD)) launch_flash_mfma(fa, exact, st);
-      else launch_flash_prefill(fa, st);
+      const int key_end = ps.start + ps.tpr;
+      const size_t need = kv_pack_elems(ps.rows, NKV, HD, key_end, exact);
+      if (planes_out && flash_mfma_supported(HD) && need <= p.kvpack_elems) {
+        // pack this pass's keys into bf16 K and V^T planes, then the tiled MFMA kernel
+        KvPackArgs ka{};
+        ka.k_cache = qa.k_cache; ka.v_cache = qa.v_cache; ka.kv_bf16 = qa.kv_bf16;
+        ka.NKV = NKV; ka.HD = HD; ka.max_seq = c.max_seq;
+        ka.rows = ps.rows; ka.b0 = ps.b0; ka.key_end = key_end; ka.LK = kv_pack_lk(key_end);
+        ka.split = exact;
+        ka.kp = md->at<uint16_t>(p.kvpack);
+        ka.vt = ka.kp + need / 2;
+        launch_kv_pack(ka, st);
+        launch_flash_tiled(fa, ka.kp, ka.vt, ka.LK, exact, st);
+      } else if (planes_out && flash_mfma_supported(HD)) {
+        launch_flash_mfma(fa, exact, st);
+      } else {
+        launch_flash_prefill(fa, st);
+      }
     }
   } else {
     DecodeAttnArgs da{};
@@ -534,6 +558,7 @@ ember_status ember_load_weights(const ember_config* cfg, const ember_tensor* ten
   const ember_config& c = *cfg;
   Plan plan = make_plan(c);
   gemm_init();
+  flash_init();
   if (workspace_bytes < plan.total)
     return fail(EMBER_E_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes, plan.total);
 

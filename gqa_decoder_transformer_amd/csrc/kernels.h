@@ -169,6 +169,33 @@ void launch_flash_prefill(const FlashArgs& a, hipStream_t st);
 bool flash_mfma_supported(int HD);
 void launch_flash_mfma(const FlashArgs& a, bool split, hipStream_t st);
 
+// Packed K and V^T bf16 planes of one prefill pass (keys 0 .. key_end-1 of each pass row,
+// zero up to LK = key_end rounded up to 64), read by the tiled attention:
+//   K   plane p: kp[(((p * rows + r) * NKV + g) * LK + key) * HD + d]
+//   V^T plane p: vt[(((p * rows + r) * NKV + g) * HD + d) * LK + key]
+// EXACT (split): plane 0 = bf16(x), plane 1 = bf16(x - plane 0); FAST: plane 0 only.
+struct KvPackArgs {
+  const void* k_cache;     // layer base [B_cache][NKV][max_seq][HD]
+  const void* v_cache;
+  bool kv_bf16;
+  int NKV, HD, max_seq;
+  int rows, b0, key_end, LK;
+  bool split;
+  uint16_t* kp;
+  uint16_t* vt;
+};
+inline int kv_pack_lk(int key_end) { return (key_end + 63) / 64 * 64; }
+inline size_t kv_pack_elems(int rows, int NKV, int HD, int key_end, bool split) {
+  return (size_t)(split ? 2 : 1) * 2 * rows * NKV * kv_pack_lk(key_end) * HD;
+}
+void launch_kv_pack(const KvPackArgs& a, hipStream_t st);
+// Tiled MFMA prefill attention (head_dim 64 / 128) over the packed planes; queries from
+// `a.q`, output to a.out_hi / a.out_lo (planes) or a.out_f32. Sets its LDS limit on the
+// first call.
+void launch_flash_tiled(const FlashArgs& a, const uint16_t* kp, const uint16_t* vt, int LK,
+                        bool split, hipStream_t st);
+void flash_init();
+
 struct DecodeAttnArgs {
   const float* qkv;        // [B, (NH + 2 NKV) HD] raw projections of the current token
   const float* rope_cur;   // cos[HD/2], sin[HD/2] of the current position

@@ -38,6 +38,8 @@ EMBER_DEV bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v)
 
 EMBER_DEV uint32_t pack2(uint32_t lo, uint32_t hi) { return (lo & 0xFFFFu) | (hi << 16); }
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
 template <int HD, bool SPLIT>
 __global__ void __launch_bounds__(256) k_flash_mfma(FlashArgs a) {
   using C = FlashCfg<HD>;
@@ -250,6 +252,326 @@ __global__ void __launch_bounds__(256) k_flash_mfma(FlashArgs a) {
     }
 }
 
+
+// ------------------------------------------------------------------ packed K / V^T planes
+// One block per (64-key tile, kv head, pass row): K is copied row-major (bf16 planes), V
+// is transposed through LDS so that every V^T row is written with 16-byte stores. Keys
+// from key_end up to the tile boundary are zero.
+template <int HD>
+__global__ void __launch_bounds__(256) k_kv_pack(KvPackArgs a) {
+  __shared__ float vs[64 * (HD + 1)];
+  const int kt = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  const int k0 = kt * 64;
+  const size_t cbase = ((size_t)(a.b0 + r) * a.NKV + g) * a.max_seq * HD;
+  const size_t kplane = (size_t)a.rows * a.NKV * a.LK * HD;      // elements per plane
+  const size_t kb = ((size_t)r * a.NKV + g) * a.LK * HD;
+  for (int it = threadIdx.x; it < 64 * HD / 8; it += 256) {
+    const int key = it / (HD / 8), d8 = (it % (HD / 8)) * 8;
+    const int pos = k0 + key;
+    float kv[8], vv[8];
+    if (pos < a.key_end) {
+      const size_t off = cbase + (size_t)pos * HD + d8;
+      if (a.kv_bf16) {
+        const u32x4_t kr = *(const u32x4_t*)((const uint16_t*)a.k_cache + off);
+        const u32x4_t vr = *(const u32x4_t*)((const uint16_t*)a.v_cache + off);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kv[2 * j] = bf16_lo(kr[j]); kv[2 * j + 1] = bf16_hi(kr[j]);
+          vv[2 * j] = bf16_lo(vr[j]); vv[2 * j + 1] = bf16_hi(vr[j]);
+        }
+      } else {
+        const float* kf = (const float*)a.k_cache + off;
+        const float* vf = (const float*)a.v_cache + off;
+        const float4 k0v = *(const float4*)kf, k1v = *(const float4*)(kf + 4);
+        const float4 v0v = *(const float4*)vf, v1v = *(const float4*)(vf + 4);
+        kv[0] = k0v.x; kv[1] = k0v.y; kv[2] = k0v.z; kv[3] = k0v.w;
+        kv[4] = k1v.x; kv[5] = k1v.y; kv[6] = k1v.z; kv[7] = k1v.w;
+        vv[0] = v0v.x; vv[1] = v0v.y; vv[2] = v0v.z; vv[3] = v0v.w;
+        vv[4] = v1v.x; vv[5] = v1v.y; vv[6] = v1v.z; vv[7] = v1v.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { kv[j] = 0.f; vv[j] = 0.f; }
+    }
+    u32x4_t hi, lo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t h0, l0, h1, l1;
+      split_bf16(kv[2 * j], h0, l0);
+      split_bf16(kv[2 * j + 1], h1, l1);
+      hi[j] = pack2(h0, h1);
+      lo[j] = pack2(l0, l1);
+    }
+    const size_t ko = kb + (size_t)pos * HD + d8;
+    *(u32x4_t*)(a.kp + ko) = hi;
+    if (a.split) *(u32x4_t*)(a.kp + kplane + ko) = lo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vs[key * (HD + 1) + d8 + j] = vv[j];
+  }
+  __syncthreads();
+  const size_t vb = ((size_t)r * a.NKV + g) * HD * a.LK;
+  for (int it = threadIdx.x; it < HD * 8; it += 256) {
+    const int d = it / 8, key8 = (it % 8) * 8;
+    u32x4_t hi, lo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t h0, l0, h1, l1;
+      split_bf16(vs[(key8 + 2 * j) * (HD + 1) + d], h0, l0);
+      split_bf16(vs[(key8 + 2 * j + 1) * (HD + 1) + d], h1, l1);
+      hi[j] = pack2(h0, h1);
+      lo[j] = pack2(l0, l1);
+    }
+    const size_t vo = vb + (size_t)d * a.LK + k0 + key8;
+    *(u32x4_t*)(a.vt + vo) = hi;
+    if (a.split) *(u32x4_t*)(a.vt + kplane + vo) = lo;
+  }
+}
+
+// ------------------------------------------------------------------ tiled MFMA attention
+// Block: 128 queries of one (pass row, query head), 4 waves x 32 queries; K tiles of 64
+// keys. v_mfma_f32_32x32x16_bf16 throughout, everything transposed so the two products
+// chain without lane shuffles:
+//   S^T = K Q^T: A = K rows (keys) x 16 head dims, B = Q^T; lane l holds query l % 32 and
+//                keys 8 (e / 4) + 4 (l / 32) + e % 4 (e < 16) of each 32-key block.
+//   O^T = V^T P^T: B = P^T must hold 8 keys of query l % 32 per lane: the lane's own 8
+//                probabilities of a 16-key half block, so MFMA slot 8 (l / 32) + i stands
+//                for key 16 t + (i < 4 ? 4 (l / 32) + i : 8 + 4 (l / 32) + i - 4), and V^T
+//                is read with the same order (two 8-byte LDS reads per fragment).
+// Both tiles are double-buffered in LDS, loaded one tile ahead through registers from the
+// packed planes (16-byte loads, rows padded by 16 bytes). The softmax is the online one
+// in base 2 (scores pre-multiplied by scale * log2 e); masks are applied only on tiles
+// that cross the causal diagonal or the end of the keys; under the causal mask a wave
+// skips the tiles wholly past its last query. Output rows go through LDS and leave as 16-byte stores.
+constexpr int kTQ = 128, kTK = 64;
+
+template <int HD, bool SPLIT>
+struct TiledCfg {
+  static constexpr int NP = SPLIT ? 2 : 1;
+  static constexpr int KS = HD + 8, VS = kTK + 8;
+  static constexpr int KTILE = kTK * KS, VTILE = HD * VS;
+  static constexpr int STAGE = NP * (KTILE + VTILE);           // bf16 elements
+  static constexpr size_t LDS = (size_t)2 * STAGE * 2;         // bytes, two stages
+  static_assert((size_t)4 * 32 * (HD + 1) * 4 <= LDS, "output staging fits");
+};
+
+template <int HD, bool SPLIT>
+__global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t* kp,
+                                                     const uint16_t* vt, int LK) {
+  using C = TiledCfg<HD, SPLIT>;
+  constexpr int NP = C::NP, KS = C::KS, VS = C::VS;
+  constexpr int NKS = HD / 16, NDB = HD / 32;
+  constexpr int CK = kTK * HD / 8 / 256;                         // 16-byte chunks per thread
+  extern __shared__ __align__(16) uint16_t sm[];
+
+  const int qt = gridDim.x - 1 - blockIdx.x;                   // late (long) tiles first
+  const int h = blockIdx.y, r = blockIdx.z;
+  const int g = h / (a.NH / a.NKV);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int lq = lane % 32, hl = lane / 32;
+  const int T = a.tokens_per_row;
+  const int q0 = qt * kTQ + wave * 32;
+  const int qc = min(q0 + lq, T - 1);
+  const int qpos = a.start_pos + qc;
+  const size_t mrow = (size_t)r * T + qc;
+  const int key_end = a.start_pos + T;
+  const int kend_blk = a.causal ? a.start_pos + min(T, (qt + 1) * kTQ) : key_end;
+  const int ntiles = (kend_blk + kTK - 1) / kTK;
+  const int wq_first = a.start_pos + min(T - 1, q0);
+  const int wq_last = a.start_pos + min(T - 1, q0 + 31);
+
+  // Q^T operand: query lq, head dims 16 ks + 8 hl .. + 8
+  bf16x8_t qh[NKS], qlo[SPLIT ? NKS : 1];
+  {
+    const float* qp = a.q + mrow * a.NH * HD + (size_t)h * HD + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const float4 x0 = *(const float4*)(qp + 16 * ks), x1 = *(const float4*)(qp + 16 * ks + 4);
+      const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      u32x4_t hv, lv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t h0, l0, h1, l1;
+        split_bf16(xv[2 * j], h0, l0);
+        split_bf16(xv[2 * j + 1], h1, l1);
+        hv[j] = pack2(h0, h1);
+        lv[j] = pack2(l0, l1);
+      }
+      qh[ks] = as_bf16x8(hv);
+      if (SPLIT) qlo[ks] = as_bf16x8(lv);
+    }
+  }
+
+  // tile staging: thread chunk c covers K key id / (HD / 8), dims (id % (HD / 8)) * 8 and
+  // V^T head dim id / 8, keys (id % 8) * 8 (id = tid + 256 c)
+  const size_t plane = (size_t)a.rows * a.NKV * LK * HD;
+  const uint16_t* kg = kp + ((size_t)r * a.NKV + g) * LK * HD;
+  const uint16_t* vg = vt + ((size_t)r * a.NKV + g) * HD * LK;
+  u32x4_t rk[NP][CK], rv[NP][CK];
+  auto gload = [&](int j) {
+    const int k0 = j * kTK;
+#pragma unroll
+    for (int c = 0; c < CK; ++c) {
+      const int id = threadIdx.x + 256 * c;
+      const size_t ko = (size_t)(k0 + id / (HD / 8)) * HD + (id % (HD / 8)) * 8;
+      const size_t vo = (size_t)(id / 8) * LK + k0 + (id % 8) * 8;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        rk[p][c] = *(const u32x4_t*)(kg + p * plane + ko);
+        rv[p][c] = *(const u32x4_t*)(vg + p * plane + vo);
+      }
+    }
+  };
+  auto sstore = [&](int s) {
+    uint16_t* st = sm + s * C::STAGE;
+#pragma unroll
+    for (int c = 0; c < CK; ++c) {
+      const int id = threadIdx.x + 256 * c;
+      const int ko = (id / (HD / 8)) * KS + (id % (HD / 8)) * 8;
+      const int vo = (id / 8) * VS + (id % 8) * 8;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        *(u32x4_t*)(st + p * C::KTILE + ko) = rk[p][c];
+        *(u32x4_t*)(st + NP * C::KTILE + p * C::VTILE + vo) = rv[p][c];
+      }
+    }
+  };
+
+  f32x16_t o[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
+  float mrun = -INFINITY, lrun = 0.f;
+  const float c2 = a.scale * 1.4426950408889634f;               // scale * log2(e)
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int s = j & 1;
+    if (j + 1 < ntiles) gload(j + 1);
+    const int k0 = j * kTK;
+    if (!a.causal || k0 <= wq_last) {                          // wave-uniform
+      const uint16_t* st = sm + s * C::STAGE;
+      f32x16_t sc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int ro = (kb * 32 + lq) * KS + 16 * ks + 8 * hl;
+          const bf16x8_t kh = as_bf16x8(*(const u32x4_t*)(st + ro));
+          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[ks], sc[kb], 0, 0, 0);
+          if (SPLIT) {
+            const bf16x8_t kl = as_bf16x8(*(const u32x4_t*)(st + C::KTILE + ro));
+            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qlo[ks], sc[kb], 0, 0, 0);
+            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[ks], sc[kb], 0, 0, 0);
+          }
+        }
+      }
+      const bool need_mask = (a.causal && k0 + kTK - 1 > wq_first) || k0 + kTK > key_end;
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float v = sc[kb][e] * c2;
+          if (need_mask) {
+            const int key = k0 + kb * 32 + 8 * (e / 4) + 4 * hl + (e % 4);
+            if (key >= key_end || (a.causal && key > qpos)) v = -INFINITY;
+          }
+          sc[kb][e] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mnew = fmaxf(mrun, mt);                      // finite: key 0 is in tile 0
+      const float alpha = exp2f(mrun - mnew);                  // mrun = -inf -> 0
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2f(sc[kb][e] - mnew);             // masked (-inf) -> 0
+          sc[kb][e] = p;
+          ps += p;
+        }
+      ps += __shfl_xor(ps, 32);
+      lrun = lrun * alpha + ps;
+      mrun = mnew;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+#pragma unroll
+      for (int t = 0; t < kTK / 16; ++t) {
+        const int kb = t / 2, e0 = 8 * (t % 2);
+        u32x4_t ph, pl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t h0, l0, h1, l1;
+          split_bf16(sc[kb][e0 + 2 * i], h0, l0);
+          split_bf16(sc[kb][e0 + 2 * i + 1], h1, l1);
+          ph[i] = pack2(h0, h1);
+          pl[i] = pack2(l0, l1);
+        }
+        const bf16x8_t pbh = as_bf16x8(ph), pbl = as_bf16x8(pl);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int vo = (db * 32 + lq) * VS + 16 * t + 4 * hl;
+          const uint16_t* vb = st + NP * C::KTILE;
+          u32x4_t vh;
+          const uint2 v0 = *(const uint2*)(vb + vo), v1 = *(const uint2*)(vb + vo + 8);
+          vh[0] = v0.x; vh[1] = v0.y; vh[2] = v1.x; vh[3] = v1.y;
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vh), pbh, o[db], 0, 0, 0);
+          if (SPLIT) {
+            u32x4_t vl;
+            const uint2 w0 = *(const uint2*)(vb + C::VTILE + vo), w1 = *(const uint2*)(vb + C::VTILE + vo + 8);
+            vl[0] = w0.x; vl[1] = w0.y; vl[2] = w1.x; vl[3] = w1.y;
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vh), pbl, o[db], 0, 0, 0);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vl), pbh, o[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (j + 1 < ntiles) sstore(s ^ 1);
+    __syncthreads();
+  }
+
+  // normalise and stage the wave's 32 output rows (f32, padded) through LDS
+  float* ow = (float*)sm + wave * 32 * (HD + 1);
+  const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      ow[lq * (HD + 1) + db * 32 + 8 * (e / 4) + 4 * hl + (e % 4)] = o[db][e] * inv;
+  __syncthreads();
+  for (int it = lane; it < 32 * (HD / 8); it += kWave) {
+    const int row = it / (HD / 8), c8 = (it % (HD / 8)) * 8;
+    if (q0 + row >= T) continue;
+    const float* src = ow + row * (HD + 1) + c8;
+    const size_t ob = ((size_t)r * T + q0 + row) * a.NH * HD + (size_t)h * HD + c8;
+    if (a.out_f32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a.out_f32[ob + i] = src[i];
+    }
+    if (a.out_hi) {
+      u32x4_t hv, lv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t h0, l0, h1, l1;
+        split_bf16(src[2 * i], h0, l0);
+        split_bf16(src[2 * i + 1], h1, l1);
+        hv[i] = pack2(h0, h1);
+        lv[i] = pack2(l0, l1);
+      }
+      *(u32x4_t*)(a.out_hi + ob) = hv;
+      if (a.out_lo) *(u32x4_t*)(a.out_lo + ob) = lv;
+    }
+  }
+}
+
 }  // namespace
 
 bool flash_mfma_supported(int HD) { return HD == 64 || HD == 128; }
@@ -263,6 +585,40 @@ void launch_flash_mfma(const FlashArgs& a, bool split, hipStream_t st) {
     if (split) hipLaunchKernelGGL((k_flash_mfma<128, true>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((k_flash_mfma<128, false>), grid, dim3(256), 0, st, a);
   }
+}
+
+}  // namespace ember
+
+namespace ember {
+
+void launch_kv_pack(const KvPackArgs& a, hipStream_t st) {
+  if (a.rows <= 0 || a.key_end <= 0) return;
+  dim3 grid(a.LK / 64, a.NKV, a.rows);
+  if (a.HD == 64) hipLaunchKernelGGL(k_kv_pack<64>, grid, dim3(256), 0, st, a);
+  else if (a.HD == 128) hipLaunchKernelGGL(k_kv_pack<128>, grid, dim3(256), 0, st, a);
+}
+
+void flash_init() {
+  (void)hipFuncSetAttribute((const void*)k_flash_tiled<64, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)TiledCfg<64, false>::LDS);
+  (void)hipFuncSetAttribute((const void*)k_flash_tiled<64, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)TiledCfg<64, true>::LDS);
+  (void)hipFuncSetAttribute((const void*)k_flash_tiled<128, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)TiledCfg<128, false>::LDS);
+  (void)hipFuncSetAttribute((const void*)k_flash_tiled<128, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)TiledCfg<128, true>::LDS);
+}
+
+void launch_flash_tiled(const FlashArgs& a, const uint16_t* kp, const uint16_t* vt, int LK,
+                        bool split, hipStream_t st) {
+  dim3 grid((a.tokens_per_row + kTQ - 1) / kTQ, a.NH, a.rows);
+#define EMBER_TILED(HDV, SP)                                                           \
+  {                                                                                    \
+    const size_t lds = TiledCfg<HDV, SP>::LDS;                                         \
+    hipLaunchKernelGGL((k_flash_tiled<HDV, SP>), grid, dim3(256), lds, st, a, kp, vt, LK); \
+  }
+  if (a.HD == 64) {
+    if (split) EMBER_TILED(64, true) else EMBER_TILED(64, false)
+  } else if (a.HD == 128) {
+    if (split) EMBER_TILED(128, true) else EMBER_TILED(128, false)
+  }
+#undef EMBER_TILED
 }
 
 }  // namespace ember
