@@ -39,7 +39,9 @@ def parse():
     ap.add_argument("--precision", default="exact", choices=["exact", "fast"])
     ap.add_argument("--kv", default=None, choices=[None, "f32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--timing-iters", type=int, default=20)
+    ap.add_argument("--timing-iters", type=int, default=100)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run one plain device copy of BYTES (counter calibration)")
     return ap.parse_args()
 
 
@@ -48,9 +50,10 @@ def weight_bytes(m):
     return es
 
 
-def kernel_work(m, kind, phase, M, S, kv_bytes, nsplit):
+def kernel_work(m, kind, phase, M, S, kv_bytes):
     """Algorithmic bytes (decode, HBM-bound) or FLOPs (prefill projections, MFMA-bound)
-    of one launch of `kind`. Weights read once at their stored dtype, activations f32."""
+    of one launch of `kind`: weights read once at their stored dtype, activations f32 in
+    and out, K/V at the cache dtype; no implementation scratch (split partials)."""
     from gqa_decoder_transformer_amd import binding as B
     es = weight_bytes(m)
     H, FF, V = m.hidden, m.ffn, m.vocab
@@ -62,14 +65,13 @@ def kernel_work(m, kind, phase, M, S, kv_bytes, nsplit):
         if kind == B.K_QKV:
             return "hbm", qn * H * es + M * (2 * H * 4 + qn * 4) + (qn * 4 if m.qkv_bias else 0)
         if kind == B.K_O:
-            return "hbm", H * qd * es + M * (m.heads * nsplit * (m.head_dim + 2) * 4 + 2 * H * 4)
+            return "hbm", H * qd * es + M * (qd * 4 + 2 * H * 4)
         if kind == B.K_GATE_UP:
             return "hbm", 2 * FF * H * es + M * (2 * H * 4 + FF * 4)
         if kind == B.K_DOWN:
             return "hbm", H * FF * es + M * (FF * 4 + 2 * H * 4)
         if kind == B.K_ATTN:
-            return "hbm", M * (2 * S * m.kv_heads * m.head_dim * kv_bytes + qd * 4 +
-                               m.heads * nsplit * (m.head_dim + 2) * 4)
+            return "hbm", M * (2 * S * m.kv_heads * m.head_dim * kv_bytes + qn * 4 + qd * 4)
     else:
         if kind == B.K_LM_HEAD:
             return "mfma", 2.0 * M * V * H
@@ -111,12 +113,45 @@ def cpu_baseline(w, ck, prompt):
             "sample": f"row 0: prefill {T} tokens + {n} greedy decode steps, f32 NumPy"}
 
 
+def measured_traffic(workload, precision, kernel):
+    """HBM bytes per launch of `kernel` from the hardware-counter record in profiles/
+    (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or None when
+    there is no record or the kernel's source changed since it was taken."""
+    from gqa_decoder_transformer_amd import profiling
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        recs = json.load(fh)
+    for r in recs:
+        if (r["name"], r["workload"], r["precision"]) != (kernel, workload, precision):
+            continue
+        src = os.path.join(ROOT, r["source"])
+        if os.path.exists(src) and profiling.source_sha256(src) == r["source_sha256"]:
+            return r["bytes_per_launch"]
+    return None
+
+
+def calibrate_copy(nbytes):
+    """One plain device-to-device copy of `nbytes` (reference for the memory counters)."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU runs are "
               "not part of this build", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     import numpy as np
     import torch
     import workloads as W
@@ -164,7 +199,6 @@ def main():
         # ---- per-kernel live timings (HIP events on the same stream)
         kv_bytes = 4 if cfg.kv_dtype == B.F32 else 2
         S_mean = T + (N + 1) / 2.0
-        nsplit = max(1, min(-(-2048 // (m.kv_heads * Bn)), -(-w.max_pos // 64)))
         kernels = {}
         phases = ([0] if N > 0 else []) + [1]
         for phase in phases:
@@ -179,7 +213,7 @@ def main():
                 launches = (1 if kind == B.K_LM_HEAD else m.layers) * (N if phase == 0 else
                                                                           -(-Bn * T // max_tokens))
                 bound, work = kernel_work(m, kind, phase, Bn if phase == 0 else max_tokens,
-                                          S_mean if phase == 0 else T, kv_bytes, nsplit)
+                                          S_mean if phase == 0 else T, kv_bytes)
                 if phase == 1 and kind == B.K_ATTN:
                     rows = max_tokens // T
                     pairs = T * (T + 1) / 2 if m.causal else T * T
@@ -237,7 +271,8 @@ def main():
         "wall_s": wall,
         "roofline": {"bound": dom["bound"], "kernel": dom_name,
                      "achieved": dom["achieved"], "peak": dom["peak"], "unit": dom["unit"],
-                     "frac": dom["frac"], "traffic": None,
+                     "frac": dom["frac"],
+                     "traffic": measured_traffic(args.workload, args.precision, dom_name),
                      "avg_us": dom["avg_us"], "work_per_launch": dom["work_per_launch"]},
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                         for kk, vv in v.items()} for k, v in kernels.items()},

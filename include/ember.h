@@ -188,9 +188,10 @@ typedef enum ember_kernel {
 
 /* Launch kernel `kernel` of the most recent decode step (phase 0) or prefill pass
  * (phase 1) `iters` times back to back on `stream`, launch i on layer i mod layers (so
- * the weights stream from HBM as in a real step), with that step's launch arguments,
- * between two HIP events recorded on `stream`, and return the mean duration per launch
- * in microseconds. The launches work on the model's own buffers: afterwards the
+ * the weights stream from HBM as in a real step), with that step's launch arguments, and
+ * return the mean duration per launch in microseconds. On a non-null stream the launches
+ * form a graph replayed twice between two HIP events, queued behind a warm-up replay
+ * so that host submission time stays outside the measured span. The launches work on the model's own buffers: afterwards the
  * activations, logits and the cache entries of the step's positions are unspecified, so
  * time only a finished sequence. EMBER_E_STATE if no such step has run. */
 ember_status ember_time_kernel(ember_model* model, ember_cache* cache, int32_t kernel,
