@@ -88,6 +88,13 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs a) {
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  // the bias of this lane's output columns, read before the main loop (a load in the
+  // epilogue raised the register pressure of the whole kernel)
+  float biasv[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+    biasv[j] = (EPI == GEMM_STORE && a.bias && !a.partial)
+                   ? a.bias[min(n0 + wn0 + j * 32 + fr, a.N - 1)] : 0.f;
 
   u32x4_t rh[PF][CA], rl[PF][SPLIT ? CA : 1], rw[PF][CB];
   bool okb[PF];
@@ -185,20 +192,22 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs a) {
   }
 
   // epilogue: element e of fragment (i, j) is C[row][col] with
-  // row = m0 + wm0 + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, col = n0 + wn0 + 32 j + lane % 32
-  const int rbase = m0 + wm0 + 4 * (lane / 32);
+  // row = m0 + wm0 + 32 i + 4 (lane / 32) + 8 (e / 4) + e % 4, col = n0 + wn0 + 32 j + lane % 32.
+  // One 64-bit base per fragment, 32-bit row offsets after it (fewer live registers
+  // across the whole kernel than a 64-bit product per element).
+  const int rb0 = m0 + wm0 + 4 * (lane / 32);
   if (a.partial) {                         // split-K: raw f32 tile into this slice's plane
-    float* pp = a.partial + (size_t)blockIdx.y * a.M * a.N;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int col = n0 + wn0 + j * 32 + fr;
-        if (col >= a.N) continue;
+        const int row0 = rb0 + i * 32;
+        float* pb = a.partial + ((size_t)blockIdx.y * a.M + row0) * a.N + col;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int row = rbase + i * 32 + 8 * (e / 4) + e % 4;
-          if (row < a.M) pp[(size_t)row * a.N + col] = acc[i][j][e];
+          const int dr = 8 * (e / 4) + e % 4;
+          if (col < a.N && row0 + dr < a.M) pb[dr * a.N] = acc[i][j][e];
         }
       }
     return;
@@ -208,16 +217,18 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int col = n0 + wn0 + j * 32 + fr;
+      const int row0 = rb0 + i * 32;
       if (EPI == GEMM_SILU) {
         // fragment j (even) holds gate outputs, fragment j + 1 the matching up outputs
         if (j % 2) continue;
         const int ocol = (col / (2 * kGuBlock)) * kGuBlock + col % kGuBlock;
+        const size_t ob = (size_t)row0 * a.ldo + ocol;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int row = rbase + i * 32 + 8 * (e / 4) + e % 4;
-          if (row >= a.M || col >= a.N) continue;
+          const int dr = 8 * (e / 4) + e % 4;
+          if (row0 + dr >= a.M || col >= a.N) continue;
           const float v = silu(acc[i][j][e]) * acc[i][j + 1][e];
-          const size_t o = (size_t)row * a.ldo + ocol;
+          const size_t o = ob + dr * a.ldo;
           if (a.o_f32) a.o_f32[o] = v;
           if (a.o_hi) {
             uint32_t h, l;
@@ -227,15 +238,14 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs a) {
           }
         }
       } else {
-        if (col >= a.N) continue;
-        const float bias = (EPI == GEMM_STORE && a.bias) ? a.bias[col] : 0.f;
+        float* cb = a.c + (size_t)row0 * a.ldc + col;
+        const int ld = (int)a.ldc;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int row = rbase + i * 32 + 8 * (e / 4) + e % 4;
-          if (row >= a.M) continue;
-          float* cp = a.c + (size_t)row * a.ldc + col;
-          if (EPI == GEMM_RESID) *cp += acc[i][j][e];
-          else *cp = acc[i][j][e] + bias;
+          const int dr = 8 * (e / 4) + e % 4;
+          if (col >= a.N || row0 + dr >= a.M) continue;
+          if (EPI == GEMM_RESID) cb[dr * ld] += acc[i][j][e];
+          else cb[dr * ld] = acc[i][j][e] + biasv[j];
         }
       }
     }
@@ -273,11 +283,13 @@ int tiles_of(const GemmArgs& a, int bm, int bn) {
   return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
 }
 
-// Largest tile that still leaves about 0.7 tiles per CU (256 CUs); small M takes 64 rows.
-// (A 256 x 256 tile holds 256 accumulators per lane and spills around its epilogue.)
+// One-plane input: 128 x 128 tiles (measured at least as fast as 128 x 256 on the 1B and
+// 0.5B shapes, with twice the blocks); the two-plane (EXACT) input does better with 128 x
+// 256 when that still leaves ~0.7 tiles per CU. Small M takes 64 rows. A 256 x 256 tile holds 256 accumulators per
+// lane and spills around its epilogue.
 int pick_cfg(const GemmArgs& a) {
   if (a.M <= 64) return CFG_64x128;
-  if (tiles_of(a, 128, 256) >= 180) return CFG_128x256;
+  if (a.a_lo && tiles_of(a, 128, 256) >= 180) return CFG_128x256;   // two-plane (EXACT) input
   return CFG_128x128;
 }
 
