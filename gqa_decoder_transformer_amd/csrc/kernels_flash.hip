@@ -39,6 +39,15 @@ EMBER_DEV bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v)
 EMBER_DEV uint32_t pack2(uint32_t lo, uint32_t hi) { return (lo & 0xFFFFu) | (hi << 16); }
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two f32 -> packed bf16 (round to nearest even) with gfx950's v_cvt_pk_bf16_f32.
+EMBER_DEV uint32_t cvt_pk_bf16(float a, float b) {
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 template <int HD, bool SPLIT>
 __global__ void __launch_bounds__(256) k_flash_mfma(FlashArgs a) {
@@ -340,7 +349,8 @@ __global__ void __launch_bounds__(256) k_kv_pack(KvPackArgs a) {
 // Both tiles are double-buffered in LDS, loaded one tile ahead through registers from the
 // packed planes (16-byte loads, rows padded by 16 bytes). The softmax is the online one
 // in base 2 (scores pre-multiplied by scale * log2 e); masks are applied only on tiles
-// that cross the causal diagonal or the end of the keys; under the causal mask a wave
+// that cross the causal diagonal or the end of the keys (scale * log2 e is folded into Q
+// before its bf16 rounding; P is rounded with the hardware pack-convert); under the causal mask a wave
 // skips the tiles wholly past its last query. Output rows go through LDS and leave as 16-byte stores.
 constexpr int kTQ = 128, kTK = 64;
 
@@ -379,14 +389,17 @@ __global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t
   const int wq_first = a.start_pos + min(T - 1, q0);
   const int wq_last = a.start_pos + min(T - 1, q0 + 31);
 
-  // Q^T operand: query lq, head dims 16 ks + 8 hl .. + 8
+  // Q^T operand: query lq, head dims 16 ks + 8 hl .. + 8, pre-multiplied by
+  // scale * log2(e) so that the products are base-2 logits directly
+  const float c2 = a.scale * 1.4426950408889634f;
   bf16x8_t qh[NKS], qlo[SPLIT ? NKS : 1];
   {
     const float* qp = a.q + mrow * a.NH * HD + (size_t)h * HD + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const float4 x0 = *(const float4*)(qp + 16 * ks), x1 = *(const float4*)(qp + 16 * ks + 4);
-      const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      const float xv[8] = {x0.x * c2, x0.y * c2, x0.z * c2, x0.w * c2,
+                           x1.x * c2, x1.y * c2, x1.z * c2, x1.w * c2};
       u32x4_t hv, lv;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -442,7 +455,6 @@ __global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
   float mrun = -INFINITY, lrun = 0.f;
-  const float c2 = a.scale * 1.4426950408889634f;               // scale * log2(e)
 
   gload(0);
   sstore(0);
@@ -476,7 +488,7 @@ __global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float v = sc[kb][e] * c2;
+          float v = sc[kb][e];
           if (need_mask) {
             const int key = k0 + kb * 32 + 8 * (e / 4) + 4 * hl + (e % 4);
             if (key >= key_end || (a.causal && key > qpos)) v = -INFINITY;
@@ -486,13 +498,13 @@ __global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t
         }
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const float mnew = fmaxf(mrun, mt);                      // finite: key 0 is in tile 0
-      const float alpha = exp2f(mrun - mnew);                  // mrun = -inf -> 0
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew); // mrun = -inf -> 0
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = exp2f(sc[kb][e] - mnew);             // masked (-inf) -> 0
+          const float p = __builtin_amdgcn_exp2f(sc[kb][e] - mnew);   // masked (-inf) -> 0
           sc[kb][e] = p;
           ps += p;
         }
@@ -509,11 +521,9 @@ __global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t
         u32x4_t ph, pl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          uint32_t h0, l0, h1, l1;
-          split_bf16(sc[kb][e0 + 2 * i], h0, l0);
-          split_bf16(sc[kb][e0 + 2 * i + 1], h1, l1);
-          ph[i] = pack2(h0, h1);
-          pl[i] = pack2(l0, l1);
+          const float p0 = sc[kb][e0 + 2 * i], p1 = sc[kb][e0 + 2 * i + 1];
+          ph[i] = cvt_pk_bf16(p0, p1);
+          if (SPLIT) pl[i] = cvt_pk_bf16(p0 - bf16_lo(ph[i]), p1 - bf16_hi(ph[i]));
         }
         const bf16x8_t pbh = as_bf16x8(ph), pbl = as_bf16x8(pl);
 #pragma unroll
