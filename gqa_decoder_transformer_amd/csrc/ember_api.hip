@@ -289,6 +289,10 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   const float scale = (float)(1.0 / std::sqrt((double)HD));
   DecodePlan dp{1, c.max_seq, NH / NKV};
   if (ps.attn == ATTN_DECODE) dp = decode_split_plan(ps.M, NH, NKV, c.max_seq);
+  // one-row decode with at most 4 key splits: the output-projection GEMV rebuilds its
+  // input from the split partials (no combine launch)
+  const bool fuse_combine = ps.attn == ATTN_DECODE && ps.path == PATH_GEMV &&
+                            dp.nsplit > 1 && dp.nsplit <= 4;
 
   // ---- attention block
   if (ps.path == PATH_GEMV) {
@@ -364,7 +368,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     da.out_hi = planes_out ? pa_hi : nullptr;
     da.out_lo = planes_out ? pa_lo : nullptr;
     if (want(cx, EMBER_K_ATTN)) launch_decode_attn(da, st);
-    if (want_aux(cx) && dp.nsplit > 1)
+    if (want_aux(cx) && dp.nsplit > 1 && !fuse_combine)
       launch_attn_combine(part, ps.M, NH, HD, dp.nsplit, ps.d_pos, dp.chunk_min,
                           da.out_f32, da.out_hi, da.out_lo, st);
   }
@@ -373,6 +377,11 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     GemvArgs g{};
     g.W = wo; g.w_bf16 = md->wbf16; g.N = H; g.K = NH * HD; g.M = ps.M;
     g.x = att; g.y = x; g.ldy = H;
+    if (fuse_combine) {
+      g.x = nullptr;
+      g.xpart = part; g.xp_nsplit = dp.nsplit; g.xp_hd = HD; g.xp_chunk_min = dp.chunk_min;
+      g.xp_pos = ps.d_pos;
+    }
     if (want(cx, EMBER_K_O)) launch_gemv(g, GEMV_RESID, st);
   } else if (ps.path == PATH_MFMA) {
     GemmArgs g{};

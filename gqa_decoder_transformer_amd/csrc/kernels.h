@@ -94,6 +94,13 @@ struct GemvArgs {
   // input: x [K] f32; when norm_w != null the kernel applies RMSNorm to x first
   const float* x;
   const float* norm_w;
+  // or (x == null) the input rebuilt from decode-attention split partials of one row:
+  // xpart [K / xp_hd heads][xp_nsplit][xp_hd + 2] = (m, l, acc[xp_hd]); xp_nsplit <= 4;
+  // x[h xp_hd + d] = sum_j acc_j[d] w_j / sum_j l_j w_j, w_j = e^(m_j - max m), over the
+  // splits that hold a key up to the position (the k_attn_combine arithmetic)
+  const float* xpart;
+  int xp_nsplit, xp_hd, xp_chunk_min;
+  const int* xp_pos;
   float eps;
   // outputs
   const float* bias;       // [N] or null (STORE)

@@ -61,6 +61,53 @@ EMBER_DEV void load_chunk_f32(const float* p, int c, bool valid, float* out) {
   }
 }
 
+// Input chunk c rebuilt from decode-attention split partials (see GemvArgs::xpart).
+// Splits at or past the number that hold keys are excluded by select (their memory may
+// hold anything).
+template <int E>
+EMBER_DEV void load_chunk_part(const GemvArgs& a, int c, bool valid, float* out) {
+  const int k0 = c * E;
+  const int h = k0 / a.xp_hd, d0 = k0 % a.xp_hd;
+  const int stride = a.xp_hd + 2;
+  const float* ph = a.xpart + (size_t)h * a.xp_nsplit * stride;
+  const int S = *a.xp_pos + 1;
+  int chunk = (S + a.xp_nsplit - 1) / a.xp_nsplit;
+  if (chunk < a.xp_chunk_min) chunk = a.xp_chunk_min;
+  const int nv = (S + chunk - 1) / chunk;
+  float m[4], l[4], ac[4][E];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float* pj = ph + (size_t)min(j, a.xp_nsplit - 1) * stride;
+    m[j] = pj[0];
+    l[j] = pj[1];
+#pragma unroll
+    for (int e = 0; e < E; ++e) ac[j][e] = pj[2 + d0 + e];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) M = j < nv ? fmaxf(M, m[j]) : M;
+  float L = 0.f, w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    w[j] = (j < nv && m[j] != -INFINITY) ? expf(m[j] - M) : 0.f;
+    L = j < nv ? fmaf(l[j], w[j], L) : L;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float x = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x = j < nv ? fmaf(ac[j][e], w[j], x) : x;
+    out[e] = valid ? x * inv : 0.f;
+  }
+}
+
+template <int E, bool XP>
+EMBER_DEV void load_input(const GemvArgs& a, int c, bool valid, float* out) {
+  if (XP) load_chunk_part<E>(a, c, valid, out);
+  else load_chunk_f32<E>(a.x, c, valid, out);
+}
+
 // Epilogue of one output unit n (value(s) already reduced).
 template <int EPI>
 EMBER_DEV void epilogue(const GemvArgs& a, int n, const float* v, bool writer,
@@ -83,7 +130,7 @@ EMBER_DEV void epilogue(const GemvArgs& a, int n, const float* v, bool writer,
 }
 
 // ---------------------------------------------------------------- row per wave
-template <typename WT, int EPI, int RPW, int U>
+template <typename WT, int EPI, int RPW, int U, bool XP>
 __global__ void __launch_bounds__(kThreads) k_gemv_wave(GemvArgs a) {
   constexpr int E = WTraits<WT>::E;
   constexpr int RU = (EPI == GEMV_SILU) ? 2 : 1;
@@ -121,7 +168,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_wave(GemvArgs a) {
 #pragma unroll
   for (int t = 0; t < U; ++t) {
     const int c = lane + kWave * t;
-    load_chunk_f32<E>(a.x, min(c, nch - 1), c < nch, xv[t]);
+    load_input<E, XP>(a, min(c, nch - 1), c < nch, xv[t]);
     if (a.norm_w) load_chunk_f32<E>(a.norm_w, min(c, nch - 1), c < nch, nv[t]);
 #pragma unroll
     for (int e = 0; e < E; ++e) ss += xv[t][e] * xv[t][e];
@@ -167,7 +214,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_wave(GemvArgs a) {
 }
 
 // ---------------------------------------------------------------- row per block
-template <typename WT, int EPI, int RPW, int U>
+template <typename WT, int EPI, int RPW, int U, bool XP>
 __global__ void __launch_bounds__(kThreads) k_gemv_block(GemvArgs a) {
   constexpr int E = WTraits<WT>::E;
   constexpr int RU = (EPI == GEMV_SILU) ? 2 : 1;
@@ -204,7 +251,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_block(GemvArgs a) {
 #pragma unroll
   for (int t = 0; t < U; ++t) {
     const int c = threadIdx.x + kThreads * t;
-    load_chunk_f32<E>(a.x, min(c, nch - 1), c < nch, xv[t]);
+    load_input<E, XP>(a, min(c, nch - 1), c < nch, xv[t]);
     if (a.norm_w) load_chunk_f32<E>(a.norm_w, min(c, nch - 1), c < nch, nv[t]);
 #pragma unroll
     for (int e = 0; e < E; ++e) ss += xv[t][e] * xv[t][e];
@@ -290,13 +337,21 @@ Shape pick(int N, int K, bool bf16, int epi) {
   return s;
 }
 
+// the input rebuilt from attention partials is built only for the residual epilogue (the
+// output projection); other instances keep their register budget
 template <typename WT, int EPI, int RPW, int U>
 void launch_wave(const GemvArgs& a, int blocks, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemv_wave<WT, EPI, RPW, U>), dim3(blocks), dim3(kThreads), 0, st, a);
+  if (EPI == GEMV_RESID && a.xpart)
+    hipLaunchKernelGGL((k_gemv_wave<WT, EPI, RPW, U, EPI == GEMV_RESID>), dim3(blocks), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemv_wave<WT, EPI, RPW, U, false>), dim3(blocks), dim3(kThreads), 0, st, a);
 }
 template <typename WT, int EPI, int RPW, int U>
 void launch_block(const GemvArgs& a, int blocks, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemv_block<WT, EPI, RPW, U>), dim3(blocks), dim3(kThreads), 0, st, a);
+  if (EPI == GEMV_RESID && a.xpart)
+    hipLaunchKernelGGL((k_gemv_block<WT, EPI, RPW, U, EPI == GEMV_RESID>), dim3(blocks), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemv_block<WT, EPI, RPW, U, false>), dim3(blocks), dim3(kThreads), 0, st, a);
 }
 
 template <typename WT, int EPI>
@@ -323,7 +378,7 @@ int gemv_num_blocks(int N, int epi, int K, bool bf16) {
 }
 
 void launch_gemv(const GemvArgs& a, int epi, hipStream_t st) {
-  if (a.M != 1 || a.N <= 0 || !a.x) return;           // one token, input vector required
+  if (a.M != 1 || a.N <= 0 || (!a.x && !a.xpart)) return;   // one token, an input required
 #define EMBER_GEMV_CASE(E)                                               \
   case E:                                                                \
     if (a.w_bf16) launch_t<uint16_t, E>(a, st);                          \
