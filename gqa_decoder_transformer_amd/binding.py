@@ -65,6 +65,10 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                           "(hipcc --offload-arch=gfx950); there is no fallback path")
+    # torch's bundled HIP runtime carries the same soname as the system one; loading torch
+    # first makes the library bind to that runtime, so the process holds one HIP runtime
+    # (a second, separately loaded runtime finds no device)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     cfgp = ctypes.POINTER(EmberConfig)

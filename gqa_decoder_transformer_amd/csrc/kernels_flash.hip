@@ -482,17 +482,18 @@ __global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t
           }
         }
       }
+      // keys past `klim` are masked: one compare and select per score, no branches
+      // (tiles wholly below the diagonal get a limit no key reaches)
       const bool need_mask = (a.causal && k0 + kTK - 1 > wq_first) || k0 + kTK > key_end;
+      const int klim = need_mask ? (a.causal ? min(key_end - 1, qpos) : key_end - 1) - k0 - 4 * hl
+                                 : kTK;
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float v = sc[kb][e];
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 8 * (e / 4) + 4 * hl + (e % 4);
-            if (key >= key_end || (a.causal && key > qpos)) v = -INFINITY;
-          }
+          const int kofs = kb * 32 + 8 * (e / 4) + (e % 4);      // key - k0 - 4 hl
+          const float v = kofs > klim ? -INFINITY : sc[kb][e];
           sc[kb][e] = v;
           mt = fmaxf(mt, v);
         }

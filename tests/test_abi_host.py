@@ -87,3 +87,20 @@ def test_host_rope_table_equals_oracle_table(name):
     assert np.abs(cos.view(np.int32) - oc.view(np.int32)).max() <= 1
     assert np.abs(sin.view(np.int32) - os_.view(np.int32)).max() <= 1
     assert (cos != oc).mean() < 1e-4 and (sin != os_).mean() < 1e-4
+
+
+def test_one_hip_runtime_in_process():
+    """The library must bind to the HIP runtime torch already holds (both carry the soname
+    libamdhip64.so.7); two runtimes in one process leave the library without a device.
+    Checked in a fresh interpreter that imports the binding before anything else."""
+    import subprocess
+    import sys
+    code = ("from gqa_decoder_transformer_amd import binding\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().split('\\n')\n"
+            "libs = sorted({l.split()[-1] for l in maps if 'libamdhip64' in l})\n"
+            "print(len(libs)); print(libs)\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split("\n")[0] == "1", out.stdout
