@@ -3,17 +3,17 @@
 //
 // At decode sizes these kernels are bound by how early and how many weight bytes are in
 // flight, so nothing is staged through LDS:
-//  * row per wave  (K <= 64 * U * E): lane l owns the 16-byte chunks c = l + 64 t of
-//    every row its wave touches. It loads the matching input elements x[E c .. E c + E)
-//    into registers once; with a fused RMSNorm the wave computes sum(x^2) itself (its
-//    lanes cover all of K) and scales by one reciprocal of the RMS. All loads are
-//    branch-free (clamped chunk indices; a clamped chunk meets x = 0), so the input loads
-//    issue right behind the weight loads instead of after them. Each wave takes one row group (RPW outputs, 16 weight loads
-//    of 16 bytes per lane, all issued before the input is read) -- more only when the
-//    grid would exceed 8192 waves -- and reduces each output with DPP row sums +
-//    readlane (no block barrier).
-//  * row per block (longer K): thread t owns chunks t + 256 u; one block-wide sum of
-//    squares for the norm; per row group the four waves' partials meet in LDS.
+//  * row per wave  (K <= 128 chunks of 16 bytes): lane l owns the chunks c = l + 64 t of
+//    its wave's rows. It first requests the matching input elements x[E c .. E c + E)
+//    (and norm weights; they come from L2), then every weight load of its row group, so
+//    the input arrives first and the RMSNorm (the wave's lanes cover all of K: sum(x^2),
+//    one reciprocal of the RMS) is done while the weights are in flight. All loads are
+//    branch-free (clamped chunk indices; a clamped chunk meets x = 0; a spare wave past
+//    the last row group reloads it), which keeps the compiler's waits counted. Each
+//    output is reduced with DPP row sums + readlane (no block barrier).
+//  * row per block (up to 1024 chunks): thread t owns chunks t + 256 u; one block-wide
+//    sum of squares for the norm; per row group the four waves' partials meet in LDS.
+//  * longer K: a block per output looping over K (shapes past the two layouts above).
 // Epilogues: store (+bias), residual add, SiLU*up (gate/up rows interleaved in blocks of
 // 32, see gu_row), logits with an argmax partial (value, then lowest index) per wave or block.
 #include "common.h"
@@ -158,21 +158,24 @@ __global__ void __launch_bounds__(kThreads) k_gemv_wave(GemvArgs a) {
     }
   };
 
-  u32x4_t wa[U][NR];
-  int grp = gw;
-  if (grp < ngroups) load_group(grp, wa);           // weights first: independent of x
-
-  // this lane's input elements (and norm weights), normalised in registers
+  // this lane's input elements (and norm weights) are requested first: they come from L2
+  // and are normalised while the weights are still in flight
   float xv[U][E], nv[U][E];
-  float ss = 0.f;
 #pragma unroll
   for (int t = 0; t < U; ++t) {
     const int c = lane + kWave * t;
     load_input<E, XP>(a, min(c, nch - 1), c < nch, xv[t]);
     if (a.norm_w) load_chunk_f32<E>(a.norm_w, min(c, nch - 1), c < nch, nv[t]);
+  }
+  u32x4_t wa[U][NR];
+  int grp = gw;
+  load_group(min(grp, ngroups - 1), wa);            // unconditional: a spare wave reloads
+
+  float ss = 0.f;
+#pragma unroll
+  for (int t = 0; t < U; ++t)
 #pragma unroll
     for (int e = 0; e < E; ++e) ss += xv[t][e] * xv[t][e];
-  }
   if (a.norm_w) {
     ss = wave_sum_uniform(ss);
     const float inv_rms = 1.0f / sqrtf(ss / (float)K + a.eps);
@@ -242,20 +245,22 @@ __global__ void __launch_bounds__(kThreads) k_gemv_block(GemvArgs a) {
     }
   };
 
-  u32x4_t wa[U][NR];
-  int grp = blockIdx.x;
-  if (grp < ngroups) load_group(grp, wa);
-
   float xv[U][E], nv[U][E];
-  float ss = 0.f;
 #pragma unroll
   for (int t = 0; t < U; ++t) {
     const int c = threadIdx.x + kThreads * t;
     load_input<E, XP>(a, min(c, nch - 1), c < nch, xv[t]);
     if (a.norm_w) load_chunk_f32<E>(a.norm_w, min(c, nch - 1), c < nch, nv[t]);
+  }
+  u32x4_t wa[U][NR];
+  int grp = blockIdx.x;
+  load_group(min(grp, ngroups - 1), wa);
+
+  float ss = 0.f;
+#pragma unroll
+  for (int t = 0; t < U; ++t)
 #pragma unroll
     for (int e = 0; e < E; ++e) ss += xv[t][e] * xv[t][e];
-  }
   if (a.norm_w) {
     ss = block_sum(ss, red);
     const float inv_rms = 1.0f / sqrtf(ss / (float)K + a.eps);
@@ -305,32 +310,110 @@ __global__ void __launch_bounds__(kThreads) k_gemv_block(GemvArgs a) {
   if (EPI == GEMV_LOGITS && threadIdx.x == 0) a.argmax_part[blockIdx.x] = best;
 }
 
+// ---------------------------------------------------------------- long K
+// K beyond 1024 chunks (1024 x 16 bytes): one block per output unit at a time, looping
+// over K; the norm's sum of squares takes its own pass over the input. Only shapes past
+// the limits of the two kernels above use it.
+template <typename WT, int EPI, bool XP>
+__global__ void __launch_bounds__(kThreads) k_gemv_long(GemvArgs a) {
+  constexpr int E = WTraits<WT>::E;
+  constexpr int RU = (EPI == GEMV_SILU) ? 2 : 1;
+  __shared__ float red[16];
+  const int K = a.K, nch = K / E;
+  float inv_rms = 1.f;
+  if (a.norm_w) {
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < nch; c += kThreads) {
+      float xv[E];
+      load_input<E, XP>(a, c, true, xv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) ss += xv[e] * xv[e];
+    }
+    ss = block_sum(ss, red);
+    inv_rms = 1.0f / sqrtf(ss / (float)K + a.eps);
+  }
+  unsigned long long best = 0;
+  for (int n = blockIdx.x; n < a.N; n += gridDim.x) {          // block-uniform
+    float acc[RU];
+#pragma unroll
+    for (int r = 0; r < RU; ++r) acc[r] = 0.f;
+    for (int c = threadIdx.x; c < nch; c += kThreads) {
+      float xv[E];
+      load_input<E, XP>(a, c, true, xv);
+      if (a.norm_w) {
+        float nv[E];
+        load_chunk_f32<E>(a.norm_w, c, true, nv);
+#pragma unroll
+        for (int e = 0; e < E; ++e) xv[e] = xv[e] * inv_rms * nv[e];
+      }
+#pragma unroll
+      for (int r = 0; r < RU; ++r) {
+        const WT* row = (const WT*)a.W + (size_t)weight_row<EPI>(n, r) * K;
+        float wf[E];
+        WTraits<WT>::widen(*(const u32x4_t*)(row + (size_t)c * E), wf);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[r] = fmaf(wf[e], xv[e], acc[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RU; ++r) acc[r] = block_sum(acc[r], red);
+    epilogue<EPI>(a, n, acc, threadIdx.x == 0, best);
+  }
+  if (EPI == GEMV_LOGITS && threadIdx.x == 0) a.argmax_part[blockIdx.x] = best;
+}
+
+enum ShapeKind { SHAPE_WAVE, SHAPE_BLOCK, SHAPE_LONG };
 struct Shape {
-  bool block_row;
+  ShapeKind kind;
   int rpw, u, blocks;
 };
 
-// Work layout. Row per wave when a wave's 64 lanes cover K with at most 4 chunks each;
-// enough waves to put every weight byte in flight, but not so many that re-reading the
-// input vector per wave costs a noticeable fraction of the weight traffic.
+// Work layout, from graph-timed sweeps over weights streamed from HBM: many waves with few
+// loads each beat few waves with many loads (each row group costs a reduction and an
+// epilogue after its last weight byte lands). Row per wave (one output unit, one or two
+// 16-byte loads per lane per row) while 128 chunks cover K; row per block up to 1024
+// chunks (two output units per block once the grid would pass 1024 blocks); a K loop
+// beyond. The logits GEMV keeps larger row groups: it loops over 128k+ rows and its
+// per-group argmax favours fewer groups.
 Shape pick(int N, int K, bool bf16, int epi) {
   const int E = bf16 ? 8 : 4;
   const int nch = K / E;
   const int ru = epi == GEMV_SILU ? 2 : 1;
   Shape s;
-  if (nch <= kWave * 4) {
-    // 16 weight loads of 16 bytes per lane, one row group per wave while the grid fits
-    s.block_row = false;
-    s.u = nch <= kWave ? 1 : (nch <= kWave * 2 ? 2 : 4);
-    s.rpw = s.u == 4 ? 4 / ru : 8 / ru;                // = the launched template
-    const int groups = (N + s.rpw - 1) / s.rpw;
-    const int waves = groups < 8192 ? groups : 8192;
+  if (nch > kThreads * 4) {
+    s.kind = SHAPE_LONG;
+    s.rpw = 1;
+    s.u = 0;
+    s.blocks = N < 2048 ? N : 2048;
+    return s;
+  }
+  if (epi == GEMV_LOGITS) {
+    if (nch <= kWave * 4) {
+      s.kind = SHAPE_WAVE;
+      s.u = nch <= kWave ? 1 : (nch <= kWave * 2 ? 2 : 4);
+      s.rpw = s.u == 4 ? 4 / ru : 8 / ru;
+      const int groups = (N + s.rpw - 1) / s.rpw;
+      const int waves = groups < 8192 ? groups : 8192;
+      s.blocks = (waves + kWaves - 1) / kWaves;
+    } else {
+      s.kind = SHAPE_BLOCK;
+      s.u = (nch + kThreads - 1) / kThreads <= 2 ? 2 : 4;
+      s.rpw = s.u == 2 ? 4 / ru : 2 / ru;
+      const int groups = (N + s.rpw - 1) / s.rpw;
+      s.blocks = groups < 2048 ? groups : 2048;
+    }
+    return s;
+  }
+  if (nch <= kWave * 2) {
+    s.kind = SHAPE_WAVE;
+    s.u = nch <= kWave ? 1 : 2;
+    s.rpw = 1;
+    const int waves = N < 8192 ? N : 8192;
     s.blocks = (waves + kWaves - 1) / kWaves;
   } else {
-    s.block_row = true;
-    s.u = (nch + kThreads - 1) / kThreads;
-    s.u = s.u <= 2 ? 2 : 4;
-    s.rpw = s.u == 2 ? 4 / ru : 2 / ru;
+    s.kind = SHAPE_BLOCK;
+    s.u = (nch + kThreads - 1) / kThreads;            // 1 .. 4
+    s.rpw = (s.u >= 3 && N > 1024) ? 2 : 1;
     const int groups = (N + s.rpw - 1) / s.rpw;
     s.blocks = groups < 2048 ? groups : 2048;
   }
@@ -358,15 +441,38 @@ template <typename WT, int EPI>
 void launch_t(const GemvArgs& a, hipStream_t st) {
   const Shape s = pick(a.N, a.K, sizeof(WT) == 2, EPI);
   constexpr int RU = EPI == GEMV_SILU ? 2 : 1;
-  if (s.block_row) {
-    if (s.u == 2) launch_block<WT, EPI, 4 / RU, 2>(a, s.blocks, st);
-    else launch_block<WT, EPI, 2 / RU, 4>(a, s.blocks, st);
+  if (s.kind == SHAPE_LONG) {
+    if (EPI == GEMV_RESID && a.xpart)
+      hipLaunchKernelGGL((k_gemv_long<WT, EPI, EPI == GEMV_RESID>), dim3(s.blocks), dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_gemv_long<WT, EPI, false>), dim3(s.blocks), dim3(kThreads), 0, st, a);
     return;
   }
-  switch (s.u) {
-    case 1: launch_wave<WT, EPI, 8 / RU, 1>(a, s.blocks, st); break;
-    case 2: launch_wave<WT, EPI, 8 / RU, 2>(a, s.blocks, st); break;
-    default: launch_wave<WT, EPI, 4 / RU, 4>(a, s.blocks, st); break;
+  if (EPI == GEMV_LOGITS) {
+    if (s.kind == SHAPE_BLOCK) {
+      if (s.u == 2) launch_block<WT, EPI, 4 / RU, 2>(a, s.blocks, st);
+      else launch_block<WT, EPI, 2 / RU, 4>(a, s.blocks, st);
+      return;
+    }
+    switch (s.u) {
+      case 1: launch_wave<WT, EPI, 8 / RU, 1>(a, s.blocks, st); break;
+      case 2: launch_wave<WT, EPI, 8 / RU, 2>(a, s.blocks, st); break;
+      default: launch_wave<WT, EPI, 4 / RU, 4>(a, s.blocks, st); break;
+    }
+    return;
+  }
+  if (s.kind == SHAPE_WAVE) {
+    if (s.u == 1) launch_wave<WT, EPI, 1, 1>(a, s.blocks, st);
+    else launch_wave<WT, EPI, 1, 2>(a, s.blocks, st);
+    return;
+  }
+  switch (s.u * 4 + s.rpw) {
+    case 1 * 4 + 1: launch_block<WT, EPI, 1, 1>(a, s.blocks, st); break;
+    case 2 * 4 + 1: launch_block<WT, EPI, 1, 2>(a, s.blocks, st); break;
+    case 3 * 4 + 1: launch_block<WT, EPI, 1, 3>(a, s.blocks, st); break;
+    case 3 * 4 + 2: launch_block<WT, EPI, 2, 3>(a, s.blocks, st); break;
+    case 4 * 4 + 1: launch_block<WT, EPI, 1, 4>(a, s.blocks, st); break;
+    default: launch_block<WT, EPI, 2, 4>(a, s.blocks, st); break;
   }
 }
 
@@ -374,7 +480,7 @@ void launch_t(const GemvArgs& a, hipStream_t st) {
 
 int gemv_num_blocks(int N, int epi, int K, bool bf16) {
   const Shape s = pick(N, K, bf16, epi);
-  return s.block_row ? s.blocks : s.blocks * kWaves;   // argmax partials written
+  return s.kind == SHAPE_WAVE ? s.blocks * kWaves : s.blocks;   // argmax partials written
 }
 
 void launch_gemv(const GemvArgs& a, int epi, hipStream_t st) {

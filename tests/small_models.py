@@ -28,3 +28,12 @@ QWEN_HD64_G7 = C.shrink_model(C.QWEN05B, name="qwen-hd64-g7", vocab=97, hidden=4
 # long K against few output tiles: the projections take the split-K path
 LLAMA_SPLITK = C.shrink_model(C.LLAMA1B, name="llama-splitk", vocab=131, hidden=256, layers=2,
                               heads=4, kv_heads=2, head_dim=64, ffn=1024)
+
+# decode GEMV layouts past row-per-wave: the down projection's K takes the row-per-block
+# layout with two chunks per thread (ffn 2304) and the K-looping kernel (ffn 8448 bf16 is
+# more than 1024 chunks of 16 bytes)
+QWEN_FF2K = C.shrink_model(C.QWEN05B, name="qwen-ff2k", vocab=97, hidden=64, layers=2,
+                           heads=4, kv_heads=2, head_dim=16, ffn=2304)
+
+LLAMA_FF8K = C.shrink_model(C.LLAMA1B, name="llama-ff8k", vocab=101, hidden=64, layers=2,
+                            heads=8, kv_heads=2, head_dim=8, ffn=8448)

@@ -10,8 +10,8 @@ import pytest
 import oracle as O
 import workloads as W
 from tests.gpu_util import TOL_EXACT, TOL_FAST, check_greedy, gpu_generate, rel_maxabs, say
-from tests.small_models import (ENCODER_HD128, ENCODER_SMALL, LLAMA_HD64, LLAMA_SMALL, LLAMA_SPLITK,
-                                QWEN_HD64_G7, QWEN_SMALL, TINY)
+from tests.small_models import (ENCODER_HD128, ENCODER_SMALL, LLAMA_FF8K, LLAMA_HD64, LLAMA_SMALL,
+                                LLAMA_SPLITK, QWEN_FF2K, QWEN_HD64_G7, QWEN_SMALL, TINY)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,7 @@ def _sharp(ck, factor=30.0):
 # ----------------------------------------------------------------------------- small shapes
 
 @pytest.mark.parametrize("model", [TINY, QWEN_SMALL, LLAMA_SMALL, LLAMA_HD64, QWEN_HD64_G7,
-                                   LLAMA_SPLITK], ids=lambda m: m.name)
+                                   LLAMA_SPLITK, QWEN_FF2K, LLAMA_FF8K], ids=lambda m: m.name)
 @pytest.mark.parametrize("sharp", [False, True], ids=["init", "peaked"])
 def test_small_decoder_exact_prefill_and_decode(model, sharp):
     from gqa_decoder_transformer_amd import binding as B
@@ -65,8 +65,8 @@ def test_small_decoder_exact_prefill_and_decode(model, sharp):
     assert rel_maxabs(allg[0].cpu().numpy(), full).max() < TOL_EXACT
 
 
-@pytest.mark.parametrize("model", [QWEN_SMALL, LLAMA_SMALL, LLAMA_HD64, QWEN_HD64_G7, LLAMA_SPLITK],
-                         ids=lambda m: m.name)
+@pytest.mark.parametrize("model", [QWEN_SMALL, LLAMA_SMALL, LLAMA_HD64, QWEN_HD64_G7, LLAMA_SPLITK,
+                                   QWEN_FF2K, LLAMA_FF8K], ids=lambda m: m.name)
 @pytest.mark.parametrize("sharp", [1.0, 4.0], ids=["init", "x4"])
 def test_small_decoder_fast_bf16_logits(model, sharp):
     # FAST rounds K/V and every GEMM input to bf16 (2^-9): with attention scores of
