@@ -221,6 +221,15 @@ def main():
                 kernels[f"{'decode' if phase == 0 else 'prefill'}.{name}"] = {
                     "avg_us": us, "launches_per_step": launches,
                     "ms_per_step": us * launches / 1000.0, "bound": bound, "work_per_launch": work}
+        # one whole layer (every kernel, back to back, cycling the layers) beside the sum of
+        # its kernels timed one kind at a time
+        layer_us = {}
+        for phase in phases:
+            tag = "decode" if phase == 0 else "prefill"
+            layer_us[tag] = eng.time_kernel(B.K_LAYER, phase, args.timing_iters)
+            layer_us[tag + "_kernel_sum"] = sum(
+                v["avg_us"] for k, v in kernels.items()
+                if k.startswith(tag + ".") and not k.endswith("lm_head"))
     for k, v in kernels.items():
         if v["bound"] == "hbm":
             v["achieved"] = v["work_per_launch"] / (v["avg_us"] * 1e-6) / 1e9
@@ -276,6 +285,7 @@ def main():
                      "avg_us": dom["avg_us"], "work_per_launch": dom["work_per_launch"]},
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                         for kk, vv in v.items()} for k, v in kernels.items()},
+        "layer_us": {k: round(v, 3) for k, v in layer_us.items()},
         **extra,
     }
     eng.close()

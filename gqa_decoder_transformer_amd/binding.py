@@ -27,7 +27,7 @@ EXPORTED = ["ember_workspace_bytes", "ember_kv_cache_bytes", "ember_load_weights
             "ember_cache_bind", "ember_prefill", "ember_decode_step", "ember_logits",
             "ember_sync", "ember_cache_free", "ember_free", "ember_last_error",
             "ember_rope_table", "ember_time_kernel"]
-K_LM_HEAD, K_QKV, K_ATTN, K_O, K_GATE_UP, K_DOWN = range(6)
+K_LM_HEAD, K_QKV, K_ATTN, K_O, K_GATE_UP, K_DOWN, K_LAYER = range(7)
 
 
 class EmberConfig(ctypes.Structure):

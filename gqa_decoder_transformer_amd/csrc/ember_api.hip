@@ -56,7 +56,7 @@ struct Plan {
   std::vector<LayerOff> layer;
   // activations
   size_t ids, pos, rope_cur, next, flags, x, xb, pa_hi, pa_lo, pb_hi, pb_lo, qkv, q, att, act, part,
-      logits, hrow, argpart, splitk, kvpack;
+      logits, argpart, splitk, kvpack;
   size_t splitk_elems, kvpack_elems;
   size_t total;
   int Mx, qkv_n, ka, nsplit_max, argparts;
@@ -157,7 +157,6 @@ Plan make_plan(const ember_config& c) {
   p.act = take((size_t)Mx * FF * 4);
   p.part = take((size_t)c.max_batch * NH * p.nsplit_max * (HD + 2) * 4);
   p.logits = take((size_t)c.max_batch * out_dim * 4);
-  p.hrow = take((size_t)c.max_batch * H * 4);
   p.argpart = take((size_t)p.argparts * 8);
   {
     // split-K partial planes for GEMMs whose tiles cannot fill the GPU (M <= 128)
@@ -220,6 +219,7 @@ struct ember_model {
   const ember_cache* graph_cache = nullptr;
   int graph_batch = -1;
   hipStream_t graph_stream = nullptr;
+  int32_t* graph_next = nullptr;
   template <typename T> T* at(size_t off) const { return (T*)(ws + off); }
   float* splitk() const { return plan.splitk_elems ? (float*)(ws + plan.splitk) : nullptr; }
 };
@@ -292,7 +292,8 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   // one-row decode with at most 4 key splits: the output-projection GEMV rebuilds its
   // input from the split partials (no combine launch)
   const bool fuse_combine = ps.attn == ATTN_DECODE && ps.path == PATH_GEMV &&
-                            dp.nsplit > 1 && dp.nsplit <= 4;
+                            dp.nsplit > 1 && dp.nsplit <= 4 &&
+                            gemv_takes_parts(H, NH * HD, md->wbf16);
 
   // ---- attention block
   if (ps.path == PATH_GEMV) {
@@ -442,13 +443,12 @@ void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, lo
   const int H = c.hidden, V = c.vocab;
   const float* fn = md->at<float>(p.fnorm);
   const void* E = md->ws + p.embed;
-  float* hrow = md->at<float>(p.hrow);
   if (R == 1 && ld == V) {
-    if (want_aux(cx))
-      launch_rmsnorm(md->at<float>(p.x), fn, c.rms_eps, 1, H, row_step, row_off, hrow, nullptr,
-                     nullptr, 0, st);
+    // the final RMSNorm is fused into the GEMV
     GemvArgs g{};
-    g.W = E; g.w_bf16 = md->wbf16; g.N = V; g.K = H; g.M = 1; g.x = hrow; g.y = out; g.ldy = V;
+    g.W = E; g.w_bf16 = md->wbf16; g.N = V; g.K = H; g.M = 1;
+    g.x = md->at<float>(p.x) + (size_t)row_off * H; g.norm_w = fn; g.eps = c.rms_eps;
+    g.y = out; g.ldy = V;
     g.argmax_part = md->at<unsigned long long>(p.argpart);
     g.flags = md->at<int>(p.flags);
     if (want(cx, EMBER_K_LM_HEAD)) launch_gemv(g, GEMV_LOGITS, st);
@@ -506,12 +506,12 @@ void run_cls_head(const Ctx& cx, int R, int row_step, int row_off, float* out, i
 }
 
 // One decode step's device work for B rows, ids in plan.ids, position in plan.pos.
-void decode_body(const Ctx& cx, int B, int only_layer = -1) {
+// The layers and the LM head of one decode step (the step's embedding and staging run
+// before it); greedy ids go to `next`.
+void decode_body(const Ctx& cx, int B, int32_t* next, int only_layer = -1) {
   ember_model* md = cx.m;
   const ember_config& c = md->cfg;
   const Plan& p = md->plan;
-  if (want_aux(cx)) launch_embed(md->at<int32_t>(p.ids), md->ws + p.embed, md->wbf16, md->at<float>(p.x), B,
-               c.hidden, c.vocab, md->at<int>(p.flags), cx.st);
   Pass ps{};
   ps.M = B; ps.rows = B; ps.tpr = 1; ps.b0 = 0; ps.start = 0; ps.d_pos = md->at<int>(p.pos);
   ps.path = B == 1 ? PATH_GEMV : (md->wbf16 ? PATH_MFMA : PATH_F32W);
@@ -519,7 +519,7 @@ void decode_body(const Ctx& cx, int B, int only_layer = -1) {
   for (int l = 0; l < c.layers; ++l)
     if (only_layer < 0 || l == only_layer) run_layer(cx, l, ps);
   if (want(cx, EMBER_K_LM_HEAD) && (cx.only >= 0 || only_layer < 0))
-    run_lm_head(cx, B, 1, 0, md->at<float>(p.logits), c.vocab, md->at<int32_t>(p.next));
+    run_lm_head(cx, B, 1, 0, md->at<float>(p.logits), c.vocab, next);
 }
 
 bool graphs_enabled() {
@@ -798,18 +798,23 @@ ember_status ember_decode_step(ember_model* md, ember_cache* cache, const int32_
   hipStream_t st = (hipStream_t)stream;
   const Plan& p = md->plan;
   Ctx cx{md, cache, st};
-  launch_stage_step(d_ids, batch, c.vocab, pos, md->at<int32_t>(p.ids), md->at<int>(p.pos),
-                    md->at<int>(p.flags), md->at<float>(p.cos_t), md->at<float>(p.sin_t),
-                    c.head_dim / 2, md->at<float>(p.rope_cur), st);
+  StepBeginArgs sb{};
+  sb.ids = d_ids; sb.R = batch; sb.V = c.vocab; sb.pos = pos;
+  sb.d_pos = md->at<int>(p.pos); sb.flags = md->at<int>(p.flags);
+  sb.cos_t = md->at<float>(p.cos_t); sb.sin_t = md->at<float>(p.sin_t); sb.half = c.head_dim / 2;
+  sb.rope_cur = md->at<float>(p.rope_cur);
+  sb.E = md->ws + p.embed; sb.e_bf16 = md->wbf16; sb.x = md->at<float>(p.x); sb.H = c.hidden;
+  launch_step_begin(sb, st);
   const bool use_graph = st != nullptr && graphs_enabled();
   if (use_graph) {
-    if (!md->graph || md->graph_cache != cache || md->graph_batch != batch || md->graph_stream != st) {
+    if (!md->graph || md->graph_cache != cache || md->graph_batch != batch || md->graph_stream != st ||
+        md->graph_next != d_next) {
       if (md->graph) {
         (void)hipGraphExecDestroy(md->graph);
         md->graph = nullptr;
       }
       HIP_TRY(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
-      decode_body(cx, batch);
+      decode_body(cx, batch, d_next);
       hipGraph_t g = nullptr;
       HIP_TRY(hipStreamEndCapture(st, &g));
       hipError_t e = hipGraphInstantiate(&md->graph, g, nullptr, nullptr, 0);
@@ -818,12 +823,12 @@ ember_status ember_decode_step(ember_model* md, ember_cache* cache, const int32_
       md->graph_cache = cache;
       md->graph_batch = batch;
       md->graph_stream = st;
+      md->graph_next = d_next;
     }
     HIP_TRY(hipGraphLaunch(md->graph, st));
   } else {
-    decode_body(cx, batch);
+    decode_body(cx, batch, d_next);
   }
-  launch_copy_ids(md->at<int32_t>(p.next), batch, d_next, st);
   HIP_TRY(hipGetLastError());
   if (pos + 1 > cache->filled) cache->filled = pos + 1;
   md->has_logits_rows = batch;
@@ -835,9 +840,9 @@ ember_status ember_time_kernel(ember_model* md, ember_cache* cache, int32_t kern
                                int32_t iters, void* stream, float* avg_us) {
   g_last_error.clear();
   if (!md || !cache || !avg_us || iters <= 0) return fail(EMBER_E_ARG, "bad arguments");
-  if (kernel < EMBER_K_LM_HEAD || kernel > EMBER_K_DOWN) return fail(EMBER_E_ARG, "unknown kernel");
+  if (kernel < EMBER_K_LM_HEAD || kernel > EMBER_K_LAYER) return fail(EMBER_E_ARG, "unknown kernel");
   hipStream_t st = (hipStream_t)stream;
-  Ctx cx{md, cache, st, kernel};
+  Ctx cx{md, cache, st, kernel == EMBER_K_LAYER ? -1 : kernel};
   const ember_config& c = md->cfg;
   const Plan& p = md->plan;
   // the launches are captured into a graph (non-null stream) so that back-to-back
@@ -845,7 +850,8 @@ ember_status ember_time_kernel(ember_model* md, ember_cache* cache, int32_t kern
   auto enqueue = [&](int n) -> ember_status {
     if (phase == 0) {
       if (md->last_decode_batch <= 0) return fail(EMBER_E_STATE, "no decode step has run");
-      for (int i = 0; i < n; ++i) decode_body(cx, md->last_decode_batch, i % c.layers);
+      for (int i = 0; i < n; ++i)
+        decode_body(cx, md->last_decode_batch, md->at<int32_t>(p.next), i % c.layers);
     } else {
       if (md->last_pass.M <= 0) return fail(EMBER_E_STATE, "no prefill has run");
       Pass ps{};

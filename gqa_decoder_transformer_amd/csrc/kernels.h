@@ -63,12 +63,23 @@ void launch_cls_head(const float* h, const void* W, bool w_bf16, const float* b,
 void launch_convert_logits(const float* src, int R, int n, long long ld, void* dst,
                            bool to_bf16, hipStream_t st);
 
-// Stage a decode step: ids_internal[r] = ids[r] (out-of-range ids -> 0 + flag) and
-// *d_pos = pos.
-void launch_stage_step(const int32_t* ids, int R, int V, int pos, int32_t* ids_internal,
-                       int* d_pos, int* flags, const float* cos_t, const float* sin_t, int half,
-                       float* rope_cur, hipStream_t st);
-void launch_copy_ids(const int32_t* src, int n, int32_t* dst, hipStream_t st);
+// Begin a decode step: *d_pos = pos, rope_cur = (cos, sin) row of pos, and row r of x the
+// embedding of ids[r] (out-of-range ids -> 0 + flag).
+struct StepBeginArgs {
+  const int32_t* ids;
+  int R, V, pos;
+  int* d_pos;
+  int* flags;
+  const float* cos_t;
+  const float* sin_t;
+  int half;
+  float* rope_cur;
+  const void* E;
+  bool e_bf16;
+  float* x;
+  int H;
+};
+void launch_step_begin(const StepBeginArgs& a, hipStream_t st);
 void launch_fill_i32(int* p, int n, int v, hipStream_t st);
 // dst[i] = widen(src[i]) for i < n (bf16 or f32 source).
 void launch_widen(const void* src, bool bf16, float* dst, long long n, hipStream_t st);
@@ -97,7 +108,8 @@ struct GemvArgs {
   // or (x == null) the input rebuilt from decode-attention split partials of one row:
   // xpart [K / xp_hd heads][xp_nsplit][xp_hd + 2] = (m, l, acc[xp_hd]); xp_nsplit <= 4;
   // x[h xp_hd + d] = sum_j acc_j[d] w_j / sum_j l_j w_j, w_j = e^(m_j - max m), over the
-  // splits that hold a key up to the position (the k_attn_combine arithmetic)
+  // splits that hold a key up to the position (the k_attn_combine arithmetic); residual
+  // epilogue only, for shapes where gemv_takes_parts holds
   const float* xpart;
   int xp_nsplit, xp_hd, xp_chunk_min;
   const int* xp_pos;
@@ -110,6 +122,8 @@ struct GemvArgs {
   int* flags;
 };
 void launch_gemv(const GemvArgs& a, int epi, hipStream_t st);
+// whether the residual GEMV of this shape takes its input as attention partials (xpart)
+bool gemv_takes_parts(int N, int K, bool bf16);
 int gemv_num_blocks(int N, int epi, int K, bool bf16);
 
 // ------------------------------------------------------------------ GEMM (kernels_gemm.hip)

@@ -61,51 +61,51 @@ EMBER_DEV void load_chunk_f32(const float* p, int c, bool valid, float* out) {
   }
 }
 
-// Input chunk c rebuilt from decode-attention split partials (see GemvArgs::xpart).
-// Splits at or past the number that hold keys are excluded by select (their memory may
-// hold anything).
-template <int E>
-EMBER_DEV void load_chunk_part(const GemvArgs& a, int c, bool valid, float* out) {
-  const int k0 = c * E;
-  const int h = k0 / a.xp_hd, d0 = k0 % a.xp_hd;
+// The input vector rebuilt from decode-attention split partials (see GemvArgs::xpart),
+// once per block into LDS (xs, 1024 entries): thread t takes elements t + 256 u (u < 4;
+// K <= 1024). Splits at
+// or past the number that hold keys are excluded by select (their memory may hold
+// anything). `ld` loads the partials; `finish` combines them and stores the LDS copy.
+struct PartIn {
+  float m[4][4], l[4][4], ac[4][4];     // [element u][split j]
+};
+EMBER_DEV void part_load(const GemvArgs& a, PartIn& p) {
   const int stride = a.xp_hd + 2;
-  const float* ph = a.xpart + (size_t)h * a.xp_nsplit * stride;
-  const int S = *a.xp_pos + 1;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int k = min((int)threadIdx.x + kThreads * u, a.K - 1);
+    const int h = k / a.xp_hd, d = k % a.xp_hd;
+    const float* ph = a.xpart + (size_t)h * a.xp_nsplit * stride;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float* pj = ph + (size_t)min(j, a.xp_nsplit - 1) * stride;
+      p.m[u][j] = pj[0];
+      p.l[u][j] = pj[1];
+      p.ac[u][j] = pj[2 + d];
+    }
+  }
+}
+EMBER_DEV void part_finish(const GemvArgs& a, const PartIn& p, int S, float* xs) {
   int chunk = (S + a.xp_nsplit - 1) / a.xp_nsplit;
   if (chunk < a.xp_chunk_min) chunk = a.xp_chunk_min;
   const int nv = (S + chunk - 1) / chunk;
-  float m[4], l[4], ac[4][E];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float* pj = ph + (size_t)min(j, a.xp_nsplit - 1) * stride;
-    m[j] = pj[0];
-    l[j] = pj[1];
+  for (int u = 0; u < 4; ++u) {
+    float M = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < E; ++e) ac[j][e] = pj[2 + d0 + e];
+    for (int j = 0; j < 4; ++j) M = j < nv ? fmaxf(M, p.m[u][j]) : M;
+    float L = 0.f, x = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float w = (j < nv && p.m[u][j] != -INFINITY) ? expf(p.m[u][j] - M) : 0.f;
+      L = j < nv ? fmaf(p.l[u][j], w, L) : L;
+      x = j < nv ? fmaf(p.ac[u][j], w, x) : x;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    // unconditional: xs holds 4 x 256 entries and entries past K are never read (a guarded
+    // store let the compiler sink its loads behind the weight loads)
+    xs[threadIdx.x + kThreads * u] = x * inv;
   }
-  float M = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) M = j < nv ? fmaxf(M, m[j]) : M;
-  float L = 0.f, w[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    w[j] = (j < nv && m[j] != -INFINITY) ? expf(m[j] - M) : 0.f;
-    L = j < nv ? fmaf(l[j], w[j], L) : L;
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    float x = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x = j < nv ? fmaf(ac[j][e], w[j], x) : x;
-    out[e] = valid ? x * inv : 0.f;
-  }
-}
-
-template <int E, bool XP>
-EMBER_DEV void load_input(const GemvArgs& a, int c, bool valid, float* out) {
-  if (XP) load_chunk_part<E>(a, c, valid, out);
-  else load_chunk_f32<E>(a.x, c, valid, out);
 }
 
 // Epilogue of one output unit n (value(s) already reduced).
@@ -161,15 +161,33 @@ __global__ void __launch_bounds__(kThreads) k_gemv_wave(GemvArgs a) {
   // this lane's input elements (and norm weights) are requested first: they come from L2
   // and are normalised while the weights are still in flight
   float xv[U][E], nv[U][E];
-#pragma unroll
-  for (int t = 0; t < U; ++t) {
-    const int c = lane + kWave * t;
-    load_input<E, XP>(a, min(c, nch - 1), c < nch, xv[t]);
-    if (a.norm_w) load_chunk_f32<E>(a.norm_w, min(c, nch - 1), c < nch, nv[t]);
-  }
   u32x4_t wa[U][NR];
   int grp = gw;
-  load_group(min(grp, ngroups - 1), wa);            // unconditional: a spare wave reloads
+  if constexpr (XP) {
+    // input rebuilt from attention partials: loads first, then the weights, then the
+    // block combines into LDS and every wave reads its chunks from there
+    __shared__ float xs[kWave * 2 * 8];
+    const int S = *a.xp_pos + 1;
+    PartIn pin;
+    part_load(a, pin);
+    load_group(min(grp, ngroups - 1), wa);
+    __builtin_amdgcn_sched_barrier(0);              // every weight load issued before any wait
+    part_finish(a, pin, S, xs);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < U; ++t) {
+      const int c = lane + kWave * t;
+      load_chunk_f32<E>(xs, min(c, nch - 1), c < nch, xv[t]);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < U; ++t) {
+      const int c = lane + kWave * t;
+      load_chunk_f32<E>(a.x, min(c, nch - 1), c < nch, xv[t]);
+      if (a.norm_w) load_chunk_f32<E>(a.norm_w, min(c, nch - 1), c < nch, nv[t]);
+    }
+    load_group(min(grp, ngroups - 1), wa);          // unconditional: a spare wave reloads
+  }
 
   float ss = 0.f;
 #pragma unroll
@@ -217,7 +235,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_wave(GemvArgs a) {
 }
 
 // ---------------------------------------------------------------- row per block
-template <typename WT, int EPI, int RPW, int U, bool XP>
+template <typename WT, int EPI, int RPW, int U>
 __global__ void __launch_bounds__(kThreads) k_gemv_block(GemvArgs a) {
   constexpr int E = WTraits<WT>::E;
   constexpr int RU = (EPI == GEMV_SILU) ? 2 : 1;
@@ -249,7 +267,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_block(GemvArgs a) {
 #pragma unroll
   for (int t = 0; t < U; ++t) {
     const int c = threadIdx.x + kThreads * t;
-    load_input<E, XP>(a, min(c, nch - 1), c < nch, xv[t]);
+    load_chunk_f32<E>(a.x, min(c, nch - 1), c < nch, xv[t]);
     if (a.norm_w) load_chunk_f32<E>(a.norm_w, min(c, nch - 1), c < nch, nv[t]);
   }
   u32x4_t wa[U][NR];
@@ -314,7 +332,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_block(GemvArgs a) {
 // K beyond 1024 chunks (1024 x 16 bytes): one block per output unit at a time, looping
 // over K; the norm's sum of squares takes its own pass over the input. Only shapes past
 // the limits of the two kernels above use it.
-template <typename WT, int EPI, bool XP>
+template <typename WT, int EPI>
 __global__ void __launch_bounds__(kThreads) k_gemv_long(GemvArgs a) {
   constexpr int E = WTraits<WT>::E;
   constexpr int RU = (EPI == GEMV_SILU) ? 2 : 1;
@@ -325,7 +343,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_long(GemvArgs a) {
     float ss = 0.f;
     for (int c = threadIdx.x; c < nch; c += kThreads) {
       float xv[E];
-      load_input<E, XP>(a, c, true, xv);
+      load_chunk_f32<E>(a.x, c, true, xv);
 #pragma unroll
       for (int e = 0; e < E; ++e) ss += xv[e] * xv[e];
     }
@@ -339,7 +357,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_long(GemvArgs a) {
     for (int r = 0; r < RU; ++r) acc[r] = 0.f;
     for (int c = threadIdx.x; c < nch; c += kThreads) {
       float xv[E];
-      load_input<E, XP>(a, c, true, xv);
+      load_chunk_f32<E>(a.x, c, true, xv);
       if (a.norm_w) {
         float nv[E];
         load_chunk_f32<E>(a.norm_w, c, true, nv);
@@ -421,7 +439,7 @@ Shape pick(int N, int K, bool bf16, int epi) {
 }
 
 // the input rebuilt from attention partials is built only for the residual epilogue (the
-// output projection); other instances keep their register budget
+// output projection) in the row-per-wave layout; other instances keep their register budget
 template <typename WT, int EPI, int RPW, int U>
 void launch_wave(const GemvArgs& a, int blocks, hipStream_t st) {
   if (EPI == GEMV_RESID && a.xpart)
@@ -431,10 +449,7 @@ void launch_wave(const GemvArgs& a, int blocks, hipStream_t st) {
 }
 template <typename WT, int EPI, int RPW, int U>
 void launch_block(const GemvArgs& a, int blocks, hipStream_t st) {
-  if (EPI == GEMV_RESID && a.xpart)
-    hipLaunchKernelGGL((k_gemv_block<WT, EPI, RPW, U, EPI == GEMV_RESID>), dim3(blocks), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_gemv_block<WT, EPI, RPW, U, false>), dim3(blocks), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((k_gemv_block<WT, EPI, RPW, U>), dim3(blocks), dim3(kThreads), 0, st, a);
 }
 
 template <typename WT, int EPI>
@@ -442,37 +457,30 @@ void launch_t(const GemvArgs& a, hipStream_t st) {
   const Shape s = pick(a.N, a.K, sizeof(WT) == 2, EPI);
   constexpr int RU = EPI == GEMV_SILU ? 2 : 1;
   if (s.kind == SHAPE_LONG) {
-    if (EPI == GEMV_RESID && a.xpart)
-      hipLaunchKernelGGL((k_gemv_long<WT, EPI, EPI == GEMV_RESID>), dim3(s.blocks), dim3(kThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL((k_gemv_long<WT, EPI, false>), dim3(s.blocks), dim3(kThreads), 0, st, a);
-    return;
-  }
-  if (EPI == GEMV_LOGITS) {
+    hipLaunchKernelGGL((k_gemv_long<WT, EPI>), dim3(s.blocks), dim3(kThreads), 0, st, a);
+  } else if constexpr (EPI == GEMV_LOGITS) {
     if (s.kind == SHAPE_BLOCK) {
       if (s.u == 2) launch_block<WT, EPI, 4 / RU, 2>(a, s.blocks, st);
       else launch_block<WT, EPI, 2 / RU, 4>(a, s.blocks, st);
-      return;
+    } else if (s.u == 1) {
+      launch_wave<WT, EPI, 8 / RU, 1>(a, s.blocks, st);
+    } else if (s.u == 2) {
+      launch_wave<WT, EPI, 8 / RU, 2>(a, s.blocks, st);
+    } else {
+      launch_wave<WT, EPI, 4 / RU, 4>(a, s.blocks, st);
     }
-    switch (s.u) {
-      case 1: launch_wave<WT, EPI, 8 / RU, 1>(a, s.blocks, st); break;
-      case 2: launch_wave<WT, EPI, 8 / RU, 2>(a, s.blocks, st); break;
-      default: launch_wave<WT, EPI, 4 / RU, 4>(a, s.blocks, st); break;
-    }
-    return;
-  }
-  if (s.kind == SHAPE_WAVE) {
+  } else if (s.kind == SHAPE_WAVE) {
     if (s.u == 1) launch_wave<WT, EPI, 1, 1>(a, s.blocks, st);
     else launch_wave<WT, EPI, 1, 2>(a, s.blocks, st);
-    return;
-  }
-  switch (s.u * 4 + s.rpw) {
-    case 1 * 4 + 1: launch_block<WT, EPI, 1, 1>(a, s.blocks, st); break;
-    case 2 * 4 + 1: launch_block<WT, EPI, 1, 2>(a, s.blocks, st); break;
-    case 3 * 4 + 1: launch_block<WT, EPI, 1, 3>(a, s.blocks, st); break;
-    case 3 * 4 + 2: launch_block<WT, EPI, 2, 3>(a, s.blocks, st); break;
-    case 4 * 4 + 1: launch_block<WT, EPI, 1, 4>(a, s.blocks, st); break;
-    default: launch_block<WT, EPI, 2, 4>(a, s.blocks, st); break;
+  } else {
+    switch (s.u * 4 + s.rpw) {
+      case 1 * 4 + 1: launch_block<WT, EPI, 1, 1>(a, s.blocks, st); break;
+      case 2 * 4 + 1: launch_block<WT, EPI, 1, 2>(a, s.blocks, st); break;
+      case 3 * 4 + 1: launch_block<WT, EPI, 1, 3>(a, s.blocks, st); break;
+      case 3 * 4 + 2: launch_block<WT, EPI, 2, 3>(a, s.blocks, st); break;
+      case 4 * 4 + 1: launch_block<WT, EPI, 1, 4>(a, s.blocks, st); break;
+      default: launch_block<WT, EPI, 2, 4>(a, s.blocks, st); break;
+    }
   }
 }
 
@@ -483,8 +491,15 @@ int gemv_num_blocks(int N, int epi, int K, bool bf16) {
   return s.kind == SHAPE_WAVE ? s.blocks * kWaves : s.blocks;   // argmax partials written
 }
 
+bool gemv_takes_parts(int N, int K, bool bf16) {
+  return pick(N, K, bf16, GEMV_RESID).kind == SHAPE_WAVE;
+}
+
 void launch_gemv(const GemvArgs& a, int epi, hipStream_t st) {
   if (a.M != 1 || a.N <= 0 || (!a.x && !a.xpart)) return;   // one token, an input required
+  if (a.xpart && (epi != GEMV_RESID || !gemv_takes_parts(a.N, a.K, a.w_bf16) ||
+                  a.xp_nsplit < 1 || a.xp_nsplit > 4))
+    return;                                                   // callers check gemv_takes_parts
 #define EMBER_GEMV_CASE(E)                                               \
   case E:                                                                \
     if (a.w_bf16) launch_t<uint16_t, E>(a, st);                          \

@@ -155,29 +155,37 @@ void launch_qkv_post(const QkvPostArgs& a, hipStream_t st) {
 // ------------------------------------------------------------------ argmax
 // Greedy choice: lowest index of the maximum ("ember scripts/reference_forward.py",
 // np.argmax in the decode loop). Keys order by value, then by lowest index.
-__global__ void __launch_bounds__(256) k_argmax_reduce(const unsigned long long* part,
-                                                       int nparts, int32_t* next) {
-  __shared__ unsigned long long red[4];
+// One block of 1024 threads per row; each thread takes 8 partials per pass, all loads
+// issued before the first comparison (indices clamped: a repeated partial cannot change
+// a maximum).
+constexpr int kArgThreads = 1024;
+__global__ void __launch_bounds__(kArgThreads) k_argmax_reduce(const unsigned long long* part,
+                                                               int nparts, int32_t* next) {
+  __shared__ unsigned long long red[kArgThreads / kWave];
   const int r = blockIdx.x;
+  const unsigned long long* pr = part + (size_t)r * nparts;
   unsigned long long k = 0;
-  for (int i = threadIdx.x; i < nparts; i += blockDim.x) {
-    unsigned long long v = part[(size_t)r * nparts + i];
-    k = v > k ? v : k;
+  for (int i0 = 0; i0 < nparts; i0 += 8 * kArgThreads) {
+    unsigned long long v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = pr[min(i0 + (int)threadIdx.x + kArgThreads * u, nparts - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) k = v[u] > k ? v[u] : k;
   }
   k = wave_max_u64(k);
   if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = k;
   __syncthreads();
   if (threadIdx.x == 0) {
     k = red[0];
-    for (int i = 1; i < (int)blockDim.x / kWave; ++i) k = red[i] > k ? red[i] : k;
+    for (int i = 1; i < kArgThreads / kWave; ++i) k = red[i] > k ? red[i] : k;
     next[r] = (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
   }
 }
 
 void launch_argmax_reduce(const unsigned long long* part, int nparts, int R, int32_t* next,
                           hipStream_t st) {
-  if (R <= 0) return;
-  hipLaunchKernelGGL(k_argmax_reduce, dim3(R), dim3(256), 0, st, part, nparts, next);
+  if (R <= 0 || nparts <= 0) return;
+  hipLaunchKernelGGL(k_argmax_reduce, dim3(R), dim3(kArgThreads), 0, st, part, nparts, next);
 }
 
 __global__ void __launch_bounds__(256) k_argmax_rows(const float* logits, int n, long long ld,
@@ -268,44 +276,38 @@ void launch_convert_logits(const float* src, int R, int n, long long ld, void* d
                      (int)to_bf16);
 }
 
-// Per decode step: position, validated ids, and the RoPE row of the position (cos, sin)
-// copied to a fixed place so that the step's kernels can read it without first reading
-// the position.
-__global__ void k_stage_step(const int32_t* ids, int R, int V, int pos, int32_t* ids_internal,
-                             int* d_pos, int* flags, const float* cos_t, const float* sin_t,
-                             int half, float* rope_cur) {
-  const int r = threadIdx.x + blockIdx.x * blockDim.x;
-  if (r == 0) *d_pos = pos;
-  if (r < half) {
-    rope_cur[r] = cos_t[(size_t)pos * half + r];
-    rope_cur[half + r] = sin_t[(size_t)pos * half + r];
-  }
-  if (r < R) {
-    int id = ids[r];
-    if (id < 0 || id >= V) {
-      atomicOr(&flags[kFlagBadToken], 1);
-      id = 0;
+// Per decode step: the position, the embedding rows of the step's ids (x = E[id] widened
+// to f32, out-of-range ids flagged and replaced by 0), and the RoPE row of the position
+// (cos, sin) copied to a fixed place so that the step's kernels can read it without
+// first reading the position. Block r embeds row r; block 0 also writes the position and
+// the RoPE row.
+__global__ void __launch_bounds__(256) k_step_begin(StepBeginArgs a) {
+  const int r = blockIdx.x;
+  if (r == 0) {
+    if (threadIdx.x == 0) *a.d_pos = a.pos;
+    for (int i = threadIdx.x; i < a.half; i += blockDim.x) {
+      a.rope_cur[i] = a.cos_t[(size_t)a.pos * a.half + i];
+      a.rope_cur[a.half + i] = a.sin_t[(size_t)a.pos * a.half + i];
     }
-    ids_internal[r] = id;
+  }
+  int id = a.ids[r];
+  if (id < 0 || id >= a.V) {
+    if (threadIdx.x == 0) atomicOr(&a.flags[kFlagBadToken], 1);
+    id = 0;
+  }
+  float* xr = a.x + (size_t)r * a.H;
+  if (a.e_bf16) {
+    const uint16_t* er = (const uint16_t*)a.E + (size_t)id * a.H;
+    for (int i = threadIdx.x; i < a.H; i += blockDim.x) xr[i] = bf16_to_f32(er[i]);
+  } else {
+    const float* er = (const float*)a.E + (size_t)id * a.H;
+    for (int i = threadIdx.x; i < a.H; i += blockDim.x) xr[i] = er[i];
   }
 }
 
-void launch_stage_step(const int32_t* ids, int R, int V, int pos, int32_t* ids_internal, int* d_pos,
-                       int* flags, const float* cos_t, const float* sin_t, int half,
-                       float* rope_cur, hipStream_t st) {
-  const int n = R > half ? R : half;
-  hipLaunchKernelGGL(k_stage_step, dim3((n + 255) / 256), dim3(256), 0, st, ids, R, V, pos,
-                     ids_internal, d_pos, flags, cos_t, sin_t, half, rope_cur);
-}
-
-__global__ void k_copy_ids(const int32_t* src, int n, int32_t* dst) {
-  const int i = threadIdx.x + blockIdx.x * blockDim.x;
-  if (i < n) dst[i] = src[i];
-}
-
-void launch_copy_ids(const int32_t* src, int n, int32_t* dst, hipStream_t st) {
-  if (n <= 0) return;
-  hipLaunchKernelGGL(k_copy_ids, dim3((n + 255) / 256), dim3(256), 0, st, src, n, dst);
+void launch_step_begin(const StepBeginArgs& a, hipStream_t st) {
+  if (a.R <= 0) return;
+  hipLaunchKernelGGL(k_step_begin, dim3(a.R), dim3(256), 0, st, a);
 }
 
 __global__ void k_fill_i32(int* p, int n, int v) {

@@ -147,8 +147,10 @@ ember_status ember_prefill(ember_model* model, ember_cache* cache, const int32_t
  * positions 0..pos, and writes the argmax of the new logits to d_next [batch] int32
  * (device; may alias d_ids). Requires pos <= the cache's filled length (EMBER_E_STATE)
  * and pos < max_seq (EMBER_E_CAPACITY). The step is replayed from a HIP graph and does
- * not synchronise. An id outside [0, vocab) is replaced by 0 and flagged; ember_sync
- * reports it as EMBER_E_TOKEN. */
+ * not synchronise; the graph is captured again whenever the batch, the cache, the stream
+ * or d_next differ from the previous step's (keep d_next fixed across steps). An id
+ * outside [0, vocab) is replaced by 0 and flagged; ember_sync reports it as
+ * EMBER_E_TOKEN. */
 ember_status ember_decode_step(ember_model* model, ember_cache* cache, const int32_t* d_ids,
                                int32_t batch, int32_t pos, int32_t* d_next, void* stream);
 
@@ -183,7 +185,8 @@ typedef enum ember_kernel {
   EMBER_K_ATTN = 2,            /* split-K decode attention, or flash prefill attention */
   EMBER_K_O = 3,               /* output projection + residual (GEMV: + split-K combine) */
   EMBER_K_GATE_UP = 4,         /* gate/up projection + SiLU*up */
-  EMBER_K_DOWN = 5             /* down projection + residual */
+  EMBER_K_DOWN = 5,            /* down projection + residual */
+  EMBER_K_LAYER = 6            /* every kernel of one layer, in step order */
 } ember_kernel;
 
 /* Launch kernel `kernel` of the most recent decode step (phase 0) or prefill pass
