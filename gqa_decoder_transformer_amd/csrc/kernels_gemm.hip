@@ -28,7 +28,6 @@ namespace {
 
 constexpr int BK = 64;
 constexpr int LDS_STRIDE = BK + 8;   // bf16 elements per LDS row (128 + 16 bytes)
-constexpr int kGemmThreads = 256;
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -37,10 +36,10 @@ constexpr size_t gemm_lds_bytes() {
   return (size_t)2 * ((SPLIT ? 2 : 1) * BM + BN) * LDS_STRIDE * 2;
 }
 
-template <int BM, int BN, int PF, bool SPLIT, int EPI, bool TAIL>
-__global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs a) {
-  constexpr int NT = kGemmThreads;
-  constexpr int TM = BM / 2 / 32, TN = BN / 2 / 32;      // 32x32 fragments per wave
+template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI, bool TAIL>
+__global__ void __launch_bounds__(WM * WN * kWave) k_gemm(GemmArgs a) {
+  constexpr int NT = WM * WN * kWave;
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;    // 32x32 fragments per wave
   constexpr int RS = NT / 8;                              // rows per load round
   constexpr int CA = BM / RS, CB = BN / RS;               // 16-byte loads per plane
   constexpr int NP = SPLIT ? 2 : 1;
@@ -60,7 +59,7 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs a) {
   const int tm = lin % mt, tn = lin / mt;
   const int m0 = tm * BM, n0 = tn * BN;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int wm0 = (wave / 2) * (BM / 2), wn0 = (wave % 2) * (BN / 2);
+  const int wm0 = (wave / WN) * (BM / WM), wn0 = (wave % WN) * (BN / WN);
   const int fr = lane % 32, fk = (lane / 32) * 8;
 
   // K range of this block (split-K over gridDim.y slices of k_chunk columns)
@@ -252,49 +251,52 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm(GemmArgs a) {
   }
 }
 
-// Tile configurations (block BM x BN, register prefetch depth PF).
-enum GemmCfg { CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x128 = 3 };
+// Tile configurations: block BM x BN, WM x WN waves, register prefetch depth PF.
+enum GemmCfg { CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x128 = 3, CFG_256x256 = 4 };
 
-template <int BM, int BN, int PF, bool SPLIT, int EPI>
+template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI>
 void set_attr() {
-  (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, PF, SPLIT, EPI, false>,
+  (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, PF, SPLIT, EPI, false>,
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)gemm_lds_bytes<BM, BN, SPLIT>());
-  (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, PF, SPLIT, EPI, true>,
+  (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, PF, SPLIT, EPI, true>,
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)gemm_lds_bytes<BM, BN, SPLIT>());
 }
 
-template <int BM, int BN, int PF, bool SPLIT, int EPI>
+template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI>
 void launch_cfg(const GemmArgs& a, int splits, hipStream_t st) {
   const int blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const size_t lds = gemm_lds_bytes<BM, BN, SPLIT>();
   // every K slice a whole number of 64-column stages: no tail handling
   const bool tail = a.K % BK != 0 || a.k_chunk % BK != 0;
   if (tail)
-    hipLaunchKernelGGL((k_gemm<BM, BN, PF, SPLIT, EPI, true>), dim3(blocks, splits),
-                       dim3(kGemmThreads), lds, st, a);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, PF, SPLIT, EPI, true>), dim3(blocks, splits),
+                       dim3(WM * WN * kWave), lds, st, a);
   else
-    hipLaunchKernelGGL((k_gemm<BM, BN, PF, SPLIT, EPI, false>), dim3(blocks, splits),
-                       dim3(kGemmThreads), lds, st, a);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, PF, SPLIT, EPI, false>), dim3(blocks, splits),
+                       dim3(WM * WN * kWave), lds, st, a);
 }
 
 int tiles_of(const GemmArgs& a, int bm, int bn) {
   return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
 }
 
-// One-plane input: 128 x 128 tiles (measured at least as fast as 128 x 256 on the 1B and
-// 0.5B shapes, with twice the blocks); the two-plane (EXACT) input does better with 128 x
-// 256 when that still leaves ~0.7 tiles per CU. Small M takes 64 rows. A 256 x 256 tile holds 256 accumulators per
-// lane and spills around its epilogue.
+// A 32x32x16 MFMA of a wave tile of TM x TN fragments reads (TM + TN) / (TM TN) fragments
+// of 1 KB from LDS, so small wave tiles are bound by LDS bandwidth: one-plane input takes
+// 256 x 256 tiles over 8 waves (128 x 64 each, two waves per SIMD) when they still make
+// ~1.5 tiles per CU, else 128 x 128; the two-plane (EXACT) input (a third LDS plane)
+// takes 128 x 256 when that leaves ~0.7 tiles per CU. Small M takes 64 rows.
 int pick_cfg(const GemmArgs& a) {
   if (a.M <= 64) return CFG_64x128;
-  if (a.a_lo && tiles_of(a, 128, 256) >= 180) return CFG_128x256;   // two-plane (EXACT) input
+  if (a.a_lo) return tiles_of(a, 128, 256) >= 180 ? CFG_128x256 : CFG_128x128;
+  if (tiles_of(a, 256, 256) >= 384) return CFG_256x256;
   return CFG_128x128;
 }
 
 void cfg_dims(int cfg, int& bm, int& bn) {
   switch (cfg) {
+    case CFG_256x256: bm = 256; bn = 256; break;
     case CFG_128x256: bm = 128; bn = 256; break;
     case CFG_128x128: bm = 128; bn = 128; break;
     default: bm = 64; bn = 128; break;
@@ -304,9 +306,12 @@ void cfg_dims(int cfg, int& bm, int& bn) {
 template <bool SPLIT, int EPI>
 void launch_split(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
   switch (cfg) {
-    case CFG_128x256: launch_cfg<128, 256, 2, SPLIT, EPI>(a, splits, st); break;
-    case CFG_128x128: launch_cfg<128, 128, 2, SPLIT, EPI>(a, splits, st); break;
-    default: launch_cfg<64, 128, 2, SPLIT, EPI>(a, splits, st); break;
+    case CFG_256x256:
+      if constexpr (!SPLIT) launch_cfg<256, 256, 2, 4, 1, false, EPI>(a, splits, st);
+      break;
+    case CFG_128x256: launch_cfg<128, 256, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
+    case CFG_128x128: launch_cfg<128, 128, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
+    default: launch_cfg<64, 128, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
   }
 }
 
@@ -318,9 +323,10 @@ void launch_epi(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
 
 template <bool SPLIT, int EPI>
 void set_attrs_split() {
-  set_attr<128, 256, 2, SPLIT, EPI>();
-  set_attr<128, 128, 2, SPLIT, EPI>();
-  set_attr<64, 128, 2, SPLIT, EPI>();
+  if constexpr (!SPLIT) set_attr<256, 256, 2, 4, 1, false, EPI>();
+  set_attr<128, 256, 2, 2, 2, SPLIT, EPI>();
+  set_attr<128, 128, 2, 2, 2, SPLIT, EPI>();
+  set_attr<64, 128, 2, 2, 2, SPLIT, EPI>();
 }
 
 template <int EPI>
