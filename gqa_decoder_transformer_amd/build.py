@@ -13,6 +13,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
          # packed-fp32 VALU ops disabled for every kernel
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-result", "-Wno-unknown-pragmas"]
+# per-file device options: the attention kernels keep MFMA results in arch VGPRs (their
+# scores and outputs feed VALU work every tile; accumulation registers would cost a move
+# per element each way)
+FILE_FLAGS = {"kernels_flash.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def build(verbose: bool = False) -> str:
@@ -22,7 +26,8 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(CSRC, "_build", src + ".o")
         os.makedirs(os.path.dirname(obj), exist_ok=True)
-        cmd = [hipcc, *[f for f in FLAGS if f != "-shared"], "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *[f for f in FLAGS if f != "-shared"], *FILE_FLAGS.get(src, []), "-c",
+               os.path.join(CSRC, src), "-o", obj]
         jobs.append((cmd, src))
         objs.append(obj)
     procs = [(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True), src)

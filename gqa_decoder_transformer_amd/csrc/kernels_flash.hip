@@ -348,7 +348,8 @@ __global__ void __launch_bounds__(256) k_kv_pack(KvPackArgs a) {
 //                is read with the same order (two 8-byte LDS reads per fragment).
 // Both tiles are double-buffered in LDS, loaded one tile ahead through registers from the
 // packed planes (16-byte loads, rows padded by 16 bytes). The softmax is the online one
-// in base 2 (scores pre-multiplied by scale * log2 e); masks are applied only on tiles
+// in base 2 (scores pre-multiplied by scale * log2 e) with lazy rescaling (the running
+// maximum moves only when exceeded by more than 2^8); masks are applied only on tiles
 // that cross the causal diagonal or the end of the keys (scale * log2 e is folded into Q
 // before its bf16 rounding; P is rounded with the hardware pack-convert); under the causal mask a wave
 // skips the tiles wholly past its last query. Output rows go through LDS and leave as 16-byte stores.
@@ -465,57 +466,78 @@ __global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t
     const int k0 = j * kTK;
     if (!a.causal || k0 <= wq_last) {                          // wave-uniform
       const uint16_t* st = sm + s * C::STAGE;
+      // every K fragment of the tile is read first; the two 32-key blocks' MFMA chains
+      // then alternate, so consecutive MFMAs are independent
       f32x16_t sc[2];
+      bf16x8_t kfh[2][NKS], kfl[2][SPLIT ? NKS : 1];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int ro = (kb * 32 + lq) * KS + 16 * ks + 8 * hl;
+          kfh[kb][ks] = as_bf16x8(*(const u32x4_t*)(st + ro));
+          if (SPLIT) kfl[kb][ks] = as_bf16x8(*(const u32x4_t*)(st + C::KTILE + ro));
+        }
+      if (HD == 64) __builtin_amdgcn_sched_barrier(0); // reads ahead of the MFMAs (HD 128: too
+                                                       // many registers for all of them)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const int ro = (kb * 32 + lq) * KS + 16 * ks + 8 * hl;
-          const bf16x8_t kh = as_bf16x8(*(const u32x4_t*)(st + ro));
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[ks], sc[kb], 0, 0, 0);
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfh[kb][ks], qh[ks], sc[kb], 0, 0, 0);
           if (SPLIT) {
-            const bf16x8_t kl = as_bf16x8(*(const u32x4_t*)(st + C::KTILE + ro));
-            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qlo[ks], sc[kb], 0, 0, 0);
-            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[ks], sc[kb], 0, 0, 0);
+            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfh[kb][ks], qlo[ks], sc[kb], 0, 0, 0);
+            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfl[kb][ks], qh[ks], sc[kb], 0, 0, 0);
           }
         }
-      }
-      // keys past `klim` are masked: one compare and select per score, no branches
-      // (tiles wholly below the diagonal get a limit no key reaches)
+      // keys past `klim` are masked with one compare and select per score, only on tiles
+      // that cross the causal diagonal or the end of the keys (a wave-uniform branch)
       const bool need_mask = (a.causal && k0 + kTK - 1 > wq_first) || k0 + kTK > key_end;
-      const int klim = need_mask ? (a.causal ? min(key_end - 1, qpos) : key_end - 1) - k0 - 4 * hl
-                                 : kTK;
+      if (__builtin_expect(__builtin_amdgcn_readfirstlane((int)need_mask), 0)) {
+        const int klim = (a.causal ? min(key_end - 1, qpos) : key_end - 1) - k0 - 4 * hl;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int kofs = kb * 32 + 8 * (e / 4) + (e % 4);    // key - k0 - 4 hl
+            sc[kb][e] = kofs > klim ? -INFINITY : sc[kb][e];
+          }
+      }
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int kofs = kb * 32 + 8 * (e / 4) + (e % 4);      // key - k0 - 4 hl
-          const float v = kofs > klim ? -INFINITY : sc[kb][e];
-          sc[kb][e] = v;
-          mt = fmaxf(mt, v);
-        }
+        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sc[kb][e]);
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mnew = fmaxf(mrun, mt);                      // finite: key 0 is in tile 0
-      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew); // mrun = -inf -> 0
+      // Lazy rescaling: the reference maximum mrun moves (and O and l are rescaled) only
+      // when a score exceeds it by more than 2^8 in any row of the wave; otherwise the
+      // probabilities are taken against the stale maximum, at most 2^8. The first tile
+      // always moves it (mrun = -inf; key 0 is in tile 0, so it becomes finite).
+      if (__ballot(mt > mrun + 8.f) != 0) {
+        const float mnew = fmaxf(mrun, mt);
+        const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);   // mrun = -inf -> 0
+        lrun *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+        mrun = mnew;
+      }
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(sc[kb][e] - mnew);   // masked (-inf) -> 0
+          const float p = __builtin_amdgcn_exp2f(sc[kb][e] - mrun);   // masked (-inf) -> 0
           sc[kb][e] = p;
           ps += p;
         }
       ps += __shfl_xor(ps, 32);
-      lrun = lrun * alpha + ps;
-      mrun = mnew;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+      lrun += ps;
 #pragma unroll
       for (int t = 0; t < kTK / 16; ++t) {
         const int kb = t / 2, e0 = 8 * (t % 2);

@@ -36,7 +36,7 @@ constexpr size_t gemm_lds_bytes() {
   return (size_t)2 * ((SPLIT ? 2 : 1) * BM + BN) * LDS_STRIDE * 2;
 }
 
-template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI, bool TAIL>
+template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI, bool TAIL, bool DB = true>
 __global__ void __launch_bounds__(WM * WN * kWave) k_gemm(GemmArgs a) {
   constexpr int NT = WM * WN * kWave;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;    // 32x32 fragments per wave
@@ -126,7 +126,8 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm(GemmArgs a) {
     for (int i = 0; i < CB; ++i)
       *(u32x4_t*)(base + NP * PLANE + RS * i * LDS_STRIDE) = !TAIL || ok ? rw[b][i] : z;
   };
-  bf16x8_t fh[2][TM], fl[2][SPLIT ? TM : 1], fw[2][TN];
+  constexpr int NF = DB ? 2 : 1;                          // fragment buffers
+  bf16x8_t fh[NF][TM], fl[NF][SPLIT ? TM : 1], fw[NF][TN];
   auto rdfrag = [&](int f, int s, int ks) {
     const uint16_t* st = smem + s * STAGE;
 #pragma unroll
@@ -167,8 +168,14 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm(GemmArgs a) {
       rdfrag(0, s, 0);
 #pragma unroll
       for (int t = 0; t < BK / 16; ++t) {
-        if (t + 1 < BK / 16) rdfrag((t + 1) & 1, s, (t + 1) * 16);
-        mfmas(t & 1);
+        if (DB) {
+          if (t + 1 < BK / 16) rdfrag((t + 1) & 1, s, (t + 1) * 16);
+          mfmas(t & 1);
+        } else {
+          // one fragment buffer: the next step's reads overwrite it behind these MFMAs
+          mfmas(0);
+          if (t + 1 < BK / 16) rdfrag(0, s, (t + 1) * 16);
+        }
       }
       sstore((ph + 1) % PF, s ^ 1);            // stage k + 1 (past the end: unused)
       __builtin_amdgcn_sched_group_barrier(0x020, NLD, 0);        // global loads
@@ -284,13 +291,14 @@ int tiles_of(const GemmArgs& a, int bm, int bn) {
 
 // A 32x32x16 MFMA of a wave tile of TM x TN fragments reads (TM + TN) / (TM TN) fragments
 // of 1 KB from LDS, so small wave tiles are bound by LDS bandwidth: one-plane input takes
-// 256 x 256 tiles over 8 waves (128 x 64 each, two waves per SIMD) when they still make
-// ~1.5 tiles per CU, else 128 x 128; the two-plane (EXACT) input (a third LDS plane)
-// takes 128 x 256 when that leaves ~0.7 tiles per CU. Small M takes 64 rows.
+// 256 x 256 tiles over 8 waves (128 x 64 each, two waves per SIMD) when they make at
+// least one tile per CU (measured faster there at every K), else 128 x 128; the
+// two-plane (EXACT) input (a third LDS plane) takes 128 x 256 when that leaves ~0.7
+// tiles per CU. Small M takes 64 rows.
 int pick_cfg(const GemmArgs& a) {
   if (a.M <= 64) return CFG_64x128;
   if (a.a_lo) return tiles_of(a, 128, 256) >= 180 ? CFG_128x256 : CFG_128x128;
-  if (tiles_of(a, 256, 256) >= 384) return CFG_256x256;
+  if (tiles_of(a, 256, 256) >= 256) return CFG_256x256;
   return CFG_128x128;
 }
 
