@@ -80,7 +80,7 @@ template <int WIDTH>
 EMBER_DEV float group_sum(float v) {
   if (WIDTH >= 2) v += dpp_move<0xB1>(v);
   if (WIDTH >= 4) v += dpp_move<0x4E>(v);
-  if (WIDTH == 8) v += __shfl_xor(v, 4);
+  if (WIDTH == 8) v += dpp_move<0x141>(v);     // row_half_mirror: the other quad of the 8
   if (WIDTH >= 16) {
     v += dpp_move<0x124>(v);
     v += dpp_move<0x128>(v);

@@ -248,11 +248,15 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
     }
   }
 
+  // q pre-multiplied by scale * log2(e): scores and the running maxima are base-2
+  // logits (hardware exp2 per probability); the partial's maximum goes out in natural
+  // units
+  const float c2 = a.scale * 1.4426950408889634f;
   float qv[G][DPL];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int d = 0; d < DPL; ++d) qv[g][d] = qs[g * HD + sub * DPL + d];
+    for (int d = 0; d < DPL; ++d) qv[g][d] = qs[g * HD + sub * DPL + d] * c2;
 
   float mrun[G], l[G], acc[G][DPL];
 #pragma unroll
@@ -298,19 +302,19 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
         float s = 0.f;
 #pragma unroll
         for (int d = 0; d < DPL; ++d) s = fmaf(qv[g][d], kf[i][d], s);
-        s = group_sum<LPK>(s) * a.scale;
+        s = group_sum<LPK>(s);
         sc[i] = valid[i] ? s : -INFINITY;
         mb = fmaxf(mb, sc[i]);
       }
       if (mb == -INFINITY) continue;           // no admissible key in this batch
       const float mnew = fmaxf(mrun[g], mb);
-      const float alpha = expf(mrun[g] - mnew); // mrun = -inf -> 0
+      const float alpha = __builtin_amdgcn_exp2f(mrun[g] - mnew);   // mrun = -inf -> 0
       l[g] *= alpha;
 #pragma unroll
       for (int d = 0; d < DPL; ++d) acc[g][d] *= alpha;
 #pragma unroll
       for (int i = 0; i < KI; ++i) {
-        const float p = valid[i] ? expf(sc[i] - mnew) : 0.f;
+        const float p = valid[i] ? __builtin_amdgcn_exp2f(sc[i] - mnew) : 0.f;
         l[g] += p;
 #pragma unroll
         for (int d = 0; d < DPL; ++d) acc[g][d] = fmaf(p, vf[i][d], acc[g][d]);
@@ -327,7 +331,8 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
   }
 
   // merge lane groups through LDS (fixed order): per head the group weights
-  // w_i = e^{m_i - M} once, then every output dimension sums acc_i w_i over the groups
+  // w_i = 2^{m_i - M} once (base-2 maxima), then every output dimension sums acc_i w_i
+  // over the groups
   const int h_base = b * a.NH + h0;
   for (int g0 = 0; g0 < G; g0 += MG) {
 #pragma unroll
@@ -350,7 +355,7 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
     __syncthreads();
     for (int e = threadIdx.x; e < NGRP * MG; e += blockDim.x) {
       const float M = smax[e % MG];
-      sm[e] = (M == -INFINITY || sm[e] == -INFINITY) ? 0.f : expf(sm[e] - M);
+      sm[e] = (M == -INFINITY || sm[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm[e] - M);
     }
     __syncthreads();
     for (int e = threadIdx.x; e < MG * HD; e += blockDim.x) {
@@ -373,7 +378,7 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
         }
       } else {
         float* out = a.part + (((size_t)(h_base + g0 + gg)) * a.nsplit + split) * (HD + 2);
-        if (d == 0) { out[0] = smax[gg]; out[1] = L; }
+        if (d == 0) { out[0] = smax[gg] * 0.6931471805599453f; out[1] = L; }   // natural units
         out[2 + d] = A;
       }
     }
