@@ -154,24 +154,25 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
     return (nkeys + KI - 1) / KI;
   };
 
+  // K/V loads are unconditional, keys clamped into [0, s_hi) (always inside the cache;
+  // entries past the valid range are zeroed before use): guarded loads made the compiler
+  // wait for every outstanding load before issuing the next batch
   u32x4_t kb0[KI], vb0[KI], kb1[KI], vb1[KI];
   auto load = [&](int batch, u32x4_t* kb, u32x4_t* vb) {
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      const int key = s0 + grp + NGRP * (batch * KI + i);
-      if (key < s_hi) {
-        const size_t off = base + (size_t)key * HD + sub * DPL;
-        if (KV_BF16) {
-          kb[i] = *(const u32x4_t*)((const uint16_t*)a.k_cache + off);
-          vb[i] = *(const u32x4_t*)((const uint16_t*)a.v_cache + off);
-        } else {
-          kb[i] = *(const u32x4_t*)((const float*)a.k_cache + off);
-          vb[i] = *(const u32x4_t*)((const float*)a.v_cache + off);
-        }
+      const int key = max(0, min(s0 + grp + NGRP * (batch * KI + i), s_hi - 1));
+      const size_t off = base + (size_t)key * HD + sub * DPL;
+      if (KV_BF16) {
+        kb[i] = *(const u32x4_t*)((const uint16_t*)a.k_cache + off);
+        vb[i] = *(const u32x4_t*)((const uint16_t*)a.v_cache + off);
+      } else {
+        kb[i] = *(const u32x4_t*)((const float*)a.k_cache + off);
+        vb[i] = *(const u32x4_t*)((const float*)a.v_cache + off);
       }
     }
   };
-  if (batches(s_hi) > 0) load(0, kb0, vb0);
+  load(0, kb0, vb0);
 
   // current token: raw q (G heads), this step's RoPE row and, in the split that holds
   // the position, raw k/v of head kvh
@@ -266,67 +267,80 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
 #pragma unroll
     for (int d = 0; d < DPL; ++d) acc[g][d] = 0.f;
   }
-  // one batch of KI keys: scores first, then one running-max update per head
+  // one batch of KI keys: scores first, then one running-max update per head, then the
+  // value accumulation; each key's K and V are widened just before use (only one key's
+  // worth of f32 values is live at a time)
+  auto widen = [&](const u32x4_t& raw, const float* cur, int key, bool valid, float* f) {
+    if (key == pos) {
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) f[d] = cur[sub * DPL + d];
+    } else if (!valid) {                       // never-written or stale entries: zeros
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) f[d] = 0.f;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (KV_BF16) {
+          f[2 * j] = bf16_lo(raw[j]);
+          f[2 * j + 1] = bf16_hi(raw[j]);
+        } else {
+          f[j] = __uint_as_float(raw[j]);
+        }
+      }
+    }
+  };
   auto compute = [&](int batch, const u32x4_t* kb, const u32x4_t* vb) {
-    float kf[KI][DPL], vf[KI][DPL];
-    bool valid[KI];
+    float sc[G][KI];
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int key = s0 + grp + NGRP * (batch * KI + i);
-      valid[i] = key < s1;
-      if (key == pos) {
+      const bool valid = key < s1;
+      float kf[DPL];
+      widen(kb[i], kc, key, valid, kf);
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) { kf[i][d] = kc[sub * DPL + d]; vf[i][d] = vc[sub * DPL + d]; }
-      } else if (!valid[i]) {                  // never-written or stale entries: zeros
+      for (int g = 0; g < G; ++g) {
+        float s = 0.f;
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) { kf[i][d] = 0.f; vf[i][d] = 0.f; }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (KV_BF16) {
-            kf[i][2 * j] = bf16_lo(kb[i][j]); kf[i][2 * j + 1] = bf16_hi(kb[i][j]);
-            vf[i][2 * j] = bf16_lo(vb[i][j]); vf[i][2 * j + 1] = bf16_hi(vb[i][j]);
-          } else {
-            kf[i][j] = __uint_as_float(kb[i][j]);
-            vf[i][j] = __uint_as_float(vb[i][j]);
-          }
-        }
+        for (int d = 0; d < DPL; ++d) s = fmaf(qv[g][d], kf[d], s);
+        s = group_sum<LPK>(s);
+        sc[g][i] = valid ? s : -INFINITY;
       }
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float sc[KI];
       float mb = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < KI; ++i) {
-        float s = 0.f;
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) s = fmaf(qv[g][d], kf[i][d], s);
-        s = group_sum<LPK>(s);
-        sc[i] = valid[i] ? s : -INFINITY;
-        mb = fmaxf(mb, sc[i]);
-      }
-      if (mb == -INFINITY) continue;           // no admissible key in this batch
+      for (int i = 0; i < KI; ++i) mb = fmaxf(mb, sc[g][i]);
       const float mnew = fmaxf(mrun[g], mb);
-      const float alpha = __builtin_amdgcn_exp2f(mrun[g] - mnew);   // mrun = -inf -> 0
+      const bool none = mnew == -INFINITY;     // no admissible key yet: nothing changes
+      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(mrun[g] - mnew);  // -inf -> 0
       l[g] *= alpha;
 #pragma unroll
       for (int d = 0; d < DPL; ++d) acc[g][d] *= alpha;
 #pragma unroll
       for (int i = 0; i < KI; ++i) {
-        const float p = valid[i] ? __builtin_amdgcn_exp2f(sc[i] - mnew) : 0.f;
+        const float p = none ? 0.f : __builtin_amdgcn_exp2f(sc[g][i] - mnew);  // -inf -> 0
+        sc[g][i] = p;
         l[g] += p;
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) acc[g][d] = fmaf(p, vf[i][d], acc[g][d]);
       }
       mrun[g] = mnew;
     }
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int key = s0 + grp + NGRP * (batch * KI + i);
+      float vf[DPL];
+      widen(vb[i], vc, key, key < s1, vf);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) acc[g][d] = fmaf(sc[g][i], vf[d], acc[g][d]);
+    }
   };
   for (int bt = 0; bt < nb; bt += 2) {
-    if (bt + 1 < nb) load(bt + 1, kb1, vb1);
+    load(bt + 1, kb1, vb1);                    // past the last batch: clamped reloads
     compute(bt, kb0, vb0);
     if (bt + 1 >= nb) break;
-    if (bt + 2 < nb) load(bt + 2, kb0, vb0);
+    load(bt + 2, kb0, vb0);
     compute(bt + 1, kb1, vb1);
   }
 
