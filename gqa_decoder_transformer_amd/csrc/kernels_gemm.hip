@@ -259,7 +259,7 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm(GemmArgs a) {
 }
 
 // Tile configurations: block BM x BN, WM x WN waves, register prefetch depth PF.
-enum GemmCfg { CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x128 = 3, CFG_256x256 = 4 };
+enum GemmCfg { CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x128 = 3, CFG_256x256 = 4, CFG_64x64 = 5 };
 
 template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI>
 void set_attr() {
@@ -294,9 +294,10 @@ int tiles_of(const GemmArgs& a, int bm, int bn) {
 // 256 x 256 tiles over 8 waves (128 x 64 each, two waves per SIMD) when they make at
 // least one tile per CU (measured faster there at every K), else 128 x 128; the
 // two-plane (EXACT) input (a third LDS plane) takes 128 x 256 when that leaves ~0.7
-// tiles per CU. Small M takes 64 rows.
+// tiles per CU. Small M (batched decode) takes 64 x 64 tiles over 2 waves, four stages
+// of weight loads in flight.
 int pick_cfg(const GemmArgs& a) {
-  if (a.M <= 64) return CFG_64x128;
+  if (a.M <= 64) return CFG_64x64;
   if (a.a_lo) return tiles_of(a, 128, 256) >= 180 ? CFG_128x256 : CFG_128x128;
   if (tiles_of(a, 256, 256) >= 256) return CFG_256x256;
   return CFG_128x128;
@@ -307,6 +308,7 @@ void cfg_dims(int cfg, int& bm, int& bn) {
     case CFG_256x256: bm = 256; bn = 256; break;
     case CFG_128x256: bm = 128; bn = 256; break;
     case CFG_128x128: bm = 128; bn = 128; break;
+    case CFG_64x64: bm = 64; bn = 64; break;
     default: bm = 64; bn = 128; break;
   }
 }
@@ -319,6 +321,7 @@ void launch_split(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
       break;
     case CFG_128x256: launch_cfg<128, 256, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
     case CFG_128x128: launch_cfg<128, 128, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
+    case CFG_64x64: launch_cfg<64, 64, 2, 1, 4, SPLIT, EPI>(a, splits, st); break;
     default: launch_cfg<64, 128, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
   }
 }
@@ -335,6 +338,7 @@ void set_attrs_split() {
   set_attr<128, 256, 2, 2, 2, SPLIT, EPI>();
   set_attr<128, 128, 2, 2, 2, SPLIT, EPI>();
   set_attr<64, 128, 2, 2, 2, SPLIT, EPI>();
+  set_attr<64, 64, 2, 1, 4, SPLIT, EPI>();
 }
 
 template <int EPI>
@@ -378,14 +382,17 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs a, int splits) {
   }
 }
 
-// Split K when the tiles cannot fill the GPU: slices of >= 256 columns, about 512 blocks.
+// Split K when the tiles cannot fill the GPU: slices of >= 256 columns, about 512 blocks
+// (256 for the 64 x 64 tiles of small M, which stream four stages ahead: every split
+// adds an f32 partial plane to write and reduce).
 int pick_splits(const GemmArgs& a, int cfg) {
   if (!a.partial) return 1;
   int bm, bn;
   cfg_dims(cfg, bm, bn);
   const int tiles = tiles_of(a, bm, bn);
   if (tiles >= 192) return 1;
-  int s = (512 + tiles - 1) / tiles;
+  const int target = cfg == CFG_64x64 ? 256 : 512;
+  int s = (target + tiles - 1) / tiles;
   const int max_s = a.K / 256;
   if (s > max_s) s = max_s;
   if ((size_t)s * a.M * a.N > a.partial_elems) s = (int)(a.partial_elems / ((size_t)a.M * a.N));
