@@ -36,9 +36,13 @@ constexpr size_t gemm_lds_bytes() {
   return (size_t)2 * ((SPLIT ? 2 : 1) * BM + BN) * LDS_STRIDE * 2;
 }
 
-template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI, bool TAIL, bool DB = true>
-__global__ void __launch_bounds__(WM * WN * kWave) k_gemm(GemmArgs a) {
-  constexpr int NT = WM * WN * kWave;
+// KG > 1: KG groups of WM x WN waves compute the same tile over consecutive parts of
+// its K range, each with its own two LDS stages; the groups' accumulators are summed
+// through LDS in group order before the epilogue (occupancy without partial planes).
+template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI, bool TAIL, bool DB = true,
+          int KG = 1>
+__global__ void __launch_bounds__(WM * WN * KG * kWave) k_gemm(GemmArgs a) {
+  constexpr int NT = WM * WN * kWave;                     // threads of one K group
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;    // 32x32 fragments per wave
   constexpr int RS = NT / 8;                              // rows per load round
   constexpr int CA = BM / RS, CB = BN / RS;               // 16-byte loads per plane
@@ -47,6 +51,8 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm(GemmArgs a) {
   constexpr int STAGE = NP * PLANE + BN * LDS_STRIDE;
   static_assert(CA * RS == BM && CB * RS == BN, "tile rows");
   static_assert(EPI != GEMM_SILU || TN % 2 == 0, "SiLU pairs gate/up fragments");
+  static_assert((size_t)(KG - 1) * WM * WN * TM * TN * 16 * kWave * 4 <= (size_t)KG * 2 * STAGE * 2,
+                "group reduction fits in the stages");
   extern __shared__ __align__(16) uint16_t smem[];
 
   // XCD-aware tile order: blocks are dealt round-robin to the 8 XCDs; give each XCD a
@@ -58,18 +64,21 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm(GemmArgs a) {
   if (nblk % 8 == 0) lin = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
   const int tm = lin % mt, tn = lin / mt;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int kg = threadIdx.x / NT, tg = threadIdx.x % NT;  // K group, thread in group
+  const int wave = tg / kWave, lane = tg % kWave;
   const int wm0 = (wave / WN) * (BM / WM), wn0 = (wave % WN) * (BN / WN);
   const int fr = lane % 32, fk = (lane / 32) * 8;
 
-  // K range of this block (split-K over gridDim.y slices of k_chunk columns)
-  const int kb0 = blockIdx.y * a.k_chunk;
-  const int kend = min(a.K, kb0 + a.k_chunk);
-  const int nk = (kend - kb0 + BK - 1) / BK;
+  // K range of this block (split-K over gridDim.y slices of k_chunk columns), then of
+  // this K group (the host gives every group the same number of stages)
+  const int kbb = blockIdx.y * a.k_chunk;
+  const int kend = min(a.K, kbb + a.k_chunk);
+  const int nk = (kend - kbb + BK - 1) / BK / KG;
+  const int kb0 = kbb + kg * nk * BK;
 
   // this thread's load rows (clamped: rows past M/N are loaded but never stored) and
   // its 8-element k chunk within a stage
-  const int r0 = threadIdx.x / 8, kc = (threadIdx.x % 8) * 8;
+  const int r0 = tg / 8, kc = (tg % 8) * 8;
   const uint16_t* pa_hi = a.a_hi + (size_t)min(m0 + r0, a.M - 1) * a.lda + kc;
   const uint16_t* pa_lo = SPLIT ? a.a_lo + (size_t)min(m0 + r0, a.M - 1) * a.lda + kc : nullptr;
   const uint16_t* pw = a.w + (size_t)min(n0 + r0, a.N - 1) * a.K + kc;
@@ -113,8 +122,9 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < CB; ++i) rw[b][i] = *(const u32x4_t*)(pw + ob[i] + kk);
   };
+  uint16_t* const sg = smem + kg * 2 * STAGE;             // this group's two stages
   auto sstore = [&](int b, int s) {
-    uint16_t* base = smem + s * STAGE + lofs;
+    uint16_t* base = sg + s * STAGE + lofs;
     const u32x4_t z = {0, 0, 0, 0};
     const bool ok = okb[b];
 #pragma unroll
@@ -129,7 +139,7 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm(GemmArgs a) {
   constexpr int NF = DB ? 2 : 1;                          // fragment buffers
   bf16x8_t fh[NF][TM], fl[NF][SPLIT ? TM : 1], fw[NF][TN];
   auto rdfrag = [&](int f, int s, int ks) {
-    const uint16_t* st = smem + s * STAGE;
+    const uint16_t* st = sg + s * STAGE;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int o = (wm0 + i * 32 + fr) * LDS_STRIDE + ks + fk;
@@ -197,6 +207,33 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm(GemmArgs a) {
     }
   }
 
+  if constexpr (KG > 1) {
+    // groups 1.. hand their accumulators to group 0 through LDS (the stages are free)
+    float* red = (float*)smem;                  // [group - 1][wave][i][j][e][lane]
+    __syncthreads();
+    if (kg > 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            red[(((((size_t)(kg - 1) * WM * WN + wave) * TM + i) * TN + j) * 16 + e) * kWave + lane] =
+                acc[i][j][e];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int g = 1; g < KG; ++g)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            acc[i][j][e] += red[(((((size_t)(g - 1) * WM * WN + wave) * TM + i) * TN + j) * 16 + e) * kWave + lane];
+  }
+
   // epilogue: element e of fragment (i, j) is C[row][col] with
   // row = m0 + wm0 + 32 i + 4 (lane / 32) + 8 (e / 4) + e % 4, col = n0 + wn0 + 32 j + lane % 32.
   // One 64-bit base per fragment, 32-bit row offsets after it (fewer live registers
@@ -258,31 +295,33 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm(GemmArgs a) {
   }
 }
 
-// Tile configurations: block BM x BN, WM x WN waves, register prefetch depth PF.
-enum GemmCfg { CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x128 = 3, CFG_256x256 = 4, CFG_64x64 = 5 };
+// Tile configurations: block BM x BN, WM x WN waves, register prefetch depth PF, KG
+// groups of waves over the K range.
+enum GemmCfg { CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x128 = 3, CFG_256x256 = 4, CFG_64x64 = 5,
+               CFG_128x128_K2 = 6 };
 
-template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI>
+template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI, int KG = 1>
 void set_attr() {
-  (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, PF, SPLIT, EPI, false>,
+  (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, PF, SPLIT, EPI, false, true, KG>,
                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)gemm_lds_bytes<BM, BN, SPLIT>());
-  (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, PF, SPLIT, EPI, true>,
+                            (int)(KG * gemm_lds_bytes<BM, BN, SPLIT>()));
+  (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, PF, SPLIT, EPI, true, true, KG>,
                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)gemm_lds_bytes<BM, BN, SPLIT>());
+                            (int)(KG * gemm_lds_bytes<BM, BN, SPLIT>()));
 }
 
-template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI>
+template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI, int KG = 1>
 void launch_cfg(const GemmArgs& a, int splits, hipStream_t st) {
   const int blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  const size_t lds = gemm_lds_bytes<BM, BN, SPLIT>();
+  const size_t lds = KG * gemm_lds_bytes<BM, BN, SPLIT>();
   // every K slice a whole number of 64-column stages: no tail handling
   const bool tail = a.K % BK != 0 || a.k_chunk % BK != 0;
   if (tail)
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, PF, SPLIT, EPI, true>), dim3(blocks, splits),
-                       dim3(WM * WN * kWave), lds, st, a);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, PF, SPLIT, EPI, true, true, KG>), dim3(blocks, splits),
+                       dim3(WM * WN * KG * kWave), lds, st, a);
   else
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, PF, SPLIT, EPI, false>), dim3(blocks, splits),
-                       dim3(WM * WN * kWave), lds, st, a);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, PF, SPLIT, EPI, false, true, KG>), dim3(blocks, splits),
+                       dim3(WM * WN * KG * kWave), lds, st, a);
 }
 
 int tiles_of(const GemmArgs& a, int bm, int bn) {
@@ -300,6 +339,10 @@ int pick_cfg(const GemmArgs& a) {
   if (a.M <= 64) return CFG_64x64;
   if (a.a_lo) return tiles_of(a, 128, 256) >= 180 ? CFG_128x256 : CFG_128x128;
   if (tiles_of(a, 256, 256) >= 256) return CFG_256x256;
+  // about one 128 x 128 tile per CU: two K groups per tile (two waves per SIMD) when the
+  // stages split evenly
+  const int t128 = tiles_of(a, 128, 128);
+  if (t128 >= 192 && t128 <= 256 && a.K % (2 * BK) == 0) return CFG_128x128_K2;
   return CFG_128x128;
 }
 
@@ -307,7 +350,7 @@ void cfg_dims(int cfg, int& bm, int& bn) {
   switch (cfg) {
     case CFG_256x256: bm = 256; bn = 256; break;
     case CFG_128x256: bm = 128; bn = 256; break;
-    case CFG_128x128: bm = 128; bn = 128; break;
+    case CFG_128x128: case CFG_128x128_K2: bm = 128; bn = 128; break;
     case CFG_64x64: bm = 64; bn = 64; break;
     default: bm = 64; bn = 128; break;
   }
@@ -321,6 +364,9 @@ void launch_split(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
       break;
     case CFG_128x256: launch_cfg<128, 256, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
     case CFG_128x128: launch_cfg<128, 128, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
+    case CFG_128x128_K2:
+      if constexpr (!SPLIT) launch_cfg<128, 128, 2, 2, 2, false, EPI, 2>(a, splits, st);
+      break;
     case CFG_64x64: launch_cfg<64, 64, 2, 1, 4, SPLIT, EPI>(a, splits, st); break;
     default: launch_cfg<64, 128, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
   }
@@ -334,7 +380,10 @@ void launch_epi(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
 
 template <bool SPLIT, int EPI>
 void set_attrs_split() {
-  if constexpr (!SPLIT) set_attr<256, 256, 2, 4, 1, false, EPI>();
+  if constexpr (!SPLIT) {
+    set_attr<256, 256, 2, 4, 1, false, EPI>();
+    set_attr<128, 128, 2, 2, 2, false, EPI, 2>();
+  }
   set_attr<128, 256, 2, 2, 2, SPLIT, EPI>();
   set_attr<128, 128, 2, 2, 2, SPLIT, EPI>();
   set_attr<64, 128, 2, 2, 2, SPLIT, EPI>();
