@@ -352,7 +352,8 @@ __global__ void __launch_bounds__(256) k_kv_pack(KvPackArgs a) {
 // maximum moves only when exceeded by more than 2^8); masks are applied only on tiles
 // that cross the causal diagonal or the end of the keys (scale * log2 e is folded into Q
 // before its bf16 rounding; P is rounded with the hardware pack-convert); under the causal mask a wave
-// skips the tiles wholly past its last query. Output rows go through LDS and leave as 16-byte stores.
+// skips the tiles wholly past its last query; blocks are ordered so that each half of the
+// grid pairs long and short causal rows. Output rows go through LDS and leave as 16-byte stores.
 constexpr int kTQ = 128, kTK = 64;
 
 template <int HD, bool SPLIT>
@@ -374,8 +375,16 @@ __global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t
   constexpr int CK = kTK * HD / 8 / 256;                         // 16-byte chunks per thread
   extern __shared__ __align__(16) uint16_t sm[];
 
-  const int qt = gridDim.x - 1 - blockIdx.x;                   // late (long) tiles first
-  const int h = blockIdx.y, r = blockIdx.z;
+  // Dispatch order L (x fastest, then heads, then rows) -> tile: the first half of the
+  // grid takes the tiles in decreasing query position (long causal rows first), the
+  // second half in increasing position, so blocks half a grid apart (dispatched into
+  // the same slots) carry complementary amounts of work.
+  const int nq = gridDim.x, HR = gridDim.y * gridDim.z, total = nq * HR;
+  const int L = blockIdx.x + nq * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int half = (total + 1) / 2;
+  const int tix = L < half ? L : total - 1 - (L - half);
+  const int qt = nq - 1 - tix / HR;
+  const int h = (tix % HR) % gridDim.y, r = (tix % HR) / gridDim.y;
   const int g = h / (a.NH / a.NKV);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int lq = lane % 32, hl = lane / 32;
