@@ -319,14 +319,19 @@ __global__ void __launch_bounds__(256) k_kv_pack(KvPackArgs a) {
   }
   __syncthreads();
   const size_t vb = ((size_t)r * a.NKV + g) * HD * a.LK;
+  // V^T keys are stored in the order the attention kernel's MFMA operand wants them:
+  // within every 16 keys the middle two runs of 4 swap places, so a lane's 8 keys
+  // (0-3 and 8-11, or 4-7 and 12-15) are 16 contiguous bytes
   for (int it = threadIdx.x; it < HD * 8; it += 256) {
     const int d = it / 8, key8 = (it % 8) * 8;
+    const int src0 = (key8 & ~15) + ((key8 & 8) ? 4 : 0);   // source keys src0 + {0..3, 8..11}
     u32x4_t hi, lo;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      const int ka = src0 + (2 * j < 4 ? 2 * j : 2 * j + 4);
       uint32_t h0, l0, h1, l1;
-      split_bf16(vs[(key8 + 2 * j) * (HD + 1) + d], h0, l0);
-      split_bf16(vs[(key8 + 2 * j + 1) * (HD + 1) + d], h1, l1);
+      split_bf16(vs[ka * (HD + 1) + d], h0, l0);
+      split_bf16(vs[(ka + 1) * (HD + 1) + d], h1, l1);
       hi[j] = pack2(h0, h1);
       lo[j] = pack2(l0, l1);
     }
@@ -345,7 +350,8 @@ __global__ void __launch_bounds__(256) k_kv_pack(KvPackArgs a) {
 //   O^T = V^T P^T: B = P^T must hold 8 keys of query l % 32 per lane: the lane's own 8
 //                probabilities of a 16-key half block, so MFMA slot 8 (l / 32) + i stands
 //                for key 16 t + (i < 4 ? 4 (l / 32) + i : 8 + 4 (l / 32) + i - 4), and V^T
-//                is read with the same order (two 8-byte LDS reads per fragment).
+//                is packed in that order (k_kv_pack swaps the middle two runs of 4 keys of every
+//                16), so each V^T fragment is one 16-byte LDS read.
 // Both tiles are double-buffered in LDS, loaded one tile ahead through registers from the
 // packed planes (16-byte loads, rows padded by 16 bytes). The softmax is the online one
 // in base 2 (scores pre-multiplied by scale * log2 e) with lazy rescaling (the running
@@ -565,16 +571,12 @@ __global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t
         if (SPLIT) lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pbl, lsum, 0, 0, 0);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int vo = (db * 32 + lq) * VS + 16 * t + 4 * hl;
+          const int vo = (db * 32 + lq) * VS + 16 * t + 8 * hl;   // keys stored permuted
           const uint16_t* vb = st + NP * C::KTILE;
-          u32x4_t vh;
-          const uint2 v0 = *(const uint2*)(vb + vo), v1 = *(const uint2*)(vb + vo + 8);
-          vh[0] = v0.x; vh[1] = v0.y; vh[2] = v1.x; vh[3] = v1.y;
+          const u32x4_t vh = *(const u32x4_t*)(vb + vo);
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vh), pbh, o[db], 0, 0, 0);
           if (SPLIT) {
-            u32x4_t vl;
-            const uint2 w0 = *(const uint2*)(vb + C::VTILE + vo), w1 = *(const uint2*)(vb + C::VTILE + vo + 8);
-            vl[0] = w0.x; vl[1] = w0.y; vl[2] = w1.x; vl[3] = w1.y;
+            const u32x4_t vl = *(const u32x4_t*)(vb + C::VTILE + vo);
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vh), pbl, o[db], 0, 0, 0);
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vl), pbh, o[db], 0, 0, 0);
           }
