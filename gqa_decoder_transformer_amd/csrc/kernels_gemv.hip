@@ -63,9 +63,9 @@ EMBER_DEV void load_chunk_f32(const float* p, int c, bool valid, float* out) {
 
 // The input vector rebuilt from decode-attention split partials (see GemvArgs::xpart),
 // once per block into LDS (xs, 1024 entries): thread t takes elements t + 256 u (u < 4;
-// K <= 1024). Splits at
-// or past the number that hold keys are excluded by select (their memory may hold
-// anything). `ld` loads the partials; `finish` combines them and stores the LDS copy.
+// K <= 1024). Splits at or past the number that hold keys are excluded by select (their
+// memory may hold anything). part_load loads the partials; part_finish combines them
+// into the LDS copy.
 struct PartIn {
   float m[4][4], l[4][4], ac[4][4];     // [element u][split j]
 };
