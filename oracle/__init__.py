@@ -4,7 +4,8 @@ A plain, slow, obviously correct CPU implementation (NumPy; scalar Python loops 
 brute-force form) of what the GPU path computes: bf16->f32 weight widening, RMSNorm,
 rotate-half RoPE with optional llama3 frequency scaling, grouped-query attention with a
 causal KV cache (or bidirectional), SwiGLU MLP, the tied LM head or a token
-classification head, and greedy argmax.
+classification head, greedy argmax, and the sampler (temperature, top-k, top-p, softmax,
+inverse-CDF draw; ``oracle.sampler``).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
 may import this package. The HIP library and its Python binding never import, call or
@@ -26,3 +27,4 @@ from .primitives import (apply_rope, attention, decode_tensor, greedy_argmax,  #
                          widen_bf16)
 from .model import KVCache, OracleModel, generate, recompute_logits  # noqa: F401
 from . import brute  # noqa: F401
+from . import sampler  # noqa: F401
