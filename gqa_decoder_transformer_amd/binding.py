@@ -26,8 +26,8 @@ HEAD_TIED_LM, HEAD_CLS = 0, 1
 EXPORTED = ["ember_workspace_bytes", "ember_kv_cache_bytes", "ember_load_weights",
             "ember_cache_bind", "ember_prefill", "ember_decode_step", "ember_logits",
             "ember_sync", "ember_cache_free", "ember_free", "ember_last_error",
-            "ember_rope_table", "ember_time_kernel"]
-K_LM_HEAD, K_QKV, K_ATTN, K_O, K_GATE_UP, K_DOWN, K_LAYER = range(7)
+            "ember_rope_table", "ember_time_kernel", "ember_set_sampler", "ember_sample"]
+K_LM_HEAD, K_QKV, K_ATTN, K_O, K_GATE_UP, K_DOWN, K_LAYER, K_SAMPLE = range(8)
 
 
 class EmberConfig(ctypes.Structure):
@@ -52,6 +52,12 @@ class EmberTensor(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("data", ctypes.c_void_p),
                 ("shape", ctypes.c_int64 * 4), ("ndim", ctypes.c_int32),
                 ("dtype", ctypes.c_int32)]
+
+
+class EmberSampler(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32),
+                ("top_p", ctypes.c_float), ("d_uniform", ctypes.c_void_p),
+                ("n_pos", ctypes.c_int32), ("ld", ctypes.c_int32)]
 
 
 class EmberError(RuntimeError):
@@ -89,6 +95,8 @@ def _load():
         "ember_rope_table": (ctypes.c_int, [cfgp, ctypes.c_int32, P, P]),
         "ember_time_kernel": (ctypes.c_int, [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                              P, ctypes.POINTER(ctypes.c_float)]),
+        "ember_set_sampler": (ctypes.c_int, [P, ctypes.POINTER(EmberSampler)]),
+        "ember_sample": (ctypes.c_int, [P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -177,6 +185,15 @@ def ember_time_kernel(model: int, cache: int, kernel: int, phase: int, iters: in
     out = ctypes.c_float()
     _check(LIB.ember_time_kernel(model, cache, kernel, phase, iters, stream, ctypes.byref(out)))
     return out.value
+
+
+def ember_set_sampler(model: int, sampler: Optional[EmberSampler]):
+    _check(LIB.ember_set_sampler(model, ctypes.byref(sampler) if sampler is not None else None))
+
+
+def ember_sample(model: int, d_logits: int, rows: int, ld_logits: int, pos: int, d_next: int,
+                 stream: int):
+    _check(LIB.ember_sample(model, d_logits, rows, ld_logits, pos, d_next, stream))
 
 
 # ------------------------------------------------------------------ marshalling helpers
@@ -289,6 +306,34 @@ class Engine:
 
     def sync(self):
         ember_sync(self.model, self.sp)
+
+    def set_sampler(self, temperature: float = 0.0, top_k: int = 0, top_p: float = 1.0,
+                    uniform=None):
+        """uniform: device f32 tensor [n_pos, ld] of draws in [0, 1), kept referenced here
+        while the sampler is set. temperature 0 returns to greedy argmax."""
+        if temperature == 0.0 and uniform is None:
+            self._uniform = None
+            ember_set_sampler(self.model, None)
+            return
+        if uniform is None or uniform.dim() != 2 or not uniform.is_contiguous():
+            raise ValueError("uniform must be a contiguous [n_pos, ld] device tensor")
+        if uniform.dtype != self.torch.float32:
+            raise ValueError("uniform must be float32")
+        s = EmberSampler(temperature, top_k, top_p, uniform.data_ptr(), uniform.shape[0],
+                         uniform.shape[1])
+        ember_set_sampler(self.model, s)
+        self._uniform = uniform
+
+    def sample(self, d_logits, pos: int, d_next=None):
+        """Next ids of the rows of device logits [rows, V] f32 with the current sampler."""
+        if d_logits.dtype != self.torch.float32 or d_logits.dim() != 2 or d_logits.stride(1) != 1:
+            raise ValueError("logits must be a [rows, V] float32 tensor with unit column stride")
+        rows = d_logits.shape[0]
+        if d_next is None:
+            d_next = self.torch.empty(rows, dtype=self.torch.int32, device=self.device)
+        ember_sample(self.model, d_logits.data_ptr(), rows, d_logits.stride(0), pos,
+                     d_next.data_ptr(), self.sp)
+        return d_next
 
     def time_kernel(self, kernel: int, phase: int, iters: int = 20) -> float:
         return ember_time_kernel(self.model, self.cache, kernel, phase, iters, self.sp)

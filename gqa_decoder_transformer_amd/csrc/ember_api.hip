@@ -220,6 +220,9 @@ struct ember_model {
   int graph_batch = -1;
   hipStream_t graph_stream = nullptr;
   int32_t* graph_next = nullptr;
+  // sampler of the next-token outputs (greedy argmax when `sampling` is false)
+  ember_sampler samp{};
+  bool sampling = false;
   template <typename T> T* at(size_t off) const { return (T*)(ws + off); }
   float* splitk() const { return plan.splitk_elems ? (float*)(ws + plan.splitk) : nullptr; }
 };
@@ -242,6 +245,33 @@ struct Ctx {
 
 bool want(const Ctx& cx, int kind) { return cx.only < 0 || cx.only == kind; }
 bool want_aux(const Ctx& cx) { return cx.only < 0; }
+
+// Next ids of R rows of logits [R, ld] drawn with the model's sampler: draw row u_pos
+// (the device position of a decode step when u_pos < 0), columns u_col0 + r.
+void launch_draw(const Ctx& cx, const float* logits, int R, long long ld, int32_t* next,
+                 int u_col0, int u_pos) {
+  ember_model* md = cx.m;
+  SampleArgs a{};
+  a.logits = logits; a.ld = ld; a.R = R; a.V = md->cfg.vocab;
+  a.temperature = md->samp.temperature; a.top_k = md->samp.top_k; a.top_p = md->samp.top_p;
+  a.uniform = md->samp.d_uniform; a.u_rows = md->samp.n_pos; a.u_ld = md->samp.ld;
+  a.col0 = u_col0; a.pos = u_pos < 0 ? 0 : u_pos;
+  a.d_pos = u_pos < 0 ? md->at<int>(md->plan.pos) : nullptr;
+  a.next = next; a.flags = md->at<int>(md->plan.flags);
+  launch_sample(a, cx.st);
+}
+
+// Whether a call drawing `rows` rows from draw row `u_pos` fits the sampler's draws.
+ember_status check_draws(const ember_model* md, int rows, long long u_pos) {
+  if (!md->sampling) return EMBER_OK;
+  if (u_pos >= md->samp.n_pos)
+    return fail(EMBER_E_CAPACITY, "draw row %lld beyond the sampler's %d rows", u_pos,
+                md->samp.n_pos);
+  if (rows > md->samp.ld)
+    return fail(EMBER_E_CAPACITY, "batch %d beyond the sampler's row stride %d", rows,
+                md->samp.ld);
+  return EMBER_OK;
+}
 
 void* k_layer(const ember_cache* c, int l) { return c->kv + (size_t)l * c->layer_bytes; }
 void* v_layer(const ember_cache* c, int l) {
@@ -433,9 +463,12 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
 
 // Tied LM head over R rows of x (row r = x[r * row_step + row_off]): final RMSNorm, then
 // logits = E . h ("ember scripts/reference_forward.py", end of forward), then the greedy
-// argmax. Writes logits [R, ld] at `out` and next ids when `next` is non-null.
+// argmax, or the sampler's draw (draw row u_pos, or the device position when u_pos < 0;
+// columns u_col0 + r). Writes logits [R, ld] at `out` and next ids when `next` is
+// non-null.
 void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, long long ld,
-                 int32_t* next) {
+                 int32_t* next, int u_col0 = 0, int u_pos = -1) {
+  const bool draw = next && cx.m->sampling && (want_aux(cx) || cx.only == EMBER_K_SAMPLE);
   ember_model* md = cx.m;
   const ember_config& c = md->cfg;
   const Plan& p = md->plan;
@@ -452,7 +485,9 @@ void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, lo
     g.argmax_part = md->at<unsigned long long>(p.argpart);
     g.flags = md->at<int>(p.flags);
     if (want(cx, EMBER_K_LM_HEAD)) launch_gemv(g, GEMV_LOGITS, st);
-    if (next && want_aux(cx))
+    if (draw)
+      launch_draw(cx, out, 1, ld, next, u_col0, u_pos);
+    else if (next && want_aux(cx))
       launch_argmax_reduce(g.argmax_part, gemv_num_blocks(V, GEMV_LOGITS, H, md->wbf16), 1, next, st);
     return;
   }
@@ -482,8 +517,10 @@ void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, lo
       g.c = out + (size_t)r0 * ld; g.ldc = ld;
       if (want(cx, EMBER_K_LM_HEAD)) launch_gemm_f32w(g, GEMM_STORE, st);
     }
-    if (next && want_aux(cx)) launch_argmax_rows(out + (size_t)r0 * ld, rn, V, ld, next + r0,
-                                 md->at<int>(p.flags), st);
+    if (draw)
+      launch_draw(cx, out + (size_t)r0 * ld, rn, ld, next + r0, u_col0 + r0, u_pos);
+    else if (next && want_aux(cx))
+      launch_argmax_rows(out + (size_t)r0 * ld, rn, V, ld, next + r0, md->at<int>(p.flags), st);
   }
 }
 
@@ -507,7 +544,7 @@ void run_cls_head(const Ctx& cx, int R, int row_step, int row_off, float* out, i
 
 // One decode step's device work for B rows, ids in plan.ids, position in plan.pos.
 // The layers and the LM head of one decode step (the step's embedding and staging run
-// before it); greedy ids go to `next`.
+// before it); the next ids (greedy or drawn) go to `next`.
 void decode_body(const Ctx& cx, int B, int32_t* next, int only_layer = -1) {
   ember_model* md = cx.m;
   const ember_config& c = md->cfg;
@@ -518,7 +555,7 @@ void decode_body(const Ctx& cx, int B, int32_t* next, int only_layer = -1) {
   ps.attn = ATTN_DECODE;
   for (int l = 0; l < c.layers; ++l)
     if (only_layer < 0 || l == only_layer) run_layer(cx, l, ps);
-  if (want(cx, EMBER_K_LM_HEAD) && (cx.only >= 0 || only_layer < 0))
+  if ((want(cx, EMBER_K_LM_HEAD) || cx.only == EMBER_K_SAMPLE) && (cx.only >= 0 || only_layer < 0))
     run_lm_head(cx, B, 1, 0, md->at<float>(p.logits), c.vocab, next);
 }
 
@@ -725,6 +762,10 @@ ember_status ember_prefill(ember_model* md, ember_cache* cache, const int32_t* h
   for (long long i = 0; i < (long long)batch * n_tokens; ++i)
     if (h_ids[i] < 0 || h_ids[i] >= c.vocab)
       return fail(EMBER_E_TOKEN, "token %d outside vocabulary", h_ids[i]);
+  if (d_next && c.head_kind == EMBER_HEAD_TIED_LM) {
+    const ember_status s = check_draws(md, batch, (long long)start_pos + n_tokens - 1);
+    if (s != EMBER_OK) return s;
+  }
 
   hipStream_t st = (hipStream_t)stream;
   const Plan& p = md->plan;
@@ -763,7 +804,7 @@ ember_status ember_prefill(ember_model* md, ember_cache* cache, const int32_t* h
         }
         if (last_chunk)
           run_lm_head(cx, rows, tpr, tpr - 1, md->at<float>(p.logits) + (size_t)b0 * out_dim,
-                      out_dim, d_next ? d_next + b0 : nullptr);
+                      out_dim, d_next ? d_next + b0 : nullptr, b0, start_pos + T - 1);
       } else {
         for (int r = 0; r < rows; ++r)
           if (d_all_logits || d_next)
@@ -795,6 +836,10 @@ ember_status ember_decode_step(ember_model* md, ember_cache* cache, const int32_
   if (cache->filled == 0) return fail(EMBER_E_STATE, "decode step before any prefill");
   if (pos > cache->filled)
     return fail(EMBER_E_STATE, "position %d leaves a gap after %d cached positions", pos, cache->filled);
+  {
+    const ember_status s = check_draws(md, batch, pos);
+    if (s != EMBER_OK) return s;
+  }
   hipStream_t st = (hipStream_t)stream;
   const Plan& p = md->plan;
   Ctx cx{md, cache, st};
@@ -840,7 +885,9 @@ ember_status ember_time_kernel(ember_model* md, ember_cache* cache, int32_t kern
                                int32_t iters, void* stream, float* avg_us) {
   g_last_error.clear();
   if (!md || !cache || !avg_us || iters <= 0) return fail(EMBER_E_ARG, "bad arguments");
-  if (kernel < EMBER_K_LM_HEAD || kernel > EMBER_K_LAYER) return fail(EMBER_E_ARG, "unknown kernel");
+  if (kernel < EMBER_K_LM_HEAD || kernel > EMBER_K_SAMPLE) return fail(EMBER_E_ARG, "unknown kernel");
+  if (kernel == EMBER_K_SAMPLE && (phase != 0 || !md->sampling))
+    return fail(EMBER_E_ARG, "the sampler is timed on decode steps with a sampler set");
   hipStream_t st = (hipStream_t)stream;
   Ctx cx{md, cache, st, kernel == EMBER_K_LAYER ? -1 : kernel};
   const ember_config& c = md->cfg;
@@ -907,6 +954,53 @@ ember_status ember_time_kernel(ember_model* md, ember_cache* cache, int32_t kern
   if (ge) (void)hipGraphExecDestroy(ge);
   HIP_TRY(hipGetLastError());
   *avg_us = ms * 1000.f / (float)(iters * reps);
+  return EMBER_OK;
+}
+
+ember_status ember_set_sampler(ember_model* md, const ember_sampler* s) {
+  g_last_error.clear();
+  if (!md) return fail(EMBER_E_ARG, "NULL model");
+  if (s && !(s->temperature >= 0.f && std::isfinite(s->temperature)))
+    return fail(EMBER_E_ARG, "temperature must be finite and >= 0");
+  const bool on = s && s->temperature > 0.f;
+  if (on) {
+    if (!std::isfinite(s->top_p) || s->top_p < 0.f) return fail(EMBER_E_ARG, "top_p must be finite and >= 0");
+    if (s->top_k < 0) return fail(EMBER_E_ARG, "top_k must be >= 0");
+    if (!s->d_uniform || s->n_pos < 1 || s->ld < 1)
+      return fail(EMBER_E_ARG, "the sampler needs draws d_uniform [n_pos >= 1, ld >= 1]");
+    if (md->cfg.head_kind != EMBER_HEAD_TIED_LM)
+      return fail(EMBER_E_STATE, "sampling needs the tied LM head");
+    if (md->cfg.vocab > kSampleMaxVocab)
+      return fail(EMBER_E_CAPACITY, "vocabulary %d beyond the sampler's %d", md->cfg.vocab,
+                  kSampleMaxVocab);
+  }
+  if (md->graph) {
+    (void)hipGraphExecDestroy(md->graph);
+    md->graph = nullptr;
+    md->graph_cache = nullptr;
+  }
+  md->sampling = on;
+  md->samp = on ? *s : ember_sampler{};
+  return EMBER_OK;
+}
+
+ember_status ember_sample(ember_model* md, const float* d_logits, int32_t rows,
+                          int64_t ld_logits, int32_t pos, int32_t* d_next, void* stream) {
+  g_last_error.clear();
+  if (!md || !d_logits || !d_next) return fail(EMBER_E_ARG, "NULL argument");
+  if (md->cfg.head_kind != EMBER_HEAD_TIED_LM) return fail(EMBER_E_STATE, "sampling needs the tied LM head");
+  if (rows < 1) return fail(EMBER_E_ARG, "rows must be >= 1");
+  if (ld_logits < md->cfg.vocab) return fail(EMBER_E_ARG, "row stride below the vocabulary");
+  if (pos < 0) return fail(EMBER_E_ARG, "negative draw row");
+  const ember_status s = check_draws(md, rows, pos);
+  if (s != EMBER_OK) return s;
+  Ctx cx{md, nullptr, (hipStream_t)stream};
+  if (md->sampling)
+    launch_draw(cx, d_logits, rows, ld_logits, d_next, 0, pos);
+  else
+    launch_argmax_rows(d_logits, rows, md->cfg.vocab, ld_logits, d_next, md->at<int>(md->plan.flags),
+                       cx.st);
+  HIP_TRY(hipGetLastError());
   return EMBER_OK;
 }
 

@@ -80,6 +80,33 @@ struct StepBeginArgs {
   int H;
 };
 void launch_step_begin(const StepBeginArgs& a, hipStream_t st);
+// ---------------------------------------------------------------- sampling (kernels_sample.hip)
+
+constexpr int kSampleMaxTiles = 4096;
+constexpr int kSampleMaxVocab = kSampleMaxTiles * 256;
+
+// next[r] = a token drawn from row r of the logits through temperature, top-k, top-p,
+// softmax and an inverse-CDF draw with u = uniform[row * u_ld + col0 + r], where row is
+// *d_pos when d_pos is non-null, else pos (clamped to u_rows - 1). temperature > 0.
+// Raises kFlagNaN when a row holds a NaN.
+struct SampleArgs {
+  const float* logits;
+  long long ld;
+  int R, V;
+  float temperature;
+  int top_k;
+  float top_p;
+  const float* uniform;
+  int u_rows;
+  long long u_ld;
+  int col0;
+  int pos;
+  const int* d_pos;
+  int32_t* next;
+  int* flags;
+};
+void launch_sample(const SampleArgs& a, hipStream_t st);
+
 void launch_fill_i32(int* p, int n, int v, hipStream_t st);
 // dst[i] = widen(src[i]) for i < n (bf16 or f32 source).
 void launch_widen(const void* src, bool bf16, float* dst, long long n, hipStream_t st);

@@ -164,6 +164,44 @@ ember_status ember_logits(ember_model* model, void* d_out, int32_t dtype, void* 
  * clear them. */
 ember_status ember_sync(ember_model* model, void* stream);
 
+/* Sampling ("ember internals" page, section "sampler"): the token of ember_prefill's and
+ * ember_decode_step's d_next is drawn instead of taken greedily. The stages, in order:
+ * z = logit / temperature; top-k (0 < top_k < vocab): z below the top_k-th largest z is
+ * dropped, ties with it kept; top-p (0 < top_p < 1): tokens whose probability under the
+ * softmax of the remaining z lies below the nucleus cutoff (the smallest probability of
+ * the shortest decreasing-order prefix whose sum exceeds top_p) are dropped; softmax of
+ * the rest (uniform when every z is -inf); the first index whose running probability sum
+ * in index order exceeds the draw u, or the last index of the maximum when rounding
+ * leaves none.
+ * The draws are inputs: d_uniform is device f32 [n_pos, ld], values in [0, 1), borrowed
+ * while the sampler is set. Row q, column b is the draw of batch row b for the token
+ * predicted from the logits at position q: a decode step at `pos` reads row pos, a
+ * prefill of positions [start_pos, start_pos + n) reads row start_pos + n - 1. */
+typedef struct ember_sampler {
+  float temperature;           /* > 0 draws; 0 = greedy argmax (the default) */
+  int32_t top_k;               /* 0 or >= vocab: stage off */
+  float top_p;                 /* outside (0, 1): stage off */
+  const float* d_uniform;      /* device [n_pos, ld] f32 */
+  int32_t n_pos;               /* rows of d_uniform */
+  int32_t ld;                  /* row stride of d_uniform in floats */
+} ember_sampler;
+
+/* Set the sampler of `model` (copied), or with NULL or temperature 0 return to greedy
+ * argmax. A negative or non-finite temperature or top_p, top_k < 0, a NULL d_uniform,
+ * n_pos < 1 or ld < 1 fail with EMBER_E_ARG, a classification-head model with
+ * EMBER_E_STATE, a vocabulary above 1048576 with EMBER_E_CAPACITY. Afterwards a prefill
+ * or decode step whose draw row lies beyond n_pos - 1 or whose batch exceeds ld fails
+ * with EMBER_E_CAPACITY. The next decode step captures its graph again. */
+ember_status ember_set_sampler(ember_model* model, const ember_sampler* sampler);
+
+/* Draw one token for each of `rows` rows of caller logits d_logits f32 [rows, vocab]
+ * (row stride ld_logits >= vocab, device) with the model's sampler, u = d_uniform[pos *
+ * ld + r], into d_next [rows] int32 (device); greedy argmax when no sampler is set. A
+ * NaN logit raises the model's NaN flag (ember_sync). EMBER_E_CAPACITY when pos lies
+ * beyond n_pos - 1 or rows exceeds ld. */
+ember_status ember_sample(ember_model* model, const float* d_logits, int32_t rows,
+                          int64_t ld_logits, int32_t pos, int32_t* d_next, void* stream);
+
 void ember_cache_free(ember_cache* cache);
 void ember_free(ember_model* model);
 
@@ -186,7 +224,8 @@ typedef enum ember_kernel {
   EMBER_K_O = 3,               /* output projection + residual (GEMV: + split-K combine) */
   EMBER_K_GATE_UP = 4,         /* gate/up projection + SiLU*up */
   EMBER_K_DOWN = 5,            /* down projection + residual */
-  EMBER_K_LAYER = 6            /* every kernel of one layer, in step order */
+  EMBER_K_LAYER = 6,          /* every kernel of one layer, in step order */
+  EMBER_K_SAMPLE = 7           /* the sampler of a decode step (phase 0, sampler set) */
 } ember_kernel;
 
 /* Launch kernel `kernel` of the most recent decode step (phase 0) or prefill pass

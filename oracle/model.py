@@ -203,23 +203,28 @@ class OracleModel:
 
 
 def generate(model: OracleModel, prompt, n_steps: int, max_seq: int | None = None,
-             progress=None):
-    """Prefill once, then ``n_steps`` greedy steps, one cached forward each (the NumPy
+             progress=None, pick=None):
+    """Prefill once, then ``n_steps`` steps, one cached forward each (the NumPy
     reference's generation loop; ember internals page: one prefill and one cached step per
     new token). End-of-sequence ids are not special: the step count is fixed.
 
-    Returns ``(ids, logits)`` with ``logits[k]`` the head output after step ``k`` (``k = 0``
-    is the prefill's last position) and ``ids[k] = argmax(logits[k])``: ``n_steps + 1``
-    of each, of which ``ids[0..n_steps-1]`` are fed back.
+    ``pick(k, logits) -> id`` chooses the token after step ``k`` (``k = 0``: the prefill);
+    by default the greedy argmax. Returns ``(ids, logits)`` with ``logits[k]`` the head
+    output after step ``k`` (``k = 0`` is the prefill's last position) and ``ids[k]`` the
+    token picked from it: ``n_steps + 1`` of each, of which ``ids[0..n_steps-1]`` are fed
+    back.
     """
+    if pick is None:
+        def pick(k, lg):
+            return int(greedy_argmax(lg))
     prompt = np.asarray(prompt)
     T = prompt.shape[0]
     cache = KVCache(model.cfg, max_seq or (T + n_steps), model.dtype)
     logits = [model.forward_sequence(prompt, 0, cache, progress=progress)]
-    ids = [int(greedy_argmax(logits[0]))]
+    ids = [int(pick(0, logits[0]))]
     for k in range(n_steps):
         logits.append(model.forward_token(ids[-1], T + k, cache))
-        ids.append(int(greedy_argmax(logits[-1])))
+        ids.append(int(pick(k + 1, logits[-1])))
     return np.array(ids, dtype=np.int64), np.stack(logits)
 
 

@@ -16,6 +16,12 @@ Recipe (all draws from ``numpy.random.default_rng(seed)``, PCG64):
   those bf16 values *are* the model.
 * prompt ids: seed = the workload's ``ids_seed``,
   ``integers(0, vocab, size=(batch, prompt_len), dtype=int32)``.
+* sampler draws: ``random((n_pos, ld), dtype=float32)``, values in [0, 1).
+* sampler logits (inputs of the sampling stage alone): per row a spread
+  s = ``uniform(1, 4)``, ``standard_normal(vocab, float32) * s``, and 16 distinct
+  tokens raised by ``uniform(2, 10) * s`` (a peaked head over a broad tail, as an LM's
+  next-token logits); with ``ties`` the values are rounded to multiples of 1/4, so many
+  tokens share a value.
 """
 from __future__ import annotations
 
@@ -112,3 +118,23 @@ def weights_for(w: Workload):
     if key not in _cache:
         _cache[key] = make_weights(w.model, w.weight_seed)
     return _cache[key]
+
+
+def make_uniforms(seed: int, n_pos: int, ld: int) -> np.ndarray:
+    """Draws of the sampler, [n_pos, ld] float32 in [0, 1)."""
+    return np.random.default_rng(seed).random((n_pos, ld), dtype=np.float32)
+
+
+def make_logits(seed: int, rows: int, vocab: int, ties: bool = False) -> np.ndarray:
+    """LM-like next-token logits [rows, vocab] float32 (recipe in the module docstring)."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((rows, vocab), np.float32)
+    for r in range(rows):
+        s = np.float32(rng.uniform(1.0, 4.0))
+        z = rng.standard_normal(vocab, dtype=np.float32) * s
+        head = rng.choice(vocab, size=min(16, vocab), replace=False)
+        z[head] += rng.uniform(2.0, 10.0, size=head.size).astype(np.float32) * s
+        if ties:
+            z = np.round(z * 4.0) / 4.0
+        out[r] = z.astype(np.float32)
+    return out
