@@ -11,6 +11,8 @@ in HBM before the timed region. Prints ONE JSON line:
                events around that kernel's own launches (ember_time_kernel, same stream
                and arguments as in the step)
   cpu_baseline the oracle timed on this host's cores on a bounded sample
+  sampler_us   the sampler of one decode step (temperature / top-k / top-p draw over the
+               vocabulary), timed after the greedy steps; not part of `value`
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload qwen05b] [--precision exact]
 """
@@ -230,6 +232,16 @@ def main():
             layer_us[tag + "_kernel_sum"] = sum(
                 v["avg_us"] for k, v in kernels.items()
                 if k.startswith(tag + ".") and not k.endswith("lm_head"))
+        # the sampler of one decode step (outside the timed steps, which are greedy): one
+        # draw per row over the vocabulary, at two settings
+        sampler_us = {}
+        if N > 0 and m.head == "tied_lm":
+            U = torch.from_numpy(W.make_uniforms(5, w.max_pos, Bn)).to(dev)
+            for tag, (t_, k_, p_) in {"t1.0": (1.0, 0, 1.0),
+                                      "t0.8_k50_p0.9": (0.8, 50, 0.9)}.items():
+                eng.set_sampler(t_, k_, p_, U)
+                sampler_us[tag] = eng.time_kernel(B.K_SAMPLE, 0, args.timing_iters)
+            eng.set_sampler()
     for k, v in kernels.items():
         if v["bound"] == "hbm":
             v["achieved"] = v["work_per_launch"] / (v["avg_us"] * 1e-6) / 1e9
@@ -286,6 +298,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                         for kk, vv in v.items()} for k, v in kernels.items()},
         "layer_us": {k: round(v, 3) for k, v in layer_us.items()},
+        "sampler_us": {k: round(v, 3) for k, v in sampler_us.items()},
         **extra,
     }
     eng.close()

@@ -56,7 +56,7 @@ struct Plan {
   std::vector<LayerOff> layer;
   // activations
   size_t ids, pos, rope_cur, next, flags, x, xb, pa_hi, pa_lo, pb_hi, pb_lo, qkv, q, att, act, part,
-      logits, argpart, splitk, kvpack;
+      logits, argpart, splitk, kvpack, samp_state, samp_tiles;
   size_t splitk_elems, kvpack_elems;
   size_t total;
   int Mx, qkv_n, ka, nsplit_max, argparts;
@@ -158,6 +158,10 @@ Plan make_plan(const ember_config& c) {
   p.part = take((size_t)c.max_batch * NH * p.nsplit_max * (HD + 2) * 4);
   p.logits = take((size_t)c.max_batch * out_dim * 4);
   p.argpart = take((size_t)p.argparts * 8);
+  // sampler state and tile sums, one per batch row (tied LM head only)
+  const bool can_sample = c.head_kind == EMBER_HEAD_TIED_LM && c.vocab <= kSampleMaxVocab;
+  p.samp_state = can_sample ? take((size_t)c.max_batch * sizeof(SampleState)) : 0;
+  p.samp_tiles = can_sample ? take((size_t)c.max_batch * sample_tiles_ld(c.vocab) * 4) : 0;
   {
     // split-K partial planes for GEMMs whose tiles cannot fill the GPU (M <= 128)
     int maxn = 2 * FF > p.qkv_n ? 2 * FF : p.qkv_n;
@@ -258,6 +262,8 @@ void launch_draw(const Ctx& cx, const float* logits, int R, long long ld, int32_
   a.col0 = u_col0; a.pos = u_pos < 0 ? 0 : u_pos;
   a.d_pos = u_pos < 0 ? md->at<int>(md->plan.pos) : nullptr;
   a.next = next; a.flags = md->at<int>(md->plan.flags);
+  a.state = md->at<SampleState>(md->plan.samp_state);
+  a.tiles = md->at<float>(md->plan.samp_tiles);
   launch_sample(a, cx.st);
 }
 
@@ -713,6 +719,9 @@ ember_status ember_load_weights(const ember_config* cfg, const ember_tensor* ten
     HIP_TRY(hipStreamSynchronize(st));
   }
   launch_fill_i32((int*)(ws + plan.flags), kNumFlags, 0, st);
+  if (plan.samp_state)
+    launch_fill_i32((int*)(ws + plan.samp_state),
+                    (int)((size_t)c.max_batch * sizeof(SampleState) / 4), 0, st);
   HIP_TRY(hipGetLastError());
   HIP_TRY(hipStreamSynchronize(st));
 
@@ -990,6 +999,8 @@ ember_status ember_sample(ember_model* md, const float* d_logits, int32_t rows,
   if (!md || !d_logits || !d_next) return fail(EMBER_E_ARG, "NULL argument");
   if (md->cfg.head_kind != EMBER_HEAD_TIED_LM) return fail(EMBER_E_STATE, "sampling needs the tied LM head");
   if (rows < 1) return fail(EMBER_E_ARG, "rows must be >= 1");
+  if (rows > md->cfg.max_batch)
+    return fail(EMBER_E_CAPACITY, "%d rows beyond max_batch %d", rows, md->cfg.max_batch);
   if (ld_logits < md->cfg.vocab) return fail(EMBER_E_ARG, "row stride below the vocabulary");
   if (pos < 0) return fail(EMBER_E_ARG, "negative draw row");
   const ember_status s = check_draws(md, rows, pos);

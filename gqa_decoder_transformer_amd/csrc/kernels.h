@@ -82,13 +82,34 @@ struct StepBeginArgs {
 void launch_step_begin(const StepBeginArgs& a, hipStream_t st);
 // ---------------------------------------------------------------- sampling (kernels_sample.hip)
 
-constexpr int kSampleMaxTiles = 4096;
+constexpr int kSampleMaxTiles = 4096;                 // 256-token tiles per row
 constexpr int kSampleMaxVocab = kSampleMaxTiles * 256;
+constexpr int kSampleBins = 2048;                     // radix digit of 11 bits
+constexpr int kSampleChunk = 2048;                    // tokens per block of a row
+
+// Per-row state the phases of one draw hand to each other through global memory. All
+// zero between draws (the last phase clears what the others leave behind).
+struct SampleState {
+  uint32_t hist_k[3][kSampleBins];                    // top-k counts per digit
+  unsigned long long hist_p[3][kSampleBins];          // top-p fixed-point weights per digit
+  unsigned long long ptotal;                          // top-p weight of all survivors
+  unsigned long long above;                           // weight above the current prefix
+  uint32_t maxkey;                                    // ordered key of the largest z
+  uint32_t count;                                     // blocks done in the current phase
+  uint32_t prefix, pmask;                             // radix search so far
+  float thr;                                          // survivors: z >= thr
+  int live_k, live_p;                                 // the searches found their keys
+  int pad;
+};
+
+// Tile sums per row: [R][sample_tiles_ld(V)] floats.
+EMBER_INLINE_HD int sample_blocks(int V) { return (V + kSampleChunk - 1) / kSampleChunk; }
+EMBER_INLINE_HD int sample_tiles_ld(int V) { return sample_blocks(V) * (kSampleChunk / 256); }
 
 // next[r] = a token drawn from row r of the logits through temperature, top-k, top-p,
 // softmax and an inverse-CDF draw with u = uniform[row * u_ld + col0 + r], where row is
 // *d_pos when d_pos is non-null, else pos (clamped to u_rows - 1). temperature > 0.
-// Raises kFlagNaN when a row holds a NaN.
+// Raises kFlagNaN when a row holds a NaN. state / tiles: R rows of the buffers above.
 struct SampleArgs {
   const float* logits;
   long long ld;
@@ -104,6 +125,8 @@ struct SampleArgs {
   const int* d_pos;
   int32_t* next;
   int* flags;
+  SampleState* state;
+  float* tiles;
 };
 void launch_sample(const SampleArgs& a, hipStream_t st);
 

@@ -197,8 +197,10 @@ ember_status ember_set_sampler(ember_model* model, const ember_sampler* sampler)
 /* Draw one token for each of `rows` rows of caller logits d_logits f32 [rows, vocab]
  * (row stride ld_logits >= vocab, device) with the model's sampler, u = d_uniform[pos *
  * ld + r], into d_next [rows] int32 (device); greedy argmax when no sampler is set. A
- * NaN logit raises the model's NaN flag (ember_sync). EMBER_E_CAPACITY when pos lies
- * beyond n_pos - 1 or rows exceeds ld. */
+ * NaN logit raises the model's NaN flag (ember_sync). EMBER_E_CAPACITY when rows exceeds
+ * max_batch (the sampler's per-row state lives in the workspace) or ld, or pos lies
+ * beyond n_pos - 1. Draws share that state with the model's own, so calls on one model
+ * stay ordered on one stream. */
 ember_status ember_sample(ember_model* model, const float* d_logits, int32_t rows,
                           int64_t ld_logits, int32_t pos, int32_t* d_next, void* stream);
 

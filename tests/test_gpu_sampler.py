@@ -76,7 +76,7 @@ SETTINGS = [(1.0, 0, 1.0), (0.7, 50, 1.0), (1.0, 0, 0.9), (0.8, 50, 0.9), (1.3, 
 
 @pytest.fixture(scope="module")
 def bigv():
-    eng, _ = _engine(BIGV)
+    eng, _ = _engine(BIGV, max_batch=8, max_seq=16)
     return eng
 
 
@@ -156,6 +156,9 @@ def test_sampler_arguments_are_validated(bigv):
     d_l = torch.zeros((3, BIGV.vocab), device="cuda")
     with pytest.raises(B.EmberError) as e:
         bigv.sample(d_l, 0)                          # 3 rows > ld 2
+    assert e.value.status == 7
+    with pytest.raises(B.EmberError) as e:
+        bigv.sample(torch.zeros((9, BIGV.vocab), device="cuda"), 0)   # 9 rows > max_batch 8
     assert e.value.status == 7
     with pytest.raises(B.EmberError) as e:
         bigv.sample(d_l[:2], 4)                      # draw row 4 of 4
