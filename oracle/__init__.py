@@ -1,7 +1,8 @@
 """Oracle for the GQA decoder forward pass -- TEST INFRASTRUCTURE, not part of the product.
 
 A plain, slow, obviously correct CPU implementation (NumPy; scalar Python loops for the
-brute-force form) of what the GPU path computes: bf16->f32 weight widening, RMSNorm,
+brute-force form) of what the GPU path computes: bf16->f32 weight widening and q8_0
+block dequantisation, RMSNorm,
 rotate-half RoPE with optional llama3 frequency scaling, grouped-query attention with a
 causal KV cache (or bidirectional), SwiGLU MLP, the tied LM head or a token
 classification head, greedy argmax, and the sampler (temperature, top-k, top-p, softmax,
@@ -22,9 +23,9 @@ the brute-force loops; end-to-end values of the pages' trained checkpoints canno
 pinned (the checkpoints are not available), so the model-level pins are invariants and
 an independent library implementation of the same architectures.
 """
-from .primitives import (apply_rope, attention, decode_tensor, greedy_argmax,  # noqa: F401
-                         rmsnorm, rope_inv_freq, rope_tables, silu, softmax, swiglu,
-                         widen_bf16)
+from .primitives import (apply_rope, attention, decode_tensor, dequant_q8_0,  # noqa: F401
+                         f16_to_f32, greedy_argmax, rmsnorm, rope_inv_freq, rope_tables,
+                         silu, softmax, swiglu, widen_bf16)
 from .model import KVCache, OracleModel, generate, recompute_logits  # noqa: F401
 from . import brute  # noqa: F401
 from . import sampler  # noqa: F401

@@ -23,13 +23,53 @@ def widen_bf16(bits: np.ndarray) -> np.ndarray:
     return (u << np.uint32(16)).view(np.float32)
 
 
+def f16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns -> f32 values (exact: every f16 value is an f32 value).
+
+    Sign bit 15, exponent bits 14..10 (bias 15), fraction bits 9..0: exponent 0 is zero or
+    subnormal (fraction * 2^-24), 1..30 normal ((1024 + fraction) * 2^(exponent - 25)),
+    31 infinity (fraction 0) or NaN."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    mag = np.where(e == 0, f * 2.0 ** -24, (1024.0 + f) * np.exp2((e - 25).astype(np.float64)))
+    mag = np.where(e == 31, np.where(f == 0, np.inf, np.nan), mag)
+    return (sign * mag).astype(np.float32)
+
+
+Q8_BLOCK = 32          # values per q8_0 block
+Q8_BLOCK_BYTES = 34    # 2-byte scale + 32 int8
+
+
+def dequant_q8_0(raw: np.ndarray, k: int) -> np.ndarray:
+    """q8_0 rows -> f32 [n, k] ("ember internals", section
+    "GGUF format and quantization", subsection "q8_0 block quantization", its
+    decompression loop): each block of 34 bytes is a
+    little-endian f16 scale d followed by 32 signed int8 values q, and block value j is
+    q_j * d in f32. Blocks run along the row (the inner dimension, a multiple of 32).
+    The product of an int8 and an f16 value is exact in f32."""
+    raw = np.asarray(raw, dtype=np.uint8)
+    if k % Q8_BLOCK:
+        raise ValueError("q8_0 rows need a multiple of 32 values")
+    n = raw.shape[0]
+    blocks = raw.reshape(n, k // Q8_BLOCK, Q8_BLOCK_BYTES)
+    d_bits = blocks[..., 0].astype(np.uint16) | (blocks[..., 1].astype(np.uint16) << np.uint16(8))
+    d = f16_to_f32(d_bits)[..., None]
+    q = blocks[..., 2:].view(np.int8).astype(np.float32)
+    return (q * d).astype(np.float32).reshape(n, k)
+
+
 def decode_tensor(dtype_tag: str, arr: np.ndarray) -> np.ndarray:
-    """A stored tensor as f32 values: BF16 is widened, F32 passes through, anything else is
-    an error ("ember scripts/reference_forward.py", ``load_safetensors``, final branch)."""
+    """A stored tensor as f32 values: BF16 is widened, F32 passes through, q8_0 rows
+    ([n, k / 32 * 34] bytes) are dequantised; anything else is an error ("ember
+    scripts/reference_forward.py", ``load_safetensors``, final branch)."""
     if dtype_tag == "bf16":
         return widen_bf16(arr)
     if dtype_tag == "f32":
         return np.asarray(arr, dtype=np.float32)
+    if dtype_tag == "q8_0":
+        return dequant_q8_0(arr, arr.shape[1] // Q8_BLOCK_BYTES * Q8_BLOCK)
     raise ValueError(f"unsupported dtype {dtype_tag}")
 
 

@@ -32,7 +32,7 @@ def test_widen_bf16_every_bit_pattern_matches_torch_and_field_decode():
 def test_decode_tensor_passes_f32_and_rejects_other_dtypes():
     a = np.random.default_rng(0).standard_normal(17).astype(np.float32)
     assert np.array_equal(O.decode_tensor("f32", a).view(np.uint32), a.view(np.uint32))
-    for tag in ("f16", "i8", "q8_0"):
+    for tag in ("f16", "i8", "q4_0"):
         with pytest.raises(ValueError):
             O.decode_tensor(tag, a)
 

@@ -15,6 +15,9 @@ Five workloads are defined, each a model shape plus a batch/prompt/decode schedu
                    RoPE, no mask, token classification head); bf16 weights.
 * ``longctx``   -- ``llama1b`` weights, 64 rows each holding an 8192-token cache, then
                    batched greedy decode.
+* ``qwen05b-q8`` -- ``qwen05b`` with every matrix stored as q8_0 blocks (32 int8 values
+                   and one f16 scale per 34 bytes), the weight format of the "ember
+                   internals" page, section "GGUF format and quantization".
 
 Hyper-parameters that the pages leave open are filled with the plainest reading: no
 bias for ``tiny``, eps 1e-5 for the Llama shape, eps 1e-6 / vocab 151936 for the
@@ -46,7 +49,7 @@ class ModelConfig:
     causal: bool = True
     head: str = "tied_lm"          # "tied_lm" (logits = E . h) or "cls" (W h + b)
     n_classes: int = 0
-    weight_dtype: str = "bf16"     # "f32" or "bf16" (storage of every tensor)
+    weight_dtype: str = "bf16"     # "f32", "bf16" (every tensor) or "q8_0" (matrices; 1-D f32)
 
     @property
     def group(self) -> int:
@@ -99,6 +102,11 @@ ENCODER = ModelConfig(
     head_dim=128, ffn=3072, rms_eps=1e-6, rope_theta=1e6, qk_norm=True, causal=False,
     head="cls", n_classes=2)
 
+# the Qwen2.5-0.5B shape with q8_0 matrices ("ember internals", section
+# "GGUF format and quantization", subsection "q8_0 block quantization"): the same seeded draws, quantised
+QWEN05B_Q8 = ModelConfig(**{**QWEN05B.__dict__, "name": "qwen2.5-0.5b-q8_0",
+                            "weight_dtype": "q8_0"})
+
 WORKLOADS = {
     "tiny": Workload("tiny", TINY, batch=1, prompt_len=16, decode_steps=16,
                      weight_seed=1, ids_seed=101,
@@ -112,6 +120,10 @@ WORKLOADS = {
     "encoder": Workload("encoder", ENCODER, batch=16, prompt_len=512, decode_steps=0,
                         weight_seed=4, ids_seed=104,
                         description="Qwen3-style bidirectional encoder, bf16, 16x512, 2-way token head"),
+    "qwen05b-q8": Workload("qwen05b-q8", QWEN05B_Q8, batch=1, prompt_len=128, decode_steps=128, weight_seed=2,
+                           ids_seed=102,
+                           description="Qwen2.5-0.5B-shaped decoder, q8_0 matrices, 1x128 "
+                                       "prompt, 128 greedy steps"),
     "longctx": Workload("longctx", LLAMA1B, batch=64, prompt_len=8192, decode_steps=128,
                         weight_seed=3, ids_seed=105,
                         description="Llama-3.2-1B-shaped decoder, bf16, 64 rows x 8192 cached, 128 greedy steps"),

@@ -14,6 +14,9 @@ Recipe (all draws from ``numpy.random.default_rng(seed)``, PCG64):
   drawn, as the Falcon-H1 Rust reference's ``synthetic_weights`` fills norm weights with 1.
 * bf16 models: each f32 draw is rounded once to bf16 (round to nearest, ties to even);
   those bf16 values *are* the model.
+* q8_0 models: every matrix is quantised to q8_0 blocks (``quantize_q8_0``: per 32
+  values d = f16(max|x| / 127), q = rint(x / d)); the dequantised values are the model.
+  Norm weights and biases stay f32.
 * prompt ids: seed = the workload's ``ids_seed``,
   ``integers(0, vocab, size=(batch, prompt_len), dtype=int32)``.
 * sampler draws: ``random((n_pos, ld), dtype=float32)``, values in [0, 1).
@@ -97,9 +100,34 @@ def make_weights(m: ModelConfig, seed: int) -> "OrderedDict[str, Tuple[str, np.n
             out[name] = ("bf16", f32_to_bf16_bits(a))
         elif m.weight_dtype == "f32":
             out[name] = ("f32", a)
+        elif m.weight_dtype == "q8_0":
+            out[name] = ("q8_0", quantize_q8_0(a)) if a.ndim == 2 else ("f32", a)
         else:
             raise ValueError(f"unknown weight dtype {m.weight_dtype}")
     return out
+
+
+def quantize_q8_0(a: np.ndarray) -> np.ndarray:
+    """f32 [n, k] -> q8_0 rows [n, k / 32 * 34] uint8 (the stored form of a q8_0 model).
+
+    Per block of 32 values along the row: d = f16(max|x| / 127), q = clip(rint(x / d),
+    -127, 127) (q = 0 when d = 0); stored as d's two bytes, little-endian, then the 32 q
+    bytes. Only makes test and benchmark inputs: the dequantised values q * d *are* the
+    model."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    n, k = a.shape
+    if k % 32:
+        raise ValueError("q8_0 rows need a multiple of 32 values")
+    blk = a.reshape(n, k // 32, 32)
+    d16 = (np.abs(blk).max(-1) / np.float32(127.0)).astype(np.float16)
+    d = d16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(d > 0, np.rint(blk / np.where(d > 0, d, 1.0)), 0.0)
+    q = np.clip(q, -127, 127).astype(np.int8)
+    out = np.empty((n, k // 32, 34), np.uint8)
+    out[..., :2] = d16.view(np.uint8).reshape(n, k // 32, 2)      # little-endian f16
+    out[..., 2:] = q.view(np.uint8)
+    return out.reshape(n, k // 32 * 34)
 
 
 def make_ids(w: Workload, batch: int | None = None, prompt_len: int | None = None) -> np.ndarray:
