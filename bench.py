@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="qwen05b",
-                    choices=["tiny", "qwen05b", "llama1b", "encoder", "longctx"])
+                    choices=["tiny", "qwen05b", "llama1b", "encoder", "longctx", "qwen05b-q8"])
     ap.add_argument("--precision", default="exact", choices=["exact", "fast"])
     ap.add_argument("--kv", default=None, choices=[None, "f32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -48,8 +48,8 @@ def parse():
 
 
 def weight_bytes(m):
-    es = 2 if m.weight_dtype == "bf16" else 4
-    return es
+    """Stored bytes per weight: bf16 2, f32 4, q8_0 34 per 32 (an f16 scale per 32 int8)."""
+    return {"bf16": 2.0, "f32": 4.0, "q8_0": 34.0 / 32.0}[m.weight_dtype]
 
 
 def kernel_work(m, kind, phase, M, S, kv_bytes):
@@ -162,6 +162,8 @@ def main():
     w = W.get(args.workload)
     m = w.model
     prec = B.EXACT if args.precision == "exact" else B.FAST
+    # multi-token passes on bf16 MFMA: bf16 weights, or q8_0 dequantised to bf16 in FAST
+    mfma_path = m.weight_dtype == "bf16" or (m.weight_dtype == "q8_0" and prec == B.FAST)
     kv = {"f32": B.F32, "bf16": B.BF16, None: None}[args.kv]
     ck = W.weights_for(w)
     prompt = W.make_ids(w)
@@ -248,7 +250,7 @@ def main():
             v["peak"], v["unit"] = PEAK_HBM_GBS, "GB/s"
         else:
             v["achieved"] = v["work_per_launch"] / (v["avg_us"] * 1e-6) / 1e12
-            peak = PEAK_BF16_TFLOPS if m.weight_dtype == "bf16" else PEAK_FP32_TFLOPS
+            peak = PEAK_BF16_TFLOPS if mfma_path else PEAK_FP32_TFLOPS
             v["peak"], v["unit"] = peak, "TFLOP/s"
         v["frac"] = v["achieved"] / v["peak"]
     dom_name = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
@@ -272,7 +274,7 @@ def main():
     pre = float(np.mean(pre_ms))
     extra["prefill_tok_s"] = Bn * T / (pre / 1000.0)
     extra["prefill_ms"] = pre
-    if m.weight_dtype == "bf16":
+    if mfma_path:
         flops = 2.0 * Bn * T * (n_params - m.vocab * m.hidden)
         pairs = T * (T + 1) / 2 if m.causal else T * T
         flops += 4.0 * m.head_dim * m.heads * m.layers * pairs * Bn

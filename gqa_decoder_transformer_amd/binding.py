@@ -19,7 +19,7 @@ EMBER_OK = 0
 STATUS_NAMES = {0: "OK", 1: "E_ARG", 2: "E_CONFIG", 3: "E_TENSOR_MISSING", 4: "E_TENSOR_SHAPE",
                 5: "E_DTYPE", 6: "E_TOKEN", 7: "E_CAPACITY", 8: "E_STATE", 9: "E_DEVICE",
                 10: "E_NONFINITE"}
-F32, BF16 = 0, 1
+F32, BF16, Q8_0 = 0, 1, 2
 EXACT, FAST = 0, 1
 HEAD_TIED_LM, HEAD_CLS = 0, 1
 
@@ -217,7 +217,7 @@ def make_config(model, *, precision: int = EXACT, kv_dtype: Optional[int] = None
     c.qkv_bias, c.qk_norm, c.causal = int(model.qkv_bias), int(model.qk_norm), int(model.causal)
     c.head_kind = HEAD_CLS if model.head == "cls" else HEAD_TIED_LM
     c.n_classes = model.n_classes
-    c.weight_dtype = BF16 if model.weight_dtype == "bf16" else F32
+    c.weight_dtype = {"bf16": BF16, "f32": F32, "q8_0": Q8_0}[model.weight_dtype]
     if kv_dtype is None:
         kv_dtype = F32 if precision == EXACT else BF16
     c.kv_dtype = kv_dtype
@@ -259,10 +259,17 @@ class Engine:
             elif tag == "f32":
                 t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(self.device)
                 dt = F32
+            elif tag == "q8_0":
+                # rows of 34-byte blocks; the tensor's shape is the logical [N, K]
+                t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.uint8)).to(self.device)
+                dt = Q8_0
             else:
                 raise ValueError(f"unsupported dtype tag {tag}")
             staged.append(t)
-            shape = (ctypes.c_int64 * 4)(*(list(arr.shape) + [0] * (4 - arr.ndim)))
+            dims = list(arr.shape)
+            if tag == "q8_0":
+                dims = [arr.shape[0], arr.shape[1] // 34 * 32]
+            shape = (ctypes.c_int64 * 4)(*(dims + [0] * (4 - arr.ndim)))
             tensors.append(EmberTensor(name.encode(), t.data_ptr(), shape, arr.ndim, dt))
         with torch.cuda.stream(self.stream):
             self.model = ember_load_weights(cfg, tensors, self.workspace.data_ptr(), ws_bytes, self.sp)

@@ -20,6 +20,11 @@ EMBER_DEV float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 EMBER_DEV float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
 EMBER_DEV float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
 
+// IEEE binary16 bits -> f32 (exact).
+EMBER_DEV float f16_to_f32(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
 // f32 -> bf16, round to nearest, ties to even (finite inputs).
 EMBER_DEV uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -46,8 +46,17 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 size_t dtype_size(int dt) { return dt == EMBER_BF16 ? 2 : 4; }
 
+int weight_kind(int dt) { return dt == EMBER_Q8_0 ? WK_Q8 : (dt == EMBER_BF16 ? WK_BF16 : WK_F32); }
+
+// The GEMMs of multi-token passes run on bf16 MFMA for bf16 weights, and for q8 weights in
+// FAST precision (from a bf16 dequantised copy); f32 weights and EXACT q8 take the f32 path.
+bool uses_mfma(const ember_config& c) {
+  return c.weight_dtype == EMBER_BF16 || (c.weight_dtype == EMBER_Q8_0 && c.precision == EMBER_FAST);
+}
+
 struct LayerOff {
   size_t ln1, wqkv, bqkv, wo, qn, kn, ln2, wgu, wd;
+  size_t wqkv_s, wo_s, wgu_s, wd_s;   // q8: scale planes
 };
 
 struct Plan {
@@ -56,7 +65,7 @@ struct Plan {
   std::vector<LayerOff> layer;
   // activations
   size_t ids, pos, rope_cur, next, flags, x, xb, pa_hi, pa_lo, pb_hi, pb_lo, qkv, q, att, act, part,
-      logits, argpart, splitk, kvpack, samp_state, samp_tiles;
+      logits, argpart, splitk, kvpack, samp_state, samp_tiles, embed_s, q8_scratch;
   size_t splitk_elems, kvpack_elems;
   size_t total;
   int Mx, qkv_n, ka, nsplit_max, argparts;
@@ -75,8 +84,10 @@ ember_status validate_config(const ember_config* c) {
   const int hd = c->head_dim;
   if (hd != 8 && hd != 16 && hd != 32 && hd != 64 && hd != 128)
     return fail(EMBER_E_CONFIG, "head_dim must be one of 8, 16, 32, 64, 128");
-  if (c->weight_dtype != EMBER_F32 && c->weight_dtype != EMBER_BF16)
+  if (c->weight_dtype != EMBER_F32 && c->weight_dtype != EMBER_BF16 && c->weight_dtype != EMBER_Q8_0)
     return fail(EMBER_E_DTYPE, "unsupported weight dtype %d", c->weight_dtype);
+  if (c->weight_dtype == EMBER_Q8_0 && c->head_kind != EMBER_HEAD_TIED_LM)
+    return fail(EMBER_E_CONFIG, "q8_0 weights need the tied LM head");
   if (c->kv_dtype != EMBER_F32 && c->kv_dtype != EMBER_BF16)
     return fail(EMBER_E_DTYPE, "unsupported KV dtype %d", c->kv_dtype);
   if (c->precision != EMBER_EXACT && c->precision != EMBER_FAST)
@@ -90,7 +101,7 @@ ember_status validate_config(const ember_config* c) {
   if (c->head_kind == EMBER_HEAD_TIED_LM && !c->causal)
     return fail(EMBER_E_CONFIG, "a tied LM head needs a causal model");
   if (c->ffn % kGuBlock != 0) return fail(EMBER_E_CONFIG, "ffn must be a multiple of %d", kGuBlock);
-  const int K8 = c->weight_dtype == EMBER_BF16 ? 8 : 4;
+  const int K8 = c->weight_dtype == EMBER_Q8_0 ? kQ8Block : (c->weight_dtype == EMBER_BF16 ? 8 : 4);
   if (c->hidden % K8 || c->ffn % K8 || (c->heads * hd) % K8)
     return fail(EMBER_E_CONFIG, "hidden, ffn and heads*head_dim must be multiples of %d", K8);
   if (c->hidden > 8192 || c->ffn > 32768 || c->heads * hd > 8192)
@@ -111,22 +122,29 @@ Plan make_plan(const ember_config& c) {
   Plan p{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
-  const size_t ws = dtype_size(c.weight_dtype);
+  const bool q8 = c.weight_dtype == EMBER_Q8_0;
+  const size_t ws = q8 ? 1 : dtype_size(c.weight_dtype);
   const int H = c.hidden, HD = c.head_dim, NH = c.heads, NKV = c.kv_heads, FF = c.ffn;
+  // a matrix [N, K]: its values (q8: the byte plane), then for q8 the scale plane
+  auto mat = [&](size_t N, size_t K, size_t& scales) {
+    const size_t o = take(N * K * ws);
+    scales = q8 ? take(N * (K / kQ8Block) * 2) : 0;
+    return o;
+  };
   p.qkv_n = (NH + 2 * NKV) * HD;
-  p.embed = take((size_t)c.vocab * H * ws);
+  p.embed = mat(c.vocab, H, p.embed_s);
   p.layer.resize(c.layers);
   for (int l = 0; l < c.layers; ++l) {
     LayerOff& L = p.layer[l];
     L.ln1 = take((size_t)H * 4);
-    L.wqkv = take((size_t)p.qkv_n * H * ws);
+    L.wqkv = mat(p.qkv_n, H, L.wqkv_s);
     L.bqkv = c.qkv_bias ? take((size_t)p.qkv_n * 4) : 0;
-    L.wo = take((size_t)H * NH * HD * ws);
+    L.wo = mat(H, (size_t)NH * HD, L.wo_s);
     L.qn = c.qk_norm ? take((size_t)HD * 4) : 0;
     L.kn = c.qk_norm ? take((size_t)HD * 4) : 0;
     L.ln2 = take((size_t)H * 4);
-    L.wgu = take((size_t)2 * FF * H * ws);
-    L.wd = take((size_t)H * FF * ws);
+    L.wgu = mat((size_t)2 * FF, H, L.wgu_s);
+    L.wd = mat(H, FF, L.wd_s);
   }
   p.fnorm = take((size_t)H * 4);
   p.cls_w = c.head_kind == EMBER_HEAD_CLS ? take((size_t)c.n_classes * H * ws) : 0;
@@ -139,7 +157,7 @@ Plan make_plan(const ember_config& c) {
   p.ka = H > NH * HD ? H : NH * HD;
   const int out_dim = c.head_kind == EMBER_HEAD_CLS ? c.n_classes : c.vocab;
   p.nsplit_max = (c.max_seq + 63) / 64;
-  p.argparts = gemv_num_blocks(c.vocab, GEMV_LOGITS, H, c.weight_dtype == EMBER_BF16);
+  p.argparts = gemv_num_blocks(c.vocab, GEMV_LOGITS, H, weight_kind(c.weight_dtype));
   p.ids = take((size_t)Mx * 4);
   p.pos = take(4);
   p.rope_cur = take((size_t)c.head_dim * 4);
@@ -167,16 +185,25 @@ Plan make_plan(const ember_config& c) {
     int maxn = 2 * FF > p.qkv_n ? 2 * FF : p.qkv_n;
     if (H > maxn) maxn = H;
     const int mrows = Mx < 128 ? Mx : 128;
-    p.splitk_elems = c.weight_dtype == EMBER_BF16 ? (size_t)16 * mrows * maxn : 0;
+    p.splitk_elems = uses_mfma(c) ? (size_t)16 * mrows * maxn : 0;
     p.splitk = p.splitk_elems ? take(p.splitk_elems * 4) : 0;
   }
   {
     // packed K / V^T planes for the tiled prefill attention: one pass holds at most Mx
     // tokens, or one row of up to max_seq keys, each row rounded up to a 64-key tile
-    const bool tiled = c.weight_dtype == EMBER_BF16 && (HD == 64 || HD == 128);
+    const bool tiled = uses_mfma(c) && (HD == 64 || HD == 128);
     const int cap_keys = (Mx > c.max_seq ? Mx : c.max_seq) + 64 * c.max_batch;
     p.kvpack_elems = tiled ? (size_t)(c.precision == EMBER_EXACT ? 2 : 1) * 2 * NKV * cap_keys * HD : 0;
     p.kvpack = p.kvpack_elems ? take(p.kvpack_elems * 2) : 0;
+  }
+  if (q8) {
+    // the dequantised copy of one matrix for the GEMMs of multi-token passes (bf16 on the
+    // MFMA path, f32 otherwise): the largest of a layer's matrices and the embedding
+    size_t elems = (size_t)c.vocab * H;
+    const size_t cand[4] = {(size_t)p.qkv_n * H, (size_t)H * NH * HD, (size_t)2 * FF * H,
+                            (size_t)H * FF};
+    for (size_t e : cand) elems = e > elems ? e : elems;
+    p.q8_scratch = take(elems * (uses_mfma(c) ? 2 : 4));
   }
   p.total = off;
   return p;
@@ -214,7 +241,8 @@ struct ember_model {
   ember_config cfg;
   Plan plan;
   char* ws;
-  bool wbf16;
+  int wk;                   // WeightKind of the matrices
+  bool mfma;                // multi-token passes on bf16 MFMA (see uses_mfma)
   int has_logits_rows;      // rows in the logits buffer, 0 before any forward
   int last_decode_batch = 0;
   struct { int M, rows, tpr, b0, start; } last_pass = {0, 0, 0, 0, 0};
@@ -249,6 +277,26 @@ struct Ctx {
 
 bool want(const Ctx& cx, int kind) { return cx.only < 0 || cx.only == kind; }
 bool want_aux(const Ctx& cx) { return cx.only < 0; }
+
+// GEMV weight arguments of one matrix (values at `off`, q8 scales at `soff`).
+void gemv_weights(const ember_model* md, GemvArgs& g, size_t off, size_t soff) {
+  g.W = md->ws + off;
+  g.w_bf16 = md->wk == WK_BF16;
+  g.w_scale = md->wk == WK_Q8 ? (const uint16_t*)(md->ws + soff) : nullptr;
+}
+
+// Weights of one matrix [N, K] for the GEMM of a multi-token pass: in place for bf16 and
+// f32; q8 matrices are first dequantised into the scratch copy (bf16 for the MFMA path,
+// f32 otherwise), stream-ordered before the GEMM that reads it.
+const void* gemm_weights(const Ctx& cx, size_t off, size_t soff, int N, int K) {
+  ember_model* md = cx.m;
+  if (md->wk != WK_Q8) return md->ws + off;
+  void* dst = md->ws + md->plan.q8_scratch;
+  if (want_aux(cx))
+    launch_q8_dequant((const uint8_t*)(md->ws + off), (const uint16_t*)(md->ws + soff), N, K, dst,
+                      md->mfma, cx.st);
+  return dst;
+}
 
 // Next ids of R rows of logits [R, ld] drawn with the model's sampler: draw row u_pos
 // (the device position of a decode step when u_pos < 0), columns u_col0 + r.
@@ -317,10 +365,6 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   uint16_t* pb_lo = exact ? md->at<uint16_t>(p.pb_lo) : nullptr;
   const float* ln1 = md->at<float>(L.ln1);
   const float* ln2 = md->at<float>(L.ln2);
-  const void* wqkv = md->ws + L.wqkv;
-  const void* wo = md->ws + L.wo;
-  const void* wgu = md->ws + L.wgu;
-  const void* wd = md->ws + L.wd;
   const float* bqkv = c.qkv_bias ? md->at<float>(L.bqkv) : nullptr;
   const float scale = (float)(1.0 / std::sqrt((double)HD));
   DecodePlan dp{1, c.max_seq, NH / NKV};
@@ -329,25 +373,28 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   // input from the split partials (no combine launch)
   const bool fuse_combine = ps.attn == ATTN_DECODE && ps.path == PATH_GEMV &&
                             dp.nsplit > 1 && dp.nsplit <= 4 &&
-                            gemv_takes_parts(H, NH * HD, md->wbf16);
+                            gemv_takes_parts(H, NH * HD, md->wk);
 
   // ---- attention block
   if (ps.path == PATH_GEMV) {
     GemvArgs g{};
-    g.W = wqkv; g.w_bf16 = md->wbf16; g.N = p.qkv_n; g.K = H; g.M = ps.M;
+    gemv_weights(md, g, L.wqkv, L.wqkv_s);
+    g.N = p.qkv_n; g.K = H; g.M = ps.M;
     g.x = x; g.norm_w = ln1; g.eps = c.rms_eps; g.bias = bqkv; g.y = qkv; g.ldy = p.qkv_n;
     if (want(cx, EMBER_K_QKV)) launch_gemv(g, GEMV_STORE, st);
   } else if (ps.path == PATH_MFMA) {
     if (want_aux(cx)) launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st);
     GemmArgs g{};
     g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
-    g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka; g.w = (const uint16_t*)wqkv;
+    g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka;
+    g.w = (const uint16_t*)gemm_weights(cx, L.wqkv, L.wqkv_s, p.qkv_n, H);
     g.M = ps.M; g.N = p.qkv_n; g.K = H; g.bias = bqkv; g.c = qkv; g.ldc = p.qkv_n;
     if (want(cx, EMBER_K_QKV)) launch_gemm(g, GEMM_STORE, st);
   } else {
     if (want_aux(cx)) launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, xb, nullptr, nullptr, 0, st);
     GemmF32Args g{};
-    g.a = xb; g.lda = H; g.w = (const float*)wqkv; g.M = ps.M; g.N = p.qkv_n; g.K = H;
+    g.a = xb; g.lda = H; g.w = (const float*)gemm_weights(cx, L.wqkv, L.wqkv_s, p.qkv_n, H);
+    g.M = ps.M; g.N = p.qkv_n; g.K = H;
     g.bias = bqkv; g.c = qkv; g.ldc = p.qkv_n;
     if (want(cx, EMBER_K_QKV)) launch_gemm_f32w(g, GEMM_STORE, st);
   }
@@ -412,7 +459,8 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
 
   if (ps.path == PATH_GEMV) {
     GemvArgs g{};
-    g.W = wo; g.w_bf16 = md->wbf16; g.N = H; g.K = NH * HD; g.M = ps.M;
+    gemv_weights(md, g, L.wo, L.wo_s);
+    g.N = H; g.K = NH * HD; g.M = ps.M;
     g.x = att; g.y = x; g.ldy = H;
     if (fuse_combine) {
       g.x = nullptr;
@@ -423,12 +471,14 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   } else if (ps.path == PATH_MFMA) {
     GemmArgs g{};
     g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
-    g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka; g.w = (const uint16_t*)wo;
+    g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka;
+    g.w = (const uint16_t*)gemm_weights(cx, L.wo, L.wo_s, H, NH * HD);
     g.M = ps.M; g.N = H; g.K = NH * HD; g.c = x; g.ldc = H;
     if (want(cx, EMBER_K_O)) launch_gemm(g, GEMM_RESID, st);
   } else {
     GemmF32Args g{};
-    g.a = att; g.lda = NH * HD; g.w = (const float*)wo; g.M = ps.M; g.N = H; g.K = NH * HD;
+    g.a = att; g.lda = NH * HD; g.w = (const float*)gemm_weights(cx, L.wo, L.wo_s, H, NH * HD);
+    g.M = ps.M; g.N = H; g.K = NH * HD;
     g.c = x; g.ldc = H;
     if (want(cx, EMBER_K_O)) launch_gemm_f32w(g, GEMM_RESID, st);
   }
@@ -436,32 +486,38 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   // ---- MLP block
   if (ps.path == PATH_GEMV) {
     GemvArgs g{};
-    g.W = wgu; g.w_bf16 = md->wbf16; g.N = FF; g.K = H; g.M = ps.M;
+    gemv_weights(md, g, L.wgu, L.wgu_s);
+    g.N = FF; g.K = H; g.M = ps.M;
     g.x = x; g.norm_w = ln2; g.eps = c.rms_eps; g.y = act; g.ldy = FF;
     if (want(cx, EMBER_K_GATE_UP)) launch_gemv(g, GEMV_SILU, st);
     GemvArgs d{};
-    d.W = wd; d.w_bf16 = md->wbf16; d.N = H; d.K = FF; d.M = ps.M; d.x = act; d.y = x; d.ldy = H;
+    gemv_weights(md, d, L.wd, L.wd_s);
+    d.N = H; d.K = FF; d.M = ps.M; d.x = act; d.y = x; d.ldy = H;
     if (want(cx, EMBER_K_DOWN)) launch_gemv(d, GEMV_RESID, st);
   } else if (ps.path == PATH_MFMA) {
     if (want_aux(cx)) launch_rmsnorm(x, ln2, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st);
     GemmArgs g{};
     g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
-    g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka; g.w = (const uint16_t*)wgu;
+    g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka;
+    g.w = (const uint16_t*)gemm_weights(cx, L.wgu, L.wgu_s, 2 * FF, H);
     g.M = ps.M; g.N = 2 * FF; g.K = H; g.o_hi = pb_hi; g.o_lo = pb_lo; g.ldo = FF;
-    if (want(cx, EMBER_K_GATE_UP)) launch_gemm(g, GEMM_SILU, st);
     GemmArgs d{};
     d.partial = md->splitk(); d.partial_elems = p.splitk_elems;
-    d.a_hi = pb_hi; d.a_lo = pb_lo; d.lda = FF; d.w = (const uint16_t*)wd;
+    d.a_hi = pb_hi; d.a_lo = pb_lo; d.lda = FF;
     d.M = ps.M; d.N = H; d.K = FF; d.c = x; d.ldc = H;
+    if (want(cx, EMBER_K_GATE_UP)) launch_gemm(g, GEMM_SILU, st);
+    d.w = (const uint16_t*)gemm_weights(cx, L.wd, L.wd_s, H, FF);   // after the gate/up GEMM
     if (want(cx, EMBER_K_DOWN)) launch_gemm(d, GEMM_RESID, st);
   } else {
     if (want_aux(cx)) launch_rmsnorm(x, ln2, c.rms_eps, ps.M, H, 1, 0, xb, nullptr, nullptr, 0, st);
     GemmF32Args g{};
-    g.a = xb; g.lda = H; g.w = (const float*)wgu; g.M = ps.M; g.N = 2 * FF; g.K = H;
+    g.a = xb; g.lda = H; g.w = (const float*)gemm_weights(cx, L.wgu, L.wgu_s, 2 * FF, H);
+    g.M = ps.M; g.N = 2 * FF; g.K = H;
     g.o_f32 = act; g.ldo = FF;
     if (want(cx, EMBER_K_GATE_UP)) launch_gemm_f32w(g, GEMM_SILU, st);
     GemmF32Args d{};
-    d.a = act; d.lda = FF; d.w = (const float*)wd; d.M = ps.M; d.N = H; d.K = FF;
+    d.a = act; d.lda = FF; d.w = (const float*)gemm_weights(cx, L.wd, L.wd_s, H, FF);
+    d.M = ps.M; d.N = H; d.K = FF;
     d.c = x; d.ldc = H;
     if (want(cx, EMBER_K_DOWN)) launch_gemm_f32w(d, GEMM_RESID, st);
   }
@@ -481,11 +537,11 @@ void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, lo
   hipStream_t st = cx.st;
   const int H = c.hidden, V = c.vocab;
   const float* fn = md->at<float>(p.fnorm);
-  const void* E = md->ws + p.embed;
   if (R == 1 && ld == V) {
     // the final RMSNorm is fused into the GEMV
     GemvArgs g{};
-    g.W = E; g.w_bf16 = md->wbf16; g.N = V; g.K = H; g.M = 1;
+    gemv_weights(md, g, p.embed, p.embed_s);
+    g.N = V; g.K = H; g.M = 1;
     g.x = md->at<float>(p.x) + (size_t)row_off * H; g.norm_w = fn; g.eps = c.rms_eps;
     g.y = out; g.ldy = V;
     g.argmax_part = md->at<unsigned long long>(p.argpart);
@@ -494,16 +550,17 @@ void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, lo
     if (draw)
       launch_draw(cx, out, 1, ld, next, u_col0, u_pos);
     else if (next && want_aux(cx))
-      launch_argmax_reduce(g.argmax_part, gemv_num_blocks(V, GEMV_LOGITS, H, md->wbf16), 1, next, st);
+      launch_argmax_reduce(g.argmax_part, gemv_num_blocks(V, GEMV_LOGITS, H, md->wk), 1, next, st);
     return;
   }
   // R rows (at most the pass capacity Mx at a time: the plane / xb buffers hold Mx rows)
   const int G = p.Mx;
   float* xb = md->at<float>(p.xb);
+  const void* Ew = gemm_weights(cx, p.embed, p.embed_s, V, H);
   for (int r0 = 0; r0 < R; r0 += G) {
     const int rn = R - r0 < G ? R - r0 : G;
     const int off = row_off + r0 * row_step;
-    if (md->wbf16) {
+    if (md->mfma) {
       uint16_t* hi = md->at<uint16_t>(p.pa_hi);
       uint16_t* lo = c.precision == EMBER_EXACT ? md->at<uint16_t>(p.pa_lo) : nullptr;
       if (want_aux(cx))
@@ -511,7 +568,7 @@ void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, lo
                        p.ka, st);
       GemmArgs g{};
       g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
-      g.a_hi = hi; g.a_lo = lo; g.lda = p.ka; g.w = (const uint16_t*)E;
+      g.a_hi = hi; g.a_lo = lo; g.lda = p.ka; g.w = (const uint16_t*)Ew;
       g.M = rn; g.N = V; g.K = H; g.c = out + (size_t)r0 * ld; g.ldc = ld;
       if (want(cx, EMBER_K_LM_HEAD)) launch_gemm(g, GEMM_STORE, st);
     } else {
@@ -519,7 +576,7 @@ void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, lo
         launch_rmsnorm(md->at<float>(p.x), fn, c.rms_eps, rn, H, row_step, off, xb, nullptr,
                        nullptr, 0, st);
       GemmF32Args g{};
-      g.a = xb; g.lda = H; g.w = (const float*)E; g.M = rn; g.N = V; g.K = H;
+      g.a = xb; g.lda = H; g.w = (const float*)Ew; g.M = rn; g.N = V; g.K = H;
       g.c = out + (size_t)r0 * ld; g.ldc = ld;
       if (want(cx, EMBER_K_LM_HEAD)) launch_gemm_f32w(g, GEMM_STORE, st);
     }
@@ -542,7 +599,7 @@ void run_cls_head(const Ctx& cx, int R, int row_step, int row_off, float* out, i
     const int rn = R - r0 < G ? R - r0 : G;
     launch_rmsnorm(md->at<float>(p.x), md->at<float>(p.fnorm), c.rms_eps, rn, H, row_step,
                    row_off + r0 * row_step, xb, nullptr, nullptr, 0, cx.st);
-    launch_cls_head(xb, md->ws + p.cls_w, md->wbf16, md->at<float>(p.cls_b), rn, H, c.n_classes,
+    launch_cls_head(xb, md->ws + p.cls_w, md->wk == WK_BF16, md->at<float>(p.cls_b), rn, H, c.n_classes,
                     out ? out + (size_t)r0 * c.n_classes : nullptr, next ? next + r0 : nullptr,
                     cx.st);
   }
@@ -557,7 +614,7 @@ void decode_body(const Ctx& cx, int B, int32_t* next, int only_layer = -1) {
   const Plan& p = md->plan;
   Pass ps{};
   ps.M = B; ps.rows = B; ps.tpr = 1; ps.b0 = 0; ps.start = 0; ps.d_pos = md->at<int>(p.pos);
-  ps.path = B == 1 ? PATH_GEMV : (md->wbf16 ? PATH_MFMA : PATH_F32W);
+  ps.path = B == 1 ? PATH_GEMV : (md->mfma ? PATH_MFMA : PATH_F32W);
   ps.attn = ATTN_DECODE;
   for (int l = 0; l < c.layers; ++l)
     if (only_layer < 0 || l == only_layer) run_layer(cx, l, ps);
@@ -620,16 +677,19 @@ ember_status ember_load_weights(const ember_config* cfg, const ember_tensor* ten
     if (!tensors[i].name || !tensors[i].data) return fail(EMBER_E_ARG, "tensor %d has NULL name/data", i);
     byname[tensors[i].name] = &tensors[i];
   }
+  const bool q8 = c.weight_dtype == EMBER_Q8_0;
   auto need = [&](const std::string& n, std::vector<int64_t> shape,
                   const ember_tensor** t) -> ember_status {
     auto it = byname.find(n);
     if (it == byname.end()) return fail(EMBER_E_TENSOR_MISSING, "missing tensor %s", n.c_str());
     const ember_tensor* e = it->second;
-    if (e->dtype != EMBER_F32 && e->dtype != EMBER_BF16)
+    if (e->dtype != EMBER_F32 && e->dtype != EMBER_BF16 && e->dtype != EMBER_Q8_0)
       return fail(EMBER_E_DTYPE, "unsupported dtype %d for %s", e->dtype, n.c_str());
-    if (e->dtype != c.weight_dtype)
-      return fail(EMBER_E_DTYPE, "tensor %s dtype %d differs from the config's weight dtype",
-                  n.c_str(), e->dtype);
+    // q8_0 configs: matrices in q8_0, vectors (norms, biases) in f32
+    const int want_dt = q8 ? (shape.size() == 2 ? EMBER_Q8_0 : EMBER_F32) : c.weight_dtype;
+    if (e->dtype != want_dt)
+      return fail(EMBER_E_DTYPE, "tensor %s dtype %d differs from the config's (%d expected)",
+                  n.c_str(), e->dtype, want_dt);
     bool ok = e->ndim == (int)shape.size();
     for (size_t d = 0; ok && d < shape.size(); ++d) ok = e->shape[d] == shape[d];
     if (!ok) return fail(EMBER_E_TENSOR_SHAPE, "bad shape for %s", n.c_str());
@@ -678,33 +738,52 @@ ember_status ember_load_weights(const ember_config* cfg, const ember_tensor* ten
   auto copy = [&](size_t dst, const ember_tensor* t, size_t bytes) -> hipError_t {
     return hipMemcpyAsync(ws + dst, t->data, bytes, hipMemcpyDeviceToDevice, st);
   };
-  HIP_TRY(copy(plan.embed, emb, (size_t)V * H * es));
+  // q8_0 blocks into the byte and scale planes (rows placed as the copies below place them)
+  auto unpack = [&](const ember_tensor* t, int N, int K, size_t off, size_t soff, int row0, int gu) {
+    launch_q8_unpack((const uint8_t*)t->data, N, K, (uint8_t*)(ws + off), (uint16_t*)(ws + soff),
+                     row0, gu, st);
+  };
+  if (q8) unpack(emb, V, H, plan.embed, plan.embed_s, 0, -1);
+  else HIP_TRY(copy(plan.embed, emb, (size_t)V * H * es));
   for (int l = 0; l < c.layers; ++l) {
     const LayerOff& L = plan.layer[l];
     const LT& t = lt[l];
     launch_widen(t.ln1->data, bf, (float*)(ws + L.ln1), H, st);
     launch_widen(t.ln2->data, bf, (float*)(ws + L.ln2), H, st);
     // fused QKV rows: q, then k, then v
-    HIP_TRY(copy(L.wqkv, t.q, (size_t)NH * HD * H * es));
-    HIP_TRY(copy(L.wqkv + (size_t)NH * HD * H * es, t.k, (size_t)NKV * HD * H * es));
-    HIP_TRY(copy(L.wqkv + (size_t)(NH + NKV) * HD * H * es, t.v, (size_t)NKV * HD * H * es));
+    if (q8) {
+      unpack(t.q, NH * HD, H, L.wqkv, L.wqkv_s, 0, -1);
+      unpack(t.k, NKV * HD, H, L.wqkv, L.wqkv_s, NH * HD, -1);
+      unpack(t.v, NKV * HD, H, L.wqkv, L.wqkv_s, (NH + NKV) * HD, -1);
+    } else {
+      HIP_TRY(copy(L.wqkv, t.q, (size_t)NH * HD * H * es));
+      HIP_TRY(copy(L.wqkv + (size_t)NH * HD * H * es, t.k, (size_t)NKV * HD * H * es));
+      HIP_TRY(copy(L.wqkv + (size_t)(NH + NKV) * HD * H * es, t.v, (size_t)NKV * HD * H * es));
+    }
     if (c.qkv_bias) {
       launch_widen(t.qb->data, bf, (float*)(ws + L.bqkv), NH * HD, st);
       launch_widen(t.kb->data, bf, (float*)(ws + L.bqkv) + NH * HD, NKV * HD, st);
       launch_widen(t.vb->data, bf, (float*)(ws + L.bqkv) + (NH + NKV) * HD, NKV * HD, st);
     }
-    HIP_TRY(copy(L.wo, t.o, (size_t)H * NH * HD * es));
+    if (q8) unpack(t.o, H, NH * HD, L.wo, L.wo_s, 0, -1);
+    else HIP_TRY(copy(L.wo, t.o, (size_t)H * NH * HD * es));
     if (c.qk_norm) {
       launch_widen(t.qn->data, bf, (float*)(ws + L.qn), HD, st);
       launch_widen(t.kn->data, bf, (float*)(ws + L.kn), HD, st);
     }
     // gate/up rows interleaved in blocks of kGuBlock (see gu_row)
-    const size_t blk = (size_t)kGuBlock * H * es;
-    HIP_TRY(hipMemcpy2DAsync(ws + L.wgu, 2 * blk, t.g->data, blk, blk, FF / kGuBlock,
-                             hipMemcpyDeviceToDevice, st));
-    HIP_TRY(hipMemcpy2DAsync(ws + L.wgu + blk, 2 * blk, t.u->data, blk, blk, FF / kGuBlock,
-                             hipMemcpyDeviceToDevice, st));
-    HIP_TRY(copy(L.wd, t.d, (size_t)H * FF * es));
+    if (q8) {
+      unpack(t.g, FF, H, L.wgu, L.wgu_s, 0, 0);
+      unpack(t.u, FF, H, L.wgu, L.wgu_s, 0, 1);
+      unpack(t.d, H, FF, L.wd, L.wd_s, 0, -1);
+    } else {
+      const size_t blk = (size_t)kGuBlock * H * es;
+      HIP_TRY(hipMemcpy2DAsync(ws + L.wgu, 2 * blk, t.g->data, blk, blk, FF / kGuBlock,
+                               hipMemcpyDeviceToDevice, st));
+      HIP_TRY(hipMemcpy2DAsync(ws + L.wgu + blk, 2 * blk, t.u->data, blk, blk, FF / kGuBlock,
+                               hipMemcpyDeviceToDevice, st));
+      HIP_TRY(copy(L.wd, t.d, (size_t)H * FF * es));
+    }
   }
   launch_widen(fn->data, bf, (float*)(ws + plan.fnorm), H, st);
   if (clsw) {
@@ -729,7 +808,8 @@ ember_status ember_load_weights(const ember_config* cfg, const ember_tensor* ten
   m->cfg = c;
   m->plan = plan;
   m->ws = ws;
-  m->wbf16 = bf;
+  m->wk = weight_kind(c.weight_dtype);
+  m->mfma = uses_mfma(c);
   m->has_logits_rows = 0;
   *out = m;
   return EMBER_OK;
@@ -795,12 +875,13 @@ ember_status ember_prefill(ember_model* md, ember_cache* cache, const int32_t* h
         memcpy(&ids[(size_t)r * tpr], h_ids + (size_t)(b0 + r) * T + t0, (size_t)tpr * 4);
       HIP_TRY(hipMemcpyAsync(md->at<int32_t>(p.ids), ids.data(), (size_t)M * 4,
                              hipMemcpyHostToDevice, st));
-      launch_embed(md->at<int32_t>(p.ids), md->ws + p.embed, md->wbf16, md->at<float>(p.x), M,
+      launch_embed(md->at<int32_t>(p.ids), md->ws + p.embed, md->wk,
+                   md->wk == WK_Q8 ? md->at<uint16_t>(p.embed_s) : nullptr, md->at<float>(p.x), M,
                    c.hidden, c.vocab, md->at<int>(p.flags), st);
       Pass ps{};
       ps.M = M; ps.rows = rows; ps.tpr = tpr; ps.b0 = b0; ps.start = start_pos + t0;
       ps.d_pos = nullptr;
-      ps.path = M == 1 ? PATH_GEMV : (md->wbf16 ? PATH_MFMA : PATH_F32W);
+      ps.path = M == 1 ? PATH_GEMV : (md->mfma ? PATH_MFMA : PATH_F32W);
       ps.attn = ATTN_FLASH;
       for (int l = 0; l < c.layers; ++l) run_layer(cx, l, ps);
       md->last_pass = {M, rows, tpr, b0, start_pos + t0};
@@ -857,7 +938,9 @@ ember_status ember_decode_step(ember_model* md, ember_cache* cache, const int32_
   sb.d_pos = md->at<int>(p.pos); sb.flags = md->at<int>(p.flags);
   sb.cos_t = md->at<float>(p.cos_t); sb.sin_t = md->at<float>(p.sin_t); sb.half = c.head_dim / 2;
   sb.rope_cur = md->at<float>(p.rope_cur);
-  sb.E = md->ws + p.embed; sb.e_bf16 = md->wbf16; sb.x = md->at<float>(p.x); sb.H = c.hidden;
+  sb.E = md->ws + p.embed; sb.e_wk = md->wk;
+  sb.e_scale = md->wk == WK_Q8 ? md->at<uint16_t>(p.embed_s) : nullptr;
+  sb.x = md->at<float>(p.x); sb.H = c.hidden;
   launch_step_begin(sb, st);
   const bool use_graph = st != nullptr && graphs_enabled();
   if (use_graph) {
@@ -913,7 +996,7 @@ ember_status ember_time_kernel(ember_model* md, ember_cache* cache, int32_t kern
       Pass ps{};
       ps.M = md->last_pass.M; ps.rows = md->last_pass.rows; ps.tpr = md->last_pass.tpr;
       ps.b0 = md->last_pass.b0; ps.start = md->last_pass.start; ps.d_pos = nullptr;
-      ps.path = ps.M == 1 ? PATH_GEMV : (md->wbf16 ? PATH_MFMA : PATH_F32W);
+      ps.path = ps.M == 1 ? PATH_GEMV : (md->mfma ? PATH_MFMA : PATH_F32W);
       ps.attn = ATTN_FLASH;
       for (int i = 0; i < n; ++i) {
         if (kernel == EMBER_K_LM_HEAD)

@@ -16,8 +16,27 @@ enum DeviceFlag { kFlagBadToken = 0, kFlagNaN = 1, kNumFlags = 4 };
 
 // x[m, :] = widen(E[ids[m], :]) for m < M; ids outside [0, V) read row 0 and raise
 // flags[kFlagBadToken] (host-validated prefill ids never do).
-void launch_embed(const int32_t* ids, const void* E, bool e_bf16, float* x, int M, int H,
-                  int V, int* flags, hipStream_t st);
+// Storage of the weight matrices. q8_0 ("ember internals", section "GGUF format and
+// quantization", subsection "q8_0 block quantization": 32 int8 values and one f16 scale per
+// block along the row) is repacked at load into two planes: [N][K] bytes holding q + 128
+// (so a byte converts to f32 in one instruction), then [N][K / 32] f16 scale bits.
+enum WeightKind { WK_F32 = 0, WK_BF16 = 1, WK_Q8 = 2 };
+constexpr int kQ8Block = 32;
+constexpr int kQ8BlockBytes = 34;
+
+// x[m] = row ids[m] of the embedding E (bf16 / f32 [V, H], or q8 planes with scales
+// e_scale); an id outside [0, V) takes row 0 and raises kFlagBadToken.
+void launch_embed(const int32_t* ids, const void* E, int e_wk, const uint16_t* e_scale, float* x,
+                  int M, int H, int V, int* flags, hipStream_t st);
+
+// q8_0 blocks of src ([N][K / 32] blocks of 34 bytes: f16 scale little-endian, 32 int8)
+// into the two planes. Destination row of source row n: dst_row0 + n (gu < 0), or
+// gu_row(n, gu) (gate: gu = 0, up: gu = 1; the interleaved gate/up matrix).
+void launch_q8_unpack(const uint8_t* src, int N, int K, uint8_t* dst_q, uint16_t* dst_s,
+                      int dst_row0, int gu, hipStream_t st);
+// The dequantised matrix q * d as bf16 (round to nearest even) or f32, [N, K] row-major.
+void launch_q8_dequant(const uint8_t* q, const uint16_t* s, int N, int K, void* dst, bool to_bf16,
+                       hipStream_t st);
 
 // Row-wise RMSNorm of rows src_row(r) = r * row_step + row_off, r < R, of x [*, H]:
 // y = x / sqrt(mean(x^2) + eps) * w. Writes any of: out_f32 [R, H], planes hi/lo
@@ -75,7 +94,8 @@ struct StepBeginArgs {
   int half;
   float* rope_cur;
   const void* E;
-  bool e_bf16;
+  int e_wk;                // WeightKind of E
+  const uint16_t* e_scale; // q8: scale plane of E
   float* x;
   int H;
 };
@@ -147,8 +167,9 @@ EMBER_INLINE_HD int gu_row(int n, int up) {
 enum GemvEpi { GEMV_STORE = 0, GEMV_RESID = 1, GEMV_SILU = 2, GEMV_LOGITS = 3 };
 
 struct GemvArgs {
-  const void* W;           // [N_rows, K] row-major, bf16 or f32
+  const void* W;           // [N_rows, K] row-major, bf16 or f32, or the q8 byte plane
   bool w_bf16;
+  const uint16_t* w_scale; // q8 weights when non-null: [N_rows][K / 32] f16 scale bits
   int N;                   // outputs per token (SILU: FF outputs from 2*FF packed rows)
   int K;
   int M;                   // tokens: must be 1
@@ -173,8 +194,8 @@ struct GemvArgs {
 };
 void launch_gemv(const GemvArgs& a, int epi, hipStream_t st);
 // whether the residual GEMV of this shape takes its input as attention partials (xpart)
-bool gemv_takes_parts(int N, int K, bool bf16);
-int gemv_num_blocks(int N, int epi, int K, bool bf16);
+bool gemv_takes_parts(int N, int K, int wk);
+int gemv_num_blocks(int N, int epi, int K, int wk);
 
 // ------------------------------------------------------------------ GEMM (kernels_gemm.hip)
 

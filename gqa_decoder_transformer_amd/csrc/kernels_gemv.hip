@@ -1,5 +1,6 @@
 // Decode GEMV: y[n] = sum_k W[n, k] x[k] for one token, streaming W from HBM once with
-// 16-byte coalesced loads (bf16 weights widened to f32 in registers, f32 FMA).
+// 16-byte coalesced loads (bf16 weights widened to f32 in registers, f32 FMA; q8_0
+// weights as bytes plus one f16 scale per 32, dequantised in registers: see chunk_dot).
 //
 // At decode sizes these kernels are bound by how early and how many weight bytes are in
 // flight, so nothing is staged through LDS:
@@ -26,21 +27,59 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
+struct Q8 {};                   // q8 weights: the byte plane (q + 128) and f16 scales
 template <typename WT> struct WTraits;
 template <> struct WTraits<uint16_t> {
+  using Elem = uint16_t;
   static constexpr int E = 8;   // elements per 16-byte chunk
+  static constexpr bool kQ8 = false;
   static EMBER_DEV void widen(const u32x4_t& v, float* f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_lo(v[i]); f[2 * i + 1] = bf16_hi(v[i]); }
   }
 };
 template <> struct WTraits<float> {
+  using Elem = float;
   static constexpr int E = 4;
+  static constexpr bool kQ8 = false;
   static EMBER_DEV void widen(const u32x4_t& v, float* f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
   }
 };
+template <> struct WTraits<Q8> {
+  using Elem = uint8_t;
+  static constexpr int E = 16;  // half a q8_0 block per chunk
+  static constexpr bool kQ8 = true;
+};
+
+// acc plus one chunk's contribution. bf16 / f32: the widened weights times x, one FMA
+// each. q8: d * (sum_e b_e x_e - 128 sum_e x_e) with b_e = q_e + 128 (a byte converts to
+// f32 in one instruction), sx = sum_e x_e and d the block's scale (f16 bits in sc).
+template <typename WT>
+EMBER_DEV float chunk_dot(const u32x4_t& w, const float* x, float sx, uint32_t sc, float acc) {
+  constexpr int E = WTraits<WT>::E;
+  if constexpr (WTraits<WT>::kQ8) {
+    float p = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) p = fmaf((float)((w[e / 4] >> (8 * (e % 4))) & 0xFFu), x[e], p);
+    p = fmaf(-128.f, sx, p);
+    return fmaf(f16_to_f32(sc), p, acc);
+  } else {
+    float wf[E];
+    WTraits<WT>::widen(w, wf);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc = fmaf(wf[e], x[e], acc);
+    return acc;
+  }
+}
+
+// scale of chunk c (16 values, half a block) of weight row `row` (q8 only)
+template <typename WT>
+EMBER_DEV uint32_t chunk_scale(const GemvArgs& a, int row, int c) {
+  if constexpr (WTraits<WT>::kQ8) return a.w_scale[(size_t)row * (a.K / kQ8Block) + (c >> 1)];
+  else return 0u;
+}
 
 
 template <int EPI>
@@ -141,18 +180,20 @@ __global__ void __launch_bounds__(kThreads) k_gemv_wave(GemvArgs a) {
   const int K = a.K, nch = K / E;
   const int ngroups = (a.N + RPW - 1) / RPW;
 
-  auto load_group = [&](int grp, u32x4_t (&w)[U][NR]) {
+  auto load_group = [&](int grp, u32x4_t (&w)[U][NR], uint32_t (&sc)[U][NR]) {
 #pragma unroll
     for (int u = 0; u < RPW; ++u) {
       int n = grp * RPW + u;
       n = n < a.N ? n : a.N - 1;                      // clamp: duplicate, never stored
 #pragma unroll
       for (int r = 0; r < RU; ++r) {
-        const WT* row = (const WT*)a.W + (size_t)weight_row<EPI>(n, r) * K;
+        const int wr = weight_row<EPI>(n, r);
+        const auto* row = (const typename WTraits<WT>::Elem*)a.W + (size_t)wr * K;
 #pragma unroll
         for (int t = 0; t < U; ++t) {
           const int c = min(lane + kWave * t, nch - 1);   // clamped chunk: x is 0 there
           w[t][u * RU + r] = *(const u32x4_t*)(row + (size_t)c * E);
+          sc[t][u * RU + r] = chunk_scale<WT>(a, wr, c);
         }
       }
     }
@@ -162,6 +203,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_wave(GemvArgs a) {
   // and are normalised while the weights are still in flight
   float xv[U][E], nv[U][E];
   u32x4_t wa[U][NR];
+  uint32_t sca[U][NR];
   int grp = gw;
   if constexpr (XP) {
     // input rebuilt from attention partials: loads first, then the weights, then the
@@ -170,7 +212,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_wave(GemvArgs a) {
     const int S = *a.xp_pos + 1;
     PartIn pin;
     part_load(a, pin);
-    load_group(min(grp, ngroups - 1), wa);
+    load_group(min(grp, ngroups - 1), wa, sca);
     __builtin_amdgcn_sched_barrier(0);              // every weight load issued before any wait
     part_finish(a, pin, S, xs);
     __syncthreads();
@@ -186,7 +228,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_wave(GemvArgs a) {
       load_chunk_f32<E>(a.x, min(c, nch - 1), c < nch, xv[t]);
       if (a.norm_w) load_chunk_f32<E>(a.norm_w, min(c, nch - 1), c < nch, nv[t]);
     }
-    load_group(min(grp, ngroups - 1), wa);          // unconditional: a spare wave reloads
+    load_group(min(grp, ngroups - 1), wa, sca);     // unconditional: a spare wave reloads
   }
 
   float ss = 0.f;
@@ -202,22 +244,24 @@ __global__ void __launch_bounds__(kThreads) k_gemv_wave(GemvArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) xv[t][e] = xv[t][e] * inv_rms * nv[t][e];
   }
+  float sx[U];
+#pragma unroll
+  for (int t = 0; t < U; ++t) {
+    sx[t] = 0.f;
+    if constexpr (WTraits<WT>::kQ8)
+#pragma unroll
+      for (int e = 0; e < E; ++e) sx[t] += xv[t][e];
+  }
 
   unsigned long long best = 0;
-  auto compute = [&](int g, const u32x4_t (&w)[U][NR]) {
+  auto compute = [&](int g, const u32x4_t (&w)[U][NR], const uint32_t (&sc)[U][NR]) {
     float acc[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int t = 0; t < U; ++t) {
+    for (int t = 0; t < U; ++t)
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        float wf[E];
-        WTraits<WT>::widen(w[t][r], wf);
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[r] = fmaf(wf[e], xv[t][e], acc[r]);
-      }
-    }
+      for (int r = 0; r < NR; ++r) acc[r] = chunk_dot<WT>(w[t][r], xv[t], sx[t], sc[t][r], acc[r]);
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[r] = wave_sum_uniform(acc[r]);
 #pragma unroll
@@ -227,9 +271,9 @@ __global__ void __launch_bounds__(kThreads) k_gemv_wave(GemvArgs a) {
     }
   };
   while (grp < ngroups) {
-    compute(grp, wa);
+    compute(grp, wa, sca);
     grp += nwaves;
-    if (grp < ngroups) load_group(grp, wa);
+    if (grp < ngroups) load_group(grp, wa, sca);
   }
   if (EPI == GEMV_LOGITS && lane == 0) a.argmax_part[gw] = best;
 }
@@ -246,18 +290,20 @@ __global__ void __launch_bounds__(kThreads) k_gemv_block(GemvArgs a) {
   const int K = a.K, nch = K / E;
   const int ngroups = (a.N + RPW - 1) / RPW;
 
-  auto load_group = [&](int grp, u32x4_t (&w)[U][NR]) {
+  auto load_group = [&](int grp, u32x4_t (&w)[U][NR], uint32_t (&sc)[U][NR]) {
 #pragma unroll
     for (int u = 0; u < RPW; ++u) {
       int n = grp * RPW + u;
       n = n < a.N ? n : a.N - 1;
 #pragma unroll
       for (int r = 0; r < RU; ++r) {
-        const WT* row = (const WT*)a.W + (size_t)weight_row<EPI>(n, r) * K;
+        const int wr = weight_row<EPI>(n, r);
+        const auto* row = (const typename WTraits<WT>::Elem*)a.W + (size_t)wr * K;
 #pragma unroll
         for (int t = 0; t < U; ++t) {
           const int c = min((int)threadIdx.x + kThreads * t, nch - 1);
           w[t][u * RU + r] = *(const u32x4_t*)(row + (size_t)c * E);
+          sc[t][u * RU + r] = chunk_scale<WT>(a, wr, c);
         }
       }
     }
@@ -271,8 +317,9 @@ __global__ void __launch_bounds__(kThreads) k_gemv_block(GemvArgs a) {
     if (a.norm_w) load_chunk_f32<E>(a.norm_w, min(c, nch - 1), c < nch, nv[t]);
   }
   u32x4_t wa[U][NR];
+  uint32_t sca[U][NR];
   int grp = blockIdx.x;
-  load_group(min(grp, ngroups - 1), wa);
+  load_group(min(grp, ngroups - 1), wa, sca);
 
   float ss = 0.f;
 #pragma unroll
@@ -287,23 +334,25 @@ __global__ void __launch_bounds__(kThreads) k_gemv_block(GemvArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) xv[t][e] = xv[t][e] * inv_rms * nv[t][e];
   }
+  float sx[U];
+#pragma unroll
+  for (int t = 0; t < U; ++t) {
+    sx[t] = 0.f;
+    if constexpr (WTraits<WT>::kQ8)
+#pragma unroll
+      for (int e = 0; e < E; ++e) sx[t] += xv[t][e];
+  }
 
   unsigned long long best = 0;
   int parity = 0;
-  auto compute = [&](int g, const u32x4_t (&w)[U][NR]) {
+  auto compute = [&](int g, const u32x4_t (&w)[U][NR], const uint32_t (&sc)[U][NR]) {
     float acc[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int t = 0; t < U; ++t) {
+    for (int t = 0; t < U; ++t)
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        float wf[E];
-        WTraits<WT>::widen(w[t][r], wf);
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[r] = fmaf(wf[e], xv[t][e], acc[r]);
-      }
-    }
+      for (int r = 0; r < NR; ++r) acc[r] = chunk_dot<WT>(w[t][r], xv[t], sx[t], sc[t][r], acc[r]);
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       acc[r] = wave_sum_uniform(acc[r]);
@@ -321,9 +370,9 @@ __global__ void __launch_bounds__(kThreads) k_gemv_block(GemvArgs a) {
     }
   };
   while (grp < ngroups) {
-    compute(grp, wa);
+    compute(grp, wa, sca);
     grp += (int)gridDim.x;
-    if (grp < ngroups) load_group(grp, wa);
+    if (grp < ngroups) load_group(grp, wa, sca);
   }
   if (EPI == GEMV_LOGITS && threadIdx.x == 0) a.argmax_part[blockIdx.x] = best;
 }
@@ -364,13 +413,16 @@ __global__ void __launch_bounds__(kThreads) k_gemv_long(GemvArgs a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) xv[e] = xv[e] * inv_rms * nv[e];
       }
+      float sx = 0.f;
+      if constexpr (WTraits<WT>::kQ8)
+#pragma unroll
+        for (int e = 0; e < E; ++e) sx += xv[e];
 #pragma unroll
       for (int r = 0; r < RU; ++r) {
-        const WT* row = (const WT*)a.W + (size_t)weight_row<EPI>(n, r) * K;
-        float wf[E];
-        WTraits<WT>::widen(*(const u32x4_t*)(row + (size_t)c * E), wf);
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[r] = fmaf(wf[e], xv[e], acc[r]);
+        const int wr = weight_row<EPI>(n, r);
+        const auto* row = (const typename WTraits<WT>::Elem*)a.W + (size_t)wr * K;
+        acc[r] = chunk_dot<WT>(*(const u32x4_t*)(row + (size_t)c * E), xv, sx,
+                               chunk_scale<WT>(a, wr, c), acc[r]);
       }
     }
 #pragma unroll
@@ -393,8 +445,8 @@ struct Shape {
 // chunks (two output units per block once the grid would pass 1024 blocks); a K loop
 // beyond. The logits GEMV keeps larger row groups: it loops over 128k+ rows and its
 // per-group argmax favours fewer groups.
-Shape pick(int N, int K, bool bf16, int epi) {
-  const int E = bf16 ? 8 : 4;
+Shape pick(int N, int K, int wk, int epi) {
+  const int E = wk == WK_Q8 ? 16 : (wk == WK_BF16 ? 8 : 4);
   const int nch = K / E;
   const int ru = epi == GEMV_SILU ? 2 : 1;
   Shape s;
@@ -452,9 +504,13 @@ void launch_block(const GemvArgs& a, int blocks, hipStream_t st) {
   hipLaunchKernelGGL((k_gemv_block<WT, EPI, RPW, U>), dim3(blocks), dim3(kThreads), 0, st, a);
 }
 
+template <typename WT> constexpr int kind_of() {
+  return WTraits<WT>::kQ8 ? WK_Q8 : (WTraits<WT>::E == 8 ? WK_BF16 : WK_F32);
+}
+
 template <typename WT, int EPI>
 void launch_t(const GemvArgs& a, hipStream_t st) {
-  const Shape s = pick(a.N, a.K, sizeof(WT) == 2, EPI);
+  const Shape s = pick(a.N, a.K, kind_of<WT>(), EPI);
   constexpr int RU = EPI == GEMV_SILU ? 2 : 1;
   if (s.kind == SHAPE_LONG) {
     hipLaunchKernelGGL((k_gemv_long<WT, EPI>), dim3(s.blocks), dim3(kThreads), 0, st, a);
@@ -486,23 +542,27 @@ void launch_t(const GemvArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int gemv_num_blocks(int N, int epi, int K, bool bf16) {
-  const Shape s = pick(N, K, bf16, epi);
+int gemv_num_blocks(int N, int epi, int K, int wk) {
+  const Shape s = pick(N, K, wk, epi);
   return s.kind == SHAPE_WAVE ? s.blocks * kWaves : s.blocks;   // argmax partials written
 }
 
-bool gemv_takes_parts(int N, int K, bool bf16) {
-  return pick(N, K, bf16, GEMV_RESID).kind == SHAPE_WAVE;
+// the rebuilt input lives in a 1024-entry LDS copy (row-per-wave layout only)
+bool gemv_takes_parts(int N, int K, int wk) {
+  return K <= 1024 && pick(N, K, wk, GEMV_RESID).kind == SHAPE_WAVE;
 }
 
 void launch_gemv(const GemvArgs& a, int epi, hipStream_t st) {
   if (a.M != 1 || a.N <= 0 || (!a.x && !a.xpart)) return;   // one token, an input required
-  if (a.xpart && (epi != GEMV_RESID || !gemv_takes_parts(a.N, a.K, a.w_bf16) ||
+  const int wk = a.w_scale ? WK_Q8 : (a.w_bf16 ? WK_BF16 : WK_F32);
+  if (wk == WK_Q8 && a.K % kQ8Block) return;                 // q8 rows are whole blocks
+  if (a.xpart && (epi != GEMV_RESID || !gemv_takes_parts(a.N, a.K, wk) ||
                   a.xp_nsplit < 1 || a.xp_nsplit > 4))
     return;                                                   // callers check gemv_takes_parts
 #define EMBER_GEMV_CASE(E)                                               \
   case E:                                                                \
-    if (a.w_bf16) launch_t<uint16_t, E>(a, st);                          \
+    if (wk == WK_Q8) launch_t<Q8, E>(a, st);                             \
+    else if (wk == WK_BF16) launch_t<uint16_t, E>(a, st);                \
     else launch_t<float, E>(a, st);                                      \
     break;
   switch (epi) {

@@ -8,28 +8,102 @@ namespace ember {
 
 // ------------------------------------------------------------------ embedding gather
 // x = E[id] widened to f32 ("ember scripts/reference_forward.py", forward: embed[tok]).
-__global__ void __launch_bounds__(256) k_embed(const int32_t* ids, const void* E, int e_bf16,
-                                               float* x, int H, int V, int* flags) {
-  const int m = blockIdx.x;
-  int id = ids[m];
-  if (id < 0 || id >= V) {
-    if (threadIdx.x == 0) atomicOr(&flags[kFlagBadToken], 1);
-    id = 0;
-  }
-  float* xr = x + (size_t)m * H;
-  if (e_bf16) {
+// Row `id` of the embedding widened to f32: bf16 and f32 exactly; q8 as (byte - 128) * d
+// with d the block's f16 scale (an exact f32 product, "ember internals", q8_0 blocks).
+EMBER_DEV void embed_row(const void* E, int wk, const uint16_t* e_scale, int id, int H, float* xr) {
+  if (wk == WK_BF16) {
     const uint16_t* er = (const uint16_t*)E + (size_t)id * H;
     for (int i = threadIdx.x; i < H; i += blockDim.x) xr[i] = bf16_to_f32(er[i]);
+  } else if (wk == WK_Q8) {
+    const uint8_t* er = (const uint8_t*)E + (size_t)id * H;
+    const uint16_t* sr = e_scale + (size_t)id * (H / kQ8Block);
+    for (int i = threadIdx.x; i < H; i += blockDim.x)
+      xr[i] = (float)((int)er[i] - 128) * f16_to_f32(sr[i / kQ8Block]);
   } else {
     const float* er = (const float*)E + (size_t)id * H;
     for (int i = threadIdx.x; i < H; i += blockDim.x) xr[i] = er[i];
   }
 }
 
-void launch_embed(const int32_t* ids, const void* E, bool e_bf16, float* x, int M, int H, int V,
-                  int* flags, hipStream_t st) {
+__global__ void __launch_bounds__(256) k_embed(const int32_t* ids, const void* E, int wk,
+                                               const uint16_t* e_scale, float* x, int H, int V,
+                                               int* flags) {
+  const int m = blockIdx.x;
+  int id = ids[m];
+  if (id < 0 || id >= V) {
+    if (threadIdx.x == 0) atomicOr(&flags[kFlagBadToken], 1);
+    id = 0;
+  }
+  embed_row(E, wk, e_scale, id, H, x + (size_t)m * H);
+}
+
+void launch_embed(const int32_t* ids, const void* E, int e_wk, const uint16_t* e_scale, float* x,
+                  int M, int H, int V, int* flags, hipStream_t st) {
   if (M <= 0) return;
-  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, ids, E, (int)e_bf16, x, H, V, flags);
+  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, ids, E, e_wk, e_scale, x, H, V, flags);
+}
+
+// ------------------------------------------------------------------ q8_0 planes
+// One thread per block: 34 source bytes (scale, then 32 int8) -> 32 bytes of q + 128 in
+// the byte plane (q xor 0x80) and the scale's bits in the scale plane.
+__global__ void __launch_bounds__(256) k_q8_unpack(const uint8_t* src, int N, int K, uint8_t* dst_q,
+                                                   uint16_t* dst_s, int dst_row0, int gu) {
+  const int nb = K / kQ8Block;
+  const long long i = threadIdx.x + (long long)blockIdx.x * blockDim.x;
+  if (i >= (long long)N * nb) return;
+  const int n = (int)(i / nb), b = (int)(i % nb);
+  const int d = gu < 0 ? dst_row0 + n : gu_row(n, gu);
+  const uint8_t* blk = src + (size_t)i * kQ8BlockBytes;
+  dst_s[(size_t)d * nb + b] = (uint16_t)(blk[0] | (blk[1] << 8));
+  uint8_t* q = dst_q + (size_t)d * K + (size_t)b * kQ8Block;
+#pragma unroll
+  for (int j = 0; j < kQ8Block; ++j) q[j] = blk[2 + j] ^ 0x80u;
+}
+
+void launch_q8_unpack(const uint8_t* src, int N, int K, uint8_t* dst_q, uint16_t* dst_s,
+                      int dst_row0, int gu, hipStream_t st) {
+  const long long n = (long long)N * (K / kQ8Block);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_q8_unpack, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, N, K,
+                     dst_q, dst_s, dst_row0, gu);
+}
+
+// One thread per 16 bytes of the byte plane: 16 values (byte - 128) * d.
+__global__ void __launch_bounds__(256) k_q8_dequant(const uint8_t* q, const uint16_t* s, int N, int K,
+                                                    void* dst, int to_bf16) {
+  const long long i = threadIdx.x + (long long)blockIdx.x * blockDim.x;
+  const long long nch = (long long)N * K / 16;
+  if (i >= nch) return;
+  const long long e0 = i * 16;
+  const int n = (int)(e0 / K), k0 = (int)(e0 % K);
+  const float d = f16_to_f32(s[(size_t)n * (K / kQ8Block) + k0 / kQ8Block]);
+  const u32x4_t w = *(const u32x4_t*)(q + e0);
+  float v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = (float)((int)((w[j / 4] >> (8 * (j % 4))) & 0xFFu) - 128) * d;
+  if (to_bf16) {
+    u32x4_t o0, o1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o0[j] = f32_to_bf16_rne(v[2 * j]) | (f32_to_bf16_rne(v[2 * j + 1]) << 16);
+      o1[j] = f32_to_bf16_rne(v[8 + 2 * j]) | (f32_to_bf16_rne(v[8 + 2 * j + 1]) << 16);
+    }
+    u32x4_t* o = (u32x4_t*)((uint16_t*)dst + e0);
+    o[0] = o0;
+    o[1] = o1;
+  } else {
+    float4* o = (float4*)((float*)dst + e0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+  }
+}
+
+void launch_q8_dequant(const uint8_t* q, const uint16_t* s, int N, int K, void* dst, bool to_bf16,
+                       hipStream_t st) {
+  const long long n = (long long)N * K / 16;
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_q8_dequant, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, q, s, N, K,
+                     dst, (int)to_bf16);
 }
 
 // ------------------------------------------------------------------ RMSNorm
@@ -295,14 +369,7 @@ __global__ void __launch_bounds__(256) k_step_begin(StepBeginArgs a) {
     if (threadIdx.x == 0) atomicOr(&a.flags[kFlagBadToken], 1);
     id = 0;
   }
-  float* xr = a.x + (size_t)r * a.H;
-  if (a.e_bf16) {
-    const uint16_t* er = (const uint16_t*)a.E + (size_t)id * a.H;
-    for (int i = threadIdx.x; i < a.H; i += blockDim.x) xr[i] = bf16_to_f32(er[i]);
-  } else {
-    const float* er = (const float*)a.E + (size_t)id * a.H;
-    for (int i = threadIdx.x; i < a.H; i += blockDim.x) xr[i] = er[i];
-  }
+  embed_row(a.E, a.e_wk, a.e_scale, id, a.H, a.x + (size_t)r * a.H);
 }
 
 void launch_step_begin(const StepBeginArgs& a, hipStream_t st) {

@@ -47,7 +47,12 @@ typedef enum ember_status {
   EMBER_E_NONFINITE = 10       /* the device saw a NaN logit */
 } ember_status;
 
-typedef enum ember_dtype { EMBER_F32 = 0, EMBER_BF16 = 1 } ember_dtype;
+/* EMBER_Q8_0: a weight matrix [N, K] (K a multiple of 32) stored as q8_0 blocks ("ember
+ * internals" page, section "GGUF format and quantization", subsection "q8_0 block
+ * quantization"): N x K/32 blocks of 34 bytes, row by row, each a little-endian f16 scale d
+ * followed by 32 signed int8 values q; the weights are q * d. The blocks run along K.
+ * Weights only (never a KV cache or an output dtype). */
+typedef enum ember_dtype { EMBER_F32 = 0, EMBER_BF16 = 1, EMBER_Q8_0 = 2 } ember_dtype;
 
 /* EXACT: every product is an f32-accurate product of the bf16 weight and the f32
  *        activation (decode: f32 FMA; prefill MFMA: activation split into two bf16
@@ -79,7 +84,13 @@ typedef struct ember_config {
   int32_t causal;              /* 1 = causal decoder, 0 = bidirectional encoder */
   int32_t head_kind;           /* ember_head_kind */
   int32_t n_classes;           /* classes of the EMBER_HEAD_CLS head */
-  int32_t weight_dtype;        /* ember_dtype of every stored tensor */
+  int32_t weight_dtype;        /* ember_dtype of every stored tensor; EMBER_Q8_0: every
+                                * matrix in q8_0 and every vector (norm weights, biases) in
+                                * F32, tied LM head only, hidden, ffn and heads * head_dim
+                                * multiples of 32. A one-token pass (batch-1 decode) reads
+                                * the blocks directly; multi-token passes dequantise each
+                                * matrix into a workspace copy first (bf16 for FAST, f32 for
+                                * EXACT) */
   int32_t kv_dtype;            /* ember_dtype of the KV cache */
   int32_t precision;           /* ember_precision */
   int32_t max_batch;           /* rows per call */

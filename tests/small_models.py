@@ -37,3 +37,15 @@ QWEN_FF2K = C.shrink_model(C.QWEN05B, name="qwen-ff2k", vocab=97, hidden=64, lay
 
 LLAMA_FF8K = C.shrink_model(C.LLAMA1B, name="llama-ff8k", vocab=101, hidden=64, layers=2,
                             heads=8, kv_heads=2, head_dim=8, ffn=8448)
+
+# q8_0 matrices (every K a multiple of 32). In the q8 GEMV a 16-byte chunk holds 16
+# weights: ffn 2304 puts the down projection in the row-per-block layout, ffn 8448 in it
+# with three chunks per thread, ffn 16896 past 1024 chunks (the K-looping kernel)
+QWEN_SMALL_Q8 = C.shrink_model(QWEN_SMALL, name="qwen-small-q8", weight_dtype="q8_0")
+LLAMA_SMALL_Q8 = C.shrink_model(LLAMA_SMALL, name="llama-small-q8", weight_dtype="q8_0")
+LLAMA_HD64_Q8 = C.shrink_model(LLAMA_HD64, name="llama-hd64-q8", weight_dtype="q8_0")
+QWEN_FF2K_Q8 = C.shrink_model(QWEN_FF2K, name="qwen-ff2k-q8", weight_dtype="q8_0")
+LLAMA_FF8K_Q8 = C.shrink_model(LLAMA_FF8K, name="llama-ff8k-q8", weight_dtype="q8_0")
+LLAMA_FF16K_Q8 = C.shrink_model(LLAMA_FF8K, name="llama-ff16k-q8", ffn=16896, weight_dtype="q8_0")
+Q8_SMALL = [QWEN_SMALL_Q8, LLAMA_SMALL_Q8, LLAMA_HD64_Q8, QWEN_FF2K_Q8, LLAMA_FF8K_Q8,
+            LLAMA_FF16K_Q8]

@@ -44,12 +44,22 @@ def test_every_workload_config_validates_and_sizes(name):
     assert ws > 0
     # the workspace holds at least the weights in their stored dtype
     m = WORKLOADS[name].model
-    es = 2 if m.weight_dtype == "bf16" else 4
+    es = {"bf16": 2, "f32": 4, "q8_0": 34 / 32}[m.weight_dtype]
     params = m.vocab * m.hidden + m.layers * (m.hidden * (m.q_dim + 2 * m.kv_dim) +
                                              m.hidden * m.q_dim + 3 * m.hidden * m.ffn)
     assert ws >= params * es
     kv = B.ember_kv_cache_bytes(c)
     assert kv == 2 * m.layers * c.max_batch * m.kv_heads * c.max_seq * m.head_dim * 4
+
+
+def test_q8_configs_need_the_lm_head_and_whole_blocks():
+    c = _cfg("qwen05b-q8")
+    assert B.ember_workspace_bytes(c) > 0
+    c.head_kind, c.n_classes = B.HEAD_CLS, 2
+    assert B.ember_workspace_bytes(c) == 0          # q8_0 with a classification head
+    c = _cfg("qwen05b-q8")
+    c.hidden = 880                                   # a multiple of 8 but not of 32
+    assert B.ember_workspace_bytes(c) == 0
 
 
 @pytest.mark.parametrize("field,value", [("heads", 0), ("kv_heads", 3), ("head_dim", 7),

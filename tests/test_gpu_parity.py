@@ -11,7 +11,7 @@ import oracle as O
 import workloads as W
 from tests.gpu_util import TOL_EXACT, TOL_FAST, check_greedy, gpu_generate, rel_maxabs, say
 from tests.small_models import (ENCODER_HD128, ENCODER_SMALL, LLAMA_FF8K, LLAMA_HD64, LLAMA_SMALL,
-                                LLAMA_SPLITK, QWEN_FF2K, QWEN_HD64_G7, QWEN_SMALL, TINY)
+                                LLAMA_SPLITK, Q8_SMALL, QWEN_FF2K, QWEN_HD64_G7, QWEN_SMALL, TINY)
 
 pytestmark = pytest.mark.gpu
 
@@ -215,6 +215,39 @@ def test_abi_errors_enqueue_nothing():
     eng.sync()                                       # flags cleared
 
 
+@pytest.mark.parametrize("model", Q8_SMALL, ids=lambda m: m.name)
+@pytest.mark.parametrize("prec_name", ["exact", "fast"])
+def test_small_q8_decoder_prefill_and_decode(model, prec_name):
+    """q8_0 matrices ("ember internals", q8_0 blocks): one-token steps dequantise in the
+    GEMV's registers; the prompt's multi-token pass runs on a dequantised copy (f32 for
+    EXACT, bf16 for FAST). The oracle runs on the dequantised f32 weights."""
+    from gqa_decoder_transformer_amd import binding as B
+    ck = W.make_weights(model, 12)
+    T, N = 37, 12
+    prompt = np.random.default_rng(6).integers(0, model.vocab, (1, T)).astype(np.int32)
+    prec = B.EXACT if prec_name == "exact" else B.FAST
+    say(f"small q8 decoder {model.name} T={T} N={N} {prec_name}")
+    om = O.OracleModel(model, ck)
+    or_ids, or_logits = O.generate(om, prompt[0], N)
+    eng = _engine(model, ck, prec)
+    if prec == B.EXACT:
+        g_ids, g_logits = gpu_generate(eng, prompt, N)
+        err = rel_maxabs(g_logits[:, 0], or_logits)
+        say(f"max rel err {err.max():.3g}")
+        assert err.max() < TOL_EXACT, err
+        check_greedy(g_ids[:, 0], or_ids, or_logits, TOL_EXACT)
+    else:
+        t_ids, t_logits = gpu_generate(eng, prompt, N, feed=or_ids[:N, None], logits_dtype=B.BF16)
+        err = rel_maxabs(t_logits[:, 0], or_logits)
+        say(f"max rel err {err.max():.3g}")
+        assert err.max() < TOL_FAST, err
+    # the prompt's all-position logits (multi-token pass on the dequantised copy)
+    _, allg = eng.prefill(prompt, all_logits=True)
+    full = om.forward_sequence(prompt[0], all_positions=True)
+    tol = TOL_EXACT if prec == B.EXACT else TOL_FAST
+    assert rel_maxabs(allg[0].cpu().numpy(), full).max() < tol
+
+
 # ----------------------------------------------------------------------------- workloads
 
 def _workload_case(name, steps=None, precision=None):
@@ -240,6 +273,23 @@ def test_tiny_workload_exact():
     g_ids, g_logits = gpu_generate(eng, prompt, n)
     assert rel_maxabs(g_logits[:, 0], or_logits).max() < TOL_EXACT
     assert check_greedy(g_ids[:, 0], or_ids, or_logits, TOL_EXACT) is None
+
+
+@pytest.mark.timeout(600)
+def test_qwen05b_q8_workload_exact_free_running_and_teacher_forced():
+    """The Qwen2.5-0.5B shape with q8_0 matrices, batch-1 decode in the launch
+    configuration the benchmark times."""
+    eng, prompt, n, or_ids, or_logits = _workload_case("qwen05b-q8")
+    g_ids, g_logits = gpu_generate(eng, prompt, n)
+    err = rel_maxabs(g_logits[:, 0], or_logits)
+    say(f"qwen05b-q8 free-running max rel err {err.max():.3g}")
+    div = check_greedy(g_ids[:, 0], or_ids, or_logits, TOL_EXACT)
+    upto = n + 1 if div is None else div + 1
+    assert err[:upto].max() < TOL_EXACT
+    t_ids, t_logits = gpu_generate(eng, prompt, n, feed=or_ids[:n, None])
+    terr = rel_maxabs(t_logits[:, 0], or_logits)
+    say(f"qwen05b-q8 teacher-forced max rel err {terr.max():.3g}")
+    assert terr.max() < TOL_EXACT
 
 
 @pytest.mark.timeout(600)
