@@ -147,6 +147,37 @@ class OracleModel:
             cache.length = max(cache.length, start_pos + T)
         return self.head(x if all_positions else x[-1])
 
+    def forward_with_activations(self, ids, start_pos: int = 0, cache: KVCache | None = None):
+        """The forward pass of one row that also keeps the hidden state after every block
+        at the last position (ember internals, "ForwardModel trait",
+        ``forward_with_activations``, and "probing pipeline": ``activations[layer][d]``).
+        Returns ``(acts [layers, H], head output at the last position)``; the states are
+        the residual stream before the final norm."""
+        ids = self._check_ids(ids)
+        T = ids.shape[0]
+        positions = np.arange(start_pos, start_pos + T)
+        x = self.w["model.embed_tokens.weight"][ids].astype(self.dtype, copy=True)
+        acts = []
+        for li in range(self.cfg.layers):
+            x = self.layer_sequence(li, x, positions, cache)
+            acts.append(x[-1].copy())
+        if cache is not None:
+            cache.length = max(cache.length, start_pos + T)
+        return np.stack(acts), self.head(x[-1])
+
+    def sensitivity(self, ids) -> float:
+        """The encoder's sequence score ("PII-Tracer serving/reference_forward.py",
+        ``forward``, sensitivity head): the final-normed hidden states averaged over the
+        row's tokens, then ``. sensitivity_head.weight + sensitivity_head.bias``."""
+        ids = self._check_ids(ids)
+        positions = np.arange(ids.shape[0])
+        x = self.w["model.embed_tokens.weight"][ids].astype(self.dtype, copy=True)
+        for li in range(self.cfg.layers):
+            x = self.layer_sequence(li, x, positions, None)
+        h = rmsnorm(x, self.w["model.norm.weight"], self.cfg.rms_eps)
+        s = h.mean(0) @ self.w["sensitivity_head.weight"].T + self.w["sensitivity_head.bias"]
+        return float(s[0])
+
     def encode(self, ids) -> np.ndarray:
         """Bidirectional encoder over a batch ``[B, T]`` -> per-token head ``[B, T, C]``."""
         ids = np.atleast_2d(ids)

@@ -234,3 +234,60 @@ def test_matches_hf_qwen3_qk_norm_bidirectional_with_token_head():
         st = _hf_state(ck)
         ref = (h @ st["token_cls_head.weight"].T + st["token_cls_head.bias"]).numpy()
     assert _rel(m.encode(ids[None])[0], ref) < 1e-6
+
+
+def test_activations_match_hf_hidden_states():
+    """forward_with_activations (ember internals, "ForwardModel trait"): the hidden state
+    after every block at the last position. HuggingFace's hidden_states[l + 1] is block
+    l's output for every block but the last, whose entry carries the final norm."""
+    from transformers import Qwen2Config, Qwen2ForCausalLM
+    c = W.shrink_model(QWEN_SMALL, layers=3)
+    hc = Qwen2Config(vocab_size=c.vocab, hidden_size=c.hidden, intermediate_size=c.ffn,
+                     num_hidden_layers=c.layers, num_attention_heads=c.heads,
+                     num_key_value_heads=c.kv_heads, rms_norm_eps=c.rms_eps,
+                     tie_word_embeddings=True, rope_theta=c.rope_theta,
+                     max_position_embeddings=256, attn_implementation="eager")
+    m, ck = _model(c)
+    hf = _load(Qwen2ForCausalLM(hc).double(), ck)
+    ids = _ids(c, 10)
+    with torch.no_grad():
+        out = hf(torch.from_numpy(ids.astype(np.int64))[None], output_hidden_states=True)
+    hs = [h[0, -1].numpy() for h in out.hidden_states]
+    acts, logits = m.forward_with_activations(ids)
+    assert acts.shape == (c.layers, c.hidden)
+    for li in range(c.layers - 1):
+        assert _rel(acts[li], hs[li + 1]) < 1e-6
+    assert _rel(O.rmsnorm(acts[-1], m.w["model.norm.weight"], c.rms_eps), hs[-1]) < 1e-6
+    assert _rel(logits, out.logits[0, -1].numpy()) < 1e-6
+    assert np.array_equal(logits, m.forward_sequence(ids))      # the same forward pass
+
+
+def test_sensitivity_matches_mean_pooled_hf_hidden_state():
+    """The encoder's mean-pooled sequence score ("PII-Tracer serving/reference_forward.py",
+    ``forward``): the final-normed states averaged over tokens, then the head."""
+    from transformers import Qwen3Config, Qwen3Model
+    c = W.shrink_model(ENCODER_SMALL, sens_head=True)
+    hc = Qwen3Config(vocab_size=c.vocab, hidden_size=c.hidden, intermediate_size=c.ffn,
+                     num_hidden_layers=c.layers, num_attention_heads=c.heads,
+                     num_key_value_heads=c.kv_heads, head_dim=c.head_dim, rms_norm_eps=c.rms_eps,
+                     rope_theta=c.rope_theta, attn_implementation="eager")
+    m, ck = _model(c)
+    assert "sensitivity_head.weight" in ck and ck["sensitivity_head.weight"][1].shape == (1, c.hidden)
+    sd = {k[len("model."):]: v for k, v in _hf_state(ck).items() if k.startswith("model.")}
+    hf = Qwen3Model(hc).double().eval()
+    hf.load_state_dict(sd, strict=True)
+    ids = _ids(c, 13)
+    T = len(ids)
+    with torch.no_grad():
+        h = hf(torch.from_numpy(ids.astype(np.int64))[None],
+               attention_mask=torch.zeros(1, 1, T, T, dtype=torch.float64)).last_hidden_state[0]
+        st = _hf_state(ck)
+        ref = float((h.mean(0) @ st["sensitivity_head.weight"].T + st["sensitivity_head.bias"])[0])
+    got = m.sensitivity(ids)
+    assert abs(got - ref) <= 1e-9 * max(1.0, abs(ref))
+    # pooling the states before the final norm gives a different number
+    x = m.w["model.embed_tokens.weight"][ids].astype(np.float64)
+    for li in range(c.layers):
+        x = m.layer_sequence(li, x, np.arange(T), None)
+    pre = float((x.mean(0) @ m.w["sensitivity_head.weight"].T + m.w["sensitivity_head.bias"])[0])
+    assert abs(pre - ref) > 1e-6

@@ -49,6 +49,9 @@ class ModelConfig:
     causal: bool = True
     head: str = "tied_lm"          # "tied_lm" (logits = E . h) or "cls" (W h + b)
     n_classes: int = 0
+    # the encoder's mean-pooled sequence score ("PII-Tracer serving/reference_forward.py",
+    # ``forward``: sensitivity_head [1, hidden] + bias [1]); off unless asked for
+    sens_head: bool = False
     weight_dtype: str = "bf16"     # "f32", "bf16" (every tensor) or "q8_0" (matrices; 1-D f32)
 
     @property

@@ -9,7 +9,8 @@ Recipe (all draws from ``numpy.random.default_rng(seed)``, PCG64):
 * weights: seed = the workload's ``weight_seed``; tensors are drawn in a fixed order --
   embedding, then per layer the order in which ember's NumPy reference reads them
   (q, q-bias, k, k-bias, v, v-bias, o, gate, up, down), then the classification head
-  weight and bias; each draw is ``standard_normal(shape, float32) * 0.02``.
+  weight and bias, then (when configured) the sensitivity head's weight and bias; each
+  draw is ``standard_normal(shape, float32) * 0.02``.
 * every RMSNorm weight (input, post-attention, final, per-head q/k) is 1.0 and is not
   drawn, as the Falcon-H1 Rust reference's ``synthetic_weights`` fills norm weights with 1.
 * bf16 models: each f32 draw is rounded once to bf16 (round to nearest, ties to even);
@@ -80,6 +81,9 @@ def tensor_shapes(m: ModelConfig) -> "OrderedDict[str, Tuple[int, ...]]":
     if m.head == "cls":
         s["token_cls_head.weight"] = (m.n_classes, m.hidden)
         s["token_cls_head.bias"] = (m.n_classes,)
+    if m.sens_head:
+        s["sensitivity_head.weight"] = (1, m.hidden)
+        s["sensitivity_head.bias"] = (1,)
     return s
 
 
