@@ -26,7 +26,8 @@ HEAD_TIED_LM, HEAD_CLS = 0, 1
 EXPORTED = ["ember_workspace_bytes", "ember_kv_cache_bytes", "ember_load_weights",
             "ember_cache_bind", "ember_prefill", "ember_decode_step", "ember_logits",
             "ember_sync", "ember_cache_free", "ember_free", "ember_last_error",
-            "ember_rope_table", "ember_time_kernel", "ember_set_sampler", "ember_sample"]
+            "ember_rope_table", "ember_time_kernel", "ember_set_sampler", "ember_sample",
+            "ember_forward_with_activations", "ember_sensitivity"]
 K_LM_HEAD, K_QKV, K_ATTN, K_O, K_GATE_UP, K_DOWN, K_LAYER, K_SAMPLE = range(8)
 
 
@@ -45,7 +46,8 @@ class EmberConfig(ctypes.Structure):
                 ("head_kind", ctypes.c_int32), ("n_classes", ctypes.c_int32),
                 ("weight_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("precision", ctypes.c_int32), ("max_batch", ctypes.c_int32),
-                ("max_seq", ctypes.c_int32), ("max_tokens", ctypes.c_int32)]
+                ("max_seq", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("sens_head", ctypes.c_int32)]
 
 
 class EmberTensor(ctypes.Structure):
@@ -97,6 +99,9 @@ def _load():
                                              P, ctypes.POINTER(ctypes.c_float)]),
         "ember_set_sampler": (ctypes.c_int, [P, ctypes.POINTER(EmberSampler)]),
         "ember_sample": (ctypes.c_int, [P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, P, P]),
+        "ember_forward_with_activations": (ctypes.c_int, [P, P, P, ctypes.c_int32, ctypes.c_int32,
+                                                          ctypes.c_int32, P, P, P]),
+        "ember_sensitivity": (ctypes.c_int, [P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -145,6 +150,19 @@ def ember_prefill(model: int, cache: int, h_ids: np.ndarray, start_pos: int,
         raise ValueError("ids must be [batch, n_tokens]")
     _check(LIB.ember_prefill(model, cache, ids.ctypes.data, ids.shape[0], ids.shape[1],
                              start_pos, d_all_logits, d_next, stream))
+
+
+def ember_forward_with_activations(model: int, cache: int, h_ids: np.ndarray, start_pos: int,
+                                   d_acts: int, d_next: int, stream: int):
+    ids = np.ascontiguousarray(h_ids, dtype=np.int32)
+    if ids.ndim != 2:
+        raise ValueError("ids must be [batch, n_tokens]")
+    _check(LIB.ember_forward_with_activations(model, cache, ids.ctypes.data, ids.shape[0],
+                                              ids.shape[1], start_pos, d_acts, d_next, stream))
+
+
+def ember_sensitivity(model: int, d_out: int, stream: int):
+    _check(LIB.ember_sensitivity(model, d_out, stream))
 
 
 def ember_decode_step(model: int, cache: int, d_ids: int, batch: int, pos: int, d_next: int,
@@ -224,6 +242,7 @@ def make_config(model, *, precision: int = EXACT, kv_dtype: Optional[int] = None
     c.precision = precision
     c.max_batch, c.max_seq = max_batch, max_seq
     c.max_tokens = max_tokens if max_tokens is not None else max(max_batch, 1)
+    c.sens_head = int(getattr(model, "sens_head", False))
     return c
 
 
@@ -296,6 +315,27 @@ class Engine:
         ember_prefill(self.model, self.cache, ids, start_pos, out.data_ptr() if out is not None else 0,
                       next_ids.data_ptr(), self.sp)
         return next_ids, out
+
+    def forward_with_activations(self, ids: np.ndarray, start_pos: int = 0, next_ids=None):
+        """Prefill that also returns the hidden state after every block at each row's last
+        position: (activations [B, layers, H] f32, next ids)."""
+        torch = self.torch
+        ids = np.atleast_2d(np.asarray(ids, dtype=np.int32))
+        B = ids.shape[0]
+        acts = torch.empty((B, self.cfg.layers, self.cfg.hidden), dtype=torch.float32,
+                           device=self.device)
+        if next_ids is None:
+            shape = (B, ids.shape[1]) if self.cfg.head_kind == HEAD_CLS else (B,)
+            next_ids = torch.empty(shape, dtype=torch.int32, device=self.device)
+        ember_forward_with_activations(self.model, self.cache, ids, start_pos, acts.data_ptr(),
+                                       next_ids.data_ptr(), self.sp)
+        return acts, next_ids
+
+    def sensitivity(self, rows: int):
+        """The mean-pooled sequence scores of the last prefill, [rows] f32."""
+        out = self.torch.empty(rows, dtype=self.torch.float32, device=self.device)
+        ember_sensitivity(self.model, out.data_ptr(), self.sp)
+        return out
 
     def decode_step(self, d_ids, pos: int, d_next=None):
         if d_next is None:

@@ -65,7 +65,8 @@ struct Plan {
   std::vector<LayerOff> layer;
   // activations
   size_t ids, pos, rope_cur, next, flags, x, xb, pa_hi, pa_lo, pb_hi, pb_lo, qkv, q, att, act, part,
-      logits, argpart, splitk, kvpack, samp_state, samp_tiles, embed_s, q8_scratch;
+      logits, argpart, splitk, kvpack, samp_state, samp_tiles, embed_s, q8_scratch, sens_w,
+      sens_b, sens_acc, sens_out;
   size_t splitk_elems, kvpack_elems;
   size_t total;
   int Mx, qkv_n, ka, nsplit_max, argparts;
@@ -100,6 +101,8 @@ ember_status validate_config(const ember_config* c) {
     return fail(EMBER_E_CONFIG, "n_classes must be in 1..64");
   if (c->head_kind == EMBER_HEAD_TIED_LM && !c->causal)
     return fail(EMBER_E_CONFIG, "a tied LM head needs a causal model");
+  if (c->sens_head != 0 && (c->sens_head != 1 || c->head_kind != EMBER_HEAD_CLS))
+    return fail(EMBER_E_CONFIG, "the sequence-score head is a 0/1 flag of classification models");
   if (c->ffn % kGuBlock != 0) return fail(EMBER_E_CONFIG, "ffn must be a multiple of %d", kGuBlock);
   const int K8 = c->weight_dtype == EMBER_Q8_0 ? kQ8Block : (c->weight_dtype == EMBER_BF16 ? 8 : 4);
   if (c->hidden % K8 || c->ffn % K8 || (c->heads * hd) % K8)
@@ -149,6 +152,10 @@ Plan make_plan(const ember_config& c) {
   p.fnorm = take((size_t)H * 4);
   p.cls_w = c.head_kind == EMBER_HEAD_CLS ? take((size_t)c.n_classes * H * ws) : 0;
   p.cls_b = c.head_kind == EMBER_HEAD_CLS ? take((size_t)c.n_classes * 4) : 0;
+  p.sens_w = c.sens_head ? take((size_t)H * 4) : 0;
+  p.sens_b = c.sens_head ? take(4) : 0;
+  p.sens_acc = c.sens_head ? take((size_t)c.max_batch * H * 4) : 0;
+  p.sens_out = c.sens_head ? take((size_t)c.max_batch * 4) : 0;
   p.cos_t = take((size_t)c.max_seq * (HD / 2) * 4);
   p.sin_t = take((size_t)c.max_seq * (HD / 2) * 4);
 
@@ -244,6 +251,7 @@ struct ember_model {
   int wk;                   // WeightKind of the matrices
   bool mfma;                // multi-token passes on bf16 MFMA (see uses_mfma)
   int has_logits_rows;      // rows in the logits buffer, 0 before any forward
+  int sens_rows = 0;        // rows of sequence scores of the last prefill
   int last_decode_batch = 0;
   struct { int M, rows, tpr, b0, start; } last_pass = {0, 0, 0, 0, 0};
   // decode graph cache
@@ -699,7 +707,8 @@ ember_status ember_load_weights(const ember_config* cfg, const ember_tensor* ten
   const int H = c.hidden, V = c.vocab, NH = c.heads, NKV = c.kv_heads, HD = c.head_dim, FF = c.ffn;
   struct LT { const ember_tensor *ln1, *q, *k, *v, *qb, *kb, *vb, *o, *qn, *kn, *ln2, *g, *u, *d; };
   std::vector<LT> lt(c.layers);
-  const ember_tensor *emb = nullptr, *fn = nullptr, *clsw = nullptr, *clsb = nullptr;
+  const ember_tensor *emb = nullptr, *fn = nullptr, *clsw = nullptr, *clsb = nullptr,
+                    *sensw = nullptr, *sensb = nullptr;
 #define NEED(n, shape, dst) do { ember_status s_ = need(n, shape, dst); if (s_ != EMBER_OK) return s_; } while (0)
   NEED("model.embed_tokens.weight", (std::vector<int64_t>{V, H}), &emb);
   for (int l = 0; l < c.layers; ++l) {
@@ -728,6 +737,10 @@ ember_status ember_load_weights(const ember_config* cfg, const ember_tensor* ten
   if (c.head_kind == EMBER_HEAD_CLS) {
     NEED("token_cls_head.weight", (std::vector<int64_t>{c.n_classes, H}), &clsw);
     NEED("token_cls_head.bias", (std::vector<int64_t>{c.n_classes}), &clsb);
+  }
+  if (c.sens_head) {
+    NEED("sensitivity_head.weight", (std::vector<int64_t>{1, H}), &sensw);
+    NEED("sensitivity_head.bias", (std::vector<int64_t>{1}), &sensb);
   }
 #undef NEED
 
@@ -790,6 +803,10 @@ ember_status ember_load_weights(const ember_config* cfg, const ember_tensor* ten
     HIP_TRY(copy(plan.cls_w, clsw, (size_t)c.n_classes * H * es));
     launch_widen(clsb->data, bf, (float*)(ws + plan.cls_b), c.n_classes, st);
   }
+  if (sensw) {
+    launch_widen(sensw->data, bf, (float*)(ws + plan.sens_w), H, st);
+    launch_widen(sensb->data, bf, (float*)(ws + plan.sens_b), 1, st);
+  }
   {
     std::vector<float> cs((size_t)c.max_seq * (HD / 2)), sn(cs.size());
     rope_host(c, c.max_seq, cs.data(), sn.data());
@@ -830,10 +847,13 @@ ember_status ember_cache_bind(ember_model* model, void* d_kv, size_t kv_bytes, e
   return EMBER_OK;
 }
 
-ember_status ember_prefill(ember_model* md, ember_cache* cache, const int32_t* h_ids,
-                           int32_t batch, int32_t n_tokens, int32_t start_pos,
-                           float* d_all_logits, int32_t* d_next, void* stream) {
-  g_last_error.clear();
+namespace {
+
+// The prefill of ember_prefill, optionally keeping each block's output at every row's
+// last position in d_acts [batch][layers][hidden].
+ember_status prefill_impl(ember_model* md, ember_cache* cache, const int32_t* h_ids,
+                          int32_t batch, int32_t n_tokens, int32_t start_pos,
+                          float* d_all_logits, int32_t* d_next, float* d_acts, void* stream) {
   if (!md || !cache || !h_ids) return fail(EMBER_E_ARG, "NULL argument");
   if (cache->model != md) return fail(EMBER_E_ARG, "cache bound to another model");
   const ember_config& c = md->cfg;
@@ -848,6 +868,9 @@ ember_status ember_prefill(ember_model* md, ember_cache* cache, const int32_t* h
                 cache->filled);
   if (!c.causal && start_pos != 0)
     return fail(EMBER_E_ARG, "a bidirectional model takes whole sequences (start_pos 0)");
+  if (!c.causal && n_tokens > (c.max_tokens > c.max_batch ? c.max_tokens : c.max_batch))
+    return fail(EMBER_E_CAPACITY, "a bidirectional row of %d tokens must fit one pass of %d",
+                n_tokens, c.max_tokens > c.max_batch ? c.max_tokens : c.max_batch);
   for (long long i = 0; i < (long long)batch * n_tokens; ++i)
     if (h_ids[i] < 0 || h_ids[i] >= c.vocab)
       return fail(EMBER_E_TOKEN, "token %d outside vocabulary", h_ids[i]);
@@ -883,9 +906,27 @@ ember_status ember_prefill(ember_model* md, ember_cache* cache, const int32_t* h
       ps.d_pos = nullptr;
       ps.path = M == 1 ? PATH_GEMV : (md->mfma ? PATH_MFMA : PATH_F32W);
       ps.attn = ATTN_FLASH;
-      for (int l = 0; l < c.layers; ++l) run_layer(cx, l, ps);
-      md->last_pass = {M, rows, tpr, b0, start_pos + t0};
       const bool last_chunk = t0 + tpr == T;
+      for (int l = 0; l < c.layers; ++l) {
+        run_layer(cx, l, ps);
+        if (d_acts && last_chunk)
+          launch_copy_rows(md->at<float>(p.x), rows, tpr, tpr - 1, c.hidden,
+                           d_acts + ((size_t)b0 * c.layers + l) * c.hidden,
+                           (long long)c.layers * c.hidden, st);
+      }
+      md->last_pass = {M, rows, tpr, b0, start_pos + t0};
+      if (c.sens_head) {
+        // the sequence score: every token's final-normed state summed per row (across the
+        // passes of a row), then mean and head at the row's last chunk
+        float* hn = md->at<float>(p.xb);
+        launch_rmsnorm(md->at<float>(p.x), md->at<float>(p.fnorm), c.rms_eps, M, c.hidden, 1, 0,
+                       hn, nullptr, nullptr, 0, st);
+        float* acc = md->at<float>(p.sens_acc) + (size_t)b0 * c.hidden;
+        launch_pool_accum(hn, rows, tpr, c.hidden, acc, t0 == 0, st);
+        if (last_chunk)
+          launch_pool_head(acc, rows, c.hidden, T, md->at<float>(p.sens_w), md->at<float>(p.sens_b),
+                           md->at<float>(p.sens_out) + b0, st);
+      }
       if (c.head_kind == EMBER_HEAD_TIED_LM) {
         if (d_all_logits) {
           for (int r = 0; r < rows; ++r)
@@ -910,6 +951,37 @@ ember_status ember_prefill(ember_model* md, ember_cache* cache, const int32_t* h
   }
   if (start_pos + T > cache->filled) cache->filled = start_pos + T;
   md->has_logits_rows = batch;
+  md->sens_rows = c.sens_head ? batch : 0;
+  return EMBER_OK;
+}
+
+}  // namespace
+
+ember_status ember_prefill(ember_model* md, ember_cache* cache, const int32_t* h_ids,
+                           int32_t batch, int32_t n_tokens, int32_t start_pos,
+                           float* d_all_logits, int32_t* d_next, void* stream) {
+  g_last_error.clear();
+  return prefill_impl(md, cache, h_ids, batch, n_tokens, start_pos, d_all_logits, d_next,
+                      nullptr, stream);
+}
+
+ember_status ember_forward_with_activations(ember_model* md, ember_cache* cache,
+                                            const int32_t* h_ids, int32_t batch,
+                                            int32_t n_tokens, int32_t start_pos, float* d_acts,
+                                            int32_t* d_next, void* stream) {
+  g_last_error.clear();
+  if (!d_acts) return fail(EMBER_E_ARG, "NULL activations buffer");
+  return prefill_impl(md, cache, h_ids, batch, n_tokens, start_pos, nullptr, d_next, d_acts,
+                      stream);
+}
+
+ember_status ember_sensitivity(ember_model* md, float* d_out, void* stream) {
+  g_last_error.clear();
+  if (!md || !d_out) return fail(EMBER_E_ARG, "NULL argument");
+  if (!md->cfg.sens_head) return fail(EMBER_E_STATE, "the model has no sequence-score head");
+  if (md->sens_rows <= 0) return fail(EMBER_E_STATE, "no prefill has run yet");
+  HIP_TRY(hipMemcpyAsync(d_out, md->at<float>(md->plan.sens_out), (size_t)md->sens_rows * 4,
+                         hipMemcpyDeviceToDevice, (hipStream_t)stream));
   return EMBER_OK;
 }
 

@@ -151,6 +151,15 @@ struct SampleArgs {
 void launch_sample(const SampleArgs& a, hipStream_t st);
 
 void launch_fill_i32(int* p, int n, int v, hipStream_t st);
+// dst[r * dst_stride + i] = src[(r * row_step + row_off) * H + i], r < R, i < H.
+void launch_copy_rows(const float* src, int R, int row_step, int row_off, int H, float* dst,
+                      long long dst_stride, hipStream_t st);
+// Mean-pooled sequence score: acc[r][d] (= if first, else +=) sum over the row's tpr tokens
+// of h[r * tpr + t][d]; then out[r] = sum_d (acc[r][d] / T) w[d] + b[0].
+void launch_pool_accum(const float* h, int R, int tpr, int H, float* acc, bool first,
+                       hipStream_t st);
+void launch_pool_head(const float* acc, int R, int H, int T, const float* w, const float* b,
+                      float* out, hipStream_t st);
 // dst[i] = widen(src[i]) for i < n (bf16 or f32 source).
 void launch_widen(const void* src, bool bf16, float* dst, long long n, hipStream_t st);
 

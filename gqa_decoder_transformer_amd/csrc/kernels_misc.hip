@@ -377,6 +377,59 @@ void launch_step_begin(const StepBeginArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_step_begin, dim3(a.R), dim3(256), 0, st, a);
 }
 
+__global__ void __launch_bounds__(256) k_copy_rows(const float* src, int row_step, int row_off, int H,
+                                                   float* dst, long long dst_stride) {
+  const int r = blockIdx.x;
+  const float* s = src + ((size_t)r * row_step + row_off) * H;
+  float* d = dst + (size_t)r * dst_stride;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) d[i] = s[i];
+}
+
+void launch_copy_rows(const float* src, int R, int row_step, int row_off, int H, float* dst,
+                      long long dst_stride, hipStream_t st) {
+  if (R <= 0) return;
+  hipLaunchKernelGGL(k_copy_rows, dim3(R), dim3(256), 0, st, src, row_step, row_off, H, dst,
+                     dst_stride);
+}
+
+// ------------------------------------------------------------------ mean-pooled head
+// The sequence score of "PII-Tracer serving/reference_forward.py" (forward, sensitivity
+// head): the final-normed states summed over the row's tokens (column sums, token order,
+// accumulated across passes of one row), then mean and dot product.
+__global__ void __launch_bounds__(256) k_pool_accum(const float* h, int tpr, int H, float* acc,
+                                                    int first) {
+  const int r = blockIdx.y;
+  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= H) return;
+  const float* hr = h + (size_t)r * tpr * H + d;
+  float s = first ? 0.f : acc[(size_t)r * H + d];
+  for (int t = 0; t < tpr; ++t) s += hr[(size_t)t * H];
+  acc[(size_t)r * H + d] = s;
+}
+
+void launch_pool_accum(const float* h, int R, int tpr, int H, float* acc, bool first,
+                       hipStream_t st) {
+  if (R <= 0 || tpr <= 0) return;
+  hipLaunchKernelGGL(k_pool_accum, dim3((H + 255) / 256, R), dim3(256), 0, st, h, tpr, H, acc,
+                     (int)first);
+}
+
+__global__ void __launch_bounds__(256) k_pool_head(const float* acc, int H, int T, const float* w,
+                                                   const float* b, float* out) {
+  __shared__ float red[16];
+  const int r = blockIdx.x;
+  float s = 0.f;
+  for (int d = threadIdx.x; d < H; d += blockDim.x) s += (acc[(size_t)r * H + d] / (float)T) * w[d];
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) out[r] = s + b[0];
+}
+
+void launch_pool_head(const float* acc, int R, int H, int T, const float* w, const float* b,
+                      float* out, hipStream_t st) {
+  if (R <= 0) return;
+  hipLaunchKernelGGL(k_pool_head, dim3(R), dim3(256), 0, st, acc, H, T, w, b, out);
+}
+
 __global__ void k_fill_i32(int* p, int n, int v) {
   const int i = threadIdx.x + blockIdx.x * blockDim.x;
   if (i < n) p[i] = v;

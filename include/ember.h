@@ -96,6 +96,10 @@ typedef struct ember_config {
   int32_t max_batch;           /* rows per call */
   int32_t max_seq;             /* positions per row: capacity of the cache and RoPE table */
   int32_t max_tokens;          /* tokens processed per prefill pass (>= max_batch) */
+  int32_t sens_head;           /* 0/1, classification-head models only: the mean-pooled
+                                * sequence score ("PII-Tracer serving/reference_forward.py",
+                                * forward: tensors sensitivity_head.weight [1, hidden] and
+                                * .bias [1]); read with ember_sensitivity after a prefill */
 } ember_config;
 
 /* A named weight tensor, HuggingFace naming ("model.embed_tokens.weight",
@@ -147,11 +151,29 @@ ember_status ember_cache_bind(ember_model* model, void* d_kv, size_t kv_bytes,
  *   d_all_logits  f32 [batch, n_tokens, out_dim]: head output at every position;
  *   d_next        int32 [batch] (decoder: argmax of the last position, lowest index on
  *                 ties) or [batch, n_tokens] (classification head: argmax per token).
- * For a bidirectional config, start_pos must be 0 and every token attends to every
- * token of its row. */
+ * For a bidirectional config, start_pos must be 0, every token attends to every token of
+ * its row, and a row must fit one pass (n_tokens <= max_tokens, else EMBER_E_CAPACITY). */
 ember_status ember_prefill(ember_model* model, ember_cache* cache, const int32_t* h_ids,
                            int32_t batch, int32_t n_tokens, int32_t start_pos,
                            float* d_all_logits, int32_t* d_next, void* stream);
+
+/* ember_prefill that also writes the hidden state after every block at each row's last
+ * position ("ember internals" page, section "ForwardModel trait",
+ * forward_with_activations; section "probing pipeline": activations[layer][d]) into
+ * d_acts, device f32 [batch][layers][hidden]: the residual stream before the final norm.
+ * The head output at the last position is kept for ember_logits as after ember_prefill;
+ * d_next as there (NULL to skip). Same errors as ember_prefill, and EMBER_E_ARG for a
+ * NULL d_acts. */
+ember_status ember_forward_with_activations(ember_model* model, ember_cache* cache,
+                                            const int32_t* h_ids, int32_t batch,
+                                            int32_t n_tokens, int32_t start_pos, float* d_acts,
+                                            int32_t* d_next, void* stream);
+
+/* The mean-pooled sequence scores of the most recent prefill, [batch] f32 into d_out
+ * (device): the final-normed hidden states averaged over each row's n_tokens tokens, then
+ * . sensitivity_head.weight + sensitivity_head.bias. EMBER_E_STATE without the head or
+ * before any prefill. */
+ember_status ember_sensitivity(ember_model* model, float* d_out, void* stream);
 
 /* One cached greedy step for `batch` rows at position `pos` (causal configs only):
  * reads the ids d_ids [batch] int32 (device), writes their K/V at `pos`, attends over
