@@ -27,7 +27,8 @@ EXPORTED = ["ember_workspace_bytes", "ember_kv_cache_bytes", "ember_load_weights
             "ember_cache_bind", "ember_prefill", "ember_decode_step", "ember_logits",
             "ember_sync", "ember_cache_free", "ember_free", "ember_last_error",
             "ember_rope_table", "ember_time_kernel", "ember_set_sampler", "ember_sample",
-            "ember_forward_with_activations", "ember_sensitivity"]
+            "ember_forward_with_activations", "ember_sensitivity", "ember_prefill_rows",
+            "ember_decode_step_rows"]
 K_LM_HEAD, K_QKV, K_ATTN, K_O, K_GATE_UP, K_DOWN, K_LAYER, K_SAMPLE = range(8)
 
 
@@ -102,6 +103,8 @@ def _load():
         "ember_forward_with_activations": (ctypes.c_int, [P, P, P, ctypes.c_int32, ctypes.c_int32,
                                                           ctypes.c_int32, P, P, P]),
         "ember_sensitivity": (ctypes.c_int, [P, P, P]),
+        "ember_prefill_rows": (ctypes.c_int, [P, P, P, P, P, ctypes.c_int32, P, P]),
+        "ember_decode_step_rows": (ctypes.c_int, [P, P, P, ctypes.c_int32, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -159,6 +162,25 @@ def ember_forward_with_activations(model: int, cache: int, h_ids: np.ndarray, st
         raise ValueError("ids must be [batch, n_tokens]")
     _check(LIB.ember_forward_with_activations(model, cache, ids.ctypes.data, ids.shape[0],
                                               ids.shape[1], start_pos, d_acts, d_next, stream))
+
+
+def ember_prefill_rows(model: int, cache: int, rows, starts, d_next: int, stream: int):
+    """rows: a list of 1-D int32 id arrays (one per batch row); starts: their positions."""
+    ids = np.ascontiguousarray(np.concatenate([np.asarray(r, np.int32) for r in rows]), np.int32)
+    lens = np.ascontiguousarray([len(r) for r in rows], np.int32)
+    st = np.ascontiguousarray(starts, np.int32)
+    if st.shape != lens.shape:
+        raise ValueError("one start position per row")
+    _check(LIB.ember_prefill_rows(model, cache, ids.ctypes.data, lens.ctypes.data, st.ctypes.data,
+                                  len(rows), d_next, stream))
+
+
+def ember_decode_step_rows(model: int, cache: int, d_ids: int, batch: int, positions,
+                           d_next: int, stream: int):
+    pos = np.ascontiguousarray(positions, np.int32)
+    if pos.shape != (batch,):
+        raise ValueError("one position per row")
+    _check(LIB.ember_decode_step_rows(model, cache, d_ids, batch, pos.ctypes.data, d_next, stream))
 
 
 def ember_sensitivity(model: int, d_out: int, stream: int):
@@ -330,6 +352,23 @@ class Engine:
         ember_forward_with_activations(self.model, self.cache, ids, start_pos, acts.data_ptr(),
                                        next_ids.data_ptr(), self.sp)
         return acts, next_ids
+
+    def prefill_rows(self, rows, starts=None, next_ids=None):
+        """Ragged prefill: rows is a list of 1-D id arrays, starts their start positions."""
+        torch = self.torch
+        starts = [0] * len(rows) if starts is None else list(starts)
+        if next_ids is None:
+            n = sum(len(r) for r in rows) if self.cfg.head_kind == HEAD_CLS else len(rows)
+            next_ids = torch.empty(n, dtype=torch.int32, device=self.device)
+        ember_prefill_rows(self.model, self.cache, rows, starts, next_ids.data_ptr(), self.sp)
+        return next_ids
+
+    def decode_step_rows(self, d_ids, positions, d_next=None):
+        if d_next is None:
+            d_next = d_ids
+        ember_decode_step_rows(self.model, self.cache, d_ids.data_ptr(), d_ids.numel(), positions,
+                               d_next.data_ptr(), self.sp)
+        return d_next
 
     def sensitivity(self, rows: int):
         """The mean-pooled sequence scores of the last prefill, [rows] f32."""

@@ -64,7 +64,7 @@ struct Plan {
   size_t embed, fnorm, cls_w, cls_b, cos_t, sin_t;
   std::vector<LayerOff> layer;
   // activations
-  size_t ids, pos, rope_cur, next, flags, x, xb, pa_hi, pa_lo, pb_hi, pb_lo, qkv, q, att, act, part,
+  size_t ids, pos, row_pos, rope_cur, next, flags, x, xb, pa_hi, pa_lo, pb_hi, pb_lo, qkv, q, att, act, part,
       logits, argpart, splitk, kvpack, samp_state, samp_tiles, embed_s, q8_scratch, sens_w,
       sens_b, sens_acc, sens_out;
   size_t splitk_elems, kvpack_elems;
@@ -167,7 +167,8 @@ Plan make_plan(const ember_config& c) {
   p.argparts = gemv_num_blocks(c.vocab, GEMV_LOGITS, H, weight_kind(c.weight_dtype));
   p.ids = take((size_t)Mx * 4);
   p.pos = take(4);
-  p.rope_cur = take((size_t)c.head_dim * 4);
+  p.row_pos = take((size_t)c.max_batch * 4);
+  p.rope_cur = take((size_t)c.max_batch * c.head_dim * 4);
   p.next = take((size_t)Mx * 4);
   p.flags = take(kNumFlags * 4);
   p.x = take((size_t)Mx * H * 4);
@@ -271,7 +272,7 @@ struct ember_cache {
   ember_model* model;
   char* kv;
   size_t layer_bytes;
-  int filled;               // positions 0..filled-1 hold K/V (all rows share positions)
+  std::vector<int> filled;  // per batch row: positions 0..filled[r]-1 hold K/V
 };
 
 namespace {
@@ -316,7 +317,7 @@ void launch_draw(const Ctx& cx, const float* logits, int R, long long ld, int32_
   a.temperature = md->samp.temperature; a.top_k = md->samp.top_k; a.top_p = md->samp.top_p;
   a.uniform = md->samp.d_uniform; a.u_rows = md->samp.n_pos; a.u_ld = md->samp.ld;
   a.col0 = u_col0; a.pos = u_pos < 0 ? 0 : u_pos;
-  a.d_pos = u_pos < 0 ? md->at<int>(md->plan.pos) : nullptr;
+  a.d_pos = u_pos < 0 ? md->at<int>(md->plan.row_pos) : nullptr;
   a.next = next; a.flags = md->at<int>(md->plan.flags);
   a.state = md->at<SampleState>(md->plan.samp_state);
   a.tiles = md->at<float>(md->plan.samp_tiles);
@@ -346,7 +347,7 @@ enum Attn { ATTN_FLASH, ATTN_DECODE };
 struct Pass {
   int M;             // tokens in the pass = rows * tpr
   int rows, tpr, b0, start;
-  const int* d_pos;  // decode: position from device
+  const int* d_pos;  // decode: each row's position, from device [rows]
   Path path;
   Attn attn;
 };
@@ -621,7 +622,7 @@ void decode_body(const Ctx& cx, int B, int32_t* next, int only_layer = -1) {
   const ember_config& c = md->cfg;
   const Plan& p = md->plan;
   Pass ps{};
-  ps.M = B; ps.rows = B; ps.tpr = 1; ps.b0 = 0; ps.start = 0; ps.d_pos = md->at<int>(p.pos);
+  ps.M = B; ps.rows = B; ps.tpr = 1; ps.b0 = 0; ps.start = 0; ps.d_pos = md->at<int>(p.row_pos);
   ps.path = B == 1 ? PATH_GEMV : (md->mfma ? PATH_MFMA : PATH_F32W);
   ps.attn = ATTN_DECODE;
   for (int l = 0; l < c.layers; ++l)
@@ -842,7 +843,7 @@ ember_status ember_cache_bind(ember_model* model, void* d_kv, size_t kv_bytes, e
   c->model = model;
   c->kv = (char*)d_kv;
   c->layer_bytes = need / (2 * (size_t)model->cfg.layers);
-  c->filled = 0;
+  c->filled.assign((size_t)model->cfg.max_batch, 0);
   *out = c;
   return EMBER_OK;
 }
@@ -853,19 +854,21 @@ namespace {
 // last position in d_acts [batch][layers][hidden].
 ember_status prefill_impl(ember_model* md, ember_cache* cache, const int32_t* h_ids,
                           int32_t batch, int32_t n_tokens, int32_t start_pos,
-                          float* d_all_logits, int32_t* d_next, float* d_acts, void* stream) {
+                          float* d_all_logits, int32_t* d_next, float* d_acts, void* stream,
+                          int row0 = 0) {
   if (!md || !cache || !h_ids) return fail(EMBER_E_ARG, "NULL argument");
   if (cache->model != md) return fail(EMBER_E_ARG, "cache bound to another model");
   const ember_config& c = md->cfg;
   if (n_tokens <= 0) return fail(EMBER_E_ARG, "input_ids must not be empty");
-  if (batch <= 0 || batch > c.max_batch)
+  if (batch <= 0 || row0 < 0 || row0 + batch > c.max_batch)
     return fail(EMBER_E_CAPACITY, "batch %d outside 1..%d", batch, c.max_batch);
   if (start_pos < 0 || (long long)start_pos + n_tokens > c.max_seq)
     return fail(EMBER_E_CAPACITY, "positions [%d, %d) exceed max_seq %d", start_pos,
                 start_pos + n_tokens, c.max_seq);
-  if (start_pos > cache->filled)
-    return fail(EMBER_E_STATE, "start_pos %d leaves a gap after %d cached positions", start_pos,
-                cache->filled);
+  for (int r = row0; r < row0 + batch; ++r)
+    if (start_pos > cache->filled[r])
+      return fail(EMBER_E_STATE, "start_pos %d leaves a gap after %d cached positions of row %d",
+                  start_pos, cache->filled[r], r);
   if (!c.causal && start_pos != 0)
     return fail(EMBER_E_ARG, "a bidirectional model takes whole sequences (start_pos 0)");
   if (!c.causal && n_tokens > (c.max_tokens > c.max_batch ? c.max_tokens : c.max_batch))
@@ -887,15 +890,16 @@ ember_status prefill_impl(ember_model* md, ember_cache* cache, const int32_t* h_
   const int T = n_tokens;
   const int rows_per_pass = T <= p.Mx ? (p.Mx / T < batch ? p.Mx / T : batch) : 1;
   const int tok_chunk = T <= p.Mx ? T : p.Mx;
-  for (int b0 = 0; b0 < batch; b0 += rows_per_pass) {
-    const int rows = batch - b0 < rows_per_pass ? batch - b0 : rows_per_pass;
+  for (int bi = 0; bi < batch; bi += rows_per_pass) {
+    const int rows = batch - bi < rows_per_pass ? batch - bi : rows_per_pass;
+    const int b0 = row0 + bi;               // cache / state row of the pass's first row
     for (int t0 = 0; t0 < T; t0 += tok_chunk) {
       const int tpr = T - t0 < tok_chunk ? T - t0 : tok_chunk;
       const int M = rows * tpr;
       // stage ids of this pass (rows x tpr)
       std::vector<int32_t> ids((size_t)M);
       for (int r = 0; r < rows; ++r)
-        memcpy(&ids[(size_t)r * tpr], h_ids + (size_t)(b0 + r) * T + t0, (size_t)tpr * 4);
+        memcpy(&ids[(size_t)r * tpr], h_ids + (size_t)(bi + r) * T + t0, (size_t)tpr * 4);
       HIP_TRY(hipMemcpyAsync(md->at<int32_t>(p.ids), ids.data(), (size_t)M * 4,
                              hipMemcpyHostToDevice, st));
       launch_embed(md->at<int32_t>(p.ids), md->ws + p.embed, md->wk,
@@ -911,7 +915,7 @@ ember_status prefill_impl(ember_model* md, ember_cache* cache, const int32_t* h_
         run_layer(cx, l, ps);
         if (d_acts && last_chunk)
           launch_copy_rows(md->at<float>(p.x), rows, tpr, tpr - 1, c.hidden,
-                           d_acts + ((size_t)b0 * c.layers + l) * c.hidden,
+                           d_acts + ((size_t)bi * c.layers + l) * c.hidden,
                            (long long)c.layers * c.hidden, st);
       }
       md->last_pass = {M, rows, tpr, b0, start_pos + t0};
@@ -931,17 +935,17 @@ ember_status prefill_impl(ember_model* md, ember_cache* cache, const int32_t* h_
         if (d_all_logits) {
           for (int r = 0; r < rows; ++r)
             run_lm_head(cx, tpr, 1, r * tpr,
-                        d_all_logits + ((size_t)(b0 + r) * T + t0) * out_dim, out_dim, nullptr);
+                        d_all_logits + ((size_t)(bi + r) * T + t0) * out_dim, out_dim, nullptr);
         }
         if (last_chunk)
           run_lm_head(cx, rows, tpr, tpr - 1, md->at<float>(p.logits) + (size_t)b0 * out_dim,
-                      out_dim, d_next ? d_next + b0 : nullptr, b0, start_pos + T - 1);
+                      out_dim, d_next ? d_next + bi : nullptr, b0, start_pos + T - 1);
       } else {
         for (int r = 0; r < rows; ++r)
           if (d_all_logits || d_next)
             run_cls_head(cx, tpr, 1, r * tpr,
-                         d_all_logits ? d_all_logits + ((size_t)(b0 + r) * T + t0) * out_dim : nullptr,
-                         d_next ? d_next + (size_t)(b0 + r) * T + t0 : nullptr);
+                         d_all_logits ? d_all_logits + ((size_t)(bi + r) * T + t0) * out_dim : nullptr,
+                         d_next ? d_next + (size_t)(bi + r) * T + t0 : nullptr);
         if (last_chunk)
           run_cls_head(cx, rows, tpr, tpr - 1, md->at<float>(p.logits) + (size_t)b0 * out_dim,
                        nullptr);
@@ -949,9 +953,10 @@ ember_status prefill_impl(ember_model* md, ember_cache* cache, const int32_t* h_
       HIP_TRY(hipGetLastError());
     }
   }
-  if (start_pos + T > cache->filled) cache->filled = start_pos + T;
-  md->has_logits_rows = batch;
-  md->sens_rows = c.sens_head ? batch : 0;
+  for (int r = row0; r < row0 + batch; ++r)
+    if (start_pos + T > cache->filled[r]) cache->filled[r] = start_pos + T;
+  md->has_logits_rows = row0 + batch;
+  md->sens_rows = c.sens_head ? row0 + batch : 0;
   return EMBER_OK;
 }
 
@@ -975,6 +980,52 @@ ember_status ember_forward_with_activations(ember_model* md, ember_cache* cache,
                       stream);
 }
 
+ember_status ember_prefill_rows(ember_model* md, ember_cache* cache, const int32_t* h_ids,
+                                const int32_t* h_lengths, const int32_t* h_start,
+                                int32_t batch, int32_t* d_next, void* stream) {
+  g_last_error.clear();
+  if (!md || !cache || !h_ids || !h_lengths || !h_start) return fail(EMBER_E_ARG, "NULL argument");
+  if (cache->model != md) return fail(EMBER_E_ARG, "cache bound to another model");
+  const ember_config& c = md->cfg;
+  if (batch <= 0 || batch > c.max_batch)
+    return fail(EMBER_E_CAPACITY, "batch %d outside 1..%d", batch, c.max_batch);
+  // every row is checked before anything is enqueued
+  long long off = 0;
+  for (int r = 0; r < batch; ++r) {
+    const int n = h_lengths[r], s0 = h_start[r];
+    if (n <= 0) return fail(EMBER_E_ARG, "row %d: input_ids must not be empty", r);
+    if (s0 < 0 || (long long)s0 + n > c.max_seq)
+      return fail(EMBER_E_CAPACITY, "row %d: positions [%d, %d) exceed max_seq %d", r, s0, s0 + n,
+                  c.max_seq);
+    if (s0 > cache->filled[r])
+      return fail(EMBER_E_STATE, "row %d: start_pos %d leaves a gap after %d cached positions", r,
+                  s0, cache->filled[r]);
+    if (!c.causal && s0 != 0)
+      return fail(EMBER_E_ARG, "a bidirectional model takes whole sequences (start_pos 0)");
+    if (!c.causal && n > (c.max_tokens > c.max_batch ? c.max_tokens : c.max_batch))
+      return fail(EMBER_E_CAPACITY, "row %d: a bidirectional row must fit one pass", r);
+    for (int i = 0; i < n; ++i)
+      if (h_ids[off + i] < 0 || h_ids[off + i] >= c.vocab)
+        return fail(EMBER_E_TOKEN, "token %d outside vocabulary", h_ids[off + i]);
+    if (d_next && c.head_kind == EMBER_HEAD_TIED_LM) {
+      const ember_status s = check_draws(md, r + 1, (long long)s0 + n - 1);
+      if (s != EMBER_OK) return s;
+    }
+    off += n;
+  }
+  const int per_row = c.head_kind == EMBER_HEAD_CLS ? 0 : 1;   // next ids per row (LM head)
+  off = 0;
+  for (int r = 0; r < batch; ++r) {
+    int32_t* nx = nullptr;
+    if (d_next) nx = per_row ? d_next + r : d_next + off;      // cls: one id per token
+    const ember_status s = prefill_impl(md, cache, h_ids + off, 1, h_lengths[r], h_start[r],
+                                        nullptr, nx, nullptr, stream, r);
+    if (s != EMBER_OK) return s;
+    off += h_lengths[r];
+  }
+  return EMBER_OK;
+}
+
 ember_status ember_sensitivity(ember_model* md, float* d_out, void* stream) {
   g_last_error.clear();
   if (!md || !d_out) return fail(EMBER_E_ARG, "NULL argument");
@@ -985,28 +1036,41 @@ ember_status ember_sensitivity(ember_model* md, float* d_out, void* stream) {
   return EMBER_OK;
 }
 
-ember_status ember_decode_step(ember_model* md, ember_cache* cache, const int32_t* d_ids,
-                               int32_t batch, int32_t pos, int32_t* d_next, void* stream) {
-  g_last_error.clear();
+namespace {
+
+// One cached step for `batch` rows: at position `pos` for every row, or (h_pos non-null)
+// at row r's own position h_pos[r].
+ember_status decode_impl(ember_model* md, ember_cache* cache, const int32_t* d_ids, int32_t batch,
+                         int32_t pos, const int32_t* h_pos, int32_t* d_next, void* stream) {
   if (!md || !cache || !d_ids || !d_next) return fail(EMBER_E_ARG, "NULL argument");
   if (cache->model != md) return fail(EMBER_E_ARG, "cache bound to another model");
   const ember_config& c = md->cfg;
   if (!c.causal) return fail(EMBER_E_STATE, "decode steps need a causal model");
   if (batch <= 0 || batch > c.max_batch)
     return fail(EMBER_E_CAPACITY, "batch %d outside 1..%d", batch, c.max_batch);
-  if (pos < 0 || pos >= c.max_seq) return fail(EMBER_E_CAPACITY, "position %d >= max_seq %d", pos, c.max_seq);
-  if (cache->filled == 0) return fail(EMBER_E_STATE, "decode step before any prefill");
-  if (pos > cache->filled)
-    return fail(EMBER_E_STATE, "position %d leaves a gap after %d cached positions", pos, cache->filled);
+  int max_pos = 0;
+  for (int r = 0; r < batch; ++r) {
+    const int pr = h_pos ? h_pos[r] : pos;
+    if (pr < 0 || pr >= c.max_seq)
+      return fail(EMBER_E_CAPACITY, "row %d: position %d outside [0, max_seq %d)", r, pr, c.max_seq);
+    if (cache->filled[r] == 0) return fail(EMBER_E_STATE, "row %d: decode step before any prefill", r);
+    if (pr > cache->filled[r])
+      return fail(EMBER_E_STATE, "row %d: position %d leaves a gap after %d cached positions", r,
+                  pr, cache->filled[r]);
+    max_pos = pr > max_pos ? pr : max_pos;
+  }
   {
-    const ember_status s = check_draws(md, batch, pos);
+    const ember_status s = check_draws(md, batch, max_pos);
     if (s != EMBER_OK) return s;
   }
   hipStream_t st = (hipStream_t)stream;
   const Plan& p = md->plan;
   Ctx cx{md, cache, st};
+  if (h_pos)
+    HIP_TRY(hipMemcpyAsync(md->at<int>(p.row_pos), h_pos, (size_t)batch * 4, hipMemcpyHostToDevice, st));
   StepBeginArgs sb{};
   sb.ids = d_ids; sb.R = batch; sb.V = c.vocab; sb.pos = pos;
+  sb.ragged = h_pos != nullptr; sb.row_pos = md->at<int>(p.row_pos);
   sb.d_pos = md->at<int>(p.pos); sb.flags = md->at<int>(p.flags);
   sb.cos_t = md->at<float>(p.cos_t); sb.sin_t = md->at<float>(p.sin_t); sb.half = c.head_dim / 2;
   sb.rope_cur = md->at<float>(p.rope_cur);
@@ -1039,10 +1103,29 @@ ember_status ember_decode_step(ember_model* md, ember_cache* cache, const int32_
     decode_body(cx, batch, d_next);
   }
   HIP_TRY(hipGetLastError());
-  if (pos + 1 > cache->filled) cache->filled = pos + 1;
+  for (int r = 0; r < batch; ++r) {
+    const int pr = h_pos ? h_pos[r] : pos;
+    if (pr + 1 > cache->filled[r]) cache->filled[r] = pr + 1;
+  }
   md->has_logits_rows = batch;
   md->last_decode_batch = batch;
   return EMBER_OK;
+}
+
+}  // namespace
+
+ember_status ember_decode_step(ember_model* md, ember_cache* cache, const int32_t* d_ids,
+                               int32_t batch, int32_t pos, int32_t* d_next, void* stream) {
+  g_last_error.clear();
+  return decode_impl(md, cache, d_ids, batch, pos, nullptr, d_next, stream);
+}
+
+ember_status ember_decode_step_rows(ember_model* md, ember_cache* cache, const int32_t* d_ids,
+                                    int32_t batch, const int32_t* h_pos, int32_t* d_next,
+                                    void* stream) {
+  g_last_error.clear();
+  if (!h_pos) return fail(EMBER_E_ARG, "NULL positions");
+  return decode_impl(md, cache, d_ids, batch, 0, h_pos, d_next, stream);
 }
 
 ember_status ember_time_kernel(ember_model* md, ember_cache* cache, int32_t kernel, int32_t phase,

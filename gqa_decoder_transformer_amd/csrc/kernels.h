@@ -82,17 +82,20 @@ void launch_cls_head(const float* h, const void* W, bool w_bf16, const float* b,
 void launch_convert_logits(const float* src, int R, int n, long long ld, void* dst,
                            bool to_bf16, hipStream_t st);
 
-// Begin a decode step: *d_pos = pos, rope_cur = (cos, sin) row of pos, and row r of x the
-// embedding of ids[r] (out-of-range ids -> 0 + flag).
+// Begin a decode step. Row r's position p_r: pos for every row, or (ragged) the value
+// already in row_pos[r]; then row_pos[r] = p_r, rope_cur[r] = (cos, sin) row of p_r, row r
+// of x the embedding of ids[r] (out-of-range ids -> 0 + flag), *d_pos = p_0.
 struct StepBeginArgs {
   const int32_t* ids;
   int R, V, pos;
+  bool ragged;
+  int* row_pos;            // [R]
   int* d_pos;
   int* flags;
   const float* cos_t;
   const float* sin_t;
   int half;
-  float* rope_cur;
+  float* rope_cur;         // [R][HD]: cos[HD/2], sin[HD/2] per row
   const void* E;
   int e_wk;                // WeightKind of E
   const uint16_t* e_scale; // q8: scale plane of E
@@ -128,7 +131,8 @@ EMBER_INLINE_HD int sample_tiles_ld(int V) { return sample_blocks(V) * (kSampleC
 
 // next[r] = a token drawn from row r of the logits through temperature, top-k, top-p,
 // softmax and an inverse-CDF draw with u = uniform[row * u_ld + col0 + r], where row is
-// *d_pos when d_pos is non-null, else pos (clamped to u_rows - 1). temperature > 0.
+// d_pos[r] (each row's position) when d_pos is non-null, else pos (clamped to u_rows - 1).
+// temperature > 0.
 // Raises kFlagNaN when a row holds a NaN. state / tiles: R rows of the buffers above.
 struct SampleArgs {
   const float* logits;
@@ -299,15 +303,15 @@ void flash_init();
 
 struct DecodeAttnArgs {
   const float* qkv;        // [B, (NH + 2 NKV) HD] raw projections of the current token
-  const float* rope_cur;   // cos[HD/2], sin[HD/2] of the current position
+  const float* rope_cur;   // [B][HD]: cos[HD/2], sin[HD/2] of each row's position
   const float* q_norm;     // [HD] or null
   const float* k_norm;
   float eps;
-  void* k_cache;           // layer base [B_cache][NKV][max_seq][HD]; K/V at *d_pos written
+  void* k_cache;           // layer base [B_cache][NKV][max_seq][HD]; K/V at d_pos[b] written
   void* v_cache;
   bool kv_bf16;
   int B, NH, NKV, HD, max_seq;
-  const int* d_pos;        // current position; keys 0..*d_pos
+  const int* d_pos;        // [B] each row's current position; row b's keys 0..d_pos[b]
   int nsplit, chunk_min;   // nsplit == 1 or chunk_min >= ceil(max_seq / nsplit)
   float scale;
   float* part;             // [B][NH][nsplit][HD + 2] split partials (m, l, acc)
@@ -319,7 +323,8 @@ struct DecodeAttnArgs {
 // Split-K decode attention with the QKV epilogue (q/k norm, RoPE, K/V store at the
 // current position) fused in.
 void launch_decode_attn(const DecodeAttnArgs& a, hipStream_t st);
-// att = combine(part) for B rows (nsplit <= 64), written as f32 [B, NH*HD] and/or planes.
+// att = combine(part) for B rows (nsplit <= 64), written as f32 [B, NH*HD] and/or planes;
+// d_pos[b] is row b's position (the splits holding keys 0..d_pos[b] are combined).
 void launch_attn_combine(const float* part, int B, int NH, int HD, int nsplit, const int* d_pos,
                          int chunk_min, float* out_f32, uint16_t* out_hi, uint16_t* out_lo,
                          hipStream_t st);

@@ -180,10 +180,10 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
   const float* row = a.qkv + (size_t)b * qkv_n;
   for (int e = threadIdx.x; e < G * HD; e += blockDim.x) qs[e] = row[h0 * HD + e];
   for (int e = threadIdx.x; e < HALF; e += blockDim.x) {
-    cs[e] = a.rope_cur[e];
-    sn[e] = a.rope_cur[HALF + e];
+    cs[e] = a.rope_cur[(size_t)b * HD + e];
+    sn[e] = a.rope_cur[(size_t)b * HD + HALF + e];
   }
-  const int pos = *a.d_pos;
+  const int pos = a.d_pos[b];
   const int S = pos + 1;
   if (s0 >= S) return;                         // beyond the valid splits: never read
   const int s1 = min(S, s_hi);
@@ -417,7 +417,7 @@ __global__ void __launch_bounds__(128) k_attn_combine(const float* part, int NH,
   const int stride = HD + 2;
   const float* ph = part + (size_t)bh * nsplit * stride;
   for (int e = threadIdx.x; e < nsplit * stride; e += blockDim.x) sp[e] = ph[e];
-  const int S = *d_pos + 1;
+  const int S = d_pos[bh / NH] + 1;
   int chunk = (S + nsplit - 1) / nsplit;
   if (chunk < chunk_min) chunk = chunk_min;
   const int nv = (S + chunk - 1) / chunk;

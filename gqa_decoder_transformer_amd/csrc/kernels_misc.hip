@@ -357,12 +357,15 @@ void launch_convert_logits(const float* src, int R, int n, long long ld, void* d
 // the RoPE row.
 __global__ void __launch_bounds__(256) k_step_begin(StepBeginArgs a) {
   const int r = blockIdx.x;
-  if (r == 0) {
-    if (threadIdx.x == 0) *a.d_pos = a.pos;
-    for (int i = threadIdx.x; i < a.half; i += blockDim.x) {
-      a.rope_cur[i] = a.cos_t[(size_t)a.pos * a.half + i];
-      a.rope_cur[a.half + i] = a.sin_t[(size_t)a.pos * a.half + i];
-    }
+  const int pos = a.ragged ? a.row_pos[r] : a.pos;
+  if (threadIdx.x == 0) {
+    if (!a.ragged) a.row_pos[r] = pos;
+    if (r == 0) *a.d_pos = pos;
+  }
+  float* rc = a.rope_cur + (size_t)r * 2 * a.half;
+  for (int i = threadIdx.x; i < a.half; i += blockDim.x) {
+    rc[i] = a.cos_t[(size_t)pos * a.half + i];
+    rc[a.half + i] = a.sin_t[(size_t)pos * a.half + i];
   }
   int id = a.ids[r];
   if (id < 0 || id >= a.V) {

@@ -295,7 +295,7 @@ __global__ void __launch_bounds__(kSB) k_sample_phase(SampleArgs a) {
     }
     __syncthreads();
     const float S2 = s.total;
-    const int did = a.d_pos ? *a.d_pos : a.pos;
+    const int did = a.d_pos ? a.d_pos[r] : a.pos;
     const int urow = min(max(did, 0), a.u_rows - 1);
     const float u = a.uniform[(size_t)urow * a.u_ld + a.col0 + r];
     const float target = u * S2;

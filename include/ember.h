@@ -157,6 +157,18 @@ ember_status ember_prefill(ember_model* model, ember_cache* cache, const int32_t
                            int32_t batch, int32_t n_tokens, int32_t start_pos,
                            float* d_all_logits, int32_t* d_next, void* stream);
 
+/* Ragged prefill: row r (r < batch) forwards h_lengths[r] tokens at positions
+ * [h_start[r], h_start[r] + h_lengths[r]) ("ember internals" page, section "ForwardModel
+ * trait": forward_with_cache(token_ids, cache, start_pos) per sequence). h_ids (host) holds
+ * the rows' tokens one after the other; h_lengths and h_start are host [batch]. Each row is
+ * checked as in ember_prefill (against its own cached length) before anything is
+ * enqueued. d_next (optional): [batch] next ids of the LM head (each row's last
+ * position), or one id per token (classification head, packed like h_ids). The rows run
+ * one pass each (a row's tokens are not batched with another row's). */
+ember_status ember_prefill_rows(ember_model* model, ember_cache* cache, const int32_t* h_ids,
+                                const int32_t* h_lengths, const int32_t* h_start,
+                                int32_t batch, int32_t* d_next, void* stream);
+
 /* ember_prefill that also writes the hidden state after every block at each row's last
  * position ("ember internals" page, section "ForwardModel trait",
  * forward_with_activations; section "probing pipeline": activations[layer][d]) into
@@ -175,7 +187,8 @@ ember_status ember_forward_with_activations(ember_model* model, ember_cache* cac
  * before any prefill. */
 ember_status ember_sensitivity(ember_model* model, float* d_out, void* stream);
 
-/* One cached greedy step for `batch` rows at position `pos` (causal configs only):
+/* One cached greedy step for `batch` rows at position `pos` (causal configs only; every
+ * row at the same position -- ember_decode_step_rows takes one per row):
  * reads the ids d_ids [batch] int32 (device), writes their K/V at `pos`, attends over
  * positions 0..pos, and writes the argmax of the new logits to d_next [batch] int32
  * (device; may alias d_ids). Requires pos <= the cache's filled length (EMBER_E_STATE)
@@ -186,6 +199,14 @@ ember_status ember_sensitivity(ember_model* model, float* d_out, void* stream);
  * EMBER_E_TOKEN. */
 ember_status ember_decode_step(ember_model* model, ember_cache* cache, const int32_t* d_ids,
                                int32_t batch, int32_t pos, int32_t* d_next, void* stream);
+
+/* ember_decode_step with a position per row: row r's token is at h_pos[r] (host [batch]),
+ * each row checked against its own cached length. The positions are copied to the device
+ * before the step's graph, which reads them there (the graph is shared with
+ * ember_decode_step). */
+ember_status ember_decode_step_rows(ember_model* model, ember_cache* cache,
+                                    const int32_t* d_ids, int32_t batch, const int32_t* h_pos,
+                                    int32_t* d_next, void* stream);
 
 /* Copy the head output of the most recent prefill / decode step, [batch, out_dim], into
  * d_out as EMBER_F32 or EMBER_BF16 (round to nearest even). EMBER_E_STATE before any
