@@ -339,6 +339,12 @@ int pick_cfg(const GemmArgs& a) {
   if (a.M <= 64) return CFG_64x64;
   if (a.a_lo) return tiles_of(a, 128, 256) >= 180 ? CFG_128x256 : CFG_128x128;
   if (tiles_of(a, 256, 256) >= 256) return CFG_256x256;
+  // long K against N (the down projection at M = 2048): 256 x 256 tiles over four K
+  // slices, whose partial planes cost less than the halved operand traffic saves there
+  // (measured slower for K <= N)
+  if (a.partial && a.K >= 4 * a.N && a.K >= 4096 && tiles_of(a, 256, 256) >= 64 &&
+      (size_t)4 * a.M * a.N <= a.partial_elems)
+    return CFG_256x256;
   // about one 128 x 128 tile per CU: two K groups per tile (two waves per SIMD) when the
   // stages split evenly
   const int t128 = tiles_of(a, 128, 128);
@@ -432,17 +438,18 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs a, int splits) {
 }
 
 // Split K when the tiles cannot fill the GPU: slices of >= 256 columns, about 512 blocks
-// (256 for the 64 x 64 tiles of small M, which stream four stages ahead: every split
-// adds an f32 partial plane to write and reduce).
+// (256 for the 64 x 64 tiles of small M, which stream four stages ahead, and for 256 x 256
+// tiles, whose slices keep >= 1024 columns: every split adds an f32 partial plane to write
+// and reduce).
 int pick_splits(const GemmArgs& a, int cfg) {
   if (!a.partial) return 1;
   int bm, bn;
   cfg_dims(cfg, bm, bn);
   const int tiles = tiles_of(a, bm, bn);
   if (tiles >= 192) return 1;
-  const int target = cfg == CFG_64x64 ? 256 : 512;
+  const int target = (cfg == CFG_64x64 || cfg == CFG_256x256) ? 256 : 512;
   int s = (target + tiles - 1) / tiles;
-  const int max_s = a.K / 256;
+  const int max_s = a.K / (cfg == CFG_256x256 ? 1024 : 256);
   if (s > max_s) s = max_s;
   if ((size_t)s * a.M * a.N > a.partial_elems) s = (int)(a.partial_elems / ((size_t)a.M * a.N));
   return s < 2 ? 1 : s;
