@@ -132,98 +132,133 @@ __global__ void __launch_bounds__(256) k_rmsnorm(const float* x, const float* w,
   }
 }
 
+// Vector form for H a multiple of 4 and at most 4096: each thread keeps its NV groups of
+// four elements in registers (one read of the row), 16-byte loads and stores, 8-byte
+// stores of the bf16 planes.
+template <int NV>
+__global__ void __launch_bounds__(256) k_rmsnorm_v(const float* x, const float* w, float eps, int H,
+                                                   int row_step, int row_off, float* out_f32,
+                                                   uint16_t* hi, uint16_t* lo, int ld_plane) {
+  __shared__ float red[16];
+  const int r = blockIdx.x;
+  const int H4 = H / 4;
+  const float4* xr = (const float4*)(x + ((size_t)r * row_step + row_off) * H);
+  float4 v[NV];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    v[j] = i < H4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += v[j].x * v[j].x;
+    ss += v[j].y * v[j].y;
+    ss += v[j].z * v[j].z;
+    ss += v[j].w * v[j].w;
+  }
+  ss = block_sum(ss, red);
+  const float rms = sqrtf(ss / (float)H + eps);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    if (i >= H4) continue;
+    const float4 wv = ((const float4*)w)[i];
+    float y[4] = {v[j].x / rms * wv.x, v[j].y / rms * wv.y, v[j].z / rms * wv.z,
+                  v[j].w / rms * wv.w};
+    if (out_f32) ((float4*)(out_f32 + (size_t)r * H))[i] = make_float4(y[0], y[1], y[2], y[3]);
+    if (hi) {
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split_bf16(y[e], h[e], l[e]);
+      ((uint2*)(hi + (size_t)r * ld_plane))[i] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      if (lo)
+        ((uint2*)(lo + (size_t)r * ld_plane))[i] = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+    }
+  }
+}
+
 void launch_rmsnorm(const float* x, const float* w, float eps, int R, int H, int row_step,
                     int row_off, float* out_f32, uint16_t* hi, uint16_t* lo, int ld_plane,
                     hipStream_t st) {
   if (R <= 0) return;
+  const int nv = (H / 4 + 255) / 256;
+  if (H % 4 == 0 && (!hi || ld_plane % 4 == 0) && nv <= 4) {
+    switch (nv) {
+      case 1: hipLaunchKernelGGL(k_rmsnorm_v<1>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, ld_plane); return;
+      case 2: hipLaunchKernelGGL(k_rmsnorm_v<2>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, ld_plane); return;
+      case 3: hipLaunchKernelGGL(k_rmsnorm_v<3>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, ld_plane); return;
+      default: hipLaunchKernelGGL(k_rmsnorm_v<4>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, ld_plane); return;
+    }
+  }
   hipLaunchKernelGGL(k_rmsnorm, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off,
                      out_f32, hi, lo, ld_plane);
 }
 
 // ------------------------------------------------------------------ QKV epilogue
-// One block per token, one wave per head. Lane i < HD/2 owns the rotated pair
-// (i, i + HD/2) (rotate-half RoPE: "ember scripts/reference_forward.py", rope); with
-// q/k norm the head is first RMS-normalised over HD ("PII-Tracer serving/
-// reference_forward.py", forward: q_norm / k_norm before RoPE). K and V are stored at
-// the token's explicit position (ember internals page, "cursor semantics").
+// One thread per rotated pair (i, i + HD/2) of a head (rotate-half RoPE: "ember
+// scripts/reference_forward.py", rope), grid (tokens, pair blocks); the HD/2 pairs of a
+// head sit in adjacent lanes of one wave, so the optional per-head RMSNorm over HD ("PII-
+// Tracer serving/reference_forward.py", forward: q_norm / k_norm before RoPE) is a lane-
+// group sum. Value heads pass through. K and V are stored at the token's explicit position
+// (ember internals page, "cursor semantics"). Every thread issues its loads at once (a
+// wave looping over heads waited for one round trip per head).
+template <int HALF>
 __global__ void __launch_bounds__(256) k_qkv_post(QkvPostArgs a) {
+  constexpr int HD = 2 * HALF;
   const int m = blockIdx.x;
-  const int HD = a.HD, half = HD / 2;
-  const int qkv_n = (a.NH + 2 * a.NKV) * HD;
+  const int pidx = blockIdx.y * 256 + threadIdx.x;
+  const bool live = pidx < (a.NH + 2 * a.NKV) * HALF;   // whole heads live or dead
+  const int h = pidx / HALF, i = pidx % HALF;
   const int start = a.d_pos ? *a.d_pos : a.start_pos;
   const int b = a.b0 + m / a.tokens_per_row;
   const int p = start + m % a.tokens_per_row;
-  const float* row = a.qkv + (size_t)m * qkv_n;
-  const float* cs = a.cos_t + (size_t)p * half;
-  const float* sn = a.sin_t + (size_t)p * half;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int nwaves = blockDim.x / kWave;
-  // heads 0..NH-1: q; NH..NH+NKV-1: k; then v
-  for (int h = wave; h < a.NH + 2 * a.NKV; h += nwaves) {
-    const float* src = row + (size_t)h * HD;
-    if (h >= a.NH + a.NKV) {          // value head: plain copy into the cache
-      const int kvh = h - a.NH - a.NKV;
-      size_t off = (((size_t)b * a.NKV + kvh) * a.max_seq + p) * HD;
-      for (int d = lane; d < HD; d += kWave) {
-        if (a.kv_bf16) ((uint16_t*)a.v_cache)[off + d] = (uint16_t)f32_to_bf16_rne(src[d]);
-        else ((float*)a.v_cache)[off + d] = src[d];
-      }
-      continue;
-    }
-    const bool is_q = h < a.NH;
-    const float* nw = is_q ? a.q_norm : a.k_norm;
-    // each lane holds pairs i = lane + 64 j (HD/2 <= 128)
-    float x0[2], x1[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = lane + j * kWave;
-      x0[j] = i < half ? src[i] : 0.f;
-      x1[j] = i < half ? src[i + half] : 0.f;
-    }
-    if (nw) {
-      float ss = 0.f;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) ss += x0[j] * x0[j] + x1[j] * x1[j];
-      ss = wave_sum(ss);
+  const bool is_q = h < a.NH, is_v = h >= a.NH + a.NKV;
+  const float* src = a.qkv + (size_t)m * (a.NH + 2 * a.NKV) * HD + (size_t)h * HD;
+  float x0 = live ? src[i] : 0.f, x1 = live ? src[i + HALF] : 0.f;
+  const float c = live && !is_v ? a.cos_t[(size_t)p * HALF + i] : 0.f;
+  const float sn = live && !is_v ? a.sin_t[(size_t)p * HALF + i] : 0.f;
+  if (a.q_norm) {                    // q and k norms come together
+    const float ss = group_sum<HALF>(x0 * x0 + x1 * x1);
+    if (live && !is_v) {
+      const float* nw = is_q ? a.q_norm : a.k_norm;
       const float rms = sqrtf(ss / (float)HD + a.eps);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int i = lane + j * kWave;
-        if (i < half) {
-          x0[j] = x0[j] / rms * nw[i];
-          x1[j] = x1[j] / rms * nw[i + half];
-        }
-      }
+      x0 = x0 / rms * nw[i];
+      x1 = x1 / rms * nw[i + HALF];
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = lane + j * kWave;
-      if (i >= half) continue;
-      const float c = cs[i], s = sn[i];
-      const float y0 = x0[j] * c - x1[j] * s;
-      const float y1 = x1[j] * c + x0[j] * s;
-      if (is_q) {
-        float* dst = a.q_out + (size_t)m * a.NH * HD + (size_t)h * HD;
-        dst[i] = y0;
-        dst[i + half] = y1;
-      } else {
-        const int kvh = h - a.NH;
-        size_t off = (((size_t)b * a.NKV + kvh) * a.max_seq + p) * HD;
-        if (a.kv_bf16) {
-          ((uint16_t*)a.k_cache)[off + i] = (uint16_t)f32_to_bf16_rne(y0);
-          ((uint16_t*)a.k_cache)[off + i + half] = (uint16_t)f32_to_bf16_rne(y1);
-        } else {
-          ((float*)a.k_cache)[off + i] = y0;
-          ((float*)a.k_cache)[off + i + half] = y1;
-        }
-      }
-    }
+  }
+  if (!live) return;
+  float y0 = x0, y1 = x1;
+  if (!is_v) {
+    y0 = x0 * c - x1 * sn;
+    y1 = x1 * c + x0 * sn;
+  }
+  if (is_q) {
+    float* dst = a.q_out + (size_t)m * a.NH * HD + (size_t)h * HD;
+    dst[i] = y0;
+    dst[i + HALF] = y1;
+    return;
+  }
+  const int kvh = is_v ? h - a.NH - a.NKV : h - a.NH;
+  const size_t off = (((size_t)b * a.NKV + kvh) * a.max_seq + p) * HD;
+  void* cache = is_v ? a.v_cache : a.k_cache;
+  if (a.kv_bf16) {
+    ((uint16_t*)cache)[off + i] = (uint16_t)f32_to_bf16_rne(y0);
+    ((uint16_t*)cache)[off + i + HALF] = (uint16_t)f32_to_bf16_rne(y1);
+  } else {
+    ((float*)cache)[off + i] = y0;
+    ((float*)cache)[off + i + HALF] = y1;
   }
 }
 
 void launch_qkv_post(const QkvPostArgs& a, hipStream_t st) {
   if (a.M <= 0) return;
-  hipLaunchKernelGGL(k_qkv_post, dim3(a.M), dim3(256), 0, st, a);
+  const dim3 grid(a.M, ((a.NH + 2 * a.NKV) * (a.HD / 2) + 255) / 256);
+  switch (a.HD) {
+    case 8: hipLaunchKernelGGL(k_qkv_post<4>, grid, dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL(k_qkv_post<8>, grid, dim3(256), 0, st, a); break;
+    case 32: hipLaunchKernelGGL(k_qkv_post<16>, grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(k_qkv_post<32>, grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL(k_qkv_post<64>, grid, dim3(256), 0, st, a); break;
+    default: break;                  // head_dim is validated to these values
+  }
 }
 
 // ------------------------------------------------------------------ argmax
