@@ -437,6 +437,58 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs a, int splits) {
   }
 }
 
+// The same sum four columns per thread (16-byte partial loads and output stores) when
+// every row length and output pointer allows it; same split order.
+template <int EPI>
+__global__ void __launch_bounds__(256) k_splitk_reduce4(GemmArgs a, int splits) {
+  const int nout = EPI == GEMM_SILU ? a.N / 2 : a.N;
+  const int nq = nout / 4;
+  const size_t total = (size_t)a.M * nq;
+  const size_t plane = (size_t)a.M * a.N;
+  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total;
+       e += (size_t)gridDim.x * blockDim.x) {
+    const int row = (int)(e / nq), col = (int)(e % nq) * 4;
+    if (EPI == GEMM_SILU) {
+      // four outputs of one block of 32 read four consecutive gate and up columns
+      const float* pg = a.partial + (size_t)row * a.N + gu_row(col, 0);
+      const float* pu = a.partial + (size_t)row * a.N + gu_row(col, 1);
+      float4 g = *(const float4*)pg, u = *(const float4*)pu;
+      for (int s = 1; s < splits; ++s) {
+        const float4 gs = *(const float4*)(pg + s * plane), us = *(const float4*)(pu + s * plane);
+        g.x += gs.x; g.y += gs.y; g.z += gs.z; g.w += gs.w;
+        u.x += us.x; u.y += us.y; u.z += us.z; u.w += us.w;
+      }
+      const float v[4] = {silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w};
+      const size_t o = (size_t)row * a.ldo + col;
+      if (a.o_f32) *(float4*)(a.o_f32 + o) = make_float4(v[0], v[1], v[2], v[3]);
+      if (a.o_hi) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split_bf16(v[i], h[i], l[i]);
+        *(uint2*)(a.o_hi + o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        if (a.o_lo) *(uint2*)(a.o_lo + o) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+      }
+    } else {
+      const float* pp = a.partial + (size_t)row * a.N + col;
+      float4 acc = *(const float4*)pp;
+      for (int s = 1; s < splits; ++s) {
+        const float4 ps = *(const float4*)(pp + s * plane);
+        acc.x += ps.x; acc.y += ps.y; acc.z += ps.z; acc.w += ps.w;
+      }
+      float4* cp = (float4*)(a.c + (size_t)row * a.ldc + col);
+      if (EPI == GEMM_RESID) {
+        const float4 c0 = *cp;
+        *cp = make_float4(c0.x + acc.x, c0.y + acc.y, c0.z + acc.z, c0.w + acc.w);
+      } else {
+        const float4 bv = a.bias ? *(const float4*)(a.bias + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+        *cp = make_float4(acc.x + bv.x, acc.y + bv.y, acc.z + bv.z, acc.w + bv.w);
+      }
+    }
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 // Split K when the tiles cannot fill the GPU: slices of >= 256 columns, about 512 blocks
 // (256 for the 64 x 64 tiles of small M, which stream four stages ahead, and for 256 x 256
 // tiles, whose slices keep >= 1024 columns: every split adds an f32 partial plane to write
@@ -510,6 +562,21 @@ void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
   const int used = (a.K + a.k_chunk - 1) / a.k_chunk;
   launch_epi<GEMM_STORE>(a, cfg, used, st);      // partial planes (epilogue skipped)
   const int nout = epi == GEMM_SILU ? a.N / 2 : a.N;
+  const bool vec = a.N % 4 == 0 && nout % 4 == 0 && aligned16(a.partial) &&
+                   (epi == GEMM_SILU ? (a.ldo % 4 == 0 && aligned16(a.o_f32) && aligned16(a.o_hi) &&
+                                        aligned16(a.o_lo))
+                                     : (a.ldc % 4 == 0 && aligned16(a.c) && aligned16(a.bias)));
+  if (vec) {
+    long long blocks = ((long long)a.M * (nout / 4) + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    switch (epi) {
+      case GEMM_STORE: hipLaunchKernelGGL(k_splitk_reduce4<GEMM_STORE>, dim3((unsigned)blocks), dim3(256), 0, st, a, used); break;
+      case GEMM_RESID: hipLaunchKernelGGL(k_splitk_reduce4<GEMM_RESID>, dim3((unsigned)blocks), dim3(256), 0, st, a, used); break;
+      case GEMM_SILU: hipLaunchKernelGGL(k_splitk_reduce4<GEMM_SILU>, dim3((unsigned)blocks), dim3(256), 0, st, a, used); break;
+      default: break;
+    }
+    return;
+  }
   long long blocks = ((long long)a.M * nout + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   switch (epi) {
