@@ -25,6 +25,10 @@ ENCODER_HD128 = C.shrink_model(C.ENCODER, name="encoder-hd128", vocab=83, hidden
 QWEN_HD64_G7 = C.shrink_model(C.QWEN05B, name="qwen-hd64-g7", vocab=97, hidden=448, layers=2,
                               heads=7, kv_heads=1, head_dim=64, ffn=320)
 
+# plain multi-head attention (one kv head per query head)
+LLAMA_MHA = C.shrink_model(C.LLAMA1B, name="llama-mha", vocab=131, hidden=128, layers=2,
+                           heads=4, kv_heads=4, head_dim=64, ffn=192)
+
 # long K against few output tiles: the projections take the split-K path
 LLAMA_SPLITK = C.shrink_model(C.LLAMA1B, name="llama-splitk", vocab=131, hidden=256, layers=2,
                               heads=4, kv_heads=2, head_dim=64, ffn=1024)

@@ -10,8 +10,9 @@ import pytest
 import oracle as O
 import workloads as W
 from tests.gpu_util import TOL_EXACT, TOL_FAST, check_greedy, gpu_generate, rel_maxabs, say
-from tests.small_models import (ENCODER_HD128, ENCODER_SMALL, LLAMA_FF8K, LLAMA_HD64, LLAMA_SMALL,
-                                LLAMA_SPLITK, Q8_SMALL, QWEN_FF2K, QWEN_HD64_G7, QWEN_SMALL, TINY)
+from tests.small_models import (ENCODER_HD128, ENCODER_SMALL, LLAMA_FF8K, LLAMA_HD64, LLAMA_MHA,
+                                LLAMA_SMALL, LLAMA_SPLITK, Q8_SMALL, QWEN_FF2K, QWEN_HD64_G7,
+                                QWEN_SMALL, TINY)
 
 pytestmark = pytest.mark.gpu
 
@@ -213,6 +214,36 @@ def test_abi_errors_enqueue_nothing():
         eng.sync()
     assert e.value.status == 6                       # device-side id check
     eng.sync()                                       # flags cleared
+
+
+@pytest.mark.parametrize("model", [LLAMA_MHA, QWEN_HD64_G7, LLAMA_SMALL], ids=lambda m: m.name)
+@pytest.mark.parametrize("prec_name", ["exact", "fast"])
+def test_one_token_prompt_decodes_until_the_cache_is_full(model, prec_name):
+    """Degenerate shapes: plain MHA (kv_heads = heads), one kv head for every query head,
+    a one-token prompt, and decode steps up to position max_seq - 1 (the cache exactly
+    full); one step further is an error that enqueues nothing."""
+    import torch
+    from gqa_decoder_transformer_amd import binding as B
+    prec = B.EXACT if prec_name == "exact" else B.FAST
+    tol = TOL_EXACT if prec == B.EXACT else TOL_FAST
+    ck = W.make_weights(model, 41)
+    S = 24
+    prompt = np.array([[7]], np.int32)
+    say(f"one-token prompt {model.name} {prec_name} to max_seq {S}")
+    eng = _engine(model, ck, prec, max_seq=S, max_tokens=S)
+    om = O.OracleModel(model, ck)
+    or_ids, or_logits = O.generate(om, prompt[0], S - 1)
+    feed = or_ids[:S - 1, None]
+    g_ids, g_logits = gpu_generate(eng, prompt, S - 1, feed=feed)
+    err = rel_maxabs(g_logits[:, 0], or_logits)
+    say(f"max rel err {err.max():.3g}")
+    assert err.max() < tol, err
+    if prec == B.EXACT:
+        check_greedy(g_ids[:, 0], or_ids, or_logits, tol)
+    with pytest.raises(B.EmberError) as e:
+        eng.decode_step(torch.zeros(1, dtype=torch.int32, device="cuda"), S)
+    assert e.value.status == 7                       # past max_seq
+    eng.sync()
 
 
 @pytest.mark.parametrize("model", Q8_SMALL, ids=lambda m: m.name)
