@@ -163,7 +163,7 @@ def main():
     m = w.model
     prec = B.EXACT if args.precision == "exact" else B.FAST
     # multi-token passes on bf16 MFMA: bf16 weights, or q8_0 dequantised to bf16 in FAST
-    mfma_path = m.weight_dtype == "bf16" or (m.weight_dtype == "q8_0" and prec == B.FAST)
+    mfma_path = m.weight_dtype in ("bf16", "q8_0")
     kv = {"f32": B.F32, "bf16": B.BF16, None: None}[args.kv]
     ck = W.weights_for(w)
     prompt = W.make_ids(w)

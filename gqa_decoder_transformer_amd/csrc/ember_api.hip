@@ -48,10 +48,14 @@ size_t dtype_size(int dt) { return dt == EMBER_BF16 ? 2 : 4; }
 
 int weight_kind(int dt) { return dt == EMBER_Q8_0 ? WK_Q8 : (dt == EMBER_BF16 ? WK_BF16 : WK_F32); }
 
-// The GEMMs of multi-token passes run on bf16 MFMA for bf16 weights, and for q8 weights in
-// FAST precision (from a bf16 dequantised copy); f32 weights and EXACT q8 take the f32 path.
+// The GEMMs of multi-token passes run on bf16 MFMA for bf16 and q8 weights (q8 from a
+// dequantised copy: bf16 in FAST precision, in EXACT a bf16 pair whose sum is the weight
+// within 2^-17, one GEMM pass per plane); f32 weights take the f32 path.
 bool uses_mfma(const ember_config& c) {
-  return c.weight_dtype == EMBER_BF16 || (c.weight_dtype == EMBER_Q8_0 && c.precision == EMBER_FAST);
+  return c.weight_dtype == EMBER_BF16 || c.weight_dtype == EMBER_Q8_0;
+}
+bool q8_pair(const ember_config& c) {
+  return c.weight_dtype == EMBER_Q8_0 && c.precision == EMBER_EXACT;
 }
 
 struct LayerOff {
@@ -194,6 +198,8 @@ Plan make_plan(const ember_config& c) {
     if (H > maxn) maxn = H;
     const int mrows = Mx < 128 ? Mx : 128;
     p.splitk_elems = uses_mfma(c) ? (size_t)16 * mrows * maxn : 0;
+    // two weight planes: both passes of a SiLU GEMM land in partial planes
+    if (q8_pair(c) && p.splitk_elems < (size_t)2 * Mx * maxn) p.splitk_elems = (size_t)2 * Mx * maxn;
     p.splitk = p.splitk_elems ? take(p.splitk_elems * 4) : 0;
   }
   {
@@ -205,13 +211,14 @@ Plan make_plan(const ember_config& c) {
     p.kvpack = p.kvpack_elems ? take(p.kvpack_elems * 2) : 0;
   }
   if (q8) {
-    // the dequantised copy of one matrix for the GEMMs of multi-token passes (bf16 on the
-    // MFMA path, f32 otherwise): the largest of a layer's matrices and the embedding
+    // the dequantised copy of one matrix for the GEMMs of multi-token passes (bf16, or
+    // the bf16 pair in EXACT precision): the largest of a layer's matrices and the
+    // embedding
     size_t elems = (size_t)c.vocab * H;
     const size_t cand[4] = {(size_t)p.qkv_n * H, (size_t)H * NH * HD, (size_t)2 * FF * H,
                             (size_t)H * FF};
     for (size_t e : cand) elems = e > elems ? e : elems;
-    p.q8_scratch = take(elems * (uses_mfma(c) ? 2 : 4));
+    p.q8_scratch = take(elems * (q8_pair(c) ? 4 : 2));
   }
   p.total = off;
   return p;
@@ -295,15 +302,19 @@ void gemv_weights(const ember_model* md, GemvArgs& g, size_t off, size_t soff) {
 }
 
 // Weights of one matrix [N, K] for the GEMM of a multi-token pass: in place for bf16 and
-// f32; q8 matrices are first dequantised into the scratch copy (bf16 for the MFMA path,
-// f32 otherwise), stream-ordered before the GEMM that reads it.
-const void* gemm_weights(const Ctx& cx, size_t off, size_t soff, int N, int K) {
+// f32; q8 matrices are first dequantised into the scratch copy, stream-ordered before the
+// GEMM that reads it: bf16, or in EXACT precision the bf16 pair (the second plane in *lo).
+const void* gemm_weights(const Ctx& cx, size_t off, size_t soff, int N, int K,
+                         const uint16_t** lo = nullptr) {
   ember_model* md = cx.m;
+  if (lo) *lo = nullptr;
   if (md->wk != WK_Q8) return md->ws + off;
   void* dst = md->ws + md->plan.q8_scratch;
+  const bool pair = q8_pair(md->cfg);
   if (want_aux(cx))
     launch_q8_dequant((const uint8_t*)(md->ws + off), (const uint16_t*)(md->ws + soff), N, K, dst,
-                      md->mfma, cx.st);
+                      pair ? Q8_TO_BF16_PAIR : Q8_TO_BF16, cx.st);
+  if (pair && lo) *lo = (const uint16_t*)dst + (size_t)N * K;
   return dst;
 }
 
@@ -396,7 +407,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     GemmArgs g{};
     g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
     g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka;
-    g.w = (const uint16_t*)gemm_weights(cx, L.wqkv, L.wqkv_s, p.qkv_n, H);
+    g.w = (const uint16_t*)gemm_weights(cx, L.wqkv, L.wqkv_s, p.qkv_n, H, &g.w_lo);
     g.M = ps.M; g.N = p.qkv_n; g.K = H; g.bias = bqkv; g.c = qkv; g.ldc = p.qkv_n;
     if (want(cx, EMBER_K_QKV)) launch_gemm(g, GEMM_STORE, st);
   } else {
@@ -481,7 +492,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     GemmArgs g{};
     g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
     g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka;
-    g.w = (const uint16_t*)gemm_weights(cx, L.wo, L.wo_s, H, NH * HD);
+    g.w = (const uint16_t*)gemm_weights(cx, L.wo, L.wo_s, H, NH * HD, &g.w_lo);
     g.M = ps.M; g.N = H; g.K = NH * HD; g.c = x; g.ldc = H;
     if (want(cx, EMBER_K_O)) launch_gemm(g, GEMM_RESID, st);
   } else {
@@ -508,14 +519,14 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     GemmArgs g{};
     g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
     g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka;
-    g.w = (const uint16_t*)gemm_weights(cx, L.wgu, L.wgu_s, 2 * FF, H);
+    g.w = (const uint16_t*)gemm_weights(cx, L.wgu, L.wgu_s, 2 * FF, H, &g.w_lo);
     g.M = ps.M; g.N = 2 * FF; g.K = H; g.o_hi = pb_hi; g.o_lo = pb_lo; g.ldo = FF;
     GemmArgs d{};
     d.partial = md->splitk(); d.partial_elems = p.splitk_elems;
     d.a_hi = pb_hi; d.a_lo = pb_lo; d.lda = FF;
     d.M = ps.M; d.N = H; d.K = FF; d.c = x; d.ldc = H;
     if (want(cx, EMBER_K_GATE_UP)) launch_gemm(g, GEMM_SILU, st);
-    d.w = (const uint16_t*)gemm_weights(cx, L.wd, L.wd_s, H, FF);   // after the gate/up GEMM
+    d.w = (const uint16_t*)gemm_weights(cx, L.wd, L.wd_s, H, FF, &d.w_lo);   // after the gate/up GEMM
     if (want(cx, EMBER_K_DOWN)) launch_gemm(d, GEMM_RESID, st);
   } else {
     if (want_aux(cx)) launch_rmsnorm(x, ln2, c.rms_eps, ps.M, H, 1, 0, xb, nullptr, nullptr, 0, st);
@@ -565,7 +576,8 @@ void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, lo
   // R rows (at most the pass capacity Mx at a time: the plane / xb buffers hold Mx rows)
   const int G = p.Mx;
   float* xb = md->at<float>(p.xb);
-  const void* Ew = gemm_weights(cx, p.embed, p.embed_s, V, H);
+  const uint16_t* Ew_lo = nullptr;
+  const void* Ew = gemm_weights(cx, p.embed, p.embed_s, V, H, &Ew_lo);
   for (int r0 = 0; r0 < R; r0 += G) {
     const int rn = R - r0 < G ? R - r0 : G;
     const int off = row_off + r0 * row_step;
@@ -577,7 +589,7 @@ void run_lm_head(const Ctx& cx, int R, int row_step, int row_off, float* out, lo
                        p.ka, st);
       GemmArgs g{};
       g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
-      g.a_hi = hi; g.a_lo = lo; g.lda = p.ka; g.w = (const uint16_t*)Ew;
+      g.a_hi = hi; g.a_lo = lo; g.lda = p.ka; g.w = (const uint16_t*)Ew; g.w_lo = Ew_lo;
       g.M = rn; g.N = V; g.K = H; g.c = out + (size_t)r0 * ld; g.ldc = ld;
       if (want(cx, EMBER_K_LM_HEAD)) launch_gemm(g, GEMM_STORE, st);
     } else {

@@ -34,8 +34,11 @@ void launch_embed(const int32_t* ids, const void* E, int e_wk, const uint16_t* e
 // gu_row(n, gu) (gate: gu = 0, up: gu = 1; the interleaved gate/up matrix).
 void launch_q8_unpack(const uint8_t* src, int N, int K, uint8_t* dst_q, uint16_t* dst_s,
                       int dst_row0, int gu, hipStream_t st);
-// The dequantised matrix q * d as bf16 (round to nearest even) or f32, [N, K] row-major.
-void launch_q8_dequant(const uint8_t* q, const uint16_t* s, int N, int K, void* dst, bool to_bf16,
+// The dequantised matrix w = q * d, [N, K] row-major: Q8_TO_F32 (exact), Q8_TO_BF16
+// (round to nearest even), or Q8_TO_BF16_PAIR: bf16(w) at dst and the bf16 rounding of
+// w - bf16(w) at dst + N K (their sum is w within 2^-17 relative).
+enum Q8DequantMode { Q8_TO_F32 = 0, Q8_TO_BF16 = 1, Q8_TO_BF16_PAIR = 2 };
+void launch_q8_dequant(const uint8_t* q, const uint16_t* s, int N, int K, void* dst, int mode,
                        hipStream_t st);
 
 // Row-wise RMSNorm of rows src_row(r) = r * row_step + row_off, r < R, of x [*, H]:
@@ -219,8 +222,13 @@ struct GemmArgs {
   const uint16_t* a_hi;
   const uint16_t* a_lo;
   int lda;
-  // B: weights bf16 [N, K] row-major (K contiguous)
+  // B: weights bf16 [N, K] row-major (K contiguous). With w_lo (same layout) the weights
+  // are w + w_lo (a value that bf16 cannot hold, such as a dequantised q8_0 weight, as a
+  // bf16 part and the bf16 rounding of its remainder), one pass per plane: the second
+  // adds into the output, or, when K is split or the epilogue is SiLU, both passes write
+  // split-K planes; `partial` must then hold 2 M N floats.
   const uint16_t* w;
+  const uint16_t* w_lo;
   int M, N, K;
   const float* bias;       // STORE: [N] or null
   float* c;                // STORE: [M, ldc] f32; RESID: [M, ldc] +=

@@ -533,34 +533,8 @@ __global__ void __launch_bounds__(256) k_gemm_f32w(GemmF32Args a) {
   else *cp = acc + (a.bias ? a.bias[n] : 0.f);
 }
 
-}  // namespace
-
-void gemm_init() {
-  set_attrs_epi<GEMM_STORE>();
-  set_attrs_epi<GEMM_RESID>();
-  set_attrs_epi<GEMM_SILU>();
-}
-
-void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
-  if (a0.M <= 0 || a0.N <= 0) return;
-  GemmArgs a = a0;
-  const int cfg = pick_cfg(a);
-  const int splits = pick_splits(a, cfg);
-  if (splits <= 1) {
-    a.partial = nullptr;
-    a.k_chunk = a.K;
-    switch (epi) {
-      case GEMM_STORE: launch_epi<GEMM_STORE>(a, cfg, 1, st); break;
-      case GEMM_RESID: launch_epi<GEMM_RESID>(a, cfg, 1, st); break;
-      case GEMM_SILU: launch_epi<GEMM_SILU>(a, cfg, 1, st); break;
-      default: break;
-    }
-    return;
-  }
-  // K slices are whole 64-column stages
-  a.k_chunk = ((a.K + splits - 1) / splits + 63) / 64 * 64;
-  const int used = (a.K + a.k_chunk - 1) / a.k_chunk;
-  launch_epi<GEMM_STORE>(a, cfg, used, st);      // partial planes (epilogue skipped)
+// Fixed-order sum of `used` partial planes with the epilogue.
+void launch_reduce(const GemmArgs& a, int epi, int used, hipStream_t st) {
   const int nout = epi == GEMM_SILU ? a.N / 2 : a.N;
   const bool vec = a.N % 4 == 0 && nout % 4 == 0 && aligned16(a.partial) &&
                    (epi == GEMM_SILU ? (a.ldo % 4 == 0 && aligned16(a.o_f32) && aligned16(a.o_hi) &&
@@ -585,6 +559,60 @@ void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
     case GEMM_SILU: hipLaunchKernelGGL(k_splitk_reduce<GEMM_SILU>, dim3((unsigned)blocks), dim3(256), 0, st, a, used); break;
     default: break;
   }
+}
+
+}  // namespace
+
+void gemm_init() {
+  set_attrs_epi<GEMM_STORE>();
+  set_attrs_epi<GEMM_RESID>();
+  set_attrs_epi<GEMM_SILU>();
+}
+
+void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
+  if (a0.M <= 0 || a0.N <= 0) return;
+  GemmArgs a = a0;
+  a.w_lo = nullptr;
+  const bool two = a0.w_lo != nullptr;
+  // two weight planes: each takes half of the partial planes
+  if (two) a.partial_elems /= 2;
+  const int cfg = pick_cfg(a);
+  int splits = pick_splits(a, cfg);
+  if (two && splits <= 1 && epi != GEMM_SILU) {
+    // tiles that fill the GPU: the second plane's pass adds into the output
+    a.partial = nullptr;
+    a.k_chunk = a.K;
+    if (epi == GEMM_STORE) launch_epi<GEMM_STORE>(a, cfg, 1, st);
+    else launch_epi<GEMM_RESID>(a, cfg, 1, st);
+    GemmArgs b = a;
+    b.w = a0.w_lo;
+    b.bias = nullptr;
+    launch_epi<GEMM_RESID>(b, cfg, 1, st);
+    return;
+  }
+  if (!two && splits <= 1) {
+    a.partial = nullptr;
+    a.k_chunk = a.K;
+    switch (epi) {
+      case GEMM_STORE: launch_epi<GEMM_STORE>(a, cfg, 1, st); break;
+      case GEMM_RESID: launch_epi<GEMM_RESID>(a, cfg, 1, st); break;
+      case GEMM_SILU: launch_epi<GEMM_SILU>(a, cfg, 1, st); break;
+      default: break;
+    }
+    return;
+  }
+  if (splits < 1) splits = 1;
+  // K slices are whole 64-column stages
+  a.k_chunk = ((a.K + splits - 1) / splits + 63) / 64 * 64;
+  const int used = (a.K + a.k_chunk - 1) / a.k_chunk;
+  launch_epi<GEMM_STORE>(a, cfg, used, st);      // partial planes (epilogue skipped)
+  if (two) {                                     // the second plane's slices follow
+    GemmArgs b = a;
+    b.w = a0.w_lo;
+    b.partial = a.partial + (size_t)used * a.M * a.N;
+    launch_epi<GEMM_STORE>(b, cfg, used, st);
+  }
+  launch_reduce(a, epi, two ? 2 * used : used, st);
 }
 
 void launch_gemm_f32w(const GemmF32Args& a, int epi, hipStream_t st) {

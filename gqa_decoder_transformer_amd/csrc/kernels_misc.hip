@@ -70,7 +70,7 @@ void launch_q8_unpack(const uint8_t* src, int N, int K, uint8_t* dst_q, uint16_t
 
 // One thread per 16 bytes of the byte plane: 16 values (byte - 128) * d.
 __global__ void __launch_bounds__(256) k_q8_dequant(const uint8_t* q, const uint16_t* s, int N, int K,
-                                                    void* dst, int to_bf16) {
+                                                    void* dst, int mode) {
   const long long i = threadIdx.x + (long long)blockIdx.x * blockDim.x;
   const long long nch = (long long)N * K / 16;
   if (i >= nch) return;
@@ -81,16 +81,29 @@ __global__ void __launch_bounds__(256) k_q8_dequant(const uint8_t* q, const uint
   float v[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = (float)((int)((w[j / 4] >> (8 * (j % 4))) & 0xFFu) - 128) * d;
-  if (to_bf16) {
+  if (mode == Q8_TO_BF16 || mode == Q8_TO_BF16_PAIR) {
+    uint32_t h[16], l[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) split_bf16(v[j], h[j], l[j]);
     u32x4_t o0, o1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      o0[j] = f32_to_bf16_rne(v[2 * j]) | (f32_to_bf16_rne(v[2 * j + 1]) << 16);
-      o1[j] = f32_to_bf16_rne(v[8 + 2 * j]) | (f32_to_bf16_rne(v[8 + 2 * j + 1]) << 16);
+      o0[j] = h[2 * j] | (h[2 * j + 1] << 16);
+      o1[j] = h[8 + 2 * j] | (h[8 + 2 * j + 1] << 16);
     }
     u32x4_t* o = (u32x4_t*)((uint16_t*)dst + e0);
     o[0] = o0;
     o[1] = o1;
+    if (mode == Q8_TO_BF16_PAIR) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o0[j] = l[2 * j] | (l[2 * j + 1] << 16);
+        o1[j] = l[8 + 2 * j] | (l[8 + 2 * j + 1] << 16);
+      }
+      u32x4_t* ol = (u32x4_t*)((uint16_t*)dst + (size_t)N * K + e0);
+      ol[0] = o0;
+      ol[1] = o1;
+    }
   } else {
     float4* o = (float4*)((float*)dst + e0);
 #pragma unroll
@@ -98,12 +111,12 @@ __global__ void __launch_bounds__(256) k_q8_dequant(const uint8_t* q, const uint
   }
 }
 
-void launch_q8_dequant(const uint8_t* q, const uint16_t* s, int N, int K, void* dst, bool to_bf16,
+void launch_q8_dequant(const uint8_t* q, const uint16_t* s, int N, int K, void* dst, int mode,
                        hipStream_t st) {
   const long long n = (long long)N * K / 16;
   if (n <= 0) return;
   hipLaunchKernelGGL(k_q8_dequant, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, q, s, N, K,
-                     dst, (int)to_bf16);
+                     dst, mode);
 }
 
 // ------------------------------------------------------------------ RMSNorm
