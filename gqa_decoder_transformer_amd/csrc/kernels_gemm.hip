@@ -578,7 +578,8 @@ void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
   if (two) a.partial_elems /= 2;
   const int cfg = pick_cfg(a);
   int splits = pick_splits(a, cfg);
-  if (two && splits <= 1 && epi != GEMM_SILU) {
+  if (two && !a.partial && epi == GEMM_SILU) return;   // needs the split-K planes (caller bug)
+  if (two && (splits <= 1 || !a.partial) && epi != GEMM_SILU) {
     // tiles that fill the GPU: the second plane's pass adds into the output
     a.partial = nullptr;
     a.k_chunk = a.K;
