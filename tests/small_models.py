@@ -29,6 +29,11 @@ QWEN_HD64_G7 = C.shrink_model(C.QWEN05B, name="qwen-hd64-g7", vocab=97, hidden=4
 LLAMA_MHA = C.shrink_model(C.LLAMA1B, name="llama-mha", vocab=131, hidden=128, layers=2,
                            heads=4, kv_heads=4, head_dim=64, ffn=192)
 
+# at most 64 rows against >= 192 output tiles of 64 (vocabulary 16384, gate/up 12288
+# rows): the 64 x 64 GEMM tiles without split-K
+LLAMA_WIDE = C.shrink_model(C.LLAMA1B, name="llama-wide", vocab=16384, hidden=256, layers=2,
+                            heads=4, kv_heads=2, head_dim=64, ffn=6144)
+
 # long K against few output tiles: the projections take the split-K path
 LLAMA_SPLITK = C.shrink_model(C.LLAMA1B, name="llama-splitk", vocab=131, hidden=256, layers=2,
                               heads=4, kv_heads=2, head_dim=64, ffn=1024)

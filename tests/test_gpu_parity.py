@@ -11,8 +11,8 @@ import oracle as O
 import workloads as W
 from tests.gpu_util import TOL_EXACT, TOL_FAST, check_greedy, gpu_generate, rel_maxabs, say
 from tests.small_models import (ENCODER_HD128, ENCODER_SMALL, LLAMA_FF8K, LLAMA_HD64, LLAMA_MHA,
-                                LLAMA_SMALL, LLAMA_SPLITK, Q8_SMALL, QWEN_FF2K, QWEN_HD64_G7,
-                                QWEN_SMALL, TINY)
+                                LLAMA_SMALL, LLAMA_SPLITK, LLAMA_WIDE, Q8_SMALL, QWEN_FF2K,
+                                QWEN_HD64_G7, QWEN_SMALL, TINY)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +85,27 @@ def test_small_decoder_fast_bf16_logits(model, sharp):
     err = rel_maxabs(g_logits[:, 0], or_logits)
     say(f"max rel err {err.max():.3g}")
     assert err.max() < TOL_FAST
+
+
+def test_few_rows_many_tiles_fast():
+    """At most 64 rows against >= 192 output tiles (the vocabulary and the gate/up
+    projection of a wide model): prefill of 48 tokens per row and batched decode of three
+    rows, teacher-forced with the oracle's ids, within the FAST tier."""
+    from gqa_decoder_transformer_amd import binding as B
+    model = LLAMA_WIDE
+    ck = W.make_weights(model, 42)
+    Bn, T, N = 3, 48, 5
+    prompt = np.random.default_rng(43).integers(0, model.vocab, (Bn, T)).astype(np.int32)
+    say(f"few rows, many tiles: {model.name} B={Bn} T={T} N={N} FAST")
+    om = O.OracleModel(model, ck)
+    orc = [O.generate(om, prompt[b], N) for b in range(Bn)]
+    feed = np.stack([ids[:N] for ids, _ in orc], 1)
+    eng = _engine(model, ck, B.FAST, max_batch=Bn, max_seq=64, max_tokens=64)
+    _, g_logits = gpu_generate(eng, prompt, N, feed=feed, logits_dtype=B.BF16)
+    for b in range(Bn):
+        err = rel_maxabs(g_logits[:, b], orc[b][1])
+        say(f"row {b}: max rel err {err.max():.3g}")
+        assert err.max() < TOL_FAST
 
 
 @pytest.mark.parametrize("model", [ENCODER_SMALL, ENCODER_HD128], ids=lambda m: m.name)
