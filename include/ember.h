@@ -89,8 +89,9 @@ typedef struct ember_config {
                                 * F32, tied LM head only, hidden, ffn and heads * head_dim
                                 * multiples of 32. A one-token pass (batch-1 decode) reads
                                 * the blocks directly; multi-token passes dequantise each
-                                * matrix into a workspace copy first (bf16 for FAST, f32 for
-                                * EXACT) */
+                                * matrix into a workspace copy first: bf16 for FAST; for
+                                * EXACT a bf16 pair hi + lo (within 2^-17 of q * d), one
+                                * MFMA pass per plane */
   int32_t kv_dtype;            /* ember_dtype of the KV cache */
   int32_t precision;           /* ember_precision */
   int32_t max_batch;           /* rows per call */
