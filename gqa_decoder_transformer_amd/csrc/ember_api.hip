@@ -395,6 +395,17 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
                             dp.nsplit > 1 && dp.nsplit <= 4 &&
                             gemv_takes_parts(H, NH * HD, md->wk);
 
+  // q/k norm, RoPE and the K/V store of a prefill pass (QKV post-processing)
+  QkvPostArgs qa{};
+  qa.qkv = qkv; qa.M = ps.M; qa.NH = NH; qa.NKV = NKV; qa.HD = HD;
+  qa.tokens_per_row = ps.tpr; qa.b0 = ps.b0; qa.start_pos = ps.start; qa.d_pos = ps.d_pos;
+  qa.cos_t = md->at<float>(p.cos_t); qa.sin_t = md->at<float>(p.sin_t);
+  qa.q_norm = c.qk_norm ? md->at<float>(L.qn) : nullptr;
+  qa.k_norm = c.qk_norm ? md->at<float>(L.kn) : nullptr;
+  qa.eps = c.rms_eps; qa.q_out = q;
+  qa.k_cache = k_layer(cx.c, li); qa.v_cache = v_layer(cx.c, li);
+  qa.kv_bf16 = c.kv_dtype == EMBER_BF16; qa.max_seq = c.max_seq;
+
   // ---- attention block
   if (ps.path == PATH_GEMV) {
     GemvArgs g{};
@@ -409,7 +420,12 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka;
     g.w = (const uint16_t*)gemm_weights(cx, L.wqkv, L.wqkv_s, p.qkv_n, H, &g.w_lo);
     g.M = ps.M; g.N = p.qkv_n; g.K = H; g.bias = bqkv; g.c = qkv; g.ldc = p.qkv_n;
-    if (want(cx, EMBER_K_QKV)) launch_gemm(g, GEMM_STORE, st);
+    if (ps.attn == ATTN_FLASH) {
+      g.post = qa;
+      if (want(cx, EMBER_K_QKV)) launch_gemm(g, GEMM_QKV, st);
+    } else if (want(cx, EMBER_K_QKV)) {
+      launch_gemm(g, GEMM_STORE, st);
+    }
   } else {
     if (want_aux(cx)) launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, xb, nullptr, nullptr, 0, st);
     GemmF32Args g{};
@@ -419,16 +435,8 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     if (want(cx, EMBER_K_QKV)) launch_gemm_f32w(g, GEMM_STORE, st);
   }
 
-  QkvPostArgs qa{};
-  qa.qkv = qkv; qa.M = ps.M; qa.NH = NH; qa.NKV = NKV; qa.HD = HD;
-  qa.tokens_per_row = ps.tpr; qa.b0 = ps.b0; qa.start_pos = ps.start; qa.d_pos = ps.d_pos;
-  qa.cos_t = md->at<float>(p.cos_t); qa.sin_t = md->at<float>(p.sin_t);
-  qa.q_norm = c.qk_norm ? md->at<float>(L.qn) : nullptr;
-  qa.k_norm = c.qk_norm ? md->at<float>(L.kn) : nullptr;
-  qa.eps = c.rms_eps; qa.q_out = q;
-  qa.k_cache = k_layer(cx.c, li); qa.v_cache = v_layer(cx.c, li);
-  qa.kv_bf16 = c.kv_dtype == EMBER_BF16; qa.max_seq = c.max_seq;
-  if (want_aux(cx) && ps.attn == ATTN_FLASH) launch_qkv_post(qa, st);
+  // prefill on MFMA: the QKV GEMM applies the post-processing itself (GEMM_QKV)
+  if (want_aux(cx) && ps.attn == ATTN_FLASH && ps.path != PATH_MFMA) launch_qkv_post(qa, st);
 
   const bool planes_out = ps.path == PATH_MFMA;
   if (ps.attn == ATTN_FLASH) {

@@ -215,7 +215,11 @@ int gemv_num_blocks(int N, int epi, int K, int wk);
 
 // ------------------------------------------------------------------ GEMM (kernels_gemm.hip)
 
-enum GemmEpi { GEMM_STORE = 0, GEMM_RESID = 1, GEMM_SILU = 2 };
+// GEMM_QKV: the QKV projection of a prefill pass with its post-processing fused when
+// head_dim is 64 and K is not split (bias, optional q/k RMSNorm, rotate-half RoPE, q to
+// post.q_out, K/V into the cache at their positions; `c` is not written); otherwise a
+// plain store into `c` followed by launch_qkv_post(post).
+enum GemmEpi { GEMM_STORE = 0, GEMM_RESID = 1, GEMM_SILU = 2, GEMM_QKV = 3 };
 
 struct GemmArgs {
   // A: activations as bf16 planes [M, lda] (hi, and lo in EXACT mode; lo == null: one pass)
@@ -243,6 +247,7 @@ struct GemmArgs {
   float* partial;
   size_t partial_elems;
   int k_chunk;             // set by launch_gemm
+  QkvPostArgs post;        // GEMM_QKV only (post.qkv = c)
 };
 void launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
 // Sets the dynamic LDS limit of every GEMM kernel (call once before the first launch).

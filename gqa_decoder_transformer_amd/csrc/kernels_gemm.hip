@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(WM * WN * KG * kWave) k_gemm(GemmArgs a) {
   float biasv[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j)
-    biasv[j] = (EPI == GEMM_STORE && a.bias && !a.partial)
+    biasv[j] = ((EPI == GEMM_STORE || EPI == GEMM_QKV) && a.bias && !a.partial)
                    ? a.bias[min(n0 + wn0 + j * 32 + fr, a.N - 1)] : 0.f;
 
   u32x4_t rh[PF][CA], rl[PF][SPLIT ? CA : 1], rw[PF][CB];
@@ -253,6 +253,69 @@ __global__ void __launch_bounds__(WM * WN * KG * kWave) k_gemm(GemmArgs a) {
           if (col < a.N && row0 + dr < a.M) pb[dr * a.N] = acc[i][j][e];
         }
       }
+    return;
+  }
+  if constexpr (EPI == GEMM_QKV) {
+    // head_dim 64: the wave's columns start on a head, so fragment j (even) holds dims
+    // 0..31 of head (n0 + wn0 + 32 j) / 64 in this lane's column and fragment j + 1 dims
+    // 32..63: the rotate-half pair (d, d + 32) of a row sits in one lane, and the 32 lanes
+    // of a half-wave hold one row's 64 dims (the per-head norm is a 5-step lane sum).
+    // Heads run q, then k, then v ("ember scripts/reference_forward.py", rope; q/k norm
+    // before RoPE: "PII-Tracer serving/reference_forward.py", forward); K and V land at the
+    // token's explicit position (ember internals page, "cursor semantics").
+    const QkvPostArgs& qp = a.post;
+    const int start = qp.d_pos ? *qp.d_pos : qp.start_pos;
+#pragma unroll
+    for (int j = 0; j < TN; j += 2) {
+      const int hcol = n0 + wn0 + 32 * j;
+      if (hcol >= a.N) continue;                            // wave-uniform
+      const int h = hcol / 64;
+      const bool is_q = h < qp.NH, is_v = h >= qp.NH + qp.NKV;
+      const float* nw = is_q ? qp.q_norm : qp.k_norm;
+      const bool norm = nw != nullptr && !is_v;             // wave-uniform
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row0 = rb0 + i * 32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = row0 + 8 * (e / 4) + e % 4;
+          float x0 = acc[i][j][e] + biasv[j], x1 = acc[i][j + 1][e] + biasv[j + 1];
+          if (norm) {
+            float ss = x0 * x0 + x1 * x1;
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o);
+            const float rms = sqrtf(ss / 64.f + qp.eps);
+            x0 = x0 / rms * nw[fr];
+            x1 = x1 / rms * nw[fr + 32];
+          }
+          if (row >= a.M) continue;
+          const int p = start + row % qp.tokens_per_row;
+          float y0 = x0, y1 = x1;
+          if (!is_v) {
+            const float cs = qp.cos_t[(size_t)p * 32 + fr], sn = qp.sin_t[(size_t)p * 32 + fr];
+            y0 = x0 * cs - x1 * sn;
+            y1 = x1 * cs + x0 * sn;
+          }
+          if (is_q) {
+            float* dst = qp.q_out + (size_t)row * qp.NH * 64 + h * 64 + fr;
+            dst[0] = y0;
+            dst[32] = y1;
+          } else {
+            const int b = qp.b0 + row / qp.tokens_per_row;
+            const int kvh = is_v ? h - qp.NH - qp.NKV : h - qp.NH;
+            const size_t off = (((size_t)b * qp.NKV + kvh) * qp.max_seq + p) * 64 + fr;
+            void* cache = is_v ? qp.v_cache : qp.k_cache;
+            if (qp.kv_bf16) {
+              ((uint16_t*)cache)[off] = (uint16_t)f32_to_bf16_rne(y0);
+              ((uint16_t*)cache)[off + 32] = (uint16_t)f32_to_bf16_rne(y1);
+            } else {
+              ((float*)cache)[off] = y0;
+              ((float*)cache)[off + 32] = y1;
+            }
+          }
+        }
+      }
+    }
     return;
   }
 #pragma unroll
@@ -568,10 +631,26 @@ void gemm_init() {
   set_attrs_epi<GEMM_STORE>();
   set_attrs_epi<GEMM_RESID>();
   set_attrs_epi<GEMM_SILU>();
+  set_attrs_epi<GEMM_QKV>();
 }
 
 void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
   if (a0.M <= 0 || a0.N <= 0) return;
+  if (epi == GEMM_QKV) {
+    GemmArgs a = a0;
+    const int cfg = pick_cfg(a);
+    if (a0.post.HD != 64 || a0.w_lo || pick_splits(a, cfg) > 1) {
+      QkvPostArgs pa = a0.post;
+      pa.qkv = a0.c;
+      launch_gemm(a, GEMM_STORE, st);                // raw projections into c, then
+      launch_qkv_post(pa, st);                       // the separate post-processing
+      return;
+    }
+    a.partial = nullptr;
+    a.k_chunk = a.K;
+    launch_epi<GEMM_QKV>(a, cfg, 1, st);
+    return;
+  }
   GemmArgs a = a0;
   a.w_lo = nullptr;
   const bool two = a0.w_lo != nullptr;

@@ -34,6 +34,12 @@ LLAMA_MHA = C.shrink_model(C.LLAMA1B, name="llama-mha", vocab=131, hidden=128, l
 LLAMA_WIDE = C.shrink_model(C.LLAMA1B, name="llama-wide", vocab=16384, hidden=256, layers=2,
                             heads=4, kv_heads=2, head_dim=64, ffn=6144)
 
+# head_dim 64 with 96 heads' worth of QKV columns (64 q + 2 x 16 kv): at 65-128 tokens per
+# pass the QKV GEMM fills >= 192 tiles without split-K, so the post-processing (bias,
+# q/k RMSNorm, RoPE, K/V store) runs in its epilogue
+QWEN_QKV_WIDE = C.shrink_model(C.QWEN05B, name="qwen-qkv-wide", vocab=256, hidden=512, layers=2,
+                               heads=64, kv_heads=16, head_dim=64, ffn=256, qk_norm=True)
+
 # long K against few output tiles: the projections take the split-K path
 LLAMA_SPLITK = C.shrink_model(C.LLAMA1B, name="llama-splitk", vocab=131, hidden=256, layers=2,
                               heads=4, kv_heads=2, head_dim=64, ffn=1024)

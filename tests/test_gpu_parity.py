@@ -12,7 +12,7 @@ import workloads as W
 from tests.gpu_util import TOL_EXACT, TOL_FAST, check_greedy, gpu_generate, rel_maxabs, say
 from tests.small_models import (ENCODER_HD128, ENCODER_SMALL, LLAMA_FF8K, LLAMA_HD64, LLAMA_MHA,
                                 LLAMA_SMALL, LLAMA_SPLITK, LLAMA_WIDE, Q8_SMALL, QWEN_FF2K,
-                                QWEN_HD64_G7, QWEN_SMALL, TINY)
+                                QWEN_HD64_G7, QWEN_QKV_WIDE, QWEN_SMALL, TINY)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +85,31 @@ def test_small_decoder_fast_bf16_logits(model, sharp):
     err = rel_maxabs(g_logits[:, 0], or_logits)
     say(f"max rel err {err.max():.3g}")
     assert err.max() < TOL_FAST
+
+
+@pytest.mark.parametrize("prec_name", ["exact", "fast"])
+def test_qkv_epilogue_with_norm_bias_and_chunked_positions(prec_name):
+    """q/k RMSNorm, QKV bias, RoPE and the K/V store inside the QKV GEMM's epilogue, over
+    two prefill passes (positions 0..127, then 128..199) and decode steps."""
+    from gqa_decoder_transformer_amd import binding as B
+    prec = B.EXACT if prec_name == "exact" else B.FAST
+    tol = TOL_EXACT if prec == B.EXACT else TOL_FAST
+    model = QWEN_QKV_WIDE
+    ck = W.make_weights(model, 44)
+    T, N = 200, 4
+    prompt = np.random.default_rng(45).integers(0, model.vocab, (1, T)).astype(np.int32)
+    say(f"QKV epilogue {model.name} T={T} N={N} {prec_name}")
+    om = O.OracleModel(model, ck)
+    or_ids, or_logits = O.generate(om, prompt[0], N)
+    eng = _engine(model, ck, prec, max_seq=256, max_tokens=128)
+    feed = or_ids[:N, None]
+    g_ids, g_logits = gpu_generate(eng, prompt, N, feed=feed,
+                                   logits_dtype=B.BF16 if prec == B.FAST else 0)
+    err = rel_maxabs(g_logits[:, 0], or_logits)
+    say(f"max rel err {err.max():.3g}")
+    assert err.max() < tol, err
+    if prec == B.EXACT:
+        check_greedy(g_ids[:, 0], or_ids, or_logits, tol)
 
 
 def test_few_rows_many_tiles_fast():
