@@ -40,6 +40,11 @@ LLAMA_WIDE = C.shrink_model(C.LLAMA1B, name="llama-wide", vocab=16384, hidden=25
 QWEN_QKV_WIDE = C.shrink_model(C.QWEN05B, name="qwen-qkv-wide", vocab=256, hidden=512, layers=2,
                                heads=64, kv_heads=16, head_dim=64, ffn=256, qk_norm=True)
 
+# 32 heads of 64 (K = 2048 for the output projection: the row-per-block GEMV); one-row
+# decode at 150+ positions of a 512-position cache runs many key splits and their combine
+LLAMA_OFOLD = C.shrink_model(C.LLAMA1B, name="llama-ofold", vocab=256, hidden=256, layers=2,
+                             heads=32, kv_heads=8, head_dim=64, ffn=512)
+
 # long K against few output tiles: the projections take the split-K path
 LLAMA_SPLITK = C.shrink_model(C.LLAMA1B, name="llama-splitk", vocab=131, hidden=256, layers=2,
                               heads=4, kv_heads=2, head_dim=64, ffn=1024)

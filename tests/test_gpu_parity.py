@@ -11,7 +11,7 @@ import oracle as O
 import workloads as W
 from tests.gpu_util import TOL_EXACT, TOL_FAST, check_greedy, gpu_generate, rel_maxabs, say
 from tests.small_models import (ENCODER_HD128, ENCODER_SMALL, LLAMA_FF8K, LLAMA_HD64, LLAMA_MHA,
-                                LLAMA_SMALL, LLAMA_SPLITK, LLAMA_WIDE, Q8_SMALL, QWEN_FF2K,
+                                LLAMA_OFOLD, LLAMA_SMALL, LLAMA_SPLITK, LLAMA_WIDE, Q8_SMALL, QWEN_FF2K,
                                 QWEN_HD64_G7, QWEN_QKV_WIDE, QWEN_SMALL, TINY)
 
 pytestmark = pytest.mark.gpu
@@ -104,6 +104,31 @@ def test_qkv_epilogue_with_norm_bias_and_chunked_positions(prec_name):
     eng = _engine(model, ck, prec, max_seq=256, max_tokens=128)
     feed = or_ids[:N, None]
     g_ids, g_logits = gpu_generate(eng, prompt, N, feed=feed,
+                                   logits_dtype=B.BF16 if prec == B.FAST else 0)
+    err = rel_maxabs(g_logits[:, 0], or_logits)
+    say(f"max rel err {err.max():.3g}")
+    assert err.max() < tol, err
+    if prec == B.EXACT:
+        check_greedy(g_ids[:, 0], or_ids, or_logits, tol)
+
+
+@pytest.mark.parametrize("prec_name", ["exact", "fast"])
+def test_split_decode_with_row_per_block_output_gemv(prec_name):
+    """One-row decode of a model whose output projection (K = 2048) takes the row-per-block
+    GEMV: at positions 150..155 of a 512-position cache only the first key splits hold
+    keys (the rest hold never-written memory) and the combine kernel merges them."""
+    from gqa_decoder_transformer_amd import binding as B
+    prec = B.EXACT if prec_name == "exact" else B.FAST
+    tol = TOL_EXACT if prec == B.EXACT else TOL_FAST
+    model = LLAMA_OFOLD
+    ck = _sharp(W.make_weights(model, 46), 4.0)
+    T, N = 150, 6
+    prompt = np.random.default_rng(47).integers(0, model.vocab, (1, T)).astype(np.int32)
+    say(f"folded split combine {model.name} T={T} N={N} {prec_name}")
+    om = O.OracleModel(model, ck)
+    or_ids, or_logits = O.generate(om, prompt[0], N)
+    eng = _engine(model, ck, prec, max_seq=512, max_tokens=256)
+    g_ids, g_logits = gpu_generate(eng, prompt, N, feed=or_ids[:N, None],
                                    logits_dtype=B.BF16 if prec == B.FAST else 0)
     err = rel_maxabs(g_logits[:, 0], or_logits)
     say(f"max rel err {err.max():.3g}")
