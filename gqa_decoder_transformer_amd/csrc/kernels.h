@@ -64,6 +64,11 @@ struct QkvPostArgs {
   void* v_cache;
   bool kv_bf16;
   int max_seq;
+  // or (splits > 0) the projections as `splits` split-K partial planes [splits][M][N]
+  // (N = (NH + 2 NKV) HD) summed in plane order, plus `bias` [N] (or null); qkv unused
+  const float* partial;
+  int splits;
+  const float* bias;
 };
 // Per-head q/k RMSNorm (optional), rotate-half RoPE from the tables, K/V store at the
 // tokens' explicit positions.

@@ -639,7 +639,20 @@ void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
   if (epi == GEMM_QKV) {
     GemmArgs a = a0;
     const int cfg = pick_cfg(a);
-    if (a0.post.HD != 64 || a0.w_lo || pick_splits(a, cfg) > 1) {
+    const int splits = pick_splits(a, cfg);
+    if (!a0.w_lo && splits > 1) {
+      // split K: the post-processing kernel sums the partial planes itself (no reduce)
+      a.k_chunk = ((a.K + splits - 1) / splits + 63) / 64 * 64;
+      const int used = (a.K + a.k_chunk - 1) / a.k_chunk;
+      launch_epi<GEMM_STORE>(a, cfg, used, st);    // partial planes (epilogue skipped)
+      QkvPostArgs pa = a0.post;
+      pa.partial = a.partial;
+      pa.splits = used;
+      pa.bias = a0.bias;
+      launch_qkv_post(pa, st);
+      return;
+    }
+    if (a0.post.HD != 64 || a0.w_lo) {
       QkvPostArgs pa = a0.post;
       pa.qkv = a0.c;
       launch_gemm(a, GEMM_STORE, st);                // raw projections into c, then

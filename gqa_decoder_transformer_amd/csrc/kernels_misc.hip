@@ -224,8 +224,28 @@ __global__ void __launch_bounds__(256) k_qkv_post(QkvPostArgs a) {
   const int b = a.b0 + m / a.tokens_per_row;
   const int p = start + m % a.tokens_per_row;
   const bool is_q = h < a.NH, is_v = h >= a.NH + a.NKV;
-  const float* src = a.qkv + (size_t)m * (a.NH + 2 * a.NKV) * HD + (size_t)h * HD;
-  float x0 = live ? src[i] : 0.f, x1 = live ? src[i + HALF] : 0.f;
+  const int N = (a.NH + 2 * a.NKV) * HD;
+  float x0 = 0.f, x1 = 0.f;
+  if (a.splits > 0) {                 // split-K planes summed in order, then the bias
+    const float* src = a.partial + (size_t)m * N + (size_t)h * HD;
+    const size_t plane = (size_t)a.M * N;
+    if (live) {
+      x0 = src[i];
+      x1 = src[i + HALF];
+      for (int s = 1; s < a.splits; ++s) {
+        x0 += src[s * plane + i];
+        x1 += src[s * plane + i + HALF];
+      }
+      if (a.bias) {
+        x0 += a.bias[h * HD + i];
+        x1 += a.bias[h * HD + i + HALF];
+      }
+    }
+  } else {
+    const float* src = a.qkv + (size_t)m * N + (size_t)h * HD;
+    x0 = live ? src[i] : 0.f;
+    x1 = live ? src[i + HALF] : 0.f;
+  }
   const float c = live && !is_v ? a.cos_t[(size_t)p * HALF + i] : 0.f;
   const float sn = live && !is_v ? a.sin_t[(size_t)p * HALF + i] : 0.f;
   if (a.q_norm) {                    // q and k norms come together
