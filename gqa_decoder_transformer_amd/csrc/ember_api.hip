@@ -387,13 +387,15 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   const float* ln2 = md->at<float>(L.ln2);
   const float* bqkv = c.qkv_bias ? md->at<float>(L.bqkv) : nullptr;
   const float scale = (float)(1.0 / std::sqrt((double)HD));
+  // one-row decode: the output-projection GEMV can rebuild its input from up to
+  // `fold_max` attention split partials (no combine launch); its row-per-block layout
+  // takes up to 8, so the plan is capped there
+  const int fold_max = ps.attn == ATTN_DECODE && ps.path == PATH_GEMV
+                           ? gemv_parts_max(H, NH * HD, md->wk) : 0;
   DecodePlan dp{1, c.max_seq, NH / NKV};
-  if (ps.attn == ATTN_DECODE) dp = decode_split_plan(ps.M, NH, NKV, c.max_seq);
-  // one-row decode with at most 4 key splits: the output-projection GEMV rebuilds its
-  // input from the split partials (no combine launch)
-  const bool fuse_combine = ps.attn == ATTN_DECODE && ps.path == PATH_GEMV &&
-                            dp.nsplit > 1 && dp.nsplit <= 4 &&
-                            gemv_takes_parts(H, NH * HD, md->wk);
+  if (ps.attn == ATTN_DECODE)
+    dp = decode_split_plan(ps.M, NH, NKV, c.max_seq, fold_max > 4 ? fold_max : 64);
+  const bool fuse_combine = fold_max > 0 && dp.nsplit > 1 && dp.nsplit <= fold_max;
 
   // q/k norm, RoPE and the K/V store of a prefill pass (QKV post-processing)
   QkvPostArgs qa{};

@@ -198,10 +198,10 @@ struct GemvArgs {
   const float* x;
   const float* norm_w;
   // or (x == null) the input rebuilt from decode-attention split partials of one row:
-  // xpart [K / xp_hd heads][xp_nsplit][xp_hd + 2] = (m, l, acc[xp_hd]); xp_nsplit <= 4;
+  // xpart [K / xp_hd heads][xp_nsplit][xp_hd + 2] = (m, l, acc[xp_hd]);
   // x[h xp_hd + d] = sum_j acc_j[d] w_j / sum_j l_j w_j, w_j = e^(m_j - max m), over the
   // splits that hold a key up to the position (the k_attn_combine arithmetic); residual
-  // epilogue only, for shapes where gemv_takes_parts holds
+  // epilogue only, 1 <= xp_nsplit <= gemv_parts_max(N, K, wk)
   const float* xpart;
   int xp_nsplit, xp_hd, xp_chunk_min;
   const int* xp_pos;
@@ -214,8 +214,10 @@ struct GemvArgs {
   int* flags;
 };
 void launch_gemv(const GemvArgs& a, int epi, hipStream_t st);
-// whether the residual GEMV of this shape takes its input as attention partials (xpart)
-bool gemv_takes_parts(int N, int K, int wk);
+// The most decode-attention splits the residual GEMV of this shape can take as its input
+// (xpart): 4 in the row-per-wave layout (K <= 1024), 8 in the row-per-block layout with one
+// chunk per thread (bf16 / f32), 0 otherwise.
+int gemv_parts_max(int N, int K, int wk);
 int gemv_num_blocks(int N, int epi, int K, int wk);
 
 // ------------------------------------------------------------------ GEMM (kernels_gemm.hip)
@@ -350,6 +352,6 @@ void launch_attn_combine(const float* part, int B, int NH, int HD, int nsplit, c
 // Launch plan of decode attention: number of splits (1: no combine), minimum chunk of
 // keys per split, threads per block.
 struct DecodePlan { int nsplit, chunk_min, heads_per_block; };
-DecodePlan decode_split_plan(int B, int NH, int NKV, int max_seq);
+DecodePlan decode_split_plan(int B, int NH, int NKV, int max_seq, int max_splits = 64);
 
 }  // namespace ember

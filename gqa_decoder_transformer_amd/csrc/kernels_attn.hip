@@ -495,7 +495,7 @@ void launch_attn_combine(const float* part, int B, int NH, int HD, int nsplit, c
                      chunk_min, out_f32, out_hi, out_lo);
 }
 
-DecodePlan decode_split_plan(int B, int NH, int NKV, int max_seq) {
+DecodePlan decode_split_plan(int B, int NH, int NKV, int max_seq, int max_splits) {
   // Keys are split so that the grid covers the CUs: chunks of >= 64 keys, at most 64
   // splits (the combine keeps per-split weights in LDS). Few (row, head) pairs: one
   // query head per block, about 512 blocks; otherwise a whole kv group per block
@@ -512,6 +512,7 @@ DecodePlan decode_split_plan(int B, int NH, int NKV, int max_seq) {
   }
   if (ns > maxs) ns = maxs;
   if (ns > 64) ns = 64;
+  if (ns > max_splits) ns = max_splits;
   if (ns >= 2) {
     p.nsplit = ns;
     p.chunk_min = (max_seq + ns - 1) / ns;     // fixed ranges: split j holds [j c, j c + c)

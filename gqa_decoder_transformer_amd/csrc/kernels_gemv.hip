@@ -279,7 +279,10 @@ __global__ void __launch_bounds__(kThreads) k_gemv_wave(GemvArgs a) {
 }
 
 // ---------------------------------------------------------------- row per block
-template <typename WT, int EPI, int RPW, int U>
+constexpr int kBlockParts = 8;   // attention splits the row-per-block layout can take
+constexpr int kBlockPartRows = 8; // output rows per block when it rebuilds its input
+
+template <typename WT, int EPI, int RPW, int U, bool XP>
 __global__ void __launch_bounds__(kThreads) k_gemv_block(GemvArgs a) {
   constexpr int E = WTraits<WT>::E;
   constexpr int RU = (EPI == GEMV_SILU) ? 2 : 1;
@@ -310,23 +313,72 @@ __global__ void __launch_bounds__(kThreads) k_gemv_block(GemvArgs a) {
   };
 
   float xv[U][E], nv[U][E];
-#pragma unroll
-  for (int t = 0; t < U; ++t) {
-    const int c = threadIdx.x + kThreads * t;
-    load_chunk_f32<E>(a.x, min(c, nch - 1), c < nch, xv[t]);
-    if (a.norm_w) load_chunk_f32<E>(a.norm_w, min(c, nch - 1), c < nch, nv[t]);
-  }
   u32x4_t wa[U][NR];
   uint32_t sca[U][NR];
   int grp = blockIdx.x;
-  load_group(min(grp, ngroups - 1), wa, sca);
+  if constexpr (XP) {
+    // input rebuilt from the attention partials, once per block (a block covers
+    // kBlockPartRows output rows): the thread's one chunk lies inside one head, so it
+    // combines that head's splits for its E elements in registers (partials requested
+    // first, then the weights; splits at or past the number that hold keys are excluded
+    // by select: their memory may hold anything)
+    static_assert(U == 1 && !WTraits<WT>::kQ8, "one bf16 / f32 chunk per thread");
+    const int c = min((int)threadIdx.x, nch - 1);
+    const int k0 = c * E, h = k0 / a.xp_hd, d0 = k0 % a.xp_hd;
+    const int stride = a.xp_hd + 2;
+    const float* ph = a.xpart + (size_t)h * a.xp_nsplit * stride;
+    float mj[kBlockParts], lj[kBlockParts], aj[kBlockParts][E];
+#pragma unroll
+    for (int j = 0; j < kBlockParts; ++j) {
+      const float* pj = ph + (size_t)min(j, a.xp_nsplit - 1) * stride;
+      mj[j] = pj[0];
+      lj[j] = pj[1];
+#pragma unroll
+      for (int e = 0; e < E; e += 2) {
+        const float2 v = *(const float2*)(pj + 2 + d0 + e);
+        aj[j][e] = v.x;
+        aj[j][e + 1] = v.y;
+      }
+    }
+    load_group(min(grp, ngroups - 1), wa, sca);
+    __builtin_amdgcn_sched_barrier(0);              // every weight load issued before any wait
+    const int S = *a.xp_pos + 1;
+    int chunk = (S + a.xp_nsplit - 1) / a.xp_nsplit;
+    if (chunk < a.xp_chunk_min) chunk = a.xp_chunk_min;
+    const int nvs = (S + chunk - 1) / chunk;
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kBlockParts; ++j) M = j < nvs ? fmaxf(M, mj[j]) : M;
+    float L = 0.f, xs[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) xs[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kBlockParts; ++j) {
+      const float w = (j < nvs && mj[j] != -INFINITY) ? expf(mj[j] - M) : 0.f;
+      L = j < nvs ? fmaf(lj[j], w, L) : L;
+#pragma unroll
+      for (int e = 0; e < E; ++e) xs[e] = j < nvs ? fmaf(aj[j][e], w, xs[e]) : xs[e];
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const bool valid = (int)threadIdx.x < nch;
+#pragma unroll
+    for (int e = 0; e < E; ++e) xv[0][e] = valid ? xs[e] * inv : 0.f;
+  } else {
+#pragma unroll
+    for (int t = 0; t < U; ++t) {
+      const int c = threadIdx.x + kThreads * t;
+      load_chunk_f32<E>(a.x, min(c, nch - 1), c < nch, xv[t]);
+      if (a.norm_w) load_chunk_f32<E>(a.norm_w, min(c, nch - 1), c < nch, nv[t]);
+    }
+    load_group(min(grp, ngroups - 1), wa, sca);
+  }
 
   float ss = 0.f;
 #pragma unroll
   for (int t = 0; t < U; ++t)
 #pragma unroll
     for (int e = 0; e < E; ++e) ss += xv[t][e] * xv[t][e];
-  if (a.norm_w) {
+  if (!XP && a.norm_w) {
     ss = block_sum(ss, red);
     const float inv_rms = 1.0f / sqrtf(ss / (float)K + a.eps);
 #pragma unroll
@@ -501,7 +553,15 @@ void launch_wave(const GemvArgs& a, int blocks, hipStream_t st) {
 }
 template <typename WT, int EPI, int RPW, int U>
 void launch_block(const GemvArgs& a, int blocks, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemv_block<WT, EPI, RPW, U>), dim3(blocks), dim3(kThreads), 0, st, a);
+  if constexpr (EPI == GEMV_RESID && U == 1 && !WTraits<WT>::kQ8) {
+    if (a.xpart) {                  // kBlockPartRows rows per block: one rebuild serves them
+      const int pb = (a.N + kBlockPartRows - 1) / kBlockPartRows;
+      hipLaunchKernelGGL((k_gemv_block<WT, EPI, kBlockPartRows, U, true>), dim3(pb), dim3(kThreads), 0,
+                         st, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_gemv_block<WT, EPI, RPW, U, false>), dim3(blocks), dim3(kThreads), 0, st, a);
 }
 
 template <typename WT> constexpr int kind_of() {
@@ -547,18 +607,22 @@ int gemv_num_blocks(int N, int epi, int K, int wk) {
   return s.kind == SHAPE_WAVE ? s.blocks * kWaves : s.blocks;   // argmax partials written
 }
 
-// the rebuilt input lives in a 1024-entry LDS copy (row-per-wave layout only)
-bool gemv_takes_parts(int N, int K, int wk) {
-  return K <= 1024 && pick(N, K, wk, GEMV_RESID).kind == SHAPE_WAVE;
+// row per wave: the rebuilt input lives in a 1024-entry LDS copy (K <= 1024, 4 splits);
+// row per block: one bf16 / f32 chunk per thread combined in registers (8 splits)
+int gemv_parts_max(int N, int K, int wk) {
+  const Shape s = pick(N, K, wk, GEMV_RESID);
+  if (s.kind == SHAPE_WAVE) return K <= 1024 ? 4 : 0;
+  if (s.kind == SHAPE_BLOCK && s.u == 1 && wk != WK_Q8) return kBlockParts;
+  return 0;
 }
 
 void launch_gemv(const GemvArgs& a, int epi, hipStream_t st) {
   if (a.M != 1 || a.N <= 0 || (!a.x && !a.xpart)) return;   // one token, an input required
   const int wk = a.w_scale ? WK_Q8 : (a.w_bf16 ? WK_BF16 : WK_F32);
   if (wk == WK_Q8 && a.K % kQ8Block) return;                 // q8 rows are whole blocks
-  if (a.xpart && (epi != GEMV_RESID || !gemv_takes_parts(a.N, a.K, wk) ||
-                  a.xp_nsplit < 1 || a.xp_nsplit > 4))
-    return;                                                   // callers check gemv_takes_parts
+  if (a.xpart && (epi != GEMV_RESID || a.xp_nsplit < 1 ||
+                  a.xp_nsplit > gemv_parts_max(a.N, a.K, wk)))
+    return;                                                   // callers check gemv_parts_max
 #define EMBER_GEMV_CASE(E)                                               \
   case E:                                                                \
     if (wk == WK_Q8) launch_t<Q8, E>(a, st);                             \
