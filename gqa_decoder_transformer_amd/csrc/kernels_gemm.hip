@@ -17,8 +17,11 @@
 //
 // Epilogues: store (+bias), residual add (x += C), SiLU*up over the gate/up rows that
 // the weight repack interleaves in blocks of 32 (the lane holding gate column j of
-// fragment 2q holds the matching up column in fragment 2q + 1), or raw f32 partial tiles
-// for split-K.
+// fragment 2q holds the matching up column in fragment 2q + 1), the QKV post-processing
+// of a prefill pass for head_dim 64 (bias, q/k RMSNorm, rotate-half RoPE with the pair
+// (d, d + 32) in one lane, q out, K/V into the cache), or raw f32 partial tiles for
+// split-K. A second weight plane (w_lo: weights that bf16 cannot hold, as a bf16 pair)
+// runs as a second pass.
 #include "common.h"
 #include "kernels.h"
 
