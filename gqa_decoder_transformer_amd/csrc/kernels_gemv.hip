@@ -14,6 +14,11 @@
 //    output is reduced with DPP row sums + readlane (no block barrier).
 //  * row per block (up to 1024 chunks): thread t owns chunks t + 256 u; one block-wide
 //    sum of squares for the norm; per row group the four waves' partials meet in LDS.
+//  * the output projection of a one-row decode step can take its input as the decode
+//    attention's split partials (no combine launch): row per wave rebuilds it once per
+//    block into LDS (<= 4 splits); row per block with one chunk per thread combines the
+//    thread's head in registers (<= 8 splits), eight output rows per block so the
+//    partials are read by few blocks.
 //  * longer K: a block per output looping over K (shapes past the two layouts above).
 // Epilogues: store (+bias), residual add, SiLU*up (gate/up rows interleaved in blocks of
 // 32, see gu_row), logits with an argmax partial (value, then lowest index) per wave or block.
