@@ -330,18 +330,53 @@ void launch_argmax_reduce(const unsigned long long* part, int nparts, int R, int
   hipLaunchKernelGGL(k_argmax_reduce, dim3(R), dim3(kArgThreads), 0, st, part, nparts, next);
 }
 
-__global__ void __launch_bounds__(256) k_argmax_rows(const float* logits, int n, long long ld,
-                                                     int32_t* next, int* flags) {
-  __shared__ unsigned long long red[4];
+// One block of 1024 threads per row of logits, four 16-byte loads in flight per thread
+// when the rows are 16-byte aligned (else four 4-byte loads); the key keeps the lowest
+// index of equal maxima whatever the visiting order.
+constexpr int kArgRowThreads = 1024;
+__global__ void __launch_bounds__(kArgRowThreads) k_argmax_rows(const float* logits, int n,
+                                                                long long ld, int32_t* next,
+                                                                int* flags, int vec) {
+  __shared__ unsigned long long red[kArgRowThreads / kWave];
   const int r = blockIdx.x;
   const float* row = logits + (size_t)r * ld;
   unsigned long long k = 0;
   bool nan = false;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const float v = row[i];
+  auto take = [&](float v, int i) {
     nan |= (v != v);
-    unsigned long long key = argmax_key(v, (uint32_t)i);
+    const unsigned long long key = argmax_key(v, (uint32_t)i);
     k = key > k ? key : k;
+  };
+  int done = 0;
+  if (vec) {
+    const int n4 = n / 4;
+    const float4* r4 = (const float4*)row;
+    for (int i0 = 0; i0 < n4; i0 += 4 * kArgRowThreads) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = r4[min(i0 + (int)threadIdx.x + kArgRowThreads * u, n4 - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + (int)threadIdx.x + kArgRowThreads * u;
+        if (i < n4) {
+          take(v[u].x, 4 * i);
+          take(v[u].y, 4 * i + 1);
+          take(v[u].z, 4 * i + 2);
+          take(v[u].w, 4 * i + 3);
+        }
+      }
+    }
+    done = 4 * n4;
+  }
+  for (int i0 = done; i0 < n; i0 += 4 * kArgRowThreads) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = row[min(i0 + (int)threadIdx.x + kArgRowThreads * u, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + (int)threadIdx.x + kArgRowThreads * u;
+      if (i < n) take(v[u], i);
+    }
   }
   if (nan) atomicOr(&flags[kFlagNaN], 1);
   k = wave_max_u64(k);
@@ -349,15 +384,17 @@ __global__ void __launch_bounds__(256) k_argmax_rows(const float* logits, int n,
   __syncthreads();
   if (threadIdx.x == 0) {
     k = red[0];
-    for (int i = 1; i < (int)blockDim.x / kWave; ++i) k = red[i] > k ? red[i] : k;
+    for (int i = 1; i < kArgRowThreads / kWave; ++i) k = red[i] > k ? red[i] : k;
     next[r] = (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
   }
 }
 
 void launch_argmax_rows(const float* logits, int R, int n, long long ld, int32_t* next, int* flags,
                         hipStream_t st) {
-  if (R <= 0) return;
-  hipLaunchKernelGGL(k_argmax_rows, dim3(R), dim3(256), 0, st, logits, n, ld, next, flags);
+  if (R <= 0 || n <= 0) return;
+  const int vec = ld % 4 == 0 && ((uintptr_t)logits & 15) == 0;
+  hipLaunchKernelGGL(k_argmax_rows, dim3(R), dim3(kArgRowThreads), 0, st, logits, n, ld, next, flags,
+                     vec);
 }
 
 // ------------------------------------------------------------------ classification head
