@@ -206,84 +206,94 @@ void launch_rmsnorm(const float* x, const float* w, float eps, int R, int H, int
 }
 
 // ------------------------------------------------------------------ QKV epilogue
-// One thread per rotated pair (i, i + HD/2) of a head (rotate-half RoPE: "ember
-// scripts/reference_forward.py", rope), grid (tokens, pair blocks); the HD/2 pairs of a
-// head sit in adjacent lanes of one wave, so the optional per-head RMSNorm over HD ("PII-
-// Tracer serving/reference_forward.py", forward: q_norm / k_norm before RoPE) is a lane-
-// group sum. Value heads pass through. K and V are stored at the token's explicit position
-// (ember internals page, "cursor semantics"). Every thread issues its loads at once (a
-// wave looping over heads waited for one round trip per head).
+// One thread per two adjacent rotated pairs (i, i + HD/2) and (i + 1, i + 1 + HD/2) of a
+// head (rotate-half RoPE: "ember scripts/reference_forward.py", rope; 8-byte loads and
+// stores), grid (tokens, pair blocks); the HD/4 threads of a head sit in adjacent lanes of
+// one wave, so the optional per-head RMSNorm over HD ("PII-Tracer serving/
+// reference_forward.py", forward: q_norm / k_norm before RoPE) is a lane-group sum. Value
+// heads pass through. K and V are stored at the token's explicit position (ember internals
+// page, "cursor semantics"). Every thread issues its loads at once (a wave looping over
+// heads waited for one round trip per head).
 template <int HALF>
 __global__ void __launch_bounds__(256) k_qkv_post(QkvPostArgs a) {
-  constexpr int HD = 2 * HALF;
+  constexpr int HD = 2 * HALF, TPH = HALF / 2;      // two adjacent pairs per thread
   const int m = blockIdx.x;
   const int pidx = blockIdx.y * 256 + threadIdx.x;
-  const bool live = pidx < (a.NH + 2 * a.NKV) * HALF;   // whole heads live or dead
-  const int h = pidx / HALF, i = pidx % HALF;
+  const bool live = pidx < (a.NH + 2 * a.NKV) * TPH;    // whole heads live or dead
+  const int h = pidx / TPH, i = 2 * (pidx % TPH);       // pairs (i, i + HALF), (i + 1, ..)
   const int start = a.d_pos ? *a.d_pos : a.start_pos;
   const int b = a.b0 + m / a.tokens_per_row;
   const int p = start + m % a.tokens_per_row;
   const bool is_q = h < a.NH, is_v = h >= a.NH + a.NKV;
   const int N = (a.NH + 2 * a.NKV) * HD;
-  float x0 = 0.f, x1 = 0.f;
+  float2 x0 = make_float2(0.f, 0.f), x1 = make_float2(0.f, 0.f);
   if (a.splits > 0) {                 // split-K planes summed in order, then the bias
     const float* src = a.partial + (size_t)m * N + (size_t)h * HD;
     const size_t plane = (size_t)a.M * N;
     if (live) {
-      x0 = src[i];
-      x1 = src[i + HALF];
+      x0 = *(const float2*)(src + i);
+      x1 = *(const float2*)(src + i + HALF);
       for (int s = 1; s < a.splits; ++s) {
-        x0 += src[s * plane + i];
-        x1 += src[s * plane + i + HALF];
+        const float2 u0 = *(const float2*)(src + s * plane + i);
+        const float2 u1 = *(const float2*)(src + s * plane + i + HALF);
+        x0.x += u0.x; x0.y += u0.y;
+        x1.x += u1.x; x1.y += u1.y;
       }
       if (a.bias) {
-        x0 += a.bias[h * HD + i];
-        x1 += a.bias[h * HD + i + HALF];
+        const float2 b0 = *(const float2*)(a.bias + h * HD + i);
+        const float2 b1 = *(const float2*)(a.bias + h * HD + i + HALF);
+        x0.x += b0.x; x0.y += b0.y;
+        x1.x += b1.x; x1.y += b1.y;
       }
     }
-  } else {
+  } else if (live) {
     const float* src = a.qkv + (size_t)m * N + (size_t)h * HD;
-    x0 = live ? src[i] : 0.f;
-    x1 = live ? src[i + HALF] : 0.f;
+    x0 = *(const float2*)(src + i);
+    x1 = *(const float2*)(src + i + HALF);
   }
-  const float c = live && !is_v ? a.cos_t[(size_t)p * HALF + i] : 0.f;
-  const float sn = live && !is_v ? a.sin_t[(size_t)p * HALF + i] : 0.f;
+  float2 c = make_float2(0.f, 0.f), sn = make_float2(0.f, 0.f);
+  if (live && !is_v) {
+    c = *(const float2*)(a.cos_t + (size_t)p * HALF + i);
+    sn = *(const float2*)(a.sin_t + (size_t)p * HALF + i);
+  }
   if (a.q_norm) {                    // q and k norms come together
-    const float ss = group_sum<HALF>(x0 * x0 + x1 * x1);
+    const float ss = group_sum<TPH>(x0.x * x0.x + x0.y * x0.y + x1.x * x1.x + x1.y * x1.y);
     if (live && !is_v) {
       const float* nw = is_q ? a.q_norm : a.k_norm;
       const float rms = sqrtf(ss / (float)HD + a.eps);
-      x0 = x0 / rms * nw[i];
-      x1 = x1 / rms * nw[i + HALF];
+      const float2 w0 = *(const float2*)(nw + i), w1 = *(const float2*)(nw + i + HALF);
+      x0.x = x0.x / rms * w0.x; x0.y = x0.y / rms * w0.y;
+      x1.x = x1.x / rms * w1.x; x1.y = x1.y / rms * w1.y;
     }
   }
   if (!live) return;
-  float y0 = x0, y1 = x1;
+  float2 y0 = x0, y1 = x1;
   if (!is_v) {
-    y0 = x0 * c - x1 * sn;
-    y1 = x1 * c + x0 * sn;
+    y0 = make_float2(x0.x * c.x - x1.x * sn.x, x0.y * c.y - x1.y * sn.y);
+    y1 = make_float2(x1.x * c.x + x0.x * sn.x, x1.y * c.y + x0.y * sn.y);
   }
   if (is_q) {
     float* dst = a.q_out + (size_t)m * a.NH * HD + (size_t)h * HD;
-    dst[i] = y0;
-    dst[i + HALF] = y1;
+    *(float2*)(dst + i) = y0;
+    *(float2*)(dst + i + HALF) = y1;
     return;
   }
   const int kvh = is_v ? h - a.NH - a.NKV : h - a.NH;
   const size_t off = (((size_t)b * a.NKV + kvh) * a.max_seq + p) * HD;
   void* cache = is_v ? a.v_cache : a.k_cache;
   if (a.kv_bf16) {
-    ((uint16_t*)cache)[off + i] = (uint16_t)f32_to_bf16_rne(y0);
-    ((uint16_t*)cache)[off + i + HALF] = (uint16_t)f32_to_bf16_rne(y1);
+    *(uint32_t*)((uint16_t*)cache + off + i) = f32_to_bf16_rne(y0.x) | (f32_to_bf16_rne(y0.y) << 16);
+    *(uint32_t*)((uint16_t*)cache + off + i + HALF) =
+        f32_to_bf16_rne(y1.x) | (f32_to_bf16_rne(y1.y) << 16);
   } else {
-    ((float*)cache)[off + i] = y0;
-    ((float*)cache)[off + i + HALF] = y1;
+    *(float2*)((float*)cache + off + i) = y0;
+    *(float2*)((float*)cache + off + i + HALF) = y1;
   }
 }
 
 void launch_qkv_post(const QkvPostArgs& a, hipStream_t st) {
   if (a.M <= 0) return;
-  const dim3 grid(a.M, ((a.NH + 2 * a.NKV) * (a.HD / 2) + 255) / 256);
+  const dim3 grid(a.M, ((a.NH + 2 * a.NKV) * (a.HD / 4) + 255) / 256);
   switch (a.HD) {
     case 8: hipLaunchKernelGGL(k_qkv_post<4>, grid, dim3(256), 0, st, a); break;
     case 16: hipLaunchKernelGGL(k_qkv_post<8>, grid, dim3(256), 0, st, a); break;
