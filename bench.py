@@ -148,8 +148,8 @@ def calibrate_copy(nbytes):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU runs are "
-              "not part of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no "
+              "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
