@@ -234,7 +234,7 @@ class OracleModel:
 
 
 def generate(model: OracleModel, prompt, n_steps: int, max_seq: int | None = None,
-             progress=None, pick=None):
+             progress=None, pick=None, return_cache: bool = False):
     """Prefill once, then ``n_steps`` steps, one cached forward each (the NumPy
     reference's generation loop; ember internals page: one prefill and one cached step per
     new token). End-of-sequence ids are not special: the step count is fixed.
@@ -243,7 +243,7 @@ def generate(model: OracleModel, prompt, n_steps: int, max_seq: int | None = Non
     by default the greedy argmax. Returns ``(ids, logits)`` with ``logits[k]`` the head
     output after step ``k`` (``k = 0`` is the prefill's last position) and ``ids[k]`` the
     token picked from it: ``n_steps + 1`` of each, of which ``ids[0..n_steps-1]`` are fed
-    back.
+    back. With ``return_cache`` the ``KVCache`` after the last step is returned third.
     """
     if pick is None:
         def pick(k, lg):
@@ -256,6 +256,8 @@ def generate(model: OracleModel, prompt, n_steps: int, max_seq: int | None = Non
     for k in range(n_steps):
         logits.append(model.forward_token(ids[-1], T + k, cache))
         ids.append(int(pick(k + 1, logits[-1])))
+    if return_cache:
+        return np.array(ids, dtype=np.int64), np.stack(logits), cache
     return np.array(ids, dtype=np.int64), np.stack(logits)
 
 

@@ -38,6 +38,48 @@ def check_greedy(gpu_ids, or_ids, or_logits, tol):
     return None
 
 
+def gpu_decode(eng, first, start, n_steps, feed=None, logits_dtype=0, rows=None):
+    """``n_steps`` decode steps at positions ``start..`` after a prefill whose next ids are
+    the device tensor ``first`` [B]. With ``feed`` ([n_steps, B] ids) the steps are
+    teacher-forced, otherwise each consumes the previous argmax. Returns (ids [n_steps, B],
+    logits [n_steps, R, V]) for the batch rows ``rows`` (all when None); ids[k] is the
+    argmax written by step k."""
+    import torch
+    B = first.shape[0]
+    sel = None if rows is None else torch.as_tensor(list(rows), device=eng.device)
+    ids, logs = [], []
+    prev = first
+    for k in range(n_steps):
+        if feed is not None:
+            cur = torch.from_numpy(np.ascontiguousarray(feed[k], dtype=np.int32)).to(eng.device)
+        else:
+            cur = prev.clone()
+        out = torch.empty_like(cur)
+        eng.decode_step(cur, start + k, out)
+        ids.append(out)
+        lg = eng.logits(B, logits_dtype)
+        logs.append((lg if sel is None else lg.index_select(0, sel)).float().cpu())
+        prev = out
+    eng.sync()
+    return torch.stack(ids).cpu().numpy(), torch.stack(logs).numpy()
+
+
+def check_teacher_forced_ids(gpu_ids, or_logits, tol):
+    """Teacher-forced steps (the GPU fed the oracle's ids): the GPU's argmax must equal the
+    oracle's wherever the oracle's top-2 gap exceeds 2*eps (eps = tol * max|logit|); at a
+    closer pair either is a legitimate greedy choice, but only a token within 2*eps of the
+    maximum. Returns the number of near-tie steps where they differ."""
+    near = 0
+    for k in range(len(gpu_ids)):
+        lg = np.asarray(or_logits[k], np.float64)
+        eps = tol * np.abs(lg).max()
+        g = int(gpu_ids[k])
+        gap = lg.max() - lg[g]
+        assert gap <= 2 * eps, f"step {k}: GPU id {g} is {gap:.3g} below the oracle's maximum (2 eps {2 * eps:.3g})"
+        near += int(g != int(np.argmax(lg)))
+    return near
+
+
 def gpu_generate(eng, prompt, n_steps, feed=None, logits_dtype=0):
     """Prefill ``prompt [B, T]`` then ``n_steps`` decode steps on the GPU. With ``feed``
     ([n_steps, B] ids) the steps are teacher-forced; otherwise each step consumes the

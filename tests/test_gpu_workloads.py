@@ -1,0 +1,272 @@
+"""GPU parity on the five full-size workloads, through the C ABI, in the launch
+configuration the benchmark times.
+
+Every decoder workload is checked over its whole schedule: the prompt's prefill and
+every greedy decode step.
+* Free-running: the GPU consumes its own argmax. The ids must equal the oracle's; a
+  divergence is accepted only at a near tie (the GPU's token within 2 eps of the oracle's
+  maximum, eps = tol * max|logit|), and the logits are compared up to it.
+* Teacher-forced: the GPU is fed the oracle's ids, so every step's logits are comparable:
+  EXACT f32 logits within 1e-4 relative max-abs, FAST bf16 logits within 2e-2, and the
+  argmax equal to the oracle's wherever the oracle's top-2 gap exceeds 2 eps.
+The oracle runs each workload once per process (cached here); rows of a batch never
+interact, so the batched workloads are checked on sampled rows exactly.
+"""
+import time
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from tests.gpu_util import (TOL_EXACT, TOL_FAST, check_greedy, check_teacher_forced_ids,
+                            gpu_decode, gpu_generate, rel_maxabs, say)
+
+pytestmark = pytest.mark.gpu
+
+_ORACLE = {}
+
+
+def oracle_run(name, row=0, keep_cache=False):
+    """The oracle's greedy generation of workload `name`, batch row `row`, over the whole
+    schedule: (ids [N + 1], logits [N + 1, V], cache or None). Cached per process."""
+    key = (name, row)
+    if key not in _ORACLE or (keep_cache and _ORACLE[key][2] is None):
+        w = W.get(name)
+        ck = W.weights_for(w)
+        ids = W.make_ids(w)
+        om = O.OracleModel(w.model, ck)
+        say(f"oracle {name} row {row}: prompt {w.prompt_len}, {w.decode_steps} steps")
+        t0 = time.time()
+        prog = (lambda li: say(f"  oracle prefill layer {li}")) if w.prompt_len >= 4096 else None
+        res = O.generate(om, ids[row], w.decode_steps, max_seq=w.max_pos, progress=prog,
+                         return_cache=True)
+        say(f"oracle {name} row {row} done in {time.time() - t0:.1f} s")
+        _ORACLE[key] = (res[0], res[1], res[2] if keep_cache else None)
+    return _ORACLE[key]
+
+
+def _engine(name, precision, max_tokens=None):
+    from gqa_decoder_transformer_amd import binding as B
+    w = W.get(name)
+    cfg = B.make_config(w.model, precision=precision, max_batch=w.batch, max_seq=w.max_pos,
+                        max_tokens=max_tokens or w.batch * w.prompt_len)
+    return B.Engine(cfg, W.weights_for(w), poison=True)
+
+
+def _decoder_exact(name, keep_cache=False):
+    """Free-running then teacher-forced EXACT run of a batch-1 decoder workload."""
+    w = W.get(name)
+    n = w.decode_steps
+    or_ids, or_logits, cache = oracle_run(name, 0, keep_cache)
+    eng = _engine(name, 0)
+    prompt = W.make_ids(w)
+    say(f"{name} EXACT free-running: prefill {w.prompt_len} + {n} steps")
+    g_ids, g_logits = gpu_generate(eng, prompt, n)
+    err = rel_maxabs(g_logits[:, 0], or_logits)
+    div = check_greedy(g_ids[:, 0], or_ids, or_logits, TOL_EXACT)
+    upto = n + 1 if div is None else div + 1
+    say(f"{name} free-running: max rel err {err[:upto].max():.3g} over {upto} logit vectors, "
+        f"ids {'identical' if div is None else f'near-tie divergence at step {div}'}")
+    assert err[:upto].max() < TOL_EXACT, err
+    say(f"{name} EXACT teacher-forced: {n} steps")
+    t_ids, t_logits = gpu_generate(eng, prompt, n, feed=or_ids[:n, None])
+    terr = rel_maxabs(t_logits[:, 0], or_logits)
+    near = check_teacher_forced_ids(t_ids[:, 0], or_logits, TOL_EXACT)
+    say(f"{name} teacher-forced: max rel err {terr.max():.3g}, {near} near-tie id differences")
+    assert terr.max() < TOL_EXACT, terr
+    return eng, cache
+
+
+def _decoder_fast(name):
+    """FAST teacher-forced run of a batch-1 decoder workload over the whole schedule."""
+    from gqa_decoder_transformer_amd import binding as B
+    w = W.get(name)
+    n = w.decode_steps
+    or_ids, or_logits, _ = oracle_run(name, 0)
+    eng = _engine(name, B.FAST)
+    say(f"{name} FAST teacher-forced: prefill {w.prompt_len} + {n} steps, bf16 logits")
+    t_ids, t_logits = gpu_generate(eng, W.make_ids(w), n, feed=or_ids[:n, None],
+                                   logits_dtype=B.BF16)
+    err = rel_maxabs(t_logits[:, 0], or_logits)
+    near = check_teacher_forced_ids(t_ids[:, 0], or_logits, TOL_FAST)
+    say(f"{name} FAST: max rel err {err.max():.3g}, {near} near-tie id differences")
+    assert err.max() < TOL_FAST, err
+    eng.close()
+
+
+def test_tiny_workload_exact():
+    _decoder_exact("tiny")[0].close()
+
+
+@pytest.mark.timeout(600)
+def test_qwen05b_workload_exact_free_running_and_teacher_forced():
+    _decoder_exact("qwen05b")[0].close()
+
+
+@pytest.mark.timeout(600)
+def test_qwen05b_workload_fast_teacher_forced():
+    _decoder_fast("qwen05b")
+
+
+@pytest.mark.timeout(600)
+def test_qwen05b_q8_workload_exact_free_running_and_teacher_forced():
+    """The Qwen2.5-0.5B shape with q8_0 matrices, batch-1 decode in the launch
+    configuration the benchmark times."""
+    _decoder_exact("qwen05b-q8")[0].close()
+
+
+def _kv_readback(eng, cache, model, max_seq, layers, batch_row=0, n_pos=None, tol=TOL_EXACT):
+    """The GPU's KV cache ([layers][max_batch][NKV][max_seq][HD], K then V) against the
+    oracle's cache ([max_seq, NKV, HD] per layer) at positions 0..n_pos-1, per layer and
+    tensor: max |g - o| / max |o|."""
+    import torch
+    from gqa_decoder_transformer_amd import binding as B
+    L, NKV, HD = model.layers, model.kv_heads, model.head_dim
+    mb = eng.cfg.max_batch
+    dt = torch.float32 if eng.cfg.kv_dtype == B.F32 else torch.bfloat16
+    kv = eng.kv.view(dt).view(2, L, mb, NKV, max_seq, HD)
+    n_pos = max_seq if n_pos is None else n_pos
+    for li in layers:
+        for t, ref in ((0, cache.k[li]), (1, cache.v[li])):
+            g = kv[t, li, batch_row, :, :n_pos].float().cpu().numpy()      # [NKV, n, HD]
+            o = np.transpose(ref[:n_pos], (1, 0, 2))
+            err = np.abs(g - o).max() / np.abs(o).max()
+            say(f"KV readback layer {li} {'KV'[t]}: rel err {err:.3g}")
+            assert err < tol, (li, t, err)
+
+
+@pytest.mark.timeout(600)
+def test_llama1b_workload_exact_prefill_2048_and_256_steps():
+    """2048-token prefill and all 256 greedy steps, free-running and teacher-forced; then
+    the KV cache of the first and last layers read back against the oracle's."""
+    w = W.get("llama1b")
+    eng, cache = _decoder_exact("llama1b", keep_cache=True)
+    eng.sync()
+    _kv_readback(eng, cache, w.model, w.max_pos, (0, w.model.layers - 1))
+    eng.close()
+
+
+@pytest.mark.timeout(600)
+def test_llama1b_workload_fast_teacher_forced():
+    _decoder_fast("llama1b")
+    _ORACLE.pop(("llama1b", 0), None)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("prec_name", ["exact", "fast"])
+def test_encoder_workload_sampled_rows(prec_name):
+    """16 x 512 bidirectional encoder, run whole on the GPU; rows are independent, the
+    oracle checks rows 0, 7 and 15: head outputs within the tier at every token, and each
+    token's label (argmax of the 2-way head) equal to the oracle's unless the oracle's two
+    logits lie within 2 eps (eps = tol * max|logit| of the row)."""
+    from gqa_decoder_transformer_amd import binding as B
+    w = W.get("encoder")
+    prec = B.EXACT if prec_name == "exact" else B.FAST
+    tol = TOL_EXACT if prec == B.EXACT else TOL_FAST
+    ids = W.make_ids(w)
+    eng = _engine("encoder", prec)
+    say(f"encoder workload 16x512 precision={prec_name}")
+    nxt, allg = eng.prefill(ids, all_logits=True)
+    g = allg.cpu().numpy()
+    nxt = nxt.cpu().numpy()
+    eng.close()
+    assert np.array_equal(nxt, np.argmax(g, -1))          # the label kernel on its own logits
+    om = O.OracleModel(w.model, W.weights_for(w))
+    for r in (0, 7, 15):
+        ref = om.forward_sequence(ids[r], all_positions=True)
+        err = np.abs(g[r] - ref).max() / np.abs(ref).max()
+        eps = tol * np.abs(ref).max()
+        lab = np.argmax(ref, -1)
+        diff = np.nonzero(nxt[r] != lab)[0]
+        gaps = np.abs(ref[diff, 0] - ref[diff, 1])
+        say(f"row {r}: max rel err {err:.3g}; {diff.size} labels differ, all within 2 eps: "
+            f"{bool((gaps <= 2 * eps).all())}")
+        assert err < tol
+        assert (gaps <= 2 * eps).all(), (r, diff[gaps > 2 * eps])
+
+
+# ------------------------------------------------------------------ long-context decode
+
+_LONG = {}
+
+
+def _longctx_gpu(prec_name):
+    """One engine per precision, kept across the long-context tests: 64 x 8192 prefill (one
+    row per pass, as the benchmark runs it), then the 128 free-running greedy steps; the
+    ids of every row and the logits of rows 0 and 63 are kept."""
+    from gqa_decoder_transformer_amd import binding as B
+    if prec_name not in _LONG:
+        for k in list(_LONG):
+            _LONG.pop(k)[0].close()
+        w = W.get("longctx")
+        prec = B.EXACT if prec_name == "exact" else B.FAST
+        ldt = B.F32 if prec == B.EXACT else B.BF16
+        eng = _engine("longctx", prec, max_tokens=w.prompt_len)
+        say(f"longctx GPU prefill 64 x 8192 precision={prec_name}")
+        first, _ = eng.prefill(W.make_ids(w))
+        lg0 = eng.logits(w.batch, ldt).index_select(0, eng.torch.tensor([0, 63], device=eng.device))
+        first_ids = first.cpu().numpy()
+        ids, logs = gpu_decode(eng, first, w.prompt_len, w.decode_steps, logits_dtype=ldt,
+                               rows=(0, 63))
+        say(f"longctx GPU {w.decode_steps} free-running steps done")
+        ids = np.concatenate([first_ids[None], ids])                      # [129, 64]
+        logs = np.concatenate([lg0.float().cpu().numpy()[None], logs])   # [129, 2, V]
+        _LONG[prec_name] = (eng, ids, logs)
+    return _LONG[prec_name]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("row", [0, 63])
+def test_longctx_workload_exact_row(row):
+    """EXACT, f32 KV: row `row` of the batch-64 decode, all 128 steps, free-running against
+    the oracle's greedy ids, then teacher-forced (the row fed the oracle's ids, the other
+    rows their own) with f32 logits within 1e-4 at every step."""
+    import torch
+    w = W.get("longctx")
+    n = w.decode_steps
+    j = (0, 63).index(row)
+    or_ids, or_logits, _ = oracle_run("longctx", row)
+    eng, ids, logs = _longctx_gpu("exact")
+    err = rel_maxabs(logs[:, j], or_logits)
+    div = check_greedy(ids[:, row], or_ids, or_logits, TOL_EXACT)
+    upto = n + 1 if div is None else div + 1
+    say(f"longctx row {row} free-running: max rel err {err[:upto].max():.3g}, ids "
+        f"{'identical' if div is None else f'near-tie divergence at step {div}'}")
+    assert err[:upto].max() < TOL_EXACT, err
+    # teacher-forced from the prefill's cache (positions 0..8191 stay as prefilled; every
+    # step rewrites its own position before attending)
+    feed = ids[:n].copy()
+    feed[:, row] = or_ids[:n]
+    first = torch.from_numpy(feed[0].copy()).to(eng.device)
+    t_ids, t_logs = gpu_decode(eng, first, w.prompt_len, n, feed=feed, rows=(row,))
+    terr = rel_maxabs(t_logs[:, 0], or_logits[1:])
+    near = check_teacher_forced_ids(t_ids[:, row], or_logits[1:], TOL_EXACT)
+    say(f"longctx row {row} teacher-forced: max rel err {terr.max():.3g}, {near} near-tie id differences")
+    assert terr.max() < TOL_EXACT, terr
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("row", [0, 63])
+def test_longctx_workload_fast_row(row):
+    """FAST, bf16 KV: row `row` teacher-forced with the oracle's ids over all 128 steps,
+    bf16 logits within 2e-2 at every step (the prefill's last position included)."""
+    import torch
+    from gqa_decoder_transformer_amd import binding as B
+    w = W.get("longctx")
+    n = w.decode_steps
+    j = (0, 63).index(row)
+    or_ids, or_logits, _ = oracle_run("longctx", row)
+    eng, ids, logs = _longctx_gpu("fast")
+    assert rel_maxabs(logs[0, j], or_logits[0]) < TOL_FAST
+    feed = ids[:n].copy()
+    feed[:, row] = or_ids[:n]
+    first = torch.from_numpy(feed[0].copy()).to(eng.device)
+    t_ids, t_logs = gpu_decode(eng, first, w.prompt_len, n, feed=feed, logits_dtype=B.BF16,
+                               rows=(row,))
+    terr = rel_maxabs(t_logs[:, 0], or_logits[1:])
+    near = check_teacher_forced_ids(t_ids[:, row], or_logits[1:], TOL_FAST)
+    say(f"longctx FAST row {row} teacher-forced: max rel err {terr.max():.3g}, {near} near-tie id differences")
+    assert terr.max() < TOL_FAST, terr
+    if row == 63:
+        _LONG.pop("fast")[0].close()
