@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libember.so")
 SOURCES = ["ember_api.hip", "kernels_misc.hip", "kernels_gemv.hip", "kernels_gemm.hip",
-           "kernels_attn.hip", "kernels_flash.hip", "kernels_sample.hip"]
+           "kernels_attn.hip", "kernels_flash.hip", "kernels_sample.hip", "kernels_peak.hip"]
 ARCH = os.environ.get("EMBER_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
          # packed-fp32 VALU ops disabled for every kernel

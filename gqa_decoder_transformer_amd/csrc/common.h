@@ -38,6 +38,15 @@ EMBER_DEV void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
   lo = f32_to_bf16_rne(x - bf16_to_f32(hi));
 }
 
+// Split x = x0 + x1 + x2 into three bf16 planes, each the nearest bf16 of what the
+// previous ones leave; |x - x0 - x1 - x2| <= 2^-25 |x| (finite x).
+EMBER_DEV void split3_bf16(float x, uint32_t& x0, uint32_t& x1, uint32_t& x2) {
+  x0 = f32_to_bf16_rne(x);
+  const float r = x - bf16_to_f32(x0);
+  x1 = f32_to_bf16_rne(r);
+  x2 = f32_to_bf16_rne(r - bf16_to_f32(x1));
+}
+
 template <typename T>
 EMBER_DEV T wave_sum(T v) {
 #pragma unroll

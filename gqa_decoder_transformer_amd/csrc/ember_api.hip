@@ -68,7 +68,7 @@ struct Plan {
   size_t embed, fnorm, cls_w, cls_b, cos_t, sin_t;
   std::vector<LayerOff> layer;
   // activations
-  size_t ids, pos, row_pos, rope_cur, next, flags, x, xb, pa_hi, pa_lo, pb_hi, pb_lo, qkv, q, att, act, part,
+  size_t ids, pos, row_pos, rope_cur, next, flags, x, xb, pa_hi, pa_lo, pa_x2, pb_hi, pb_lo, qkv, q, att, act, part,
       logits, argpart, splitk, kvpack, samp_state, samp_tiles, embed_s, q8_scratch, sens_w,
       sens_b, sens_acc, sens_out;
   size_t splitk_elems, kvpack_elems;
@@ -179,6 +179,9 @@ Plan make_plan(const ember_config& c) {
   p.xb = take((size_t)Mx * H * 4);
   p.pa_hi = take((size_t)Mx * p.ka * 2);
   p.pa_lo = take((size_t)Mx * p.ka * 2);
+  // EXACT multi-token passes: the third plane of the QKV projection's input (q and k
+  // feed the attention scores, whose absolute error the softmax amplifies)
+  p.pa_x2 = uses_mfma(c) && c.precision == EMBER_EXACT ? take((size_t)Mx * p.ka * 2) : 0;
   p.pb_hi = take((size_t)Mx * FF * 2);
   p.pb_lo = take((size_t)Mx * FF * 2);
   p.qkv = take((size_t)Mx * p.qkv_n * 4);
@@ -207,7 +210,8 @@ Plan make_plan(const ember_config& c) {
     // tokens, or one row of up to max_seq keys, each row rounded up to a 64-key tile
     const bool tiled = uses_mfma(c) && (HD == 64 || HD == 128);
     const int cap_keys = (Mx > c.max_seq ? Mx : c.max_seq) + 64 * c.max_batch;
-    p.kvpack_elems = tiled ? (size_t)(c.precision == EMBER_EXACT ? 2 : 1) * 2 * NKV * cap_keys * HD : 0;
+    const bool ex = c.precision == EMBER_EXACT;
+    p.kvpack_elems = tiled ? (size_t)(kv_pack_kplanes(ex) + kv_pack_vplanes(ex)) * NKV * cap_keys * HD : 0;
     p.kvpack = p.kvpack_elems ? take(p.kvpack_elems * 2) : 0;
   }
   if (q8) {
@@ -416,13 +420,26 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     g.x = x; g.norm_w = ln1; g.eps = c.rms_eps; g.bias = bqkv; g.y = qkv; g.ldy = p.qkv_n;
     if (want(cx, EMBER_K_QKV)) launch_gemv(g, GEMV_STORE, st);
   } else if (ps.path == PATH_MFMA) {
-    if (want_aux(cx)) launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st);
+    uint16_t* pa_x2 = exact ? md->at<uint16_t>(p.pa_x2) : nullptr;
+    if (want_aux(cx))
+      launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st, pa_x2);
     GemmArgs g{};
     g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
     g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka;
     g.w = (const uint16_t*)gemm_weights(cx, L.wqkv, L.wqkv_s, p.qkv_n, H, &g.w_lo);
     g.M = ps.M; g.N = p.qkv_n; g.K = H; g.bias = bqkv; g.c = qkv; g.ldc = p.qkv_n;
-    if (ps.attn == ATTN_FLASH) {
+    if (exact) {
+      // EXACT: the input as three bf16 planes (within ~2^-25), so q and k are f32-level:
+      // planes hi + lo store the projections (+bias), the third plane adds into them;
+      // the post-processing (prefill) or the decode attention then reads them
+      if (want(cx, EMBER_K_QKV)) {
+        launch_gemm(g, GEMM_STORE, st);
+        GemmArgs g3 = g;
+        g3.a_hi = pa_x2; g3.a_lo = nullptr; g3.bias = nullptr;
+        launch_gemm(g3, GEMM_RESID, st);
+      }
+      if (want_aux(cx) && ps.attn == ATTN_FLASH) launch_qkv_post(qa, st);
+    } else if (ps.attn == ATTN_FLASH) {
       g.post = qa;
       if (want(cx, EMBER_K_QKV)) launch_gemm(g, GEMM_QKV, st);
     } else if (want(cx, EMBER_K_QKV)) {
@@ -461,7 +478,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
         ka.rows = ps.rows; ka.b0 = ps.b0; ka.key_end = key_end; ka.LK = kv_pack_lk(key_end);
         ka.split = exact;
         ka.kp = md->at<uint16_t>(p.kvpack);
-        ka.vt = ka.kp + need / 2;
+        ka.vt = ka.kp + (size_t)kv_pack_kplanes(exact) * ps.rows * NKV * ka.LK * HD;
         launch_kv_pack(ka, st);
         launch_flash_tiled(fa, ka.kp, ka.vt, ka.LK, exact, st);
       } else if (planes_out && flash_mfma_supported(HD)) {
@@ -1223,6 +1240,54 @@ ember_status ember_time_kernel(ember_model* md, ember_cache* cache, int32_t kern
   if (ge) (void)hipGraphExecDestroy(ge);
   HIP_TRY(hipGetLastError());
   *avg_us = ms * 1000.f / (float)(iters * reps);
+  return EMBER_OK;
+}
+
+ember_status ember_measure_peak(int32_t kind, void* d_buf, size_t bytes, int32_t iters,
+                                void* stream, float* out) {
+  g_last_error.clear();
+  if (!d_buf || !out || iters <= 0) return fail(EMBER_E_ARG, "bad arguments");
+  hipStream_t st = (hipStream_t)stream;
+  const size_t half = bytes / 2 / 4096 * 4096;
+  const size_t read_out = (size_t)kPeakReadBlocks * 256 * 4;
+  if (kind == EMBER_PEAK_COPY) {
+    if (half == 0) return fail(EMBER_E_ARG, "buffer too small for the copy");
+  } else if (kind == EMBER_PEAK_READ) {
+    if (bytes < 2 * read_out) return fail(EMBER_E_ARG, "buffer too small for the read");
+  } else if (kind == EMBER_PEAK_MFMA) {
+    if (bytes < (size_t)kPeakMfmaBlocks * 256 * 4)
+      return fail(EMBER_E_ARG, "the MFMA loop needs %zu bytes", (size_t)kPeakMfmaBlocks * 256 * 4);
+  } else {
+    return fail(EMBER_E_ARG, "unknown peak kind %d", kind);
+  }
+  double work = 0.0;
+  auto launch = [&]() {
+    if (kind == EMBER_PEAK_COPY) {
+      launch_peak_copy(d_buf, (char*)d_buf + half, half, st);
+      work = 2.0 * (double)half;
+    } else if (kind == EMBER_PEAK_READ) {
+      const size_t n = (bytes - read_out) / 4096 * 4096;
+      launch_peak_read((const char*)d_buf + read_out, n, (uint32_t*)d_buf, st);
+      work = (double)n;
+    } else {
+      work = launch_peak_mfma((float*)d_buf, st);
+    }
+  };
+  launch();                                  // warm-up
+  hipEvent_t e0, e1;
+  HIP_TRY(hipEventCreate(&e0));
+  HIP_TRY(hipEventCreate(&e1));
+  HIP_TRY(hipEventRecord(e0, st));
+  for (int i = 0; i < iters; ++i) launch();
+  HIP_TRY(hipEventRecord(e1, st));
+  HIP_TRY(hipEventSynchronize(e1));
+  float ms = 0.f;
+  HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  HIP_TRY(hipGetLastError());
+  const double per_s = work * iters / (ms * 1e-3);
+  *out = (float)(kind == EMBER_PEAK_MFMA ? per_s / 1e12 : per_s / 1e9);
   return EMBER_OK;
 }
 

@@ -43,10 +43,11 @@ void launch_q8_dequant(const uint8_t* q, const uint16_t* s, int N, int K, void* 
 
 // Row-wise RMSNorm of rows src_row(r) = r * row_step + row_off, r < R, of x [*, H]:
 // y = x / sqrt(mean(x^2) + eps) * w. Writes any of: out_f32 [R, H], planes hi/lo
-// [R, ld_plane] bf16 (lo may be null: single plane).
+// [R, ld_plane] bf16 (lo may be null: single plane); with x2 (needs lo) the three planes
+// y = hi + lo + x2 of split3_bf16 instead of the pair.
 void launch_rmsnorm(const float* x, const float* w, float eps, int R, int H, int row_step,
                     int row_off, float* out_f32, uint16_t* hi, uint16_t* lo, int ld_plane,
-                    hipStream_t st);
+                    hipStream_t st, uint16_t* x2 = nullptr);
 
 struct QkvPostArgs {
   const float* qkv;        // [M, (NH + 2 NKV) HD] raw projections (bias included)
@@ -298,7 +299,10 @@ void launch_flash_mfma(const FlashArgs& a, bool split, hipStream_t st);
 // zero up to LK = key_end rounded up to 64), read by the tiled attention:
 //   K   plane p: kp[(((p * rows + r) * NKV + g) * LK + key) * HD + d]
 //   V^T plane p: vt[(((p * rows + r) * NKV + g) * HD + d) * LK + key]
-// EXACT (split): plane 0 = bf16(x), plane 1 = bf16(x - plane 0); FAST: plane 0 only.
+// FAST: one plane each, bf16(x). EXACT (split): K in three planes x0 = bf16(x),
+// x1 = bf16(x - x0), x2 = bf16(x - x0 - x1) (their sum is x within ~2^-25 relative: the
+// scores q.k feed exp, so their absolute error must stay at f32 level however large they
+// are); V in two planes x0, x1 (within 2^-17: the P V product is a weighted mean).
 struct KvPackArgs {
   const void* k_cache;     // layer base [B_cache][NKV][max_seq][HD]
   const void* v_cache;
@@ -310,16 +314,30 @@ struct KvPackArgs {
   uint16_t* vt;
 };
 inline int kv_pack_lk(int key_end) { return (key_end + 63) / 64 * 64; }
+inline int kv_pack_kplanes(bool split) { return split ? 3 : 1; }
+inline int kv_pack_vplanes(bool split) { return split ? 2 : 1; }
 inline size_t kv_pack_elems(int rows, int NKV, int HD, int key_end, bool split) {
-  return (size_t)(split ? 2 : 1) * 2 * rows * NKV * kv_pack_lk(key_end) * HD;
+  return (size_t)(kv_pack_kplanes(split) + kv_pack_vplanes(split)) * rows * NKV *
+         kv_pack_lk(key_end) * HD;
 }
 void launch_kv_pack(const KvPackArgs& a, hipStream_t st);
+
 // Tiled MFMA prefill attention (head_dim 64 / 128) over the packed planes; queries from
 // `a.q`, output to a.out_hi / a.out_lo (planes) or a.out_f32. Sets its LDS limit on the
 // first call.
 void launch_flash_tiled(const FlashArgs& a, const uint16_t* kp, const uint16_t* vt, int LK,
                         bool split, hipStream_t st);
 void flash_init();
+
+// Measurement kernels (kernels_peak.hip): a streaming copy of `bytes` from src to dst, and
+// an MFMA-only loop over kPeakMfmaBlocks blocks of 256 threads that writes one float per
+// thread to `out` and returns the flops of one launch.
+constexpr int kPeakMfmaBlocks = 2048;
+constexpr int kPeakReadBlocks = 256 * 16;
+void launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
+// A streaming read of `bytes` at src; one word per thread of kPeakReadBlocks x 256 to out.
+void launch_peak_read(const void* src, size_t bytes, uint32_t* out, hipStream_t st);
+double launch_peak_mfma(float* out, hipStream_t st);
 
 struct DecodeAttnArgs {
   const float* qkv;        // [B, (NH + 2 NKV) HD] raw projections of the current token

@@ -17,8 +17,10 @@
 // Scores, the running max/sum and the rescaling are per lane (query l%16): the row
 // statistics only need the lanes l, l^16, l^32, l^48.
 //
-// Precision: EXACT splits q, k, v and p into bf16 hi + lo and forms hi*hi + hi*lo + lo*hi
-// (3 MFMAs per product, ~2^-17 relative); FAST uses bf16 hi only.
+// Precision: EXACT splits q and k into three bf16 planes and forms the six products
+// q_i k_j with i + j <= 2 (the scores are exponentiated, so their absolute error must stay
+// at the f32 level of q.k whatever their size); v and p into two planes hi + lo with
+// hi*hi + hi*lo + lo*hi (~2^-17 relative, 3 MFMAs). FAST uses one bf16 plane of each.
 #include "common.h"
 #include "kernels.h"
 
@@ -58,6 +60,7 @@ __global__ void __launch_bounds__(256) k_flash_mfma(FlashArgs a) {
   constexpr int NKS = HD / 32;         // 32-dim MFMA steps (Q K)
   constexpr int NDB = HD / 16;         // 16-dim output blocks
   __shared__ __align__(16) uint16_t Kh[BK * KS];
+  __shared__ __align__(16) uint16_t Km[SPLIT ? BK * KS : 8];
   __shared__ __align__(16) uint16_t Kl[SPLIT ? BK * KS : 8];
   __shared__ __align__(16) uint16_t Vh[HD * VS];
   __shared__ __align__(16) uint16_t Vl[SPLIT ? HD * VS : 8];
@@ -73,22 +76,24 @@ __global__ void __launch_bounds__(256) k_flash_mfma(FlashArgs a) {
   const int qpos = a.start_pos + qc;
   const size_t mrow = (size_t)r * a.tokens_per_row + qc;
 
-  // Q^T operand: lane holds q[query ql][ks*32 + 8g .. +7], split into hi/lo
-  bf16x8_t qh[NKS], qlo[NKS];
+  // Q^T operand: lane holds q[query ql][ks*32 + 8g .. +7], split into three planes
+  bf16x8_t qh[NKS], qm[NKS], qlo[NKS];
   {
     const float* qp = a.q + mrow * a.NH * HD + (size_t)h * HD;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      u32x4_t hv, lv;
+      u32x4_t hv, mv, lv;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t h0, l0, h1, l1;
-        split_bf16(qp[ks * 32 + 8 * g + 2 * j], h0, l0);
-        split_bf16(qp[ks * 32 + 8 * g + 2 * j + 1], h1, l1);
-        hv[j] = pack2(h0, h1);
-        lv[j] = pack2(l0, l1);
+        uint32_t a0, a1, a2, b0, b1, b2;
+        split3_bf16(qp[ks * 32 + 8 * g + 2 * j], a0, a1, a2);
+        split3_bf16(qp[ks * 32 + 8 * g + 2 * j + 1], b0, b1, b2);
+        hv[j] = pack2(a0, b0);
+        mv[j] = pack2(a1, b1);
+        lv[j] = pack2(a2, b2);
       }
       qh[ks] = as_bf16x8(hv);
+      qm[ks] = as_bf16x8(mv);
       qlo[ks] = as_bf16x8(lv);
     }
   }
@@ -132,11 +137,14 @@ __global__ void __launch_bounds__(256) k_flash_mfma(FlashArgs a) {
     for (int c = 0; c < CH; ++c) {
       const int id = threadIdx.x + 256 * c;
       const int key = id / (HD / 4), d4 = (id % (HD / 4)) * 4;
-      uint32_t hi[4], lo[4];
+      uint32_t hi[4], mi[4], lo[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) split_bf16(kreg[c][j], hi[j], lo[j]);
+      for (int j = 0; j < 4; ++j) split3_bf16(kreg[c][j], hi[j], mi[j], lo[j]);
       *(uint2*)(Kh + key * KS + d4) = make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
-      if (SPLIT) *(uint2*)(Kl + key * KS + d4) = make_uint2(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
+      if (SPLIT) {
+        *(uint2*)(Km + key * KS + d4) = make_uint2(pack2(mi[0], mi[1]), pack2(mi[2], mi[3]));
+        *(uint2*)(Kl + key * KS + d4) = make_uint2(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t vh, vl;
@@ -163,12 +171,16 @@ __global__ void __launch_bounds__(256) k_flash_mfma(FlashArgs a) {
       for (int ks = 0; ks < NKS; ++ks) {
         const int ro = (kb * 16 + ql) * KS + ks * 32 + 8 * g;
         const bf16x8_t kh = as_bf16x8(*(const u32x4_t*)(Kh + ro));
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[ks], s[kb], 0, 0, 0);
         if (SPLIT) {
+          const bf16x8_t km = as_bf16x8(*(const u32x4_t*)(Km + ro));
           const bf16x8_t kl = as_bf16x8(*(const u32x4_t*)(Kl + ro));
-          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qlo[ks], s[kb], 0, 0, 0);
           s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh[ks], s[kb], 0, 0, 0);
+          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qlo[ks], s[kb], 0, 0, 0);
+          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(km, qm[ks], s[kb], 0, 0, 0);
+          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(km, qh[ks], s[kb], 0, 0, 0);
+          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qm[ks], s[kb], 0, 0, 0);
         }
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[ks], s[kb], 0, 0, 0);
       }
     }
     // ---- mask, scale, online softmax (lane = query ql, keys k0 + 16kb + 4g + i)
@@ -302,18 +314,22 @@ __global__ void __launch_bounds__(256) k_kv_pack(KvPackArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) { kv[j] = 0.f; vv[j] = 0.f; }
     }
-    u32x4_t hi, lo;
+    u32x4_t k0p, k1p, k2p;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t h0, l0, h1, l1;
-      split_bf16(kv[2 * j], h0, l0);
-      split_bf16(kv[2 * j + 1], h1, l1);
-      hi[j] = pack2(h0, h1);
-      lo[j] = pack2(l0, l1);
+      uint32_t a0, a1, a2, b0, b1, b2;
+      split3_bf16(kv[2 * j], a0, a1, a2);
+      split3_bf16(kv[2 * j + 1], b0, b1, b2);
+      k0p[j] = pack2(a0, b0);
+      k1p[j] = pack2(a1, b1);
+      k2p[j] = pack2(a2, b2);
     }
     const size_t ko = kb + (size_t)pos * HD + d8;
-    *(u32x4_t*)(a.kp + ko) = hi;
-    if (a.split) *(u32x4_t*)(a.kp + kplane + ko) = lo;
+    *(u32x4_t*)(a.kp + ko) = k0p;
+    if (a.split) {
+      *(u32x4_t*)(a.kp + kplane + ko) = k1p;
+      *(u32x4_t*)(a.kp + 2 * kplane + ko) = k2p;
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) vs[key * (HD + 1) + d8 + j] = vv[j];
   }
@@ -360,25 +376,34 @@ __global__ void __launch_bounds__(256) k_kv_pack(KvPackArgs a) {
 // before its bf16 rounding; P is rounded with the hardware pack-convert); under the causal mask a wave
 // skips the tiles wholly past its last query; blocks are ordered so that each half of the
 // grid pairs long and short causal rows. Output rows go through LDS and leave as 16-byte stores.
-constexpr int kTQ = 128, kTK = 64;
+constexpr int kTK = 64;
 
+// EXACT keeps three K planes and two V planes per stage (k_kv_pack); at head_dim 128 two
+// such stages exceed the LDS, so that form runs one stage (tile j + 1 waits in registers
+// while tile j is consumed, then one more barrier per tile).
 template <int HD, bool SPLIT>
 struct TiledCfg {
-  static constexpr int NP = SPLIT ? 2 : 1;
+  static constexpr int NW = 4;                                 // waves of 32 queries
+  static constexpr int NT = NW * kWave, TQ = NW * 32;
+  static constexpr int NPK = SPLIT ? 3 : 1, NPV = SPLIT ? 2 : 1;
   static constexpr int KS = HD + 8, VS = kTK + 8;
   static constexpr int KTILE = kTK * KS, VTILE = HD * VS;
-  static constexpr int STAGE = NP * (KTILE + VTILE);           // bf16 elements
-  static constexpr size_t LDS = (size_t)2 * STAGE * 2;         // bytes, two stages
-  static_assert((size_t)4 * 32 * (HD + 1) * 4 <= LDS, "output staging fits");
+  static constexpr int STAGE = NPK * KTILE + NPV * VTILE;      // bf16 elements
+  static constexpr int NST = (SPLIT && HD == 128) ? 1 : 2;     // LDS stages
+  static constexpr size_t LDS = (size_t)NST * STAGE * 2;       // bytes
+  static_assert(LDS <= 160 * 1024, "LDS of one CU");
+  static_assert((size_t)NW * 32 * (HD + 1) * 4 <= LDS, "output staging fits");
+  static_assert(kTK * HD / 8 % NT == 0, "tile chunks per thread");
 };
 
 template <int HD, bool SPLIT>
-__global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t* kp,
-                                                     const uint16_t* vt, int LK) {
+__global__ void __launch_bounds__((TiledCfg<HD, SPLIT>::NT)) k_flash_tiled(FlashArgs a,
+                                                                         const uint16_t* kp,
+                                                                         const uint16_t* vt, int LK) {
   using C = TiledCfg<HD, SPLIT>;
-  constexpr int NP = C::NP, KS = C::KS, VS = C::VS;
+  constexpr int NPK = C::NPK, NPV = C::NPV, KS = C::KS, VS = C::VS, NT = C::NT, TQ = C::TQ;
   constexpr int NKS = HD / 16, NDB = HD / 32;
-  constexpr int CK = kTK * HD / 8 / 256;                         // 16-byte chunks per thread
+  constexpr int CK = kTK * HD / 8 / NT;                          // 16-byte chunks per thread
   extern __shared__ __align__(16) uint16_t sm[];
 
   // Dispatch order L (x fastest, then heads, then rows) -> tile: the first half of the
@@ -395,20 +420,22 @@ __global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int lq = lane % 32, hl = lane / 32;
   const int T = a.tokens_per_row;
-  const int q0 = qt * kTQ + wave * 32;
+  const int q0 = qt * TQ + wave * 32;
   const int qc = min(q0 + lq, T - 1);
   const int qpos = a.start_pos + qc;
   const size_t mrow = (size_t)r * T + qc;
   const int key_end = a.start_pos + T;
-  const int kend_blk = a.causal ? a.start_pos + min(T, (qt + 1) * kTQ) : key_end;
+  const int kend_blk = a.causal ? a.start_pos + min(T, (qt + 1) * TQ) : key_end;
   const int ntiles = (kend_blk + kTK - 1) / kTK;
   const int wq_first = a.start_pos + min(T - 1, q0);
   const int wq_last = a.start_pos + min(T - 1, q0 + 31);
 
   // Q^T operand: query lq, head dims 16 ks + 8 hl .. + 8, pre-multiplied by
-  // scale * log2(e) so that the products are base-2 logits directly
+  // scale * log2(e) so that the products are base-2 logits directly; EXACT: three planes
+  // q0 + q1 + q2 (as K), and the score is the sum of the six products q_i k_j with
+  // i + j <= 2 (the three left out are below 2^-24 of |q| |k|)
   const float c2 = a.scale * 1.4426950408889634f;
-  bf16x8_t qh[NKS], qlo[SPLIT ? NKS : 1];
+  bf16x8_t qh[NKS], qm[SPLIT ? NKS : 1], qlo[SPLIT ? NKS : 1];
   {
     const float* qp = a.q + mrow * a.NH * HD + (size_t)h * HD + 8 * hl;
 #pragma unroll
@@ -416,52 +443,54 @@ __global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t
       const float4 x0 = *(const float4*)(qp + 16 * ks), x1 = *(const float4*)(qp + 16 * ks + 4);
       const float xv[8] = {x0.x * c2, x0.y * c2, x0.z * c2, x0.w * c2,
                            x1.x * c2, x1.y * c2, x1.z * c2, x1.w * c2};
-      u32x4_t hv, lv;
+      u32x4_t hv, mv, lv;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t h0, l0, h1, l1;
-        split_bf16(xv[2 * j], h0, l0);
-        split_bf16(xv[2 * j + 1], h1, l1);
-        hv[j] = pack2(h0, h1);
-        lv[j] = pack2(l0, l1);
+        uint32_t a0, a1, a2, b0, b1, b2;
+        split3_bf16(xv[2 * j], a0, a1, a2);
+        split3_bf16(xv[2 * j + 1], b0, b1, b2);
+        hv[j] = pack2(a0, b0);
+        mv[j] = pack2(a1, b1);
+        lv[j] = pack2(a2, b2);
       }
       qh[ks] = as_bf16x8(hv);
-      if (SPLIT) qlo[ks] = as_bf16x8(lv);
+      if (SPLIT) {
+        qm[ks] = as_bf16x8(mv);
+        qlo[ks] = as_bf16x8(lv);
+      }
     }
   }
 
   // tile staging: thread chunk c covers K key id / (HD / 8), dims (id % (HD / 8)) * 8 and
-  // V^T head dim id / 8, keys (id % 8) * 8 (id = tid + 256 c)
+  // V^T head dim id / 8, keys (id % 8) * 8 (id = tid + NT c)
   const size_t plane = (size_t)a.rows * a.NKV * LK * HD;
   const uint16_t* kg = kp + ((size_t)r * a.NKV + g) * LK * HD;
   const uint16_t* vg = vt + ((size_t)r * a.NKV + g) * HD * LK;
-  u32x4_t rk[NP][CK], rv[NP][CK];
+  u32x4_t rk[NPK][CK], rv[NPV][CK];
   auto gload = [&](int j) {
     const int k0 = j * kTK;
 #pragma unroll
     for (int c = 0; c < CK; ++c) {
-      const int id = threadIdx.x + 256 * c;
+      const int id = threadIdx.x + NT * c;
       const size_t ko = (size_t)(k0 + id / (HD / 8)) * HD + (id % (HD / 8)) * 8;
       const size_t vo = (size_t)(id / 8) * LK + k0 + (id % 8) * 8;
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        rk[p][c] = *(const u32x4_t*)(kg + p * plane + ko);
-        rv[p][c] = *(const u32x4_t*)(vg + p * plane + vo);
-      }
+      for (int p = 0; p < NPK; ++p) rk[p][c] = *(const u32x4_t*)(kg + p * plane + ko);
+#pragma unroll
+      for (int p = 0; p < NPV; ++p) rv[p][c] = *(const u32x4_t*)(vg + p * plane + vo);
     }
   };
   auto sstore = [&](int s) {
     uint16_t* st = sm + s * C::STAGE;
 #pragma unroll
     for (int c = 0; c < CK; ++c) {
-      const int id = threadIdx.x + 256 * c;
+      const int id = threadIdx.x + NT * c;
       const int ko = (id / (HD / 8)) * KS + (id % (HD / 8)) * 8;
       const int vo = (id / 8) * VS + (id % 8) * 8;
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        *(u32x4_t*)(st + p * C::KTILE + ko) = rk[p][c];
-        *(u32x4_t*)(st + NP * C::KTILE + p * C::VTILE + vo) = rv[p][c];
-      }
+      for (int p = 0; p < NPK; ++p) *(u32x4_t*)(st + p * C::KTILE + ko) = rk[p][c];
+#pragma unroll
+      for (int p = 0; p < NPV; ++p) *(u32x4_t*)(st + NPK * C::KTILE + p * C::VTILE + vo) = rv[p][c];
     }
   };
 
@@ -484,39 +513,62 @@ __global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t
   sstore(0);
   __syncthreads();
   for (int j = 0; j < ntiles; ++j) {
-    const int s = j & 1;
+    const int s = C::NST == 2 ? (j & 1) : 0;
     if (j + 1 < ntiles) gload(j + 1);
     const int k0 = j * kTK;
     if (!a.causal || k0 <= wq_last) {                          // wave-uniform
       const uint16_t* st = sm + s * C::STAGE;
-      // every K fragment of the tile is read first; the two 32-key blocks' MFMA chains
-      // then alternate, so consecutive MFMAs are independent
       f32x16_t sc[2];
-      bf16x8_t kfh[2][NKS], kfl[2][SPLIT ? NKS : 1];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int ro = (kb * 32 + lq) * KS + 16 * ks + 8 * hl;
-          kfh[kb][ks] = as_bf16x8(*(const u32x4_t*)(st + ro));
-          if (SPLIT) kfl[kb][ks] = as_bf16x8(*(const u32x4_t*)(st + C::KTILE + ro));
-        }
-      if (HD == 64) __builtin_amdgcn_sched_barrier(0); // reads ahead of the MFMAs (HD 128: too
-                                                       // many registers for all of them)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
+      if (!SPLIT) {
+        // every K fragment of the tile is read first; the two 32-key blocks' MFMA chains
+        // then alternate, so consecutive MFMAs are independent
+        bf16x8_t kfh[2][NKS];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfh[kb][ks], qh[ks], sc[kb], 0, 0, 0);
-          if (SPLIT) {
-            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfh[kb][ks], qlo[ks], sc[kb], 0, 0, 0);
-            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfl[kb][ks], qh[ks], sc[kb], 0, 0, 0);
+          for (int kb = 0; kb < 2; ++kb)
+            kfh[kb][ks] = as_bf16x8(*(const u32x4_t*)(st + (kb * 32 + lq) * KS + 16 * ks + 8 * hl));
+        if (HD == 64) __builtin_amdgcn_sched_barrier(0); // reads ahead of the MFMAs (HD 128:
+                                                         // too many registers for all of them)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfh[kb][ks], qh[ks], sc[kb], 0, 0, 0);
+      } else {
+        // one 16-dim step at a time (three K planes of both 32-key blocks), the smaller
+        // products first; the two blocks' chains alternate
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          bf16x8_t k0f[2], k1f[2], k2f[2];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const int ro = (kb * 32 + lq) * KS + 16 * ks + 8 * hl;
+            k0f[kb] = as_bf16x8(*(const u32x4_t*)(st + ro));
+            k1f[kb] = as_bf16x8(*(const u32x4_t*)(st + C::KTILE + ro));
+            k2f[kb] = as_bf16x8(*(const u32x4_t*)(st + 2 * C::KTILE + ro));
+          }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k2f[kb], qh[ks], sc[kb], 0, 0, 0);
+            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f[kb], qlo[ks], sc[kb], 0, 0, 0);
+          }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f[kb], qm[ks], sc[kb], 0, 0, 0);
+            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f[kb], qh[ks], sc[kb], 0, 0, 0);
+          }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f[kb], qm[ks], sc[kb], 0, 0, 0);
+            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f[kb], qh[ks], sc[kb], 0, 0, 0);
           }
         }
+      }
       // keys past `klim` are masked with one compare and select per score, only on tiles
       // that cross the causal diagonal or the end of the keys (a wave-uniform branch)
       const bool need_mask = (a.causal && k0 + kTK - 1 > wq_first) || k0 + kTK > key_end;
@@ -572,7 +624,7 @@ __global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int vo = (db * 32 + lq) * VS + 16 * t + 8 * hl;   // keys stored permuted
-          const uint16_t* vb = st + NP * C::KTILE;
+          const uint16_t* vb = st + NPK * C::KTILE;
           const u32x4_t vh = *(const u32x4_t*)(vb + vo);
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vh), pbh, o[db], 0, 0, 0);
           if (SPLIT) {
@@ -583,8 +635,16 @@ __global__ void __launch_bounds__(256) k_flash_tiled(FlashArgs a, const uint16_t
         }
       }
     }
-    if (j + 1 < ntiles) sstore(s ^ 1);
-    __syncthreads();
+    if (C::NST == 2) {
+      if (j + 1 < ntiles) sstore(s ^ 1);
+      __syncthreads();
+    } else {
+      __syncthreads();                                         // tile j consumed
+      if (j + 1 < ntiles) {
+        sstore(0);
+        __syncthreads();
+      }
+    }
   }
 
   // normalise and stage the wave's 32 output rows (f32, padded) through LDS
@@ -657,11 +717,11 @@ void flash_init() {
 
 void launch_flash_tiled(const FlashArgs& a, const uint16_t* kp, const uint16_t* vt, int LK,
                         bool split, hipStream_t st) {
-  dim3 grid((a.tokens_per_row + kTQ - 1) / kTQ, a.NH, a.rows);
 #define EMBER_TILED(HDV, SP)                                                           \
   {                                                                                    \
-    const size_t lds = TiledCfg<HDV, SP>::LDS;                                         \
-    hipLaunchKernelGGL((k_flash_tiled<HDV, SP>), grid, dim3(256), lds, st, a, kp, vt, LK); \
+    using TC = TiledCfg<HDV, SP>;                                                      \
+    const dim3 grid((a.tokens_per_row + TC::TQ - 1) / TC::TQ, a.NH, a.rows);            \
+    hipLaunchKernelGGL((k_flash_tiled<HDV, SP>), grid, dim3(TC::NT), TC::LDS, st, a, kp, vt, LK); \
   }
   if (a.HD == 64) {
     if (split) EMBER_TILED(64, true) else EMBER_TILED(64, false)

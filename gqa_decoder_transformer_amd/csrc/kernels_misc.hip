@@ -125,7 +125,8 @@ void launch_q8_dequant(const uint8_t* q, const uint16_t* s, int N, int K, void* 
 // fixed-order block reduction.
 __global__ void __launch_bounds__(256) k_rmsnorm(const float* x, const float* w, float eps, int H,
                                                  int row_step, int row_off, float* out_f32,
-                                                 uint16_t* hi, uint16_t* lo, int ld_plane) {
+                                                 uint16_t* hi, uint16_t* lo, uint16_t* x2,
+                                                 int ld_plane) {
   __shared__ float red[16];
   const int r = blockIdx.x;
   const float* xr = x + ((size_t)r * row_step + row_off) * H;
@@ -137,10 +138,12 @@ __global__ void __launch_bounds__(256) k_rmsnorm(const float* x, const float* w,
     const float y = xr[i] / rms * w[i];
     if (out_f32) out_f32[(size_t)r * H + i] = y;
     if (hi) {
-      uint32_t h, l;
-      split_bf16(y, h, l);
+      uint32_t h, l, t = 0;
+      if (x2) split3_bf16(y, h, l, t);
+      else split_bf16(y, h, l);
       hi[(size_t)r * ld_plane + i] = (uint16_t)h;
       if (lo) lo[(size_t)r * ld_plane + i] = (uint16_t)l;
+      if (x2) x2[(size_t)r * ld_plane + i] = (uint16_t)t;
     }
   }
 }
@@ -151,7 +154,8 @@ __global__ void __launch_bounds__(256) k_rmsnorm(const float* x, const float* w,
 template <int NV>
 __global__ void __launch_bounds__(256) k_rmsnorm_v(const float* x, const float* w, float eps, int H,
                                                    int row_step, int row_off, float* out_f32,
-                                                   uint16_t* hi, uint16_t* lo, int ld_plane) {
+                                                   uint16_t* hi, uint16_t* lo, uint16_t* x2,
+                                                   int ld_plane) {
   __shared__ float red[16];
   const int r = blockIdx.x;
   const int H4 = H / 4;
@@ -178,9 +182,15 @@ __global__ void __launch_bounds__(256) k_rmsnorm_v(const float* x, const float* 
                   v[j].w / rms * wv.w};
     if (out_f32) ((float4*)(out_f32 + (size_t)r * H))[i] = make_float4(y[0], y[1], y[2], y[3]);
     if (hi) {
-      uint32_t h[4], l[4];
+      uint32_t h[4], l[4], t[4];
+      if (x2) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) split_bf16(y[e], h[e], l[e]);
+        for (int e = 0; e < 4; ++e) split3_bf16(y[e], h[e], l[e], t[e]);
+        ((uint2*)(x2 + (size_t)r * ld_plane))[i] = make_uint2(t[0] | (t[1] << 16), t[2] | (t[3] << 16));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_bf16(y[e], h[e], l[e]);
+      }
       ((uint2*)(hi + (size_t)r * ld_plane))[i] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       if (lo)
         ((uint2*)(lo + (size_t)r * ld_plane))[i] = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
@@ -190,19 +200,19 @@ __global__ void __launch_bounds__(256) k_rmsnorm_v(const float* x, const float* 
 
 void launch_rmsnorm(const float* x, const float* w, float eps, int R, int H, int row_step,
                     int row_off, float* out_f32, uint16_t* hi, uint16_t* lo, int ld_plane,
-                    hipStream_t st) {
+                    hipStream_t st, uint16_t* x2) {
   if (R <= 0) return;
   const int nv = (H / 4 + 255) / 256;
   if (H % 4 == 0 && (!hi || ld_plane % 4 == 0) && nv <= 4) {
     switch (nv) {
-      case 1: hipLaunchKernelGGL(k_rmsnorm_v<1>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, ld_plane); return;
-      case 2: hipLaunchKernelGGL(k_rmsnorm_v<2>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, ld_plane); return;
-      case 3: hipLaunchKernelGGL(k_rmsnorm_v<3>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, ld_plane); return;
-      default: hipLaunchKernelGGL(k_rmsnorm_v<4>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, ld_plane); return;
+      case 1: hipLaunchKernelGGL(k_rmsnorm_v<1>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, x2, ld_plane); return;
+      case 2: hipLaunchKernelGGL(k_rmsnorm_v<2>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, x2, ld_plane); return;
+      case 3: hipLaunchKernelGGL(k_rmsnorm_v<3>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, x2, ld_plane); return;
+      default: hipLaunchKernelGGL(k_rmsnorm_v<4>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, x2, ld_plane); return;
     }
   }
   hipLaunchKernelGGL(k_rmsnorm, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off,
-                     out_f32, hi, lo, ld_plane);
+                     out_f32, hi, lo, x2, ld_plane);
 }
 
 // ------------------------------------------------------------------ QKV epilogue

@@ -54,9 +54,16 @@ typedef enum ember_status {
  * Weights only (never a KV cache or an output dtype). */
 typedef enum ember_dtype { EMBER_F32 = 0, EMBER_BF16 = 1, EMBER_Q8_0 = 2 } ember_dtype;
 
-/* EXACT: every product is an f32-accurate product of the bf16 weight and the f32
- *        activation (decode: f32 FMA; prefill MFMA: activation split into two bf16
- *        planes hi + lo). KV cache must be F32 (f32 logits, 1e-4 tier).
+/* EXACT: f32 arithmetic on the bf16 weights (f32 logits, 1e-4 tier). Decode: f32 FMA on
+ *        weights widened in registers. Multi-token passes on bf16 MFMA: every GEMM
+ *        activation is split into two bf16 planes hi + lo (their sum within 2^-17 of the
+ *        f32 value; weights are exact in bf16, products exact in f32); the attention
+ *        scores q.k are formed from three planes of q and of k (six products, absolute
+ *        error at the f32 level of q.k however large the scores: they are exponentiated),
+ *        P and V from two planes each. KV cache must be F32. The softmax amplifies a
+ *        score error by its size, so with scores of magnitude ~100 and more (far beyond
+ *        initialised or typical trained models) f32 implementations themselves, this one
+ *        and a plain f32 reference, differ from the exact result by more than 1e-4.
  * FAST:  single-pass bf16 activations into the MFMA GEMMs and attention, f32
  *        accumulation, norms, softmax and residual (bf16 logits, 2e-2 tier). */
 typedef enum ember_precision { EMBER_EXACT = 0, EMBER_FAST = 1 } ember_precision;
@@ -120,15 +127,26 @@ typedef struct ember_cache ember_cache;
 
 /* Bytes of workspace ember_load_weights needs for `cfg` (repacked weights, RoPE tables,
  * activations for max_tokens tokens, split-K partials, logits [max_batch, out_dim] f32).
- * 0 if the config is invalid. */
+ * Sized once for the capacities in `cfg` so that no step allocates: the "ember internals"
+ * page, section "qk_scratch", keeps one score buffer reserved for max_seq_len and resized
+ * in place, so the hot path never calls the allocator; here every such buffer (scores,
+ * split partials, activations) is a fixed region of this workspace.
+ * Returns 0 if the config is invalid (no error code; ember_last_error() explains). */
 size_t ember_workspace_bytes(const ember_config* cfg);
 
 /* Bytes of a KV cache for `cfg`: K and V, [layers][max_batch][kv_heads][max_seq][head_dim]
- * of kv_dtype. 0 if the config is invalid. */
+ * of kv_dtype. Layout of the "ember internals" page, section "kv cache" / "layout": one
+ * contiguous block per layer holding every (kv) head and position, addressed by fixed
+ * strides; only kv_heads heads are stored (section "grouped-query attention (GQA)": the
+ * cache shrinks by heads / kv_heads). Returns 0 if the config is invalid. */
 size_t ember_kv_cache_bytes(const ember_config* cfg);
 
-/* Validate the config (zero dimensions, heads % kv_heads, even head_dim, dtypes,
- * capacities) and every tensor (presence, shape, dtype), then repack the weights into
+/* Model::new of "Falcon-H1-0.5B-Rust src/lib.rs": validate the config as its
+ * Config::validate does (zero dimensions -> EMBER_E_CONFIG, heads % kv_heads or odd
+ * head_dim -> EMBER_E_CONFIG; here also dtypes and capacities) and every tensor as its
+ * validate_weights does (a missing name -> EMBER_E_TENSOR_MISSING, a shape other than the
+ * config's -> EMBER_E_TENSOR_SHAPE; here also the dtype -> EMBER_E_DTYPE), then repack the
+ * weights into
  * `d_workspace` (QKV rows fused, gate/up rows interleaved, norm vectors and biases as
  * f32) and upload the RoPE cos/sin tables (angles in f64, rounded once to f32).
  * `d_workspace` must stay allocated and untouched while the model lives. Synchronises
@@ -189,7 +207,10 @@ ember_status ember_forward_with_activations(ember_model* model, ember_cache* cac
 ember_status ember_sensitivity(ember_model* model, float* d_out, void* stream);
 
 /* One cached greedy step for `batch` rows at position `pos` (causal configs only; every
- * row at the same position -- ember_decode_step_rows takes one per row):
+ * row at the same position -- ember_decode_step_rows takes one per row). The "ember
+ * internals" page, section "attention": after one prefill, one cached step per new token;
+ * section "cursor semantics": the step's K/V are written at the explicit position `pos`
+ * (never at an implicit cursor), read back by the same step's attention over 0..pos:
  * reads the ids d_ids [batch] int32 (device), writes their K/V at `pos`, attends over
  * positions 0..pos, and writes the argmax of the new logits to d_next [batch] int32
  * (device; may alias d_ids). Requires pos <= the cache's filled length (EMBER_E_STATE)
@@ -210,13 +231,19 @@ ember_status ember_decode_step_rows(ember_model* model, ember_cache* cache,
                                     int32_t* d_next, void* stream);
 
 /* Copy the head output of the most recent prefill / decode step, [batch, out_dim], into
- * d_out as EMBER_F32 or EMBER_BF16 (round to nearest even). EMBER_E_STATE before any
- * forward. */
+ * d_out (device, caller-owned) as EMBER_F32 or EMBER_BF16 (round to nearest even). For
+ * the tied LM head these are the logits E . rmsnorm(h) at each row's last position
+ * ("ember scripts/reference_forward.py", end of forward: the final norm, then the
+ * embedding matrix as the output projection). EMBER_E_STATE before any forward,
+ * EMBER_E_DTYPE for another dtype. Asynchronous on `stream`. */
 ember_status ember_logits(ember_model* model, void* d_out, int32_t dtype, void* stream);
 
 /* Synchronise `stream` and report device-side conditions raised since the last call:
  * an out-of-range decode id (EMBER_E_TOKEN) or a NaN logit (EMBER_E_NONFINITE); then
- * clear them. */
+ * clear them. These are the errors Model::logits of "Falcon-H1-0.5B-Rust src/lib.rs"
+ * returns as Result::Err(String) ("token ... outside vocabulary"; its test_cpu_logits
+ * requires finite logits), found here on the device after the work was enqueued, hence
+ * reported at the next sync. A HIP runtime error is EMBER_E_DEVICE. */
 ember_status ember_sync(ember_model* model, void* stream);
 
 /* Sampling ("ember internals" page, section "sampler"): the token of ember_prefill's and
@@ -259,10 +286,17 @@ ember_status ember_set_sampler(ember_model* model, const ember_sampler* sampler)
 ember_status ember_sample(ember_model* model, const float* d_logits, int32_t rows,
                           int64_t ld_logits, int32_t pos, int32_t* d_next, void* stream);
 
+/* Release the host handles of ember_cache_bind ("ForwardModel::create_cache" of the "ember
+ * internals" page) and ember_load_weights (Model::new of "Falcon-H1-0.5B-Rust
+ * src/lib.rs"). The caller's device buffers are not touched or freed; NULL is a no-op.
+ * Free a cache before the model it is bound to. */
 void ember_cache_free(ember_cache* cache);
 void ember_free(ember_model* model);
 
-/* Thread-local message describing the last error of this thread ("" if none). */
+/* Thread-local message describing the last error of this thread ("" if none): the
+ * String of the Result::Err that Config::validate, validate_weights and Model::logits of
+ * "Falcon-H1-0.5B-Rust src/lib.rs" return, here beside the ember_status code. The pointer
+ * stays valid until the thread's next ember_* call. */
 const char* ember_last_error(void);
 
 /* Host-only: the RoPE tables the library uploads, cos/sin [n_pos, head_dim/2] f32
@@ -295,6 +329,22 @@ typedef enum ember_kernel {
  * time only a finished sequence. EMBER_E_STATE if no such step has run. */
 ember_status ember_time_kernel(ember_model* model, ember_cache* cache, int32_t kernel,
                                int32_t phase, int32_t iters, void* stream, float* avg_us);
+
+/* Measurement support (not part of the forward pass): the achievable peaks that the
+ * kernels' roofline fractions are also reported against, beside the published ones.
+ *   EMBER_PEAK_COPY: a plain streaming copy from the first half of d_buf to the second
+ *     (16-byte loads and stores); *out = GB/s, counting bytes read plus bytes written.
+ *   EMBER_PEAK_READ: a streaming read of d_buf past its first 4 MiB (16-byte loads, four
+ *     in flight per thread), which receive one word per thread; *out = GB/s read.
+ *   EMBER_PEAK_MFMA: chains of v_mfma_f32_32x32x16_bf16 on register operands with no
+ *     memory traffic, 2048 blocks of 256 threads; *out = TFLOP/s (dense bf16); d_buf (at
+ *     least 2 MiB, device) receives one float per thread.
+ * One warm-up launch, then `iters` launches between two HIP events on `stream`
+ * (synchronised before returning). EMBER_E_ARG for a NULL pointer, iters < 1, an unknown
+ * kind or a buffer too small. */
+typedef enum ember_peak { EMBER_PEAK_COPY = 0, EMBER_PEAK_MFMA = 1, EMBER_PEAK_READ = 2 } ember_peak;
+ember_status ember_measure_peak(int32_t kind, void* d_buf, size_t bytes, int32_t iters,
+                                void* stream, float* out);
 
 #ifdef __cplusplus
 }

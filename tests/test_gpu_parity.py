@@ -45,9 +45,7 @@ def test_small_decoder_exact_prefill_and_decode(model, sharp):
     ck = W.make_weights(model, 11)
     if sharp:
         # scale q/k so the attention scores have standard deviation 5 (their std is
-        # (0.02 f)^2 H at init): strongly peaked, within the range of trained models. Far
-        # beyond that (std ~50+) the MFMA path's 2^-17 operand split alone moves the
-        # scores by ~1e-3.
+        # (0.02 f)^2 H at init): strongly peaked, within the range of trained models
         ck = _sharp(ck, float(np.sqrt(5.0 / (0.0004 * model.hidden))))
     T, N = 37, 12                     # ragged against 64-wide tiles
     prompt = np.random.default_rng(5).integers(0, model.vocab, (1, T)).astype(np.int32)
@@ -64,6 +62,48 @@ def test_small_decoder_exact_prefill_and_decode(model, sharp):
     _, allg = eng.prefill(prompt, all_logits=True)
     full = om.forward_sequence(prompt[0], all_positions=True)
     assert rel_maxabs(allg[0].cpu().numpy(), full).max() < TOL_EXACT
+
+
+@pytest.mark.parametrize("model", [LLAMA_HD64, QWEN_HD64_G7, LLAMA_SPLITK, ENCODER_HD128],
+                         ids=lambda m: m.name)
+def test_exact_x30_scores_within_the_f32_envelope(model):
+    """q and k scaled x30: attention scores with standard deviation 0.36 H (up to ~160 at
+    hidden 448), so a softmax weight moves by the score's absolute error. There the f32
+    oracle itself is off the exact (float64) result by up to ~7e-4, more than the 1e-4
+    tier, so the tier against it is not a meaningful test; the EXACT path is checked
+    against the float64 shadow instead, within twice the f32 oracle's own error at each
+    step (or 1e-4 where that is larger), teacher-forced with the f32 oracle's ids. The
+    MFMA attention reaches this only because q.k is formed from three bf16 planes of each
+    operand: with two, the planes' 2^-17 residual alone moved the scores by ~1e-3."""
+    from gqa_decoder_transformer_amd import binding as B
+    ck = _sharp(W.make_weights(model, 11), 30.0)
+    T, N = 37, 12
+    prompt = np.random.default_rng(5).integers(0, model.vocab, (1, T)).astype(np.int32)
+    say(f"x30 stress {model.name} T={T} N={N} EXACT")
+    if not model.causal:
+        ids = np.random.default_rng(7).integers(0, model.vocab, (3, 45)).astype(np.int32)
+        o32 = O.OracleModel(model, ck).encode(ids)
+        o64 = O.OracleModel(model, ck, dtype=np.float64).encode(ids)
+        eng = _engine(model, ck, B.EXACT, max_batch=3, max_seq=64, max_tokens=3 * 64)
+        _, allg = eng.prefill(ids, all_logits=True)
+        g = allg.cpu().numpy()
+        env = np.abs(o32 - o64).max() / np.abs(o64).max()
+        gerr = np.abs(g - o64).max() / np.abs(o64).max()
+        say(f"f32 oracle vs f64 {env:.3g}; GPU vs f64 {gerr:.3g}; GPU vs f32 "
+            f"{np.abs(g - o32).max() / np.abs(o32).max():.3g}")
+        assert gerr <= max(TOL_EXACT, 2 * env)
+        return
+    om32 = O.OracleModel(model, ck)
+    or_ids, or_logits = O.generate(om32, prompt[0], N)
+    _, l64 = O.generate(O.OracleModel(model, ck, dtype=np.float64), prompt[0], N,
+                        pick=lambda k, lg: int(or_ids[k]))
+    eng = _engine(model, ck, B.EXACT)
+    _, g = gpu_generate(eng, prompt, N, feed=or_ids[:N, None])
+    env = rel_maxabs(or_logits, l64)
+    gerr = rel_maxabs(g[:, 0], l64)
+    say(f"f32 oracle vs f64 max {env.max():.3g}; GPU vs f64 max {gerr.max():.3g}; GPU vs f32 "
+        f"max {rel_maxabs(g[:, 0], or_logits).max():.3g}")
+    assert (gerr <= np.maximum(TOL_EXACT, 2 * env)).all(), (gerr, env)
 
 
 @pytest.mark.parametrize("model", [QWEN_SMALL, LLAMA_SMALL, LLAMA_HD64, QWEN_HD64_G7, LLAMA_SPLITK,
@@ -321,8 +361,9 @@ def test_one_token_prompt_decodes_until_the_cache_is_full(model, prec_name):
 @pytest.mark.parametrize("prec_name", ["exact", "fast"])
 def test_small_q8_decoder_prefill_and_decode(model, prec_name):
     """q8_0 matrices ("ember internals", q8_0 blocks): one-token steps dequantise in the
-    GEMV's registers; the prompt's multi-token pass runs on a dequantised copy (f32 for
-    EXACT, bf16 for FAST). The oracle runs on the dequantised f32 weights."""
+    GEMV's registers; the prompt's multi-token pass runs on a dequantised copy (bf16 for
+    FAST; for EXACT the bf16 pair hi + lo, one MFMA pass per plane). The oracle runs on the
+    dequantised f32 weights."""
     from gqa_decoder_transformer_amd import binding as B
     ck = W.make_weights(model, 12)
     T, N = 37, 12
@@ -350,65 +391,6 @@ def test_small_q8_decoder_prefill_and_decode(model, prec_name):
     assert rel_maxabs(allg[0].cpu().numpy(), full).max() < tol
 
 
-# ----------------------------------------------------------------------------- workloads
-
-def _workload_case(name, steps=None, precision=None):
-    from gqa_decoder_transformer_amd import binding as B
-    w = W.get(name)
-    prec = B.EXACT if precision is None else precision
-    n = w.decode_steps if steps is None else steps
-    ck = W.weights_for(w)
-    prompt = W.make_ids(w)
-    say(f"workload {name}: weights seed {w.weight_seed}, ids seed {w.ids_seed}, "
-        f"{prompt.shape}, {n} steps, precision {prec}")
-    om = O.OracleModel(w.model, ck)
-    or_ids, or_logits = O.generate(om, prompt[0], n)
-    say(f"oracle done for {name}")
-    cfg = B.make_config(w.model, precision=prec, max_batch=w.batch, max_seq=w.max_pos,
-                        max_tokens=w.batch * w.prompt_len)
-    eng = B.Engine(cfg, ck, poison=True)
-    return eng, prompt, n, or_ids, or_logits
-
-
-def test_tiny_workload_exact():
-    eng, prompt, n, or_ids, or_logits = _workload_case("tiny")
-    g_ids, g_logits = gpu_generate(eng, prompt, n)
-    assert rel_maxabs(g_logits[:, 0], or_logits).max() < TOL_EXACT
-    assert check_greedy(g_ids[:, 0], or_ids, or_logits, TOL_EXACT) is None
-
-
-@pytest.mark.timeout(600)
-def test_qwen05b_q8_workload_exact_free_running_and_teacher_forced():
-    """The Qwen2.5-0.5B shape with q8_0 matrices, batch-1 decode in the launch
-    configuration the benchmark times."""
-    eng, prompt, n, or_ids, or_logits = _workload_case("qwen05b-q8")
-    g_ids, g_logits = gpu_generate(eng, prompt, n)
-    err = rel_maxabs(g_logits[:, 0], or_logits)
-    say(f"qwen05b-q8 free-running max rel err {err.max():.3g}")
-    div = check_greedy(g_ids[:, 0], or_ids, or_logits, TOL_EXACT)
-    upto = n + 1 if div is None else div + 1
-    assert err[:upto].max() < TOL_EXACT
-    t_ids, t_logits = gpu_generate(eng, prompt, n, feed=or_ids[:n, None])
-    terr = rel_maxabs(t_logits[:, 0], or_logits)
-    say(f"qwen05b-q8 teacher-forced max rel err {terr.max():.3g}")
-    assert terr.max() < TOL_EXACT
-
-
-@pytest.mark.timeout(600)
-def test_qwen05b_workload_exact_free_running_and_teacher_forced():
-    eng, prompt, n, or_ids, or_logits = _workload_case("qwen05b")
-    g_ids, g_logits = gpu_generate(eng, prompt, n)
-    err = rel_maxabs(g_logits[:, 0], or_logits)
-    say(f"qwen05b free-running max rel err {err.max():.3g}")
-    div = check_greedy(g_ids[:, 0], or_ids, or_logits, TOL_EXACT)
-    upto = n + 1 if div is None else div + 1
-    assert err[:upto].max() < TOL_EXACT
-    t_ids, t_logits = gpu_generate(eng, prompt, n, feed=or_ids[:n, None])
-    terr = rel_maxabs(t_logits[:, 0], or_logits)
-    say(f"qwen05b teacher-forced max rel err {terr.max():.3g}")
-    assert terr.max() < TOL_EXACT
-
-
 def test_long_ragged_prefill_mfma_attention_tiles():
     """130 tokens: three 64-query tiles (the last ragged) and several key tiles on the
     MFMA attention path, prefilled in two chunks at explicit positions."""
@@ -430,97 +412,35 @@ def test_long_ragged_prefill_mfma_attention_tiles():
             assert err < tol
 
 
-@pytest.mark.timeout(600)
-def test_llama1b_workload_exact_prefill_2048_and_decode():
-    eng, prompt, n, or_ids, or_logits = _workload_case("llama1b", steps=48)
-    g_ids, g_logits = gpu_generate(eng, prompt, n)
-    err = rel_maxabs(g_logits[:, 0], or_logits)
-    say(f"llama1b free-running max rel err {err.max():.3g}")
-    div = check_greedy(g_ids[:, 0], or_ids, or_logits, TOL_EXACT)
-    upto = n + 1 if div is None else div + 1
-    assert err[:upto].max() < TOL_EXACT
-
-
-@pytest.mark.timeout(600)
-def test_llama1b_workload_fast_bf16_logits_teacher_forced():
-    from gqa_decoder_transformer_amd import binding as B
-    eng, prompt, n, or_ids, or_logits = _workload_case("llama1b", steps=16, precision=B.FAST)
-    g_ids, g_logits = gpu_generate(eng, prompt, n, feed=or_ids[:n, None], logits_dtype=B.BF16)
-    err = rel_maxabs(g_logits[:, 0], or_logits)
-    say(f"llama1b FAST teacher-forced max rel err {err.max():.3g}")
-    assert err.max() < TOL_FAST
-
-
-@pytest.mark.timeout(600)
+@pytest.mark.parametrize("model", [LLAMA_HD64, QWEN_SMALL], ids=lambda m: m.name)
 @pytest.mark.parametrize("prec_name", ["exact", "fast"])
-def test_encoder_workload_sampled_rows(prec_name):
-    """16 x 512 bidirectional encoder, run whole on the GPU; rows are independent, the
-    oracle checks rows 0, 7 and 15."""
-    from gqa_decoder_transformer_amd import binding as B
-    w = W.get("encoder")
-    prec = B.EXACT if prec_name == "exact" else B.FAST
-    tol = TOL_EXACT if prec == B.EXACT else TOL_FAST
-    ck = W.weights_for(w)
-    ids = W.make_ids(w)
-    cfg = B.make_config(w.model, precision=prec, max_batch=w.batch, max_seq=w.prompt_len,
-                        max_tokens=w.batch * w.prompt_len)
-    eng = B.Engine(cfg, ck, poison=True)
-    say(f"encoder workload 16x512 precision={prec_name}")
-    nxt, allg = eng.prefill(ids, all_logits=True)
-    g = allg.cpu().numpy()
-    nxt = nxt.cpu().numpy()
-    om = O.OracleModel(w.model, ck)
-    for r in (0, 7, 15):
-        ref = om.forward_sequence(ids[r], all_positions=True)
-        err = np.abs(g[r] - ref).max() / np.abs(ref).max()
-        say(f"row {r}: max rel err {err:.3g}")
-        assert err < tol
-        if prec == B.EXACT:
-            assert np.array_equal(nxt[r], np.argmax(g[r], -1))
-
-
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("prec_name", ["exact", "fast"])
-def test_longctx_workload_sampled_rows(prec_name):
-    """64 rows x 8192 prompt tokens prefilled, then batched greedy decode at positions
-    8192.., run whole on the GPU (the benchmark's launch configuration: one row per
-    prefill pass, the batch-64 decode path). Rows never interact, so the oracle checks
-    sampled rows exactly: rows 0 and 63 (EXACT, f32 KV) or row 0 (FAST, bf16 KV), over the
-    first 6 decode steps, teacher-forced with the oracle's ids."""
+def test_kv_cache_contents_match_the_oracle(model, prec_name):
+    """The KV cache after a 37-token prefill and 5 decode steps, read back from the
+    caller's buffer ([layers][max_batch][NKV][max_seq][HD], K then V: the "ember internals"
+    page's "kv cache" layout) against the oracle's cache (k after q/k-norm and RoPE, v as
+    projected), every layer and position; positions never written keep the poison bytes
+    (no write lands past the explicit positions)."""
     import torch
     from gqa_decoder_transformer_amd import binding as B
-    w = W.get("longctx")
     prec = B.EXACT if prec_name == "exact" else B.FAST
     tol = TOL_EXACT if prec == B.EXACT else TOL_FAST
-    steps = 6
-    rows = (0, 63) if prec == B.EXACT else (0,)
-    ck = W.weights_for(w)
-    ids = W.make_ids(w)
-    om = O.OracleModel(w.model, ck)
-    ref = {}
-    for r in rows:
-        say(f"longctx oracle row {r}: 8192-token prefill + {steps} steps")
-        ref[r] = O.generate(om, ids[r], steps, max_seq=w.max_pos,
-                            progress=lambda li, r=r: say(f"  oracle row {r} layer {li}") if li % 4 == 3 else None)
-    del om
-    cfg = B.make_config(w.model, precision=prec, max_batch=w.batch, max_seq=w.max_pos,
-                        max_tokens=w.prompt_len)
-    eng = B.Engine(cfg, ck, poison=True)
-    say(f"longctx GPU prefill 64 x 8192 precision={prec_name}")
-    eng.prefill(ids)
-    logs = [eng.logits(w.batch, B.F32 if prec == B.EXACT else B.BF16).float().cpu().numpy()]
-    feed = np.zeros((steps, w.batch), np.int32)
-    for r in rows:
-        feed[:, r] = ref[r][0][:steps]
-    for k in range(steps):
-        cur = torch.from_numpy(feed[k].copy()).to(eng.device)
-        out = torch.empty_like(cur)
-        eng.decode_step(cur, w.prompt_len + k, out)
-        logs.append(eng.logits(w.batch, B.F32 if prec == B.EXACT else B.BF16).float().cpu().numpy())
-        say(f"decode step {k} done")
-    eng.sync()
-    logs = np.stack(logs)                        # [steps + 1, 64, V]
-    for r in rows:
-        err = rel_maxabs(logs[:, r], ref[r][1])
-        say(f"row {r}: max rel err {err.max():.3g}")
-        assert err.max() < tol
+    ck = _sharp(W.make_weights(model, 48), 4.0)
+    T, N, S = 37, 5, 64
+    prompt = np.random.default_rng(49).integers(0, model.vocab, (1, T)).astype(np.int32)
+    om = O.OracleModel(model, ck)
+    or_ids, _, cache = O.generate(om, prompt[0], N, max_seq=S, return_cache=True)
+    eng = _engine(model, ck, prec, max_seq=S)
+    gpu_generate(eng, prompt, N, feed=or_ids[:N, None])
+    L, NKV, HD = model.layers, model.kv_heads, model.head_dim
+    dt = torch.float32 if prec == B.EXACT else torch.bfloat16
+    kv = eng.kv.view(dt).view(2, L, 1, NKV, S, HD)
+    n = T + N
+    for li in range(L):
+        for t, ref in ((0, cache.k[li]), (1, cache.v[li])):
+            g = kv[t, li, 0, :, :n].float().cpu().numpy()
+            o = np.transpose(ref[:n], (1, 0, 2))
+            err = np.abs(g - o).max() / np.abs(o).max()
+            say(f"layer {li} {'KV'[t]}: rel err {err:.3g}")
+            assert err < tol
+    raw = eng.kv.view(2, L, 1, NKV, S, HD * (4 if prec == B.EXACT else 2))
+    assert bool((raw[:, :, :, :, n:] == 255).all())

@@ -231,7 +231,8 @@ def test_longctx_workload_exact_row(row):
     err = rel_maxabs(logs[:, j], or_logits)
     div = check_greedy(ids[:, row], or_ids, or_logits, TOL_EXACT)
     upto = n + 1 if div is None else div + 1
-    say(f"longctx row {row} free-running: max rel err {err[:upto].max():.3g}, ids "
+    say(f"longctx row {row} free-running: max rel err {err[:upto].max():.6g} (step "
+        f"{int(np.argmax(err[:upto]))}), ids {or_ids[:6].tolist()}... "
         f"{'identical' if div is None else f'near-tie divergence at step {div}'}")
     assert err[:upto].max() < TOL_EXACT, err
     # teacher-forced from the prefill's cache (positions 0..8191 stay as prefilled; every
