@@ -28,7 +28,7 @@ EXPORTED = ["ember_workspace_bytes", "ember_kv_cache_bytes", "ember_load_weights
             "ember_sync", "ember_cache_free", "ember_free", "ember_last_error",
             "ember_rope_table", "ember_time_kernel", "ember_set_sampler", "ember_sample",
             "ember_forward_with_activations", "ember_sensitivity", "ember_prefill_rows",
-            "ember_decode_step_rows", "ember_measure_peak"]
+            "ember_decode_step_rows", "ember_measure_peak", "ember_sample_noalloc"]
 K_LM_HEAD, K_QKV, K_ATTN, K_O, K_GATE_UP, K_DOWN, K_LAYER, K_SAMPLE = range(8)
 
 
@@ -107,6 +107,8 @@ def _load():
         "ember_decode_step_rows": (ctypes.c_int, [P, P, P, ctypes.c_int32, P, P, P]),
         "ember_measure_peak": (ctypes.c_int, [ctypes.c_int32, P, ctypes.c_size_t, ctypes.c_int32,
                                               P, ctypes.POINTER(ctypes.c_float)]),
+        "ember_sample_noalloc": (ctypes.c_int, [P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                                P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -245,6 +247,14 @@ def ember_measure_peak(kind: int, d_buf: int, nbytes: int, iters: int, stream: i
     out = ctypes.c_float()
     _check(LIB.ember_measure_peak(kind, d_buf, nbytes, iters, stream, ctypes.byref(out)))
     return out.value
+
+
+NOALLOC_MAX_ROWS = 16
+
+
+def ember_sample_noalloc(model: int, d_logits: int, rows: int, ld_logits: int, pos: int,
+                         d_next: int, stream: int):
+    _check(LIB.ember_sample_noalloc(model, d_logits, rows, ld_logits, pos, d_next, stream))
 
 
 # ------------------------------------------------------------------ marshalling helpers

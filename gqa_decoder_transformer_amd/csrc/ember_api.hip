@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1336,6 +1337,89 @@ ember_status ember_sample(ember_model* md, const float* d_logits, int32_t rows,
   else
     launch_argmax_rows(d_logits, rows, md->cfg.vocab, ld_logits, d_next, md->at<int>(md->plan.flags),
                        cx.st);
+  HIP_TRY(hipGetLastError());
+  return EMBER_OK;
+}
+
+// ------------------------------------------------------------------ no-allocation draw
+// ember_sample_noalloc keeps the sampler's per-row state and tile sums in this file-scope
+// device array instead of the model's workspace. Each GPU holds its own copy; host code
+// uses only the address hipGetSymbolAddress returns for the current device (the array's
+// name is a host-side stand-in, not a device address).
+namespace {
+
+constexpr size_t kNoAllocRowBytes =
+    (sizeof(SampleState) + (size_t)kSampleMaxTiles * 4 + 255) / 256 * 256;
+constexpr size_t kNoAllocBytes = (size_t)EMBER_NOALLOC_MAX_ROWS * kNoAllocRowBytes;
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device.
+ember_status scratch_for_device(char** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(EMBER_E_DEVICE, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(EMBER_E_DEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return EMBER_OK;
+}
+
+}  // namespace
+
+ember_status ember_sample_noalloc(ember_model* md, const float* d_logits, int32_t rows,
+                                  int64_t ld_logits, int32_t pos, int32_t* d_next, void* stream) {
+  g_last_error.clear();
+  if (!md || !d_logits || !d_next) return fail(EMBER_E_ARG, "NULL argument");
+  if (md->cfg.head_kind != EMBER_HEAD_TIED_LM) return fail(EMBER_E_STATE, "sampling needs the tied LM head");
+  if (rows < 1) return fail(EMBER_E_ARG, "rows must be >= 1");
+  if (rows > EMBER_NOALLOC_MAX_ROWS)
+    return fail(EMBER_E_CAPACITY, "%d rows beyond the no-allocation draw's maximum of %d", rows,
+                EMBER_NOALLOC_MAX_ROWS);
+  if (md->cfg.vocab > kSampleMaxVocab)
+    return fail(EMBER_E_CAPACITY, "vocabulary %d beyond the sampler's %d", md->cfg.vocab, kSampleMaxVocab);
+  if (ld_logits < md->cfg.vocab) return fail(EMBER_E_ARG, "row stride below the vocabulary");
+  if (pos < 0) return fail(EMBER_E_ARG, "negative draw row");
+  {
+    const ember_status s = check_draws(md, rows, pos);
+    if (s != EMBER_OK) return s;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (!md->sampling) {
+    // greedy: one block per row, no scratch
+    launch_argmax_rows(d_logits, rows, md->cfg.vocab, ld_logits, d_next, md->at<int>(md->plan.flags), st);
+    HIP_TRY(hipGetLastError());
+    return EMBER_OK;
+  }
+  char* base = nullptr;
+  {
+    const ember_status s = scratch_for_device(&base);
+    if (s != EMBER_OK) return s;
+  }
+  // the phases expect zeroed per-row state: clear it (a fill kernel, capture-safe) rather
+  // than trusting what the previous call on this GPU left
+  SampleState* state = (SampleState*)base;
+  float* tiles = (float*)(base + (size_t)EMBER_NOALLOC_MAX_ROWS * sizeof(SampleState));
+  launch_fill_i32((int*)state, (int)((size_t)rows * sizeof(SampleState) / 4), 0, st);
+  SampleArgs a{};
+  a.logits = d_logits; a.ld = ld_logits; a.R = rows; a.V = md->cfg.vocab;
+  a.temperature = md->samp.temperature; a.top_k = md->samp.top_k; a.top_p = md->samp.top_p;
+  a.uniform = md->samp.d_uniform; a.u_rows = md->samp.n_pos; a.u_ld = md->samp.ld;
+  a.col0 = 0; a.pos = pos; a.d_pos = nullptr;
+  a.next = d_next; a.flags = md->at<int>(md->plan.flags);
+  a.state = state;
+  a.tiles = tiles;
+  launch_sample(a, st);
   HIP_TRY(hipGetLastError());
   return EMBER_OK;
 }

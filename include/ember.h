@@ -286,6 +286,21 @@ ember_status ember_set_sampler(ember_model* model, const ember_sampler* sampler)
 ember_status ember_sample(ember_model* model, const float* d_logits, int32_t rows,
                           int64_t ld_logits, int32_t pos, int32_t* d_next, void* stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid device allocation): ember_sample with the same arguments and
+ * results, whose draw keeps its per-row scratch (radix-search histograms, counters and
+ * tile sums) in a fixed device array inside the library instead of the model's
+ * workspace. It calls no allocator. The array holds EMBER_NOALLOC_MAX_ROWS rows (about
+ * 90 KB each, ~1.4 MB per GPU, kept until the process ends); more rows fail with
+ * EMBER_E_CAPACITY and enqueue nothing. Each GPU has one such array shared by every call
+ * on it (every model): calls that overlap on one GPU (different streams, or threads)
+ * race and must not be issued; calls ordered on one stream are safe (each clears the
+ * state it uses first). With no sampler set it is the greedy argmax, which needs no
+ * scratch. Other errors as ember_sample. */
+#define EMBER_NOALLOC_MAX_ROWS 16
+ember_status ember_sample_noalloc(ember_model* model, const float* d_logits, int32_t rows,
+                                  int64_t ld_logits, int32_t pos, int32_t* d_next, void* stream);
+
 /* Release the host handles of ember_cache_bind ("ForwardModel::create_cache" of the "ember
  * internals" page) and ember_load_weights (Model::new of "Falcon-H1-0.5B-Rust
  * src/lib.rs"). The caller's device buffers are not touched or freed; NULL is a no-op.
