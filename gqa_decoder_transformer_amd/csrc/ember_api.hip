@@ -36,6 +36,26 @@ ember_status fail(ember_status s, const char* fmt, ...) {
   return s;
 }
 
+// The first launch wrapper of this thread's current call that found no kernel for its
+// arguments (see report_unlaunched), or null.
+thread_local const char* g_unlaunched = nullptr;
+
+}  // namespace
+
+void ember::report_unlaunched(const char* what) {
+  if (!g_unlaunched) g_unlaunched = what;
+}
+
+namespace {
+
+// EMBER_E_DEVICE if a launch of the current call launched nothing; clears the record.
+ember_status check_launched() {
+  const char* w = g_unlaunched;
+  g_unlaunched = nullptr;
+  if (w) return fail(EMBER_E_DEVICE, "internal error: no kernel for these arguments (%s)", w);
+  return EMBER_OK;
+}
+
 #define HIP_TRY(expr)                                                                   \
   do {                                                                                  \
     hipError_t e_ = (expr);                                                             \
@@ -926,6 +946,7 @@ ember_status prefill_impl(ember_model* md, ember_cache* cache, const int32_t* h_
   const Plan& p = md->plan;
   Ctx cx{md, cache, st};
   const int out_dim = c.head_kind == EMBER_HEAD_CLS ? c.n_classes : c.vocab;
+  g_unlaunched = nullptr;
   // passes: whole rows when a row fits max_tokens, else position chunks of one row
   const int T = n_tokens;
   const int rows_per_pass = T <= p.Mx ? (p.Mx / T < batch ? p.Mx / T : batch) : 1;
@@ -991,6 +1012,8 @@ ember_status prefill_impl(ember_model* md, ember_cache* cache, const int32_t* h_
                        nullptr);
       }
       HIP_TRY(hipGetLastError());
+      const ember_status ls = check_launched();
+      if (ls != EMBER_OK) return ls;
     }
   }
   for (int r = row0; r < row0 + batch; ++r)
@@ -1106,6 +1129,7 @@ ember_status decode_impl(ember_model* md, ember_cache* cache, const int32_t* d_i
   hipStream_t st = (hipStream_t)stream;
   const Plan& p = md->plan;
   Ctx cx{md, cache, st};
+  g_unlaunched = nullptr;
   if (h_pos)
     HIP_TRY(hipMemcpyAsync(md->at<int>(p.row_pos), h_pos, (size_t)batch * 4, hipMemcpyHostToDevice, st));
   StepBeginArgs sb{};
@@ -1133,6 +1157,12 @@ ember_status decode_impl(ember_model* md, ember_cache* cache, const int32_t* d_i
       hipError_t e = hipGraphInstantiate(&md->graph, g, nullptr, nullptr, 0);
       (void)hipGraphDestroy(g);
       if (e != hipSuccess) return fail(EMBER_E_DEVICE, "graph instantiate: %s", hipGetErrorString(e));
+      const ember_status ls = check_launched();
+      if (ls != EMBER_OK) {                 // never replay a step that misses a kernel
+        (void)hipGraphExecDestroy(md->graph);
+        md->graph = nullptr;
+        return ls;
+      }
       md->graph_cache = cache;
       md->graph_batch = batch;
       md->graph_stream = st;
@@ -1143,6 +1173,10 @@ ember_status decode_impl(ember_model* md, ember_cache* cache, const int32_t* d_i
     decode_body(cx, batch, d_next);
   }
   HIP_TRY(hipGetLastError());
+  {
+    const ember_status ls = check_launched();
+    if (ls != EMBER_OK) return ls;
+  }
   for (int r = 0; r < batch; ++r) {
     const int pr = h_pos ? h_pos[r] : pos;
     if (pr + 1 > cache->filled[r]) cache->filled[r] = pr + 1;
@@ -1203,6 +1237,7 @@ ember_status ember_time_kernel(ember_model* md, ember_cache* cache, int32_t kern
     return EMBER_OK;
   };
   hipGraphExec_t ge = nullptr;
+  g_unlaunched = nullptr;
   if (st != nullptr && graphs_enabled()) {
     HIP_TRY(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
     ember_status s0 = enqueue(iters);
@@ -1241,7 +1276,7 @@ ember_status ember_time_kernel(ember_model* md, ember_cache* cache, int32_t kern
   if (ge) (void)hipGraphExecDestroy(ge);
   HIP_TRY(hipGetLastError());
   *avg_us = ms * 1000.f / (float)(iters * reps);
-  return EMBER_OK;
+  return check_launched();
 }
 
 ember_status ember_measure_peak(int32_t kind, void* d_buf, size_t bytes, int32_t iters,
@@ -1267,7 +1302,7 @@ ember_status ember_measure_peak(int32_t kind, void* d_buf, size_t bytes, int32_t
       launch_peak_copy(d_buf, (char*)d_buf + half, half, st);
       work = 2.0 * (double)half;
     } else if (kind == EMBER_PEAK_READ) {
-      const size_t n = (bytes - read_out) / 4096 * 4096;
+      const size_t n = (bytes - read_out) / 65536 * 65536;      // whole 64 KB segments
       launch_peak_read((const char*)d_buf + read_out, n, (uint32_t*)d_buf, st);
       work = (double)n;
     } else {
@@ -1332,13 +1367,14 @@ ember_status ember_sample(ember_model* md, const float* d_logits, int32_t rows,
   const ember_status s = check_draws(md, rows, pos);
   if (s != EMBER_OK) return s;
   Ctx cx{md, nullptr, (hipStream_t)stream};
+  g_unlaunched = nullptr;
   if (md->sampling)
     launch_draw(cx, d_logits, rows, ld_logits, d_next, 0, pos);
   else
     launch_argmax_rows(d_logits, rows, md->cfg.vocab, ld_logits, d_next, md->at<int>(md->plan.flags),
                        cx.st);
   HIP_TRY(hipGetLastError());
-  return EMBER_OK;
+  return check_launched();
 }
 
 // ------------------------------------------------------------------ no-allocation draw
@@ -1395,11 +1431,12 @@ ember_status ember_sample_noalloc(ember_model* md, const float* d_logits, int32_
     if (s != EMBER_OK) return s;
   }
   hipStream_t st = (hipStream_t)stream;
+  g_unlaunched = nullptr;
   if (!md->sampling) {
     // greedy: one block per row, no scratch
     launch_argmax_rows(d_logits, rows, md->cfg.vocab, ld_logits, d_next, md->at<int>(md->plan.flags), st);
     HIP_TRY(hipGetLastError());
-    return EMBER_OK;
+    return check_launched();
   }
   char* base = nullptr;
   {
@@ -1421,7 +1458,7 @@ ember_status ember_sample_noalloc(ember_model* md, const float* d_logits, int32_
   a.tiles = tiles;
   launch_sample(a, st);
   HIP_TRY(hipGetLastError());
-  return EMBER_OK;
+  return check_launched();
 }
 
 ember_status ember_logits(ember_model* md, void* d_out, int32_t dtype, void* stream) {

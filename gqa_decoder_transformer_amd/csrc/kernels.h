@@ -12,6 +12,11 @@ namespace ember {
 // Flags raised by kernels and reported by ember_sync.
 enum DeviceFlag { kFlagBadToken = 0, kFlagNaN = 1, kNumFlags = 4 };
 
+// A launch wrapper that has no kernel for its arguments (a shape the host validation
+// should have refused) launches nothing and records `what` here; the C ABI call that
+// enqueued it then fails with EMBER_E_DEVICE instead of leaving stale outputs.
+void report_unlaunched(const char* what);
+
 // ------------------------------------------------------------------ misc (kernels_misc.hip)
 
 // x[m, :] = widen(E[ids[m], :]) for m < M; ids outside [0, V) read row 0 and raise
@@ -333,7 +338,7 @@ void flash_init();
 // an MFMA-only loop over kPeakMfmaBlocks blocks of 256 threads that writes one float per
 // thread to `out` and returns the flops of one launch.
 constexpr int kPeakMfmaBlocks = 2048;
-constexpr int kPeakReadBlocks = 256 * 16;
+constexpr int kPeakReadBlocks = 256 * 8;
 void launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 // A streaming read of `bytes` at src; one word per thread of kPeakReadBlocks x 256 to out.
 void launch_peak_read(const void* src, size_t bytes, uint32_t* out, hipStream_t st);

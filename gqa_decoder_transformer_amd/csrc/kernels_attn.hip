@@ -455,7 +455,7 @@ void launch_decode_hd(const DecodeAttnArgs& a, hipStream_t st) {
   case GV: hipLaunchKernelGGL((k_decode_attn<HD, BF, GV>), grid, dim3(256), 0, st, a); break;
   switch (G) {
     EMBER_G(1) EMBER_G(2) EMBER_G(3) EMBER_G(4) EMBER_G(5) EMBER_G(6) EMBER_G(7) EMBER_G(8)
-    default: break;
+    default: report_unlaunched("decode attention: more than 8 heads per block"); break;
   }
 #undef EMBER_G
 }
@@ -470,7 +470,7 @@ void launch_flash_prefill(const FlashArgs& a, hipStream_t st) {
     case 32: hipLaunchKernelGGL(k_flash_prefill<32>, grid, dim3(256), 0, st, a); break;
     case 64: hipLaunchKernelGGL(k_flash_prefill<64>, grid, dim3(256), 0, st, a); break;
     case 128: hipLaunchKernelGGL(k_flash_prefill<128>, grid, dim3(256), 0, st, a); break;
-    default: break;
+    default: report_unlaunched("prefill attention: head_dim"); break;
   }
 }
 
@@ -483,7 +483,7 @@ void launch_decode_attn(const DecodeAttnArgs& a, hipStream_t st) {
     break;
     EMBER_HD(8) EMBER_HD(16) EMBER_HD(32) EMBER_HD(64) EMBER_HD(128)
 #undef EMBER_HD
-    default: break;
+    default: report_unlaunched("decode attention: head_dim"); break;
   }
 }
 

@@ -358,7 +358,8 @@ __global__ void __launch_bounds__(256) k_kv_pack(KvPackArgs a) {
 }
 
 // ------------------------------------------------------------------ tiled MFMA attention
-// Block: 128 queries of one (pass row, query head), 4 waves x 32 queries; K tiles of 64
+// Block: 128 queries of one (pass row, query head), 4 waves x 32 queries (EXACT head_dim
+// 64: 8 waves, 256 queries); K tiles of 64
 // keys. v_mfma_f32_32x32x16_bf16 throughout, everything transposed so the two products
 // chain without lane shuffles:
 //   S^T = K Q^T: A = K rows (keys) x 16 head dims, B = Q^T; lane l holds query l % 32 and
@@ -378,12 +379,14 @@ __global__ void __launch_bounds__(256) k_kv_pack(KvPackArgs a) {
 // grid pairs long and short causal rows. Output rows go through LDS and leave as 16-byte stores.
 constexpr int kTK = 64;
 
-// EXACT keeps three K planes and two V planes per stage (k_kv_pack); at head_dim 128 two
-// such stages exceed the LDS, so that form runs one stage (tile j + 1 waits in registers
-// while tile j is consumed, then one more barrier per tile).
+// EXACT keeps three K planes and two V planes per stage (k_kv_pack). At head_dim 64 two
+// such stages take 92 KB, one block per CU: the block has 8 waves (256 queries) so every
+// SIMD still runs two. At head_dim 128 two stages exceed the LDS, so that form runs one
+// stage (tile j + 1 waits in registers while tile j is consumed, then one more barrier
+// per tile) with 4 waves.
 template <int HD, bool SPLIT>
 struct TiledCfg {
-  static constexpr int NW = 4;                                 // waves of 32 queries
+  static constexpr int NW = (SPLIT && HD == 64) ? 8 : 4;       // waves of 32 queries
   static constexpr int NT = NW * kWave, TQ = NW * 32;
   static constexpr int NPK = SPLIT ? 3 : 1, NPV = SPLIT ? 2 : 1;
   static constexpr int KS = HD + 8, VS = kTK + 8;
@@ -694,6 +697,8 @@ void launch_flash_mfma(const FlashArgs& a, bool split, hipStream_t st) {
   } else if (a.HD == 128) {
     if (split) hipLaunchKernelGGL((k_flash_mfma<128, true>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((k_flash_mfma<128, false>), grid, dim3(256), 0, st, a);
+  } else {
+    report_unlaunched("MFMA attention: head_dim");
   }
 }
 
@@ -706,6 +711,7 @@ void launch_kv_pack(const KvPackArgs& a, hipStream_t st) {
   dim3 grid(a.LK / 64, a.NKV, a.rows);
   if (a.HD == 64) hipLaunchKernelGGL(k_kv_pack<64>, grid, dim3(256), 0, st, a);
   else if (a.HD == 128) hipLaunchKernelGGL(k_kv_pack<128>, grid, dim3(256), 0, st, a);
+  else report_unlaunched("K/V packing: head_dim");
 }
 
 void flash_init() {
@@ -727,6 +733,8 @@ void launch_flash_tiled(const FlashArgs& a, const uint16_t* kp, const uint16_t* 
     if (split) EMBER_TILED(64, true) else EMBER_TILED(64, false)
   } else if (a.HD == 128) {
     if (split) EMBER_TILED(128, true) else EMBER_TILED(128, false)
+  } else {
+    report_unlaunched("tiled attention: head_dim");
   }
 #undef EMBER_TILED
 }

@@ -614,7 +614,7 @@ void launch_reduce(const GemmArgs& a, int epi, int used, hipStream_t st) {
       case GEMM_STORE: hipLaunchKernelGGL(k_splitk_reduce4<GEMM_STORE>, dim3((unsigned)blocks), dim3(256), 0, st, a, used); break;
       case GEMM_RESID: hipLaunchKernelGGL(k_splitk_reduce4<GEMM_RESID>, dim3((unsigned)blocks), dim3(256), 0, st, a, used); break;
       case GEMM_SILU: hipLaunchKernelGGL(k_splitk_reduce4<GEMM_SILU>, dim3((unsigned)blocks), dim3(256), 0, st, a, used); break;
-      default: break;
+      default: report_unlaunched("split-K reduce: epilogue"); break;
     }
     return;
   }
@@ -624,7 +624,7 @@ void launch_reduce(const GemmArgs& a, int epi, int used, hipStream_t st) {
     case GEMM_STORE: hipLaunchKernelGGL(k_splitk_reduce<GEMM_STORE>, dim3((unsigned)blocks), dim3(256), 0, st, a, used); break;
     case GEMM_RESID: hipLaunchKernelGGL(k_splitk_reduce<GEMM_RESID>, dim3((unsigned)blocks), dim3(256), 0, st, a, used); break;
     case GEMM_SILU: hipLaunchKernelGGL(k_splitk_reduce<GEMM_SILU>, dim3((unsigned)blocks), dim3(256), 0, st, a, used); break;
-    default: break;
+    default: report_unlaunched("split-K reduce: epilogue"); break;
   }
 }
 
@@ -674,7 +674,10 @@ void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
   if (two) a.partial_elems /= 2;
   const int cfg = pick_cfg(a);
   int splits = pick_splits(a, cfg);
-  if (two && !a.partial && epi == GEMM_SILU) return;   // needs the split-K planes (caller bug)
+  if (two && !a.partial && epi == GEMM_SILU) {          // needs the split-K planes
+    report_unlaunched("two-plane SiLU GEMM without split-K planes");
+    return;
+  }
   if (two && (splits <= 1 || !a.partial) && epi != GEMM_SILU) {
     // tiles that fill the GPU: the second plane's pass adds into the output
     a.partial = nullptr;
@@ -694,7 +697,7 @@ void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
       case GEMM_STORE: launch_epi<GEMM_STORE>(a, cfg, 1, st); break;
       case GEMM_RESID: launch_epi<GEMM_RESID>(a, cfg, 1, st); break;
       case GEMM_SILU: launch_epi<GEMM_SILU>(a, cfg, 1, st); break;
-      default: break;
+      default: report_unlaunched("GEMM: epilogue"); break;
     }
     return;
   }
@@ -720,7 +723,7 @@ void launch_gemm_f32w(const GemmF32Args& a, int epi, hipStream_t st) {
     case GEMM_STORE: hipLaunchKernelGGL(k_gemm_f32w<GEMM_STORE>, grid, dim3(256), 0, st, a); break;
     case GEMM_RESID: hipLaunchKernelGGL(k_gemm_f32w<GEMM_RESID>, grid, dim3(256), 0, st, a); break;
     case GEMM_SILU: hipLaunchKernelGGL(k_gemm_f32w<GEMM_SILU>, grid, dim3(256), 0, st, a); break;
-    default: break;
+    default: report_unlaunched("f32-weight GEMM: epilogue"); break;
   }
 }
 

@@ -623,12 +623,20 @@ int gemv_parts_max(int N, int K, int wk) {
 }
 
 void launch_gemv(const GemvArgs& a, int epi, hipStream_t st) {
-  if (a.M != 1 || a.N <= 0 || (!a.x && !a.xpart)) return;   // one token, an input required
+  if (a.M != 1 || a.N <= 0 || (!a.x && !a.xpart)) {          // one token, an input required
+    report_unlaunched("decode GEMV: one token with an input");
+    return;
+  }
   const int wk = a.w_scale ? WK_Q8 : (a.w_bf16 ? WK_BF16 : WK_F32);
-  if (wk == WK_Q8 && a.K % kQ8Block) return;                 // q8 rows are whole blocks
+  if (wk == WK_Q8 && a.K % kQ8Block) {                        // q8 rows are whole blocks
+    report_unlaunched("decode GEMV: q8_0 rows of whole blocks");
+    return;
+  }
   if (a.xpart && (epi != GEMV_RESID || a.xp_nsplit < 1 ||
-                  a.xp_nsplit > gemv_parts_max(a.N, a.K, wk)))
-    return;                                                   // callers check gemv_parts_max
+                  a.xp_nsplit > gemv_parts_max(a.N, a.K, wk))) {
+    report_unlaunched("decode GEMV: attention splits as input");   // callers check gemv_parts_max
+    return;
+  }
 #define EMBER_GEMV_CASE(E)                                               \
   case E:                                                                \
     if (wk == WK_Q8) launch_t<Q8, E>(a, st);                             \
@@ -640,7 +648,7 @@ void launch_gemv(const GemvArgs& a, int epi, hipStream_t st) {
     EMBER_GEMV_CASE(GEMV_RESID)
     EMBER_GEMV_CASE(GEMV_SILU)
     EMBER_GEMV_CASE(GEMV_LOGITS)
-    default: break;
+    default: report_unlaunched("decode GEMV: epilogue"); break;
   }
 #undef EMBER_GEMV_CASE
 }

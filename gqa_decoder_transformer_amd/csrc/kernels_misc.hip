@@ -310,7 +310,7 @@ void launch_qkv_post(const QkvPostArgs& a, hipStream_t st) {
     case 32: hipLaunchKernelGGL(k_qkv_post<16>, grid, dim3(256), 0, st, a); break;
     case 64: hipLaunchKernelGGL(k_qkv_post<32>, grid, dim3(256), 0, st, a); break;
     case 128: hipLaunchKernelGGL(k_qkv_post<64>, grid, dim3(256), 0, st, a); break;
-    default: break;                  // head_dim is validated to these values
+    default: report_unlaunched("QKV post-processing: head_dim"); break;
   }
 }
 

@@ -2,8 +2,8 @@
 // the kernels' roofline fractions are also reported against.
 //   k_peak_copy: a plain streaming copy, 16-byte loads and stores, grid-stride (bytes
 //                read plus bytes written per second);
-//   k_peak_read: a streaming read, 16-byte loads (the reference for kernels that mostly
-//                read: weights and KV cache);
+//   k_peak_read: a streaming read, 16-byte loads, sixteen in flight per thread (the
+//                reference for kernels that mostly read: weights and KV cache);
 //   k_peak_mfma: independent chains of v_mfma_f32_32x32x16_bf16 on register operands, no
 //                memory traffic (the matrix-core reference for bf16 work).
 #include "common.h"
@@ -22,25 +22,23 @@ __global__ void __launch_bounds__(256) k_peak_copy(const u32x4_t* __restrict__ s
     dst[i] = src[i];
 }
 
-// a streaming read: every 16-byte chunk is loaded once and folded into one word per thread
-// (written, so the loads cannot be dropped); four loads in flight per thread per round
+// a streaming read: each block takes 64 KB segments in turn (sixteen 16-byte loads per
+// thread, all in flight before any is used), every chunk folded into one word per thread
+// (written, so the loads cannot be dropped)
 __global__ void __launch_bounds__(256) k_peak_read(const u32x4_t* __restrict__ src, size_t n,
                                                    uint32_t* __restrict__ out) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int U = 16;
+  const size_t nseg = n / (256 * U);
   uint32_t acc = 0;
-  size_t i = t;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const u32x4_t a0 = src[i], a1 = src[i + stride], a2 = src[i + 2 * stride],
-                  a3 = src[i + 3 * stride];
-    acc ^= a0[0] ^ a0[1] ^ a0[2] ^ a0[3] ^ a1[0] ^ a1[1] ^ a1[2] ^ a1[3];
-    acc ^= a2[0] ^ a2[1] ^ a2[2] ^ a2[3] ^ a3[0] ^ a3[1] ^ a3[2] ^ a3[3];
+  for (size_t sg = blockIdx.x; sg < nseg; sg += gridDim.x) {
+    const u32x4_t* p = src + sg * 256 * U + threadIdx.x;
+    u32x4_t v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) v[j] = p[256 * j];
+#pragma unroll
+    for (int j = 0; j < U; ++j) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
   }
-  for (; i < n; i += stride) {
-    const u32x4_t a0 = src[i];
-    acc ^= a0[0] ^ a0[1] ^ a0[2] ^ a0[3];
-  }
-  out[t] = acc;
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
 constexpr int kMfmaChains = 4;
