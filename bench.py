@@ -57,6 +57,11 @@ def parse():
     return ap.parse_args()
 
 
+def progress(msg):
+    """One progress line on stderr (the JSON result is the only line on stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def weight_bytes(m):
     """Stored bytes per weight: bf16 2, f32 4, q8_0 34 per 32 (an f16 scale per 32 int8)."""
     return {"bf16": 2.0, "f32": 4.0, "q8_0": 34.0 / 32.0}[m.weight_dtype]
@@ -166,6 +171,7 @@ class Run:
             self.eng = B.Engine(self.cfg, self.ck, device="cuda:0", stream=s)
             self.ids = torch.empty((Bn,) if self.m.causal else (Bn, T), dtype=torch.int32,
                                    device="cuda:0")
+        progress(f"engine ready: {w.name}, precision {'exact' if prec == B.EXACT else 'fast'}")
 
     def step(self, ev, decode=True, prefill=True):
         w = self.w
@@ -183,14 +189,18 @@ class Run:
         import numpy as np
         import torch
         with torch.cuda.stream(self.s):
-            for _ in range(warmup):
+            for i in range(warmup):
                 self.step([torch.cuda.Event(enable_timing=True) for _ in range(3)], decode, prefill)
-            torch.cuda.synchronize()
+                torch.cuda.synchronize()
+                progress(f"warm-up step {i + 1}/{warmup} done")
             evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
             t0 = time.perf_counter()
-            for e in evs:
+            for i, e in enumerate(evs):
                 self.step(e, decode, prefill)
+                if len(evs) <= 3 or i == len(evs) - 1:
+                    progress(f"timed step {i + 1}/{len(evs)} enqueued")
             torch.cuda.synchronize()
+            progress("timed steps done")
             wall = time.perf_counter() - t0
             self.eng.sync()
         pre = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
@@ -211,6 +221,7 @@ class Run:
                 if kind == B.K_LM_HEAD and (m.head != "tied_lm" or phase == 1):
                     continue
                 us = self.eng.time_kernel(kind, phase, iters)
+                progress(f"kernel {'decode' if phase == 0 else 'prefill'}.{name}: {us:.2f} us")
                 passes = -(-Bn * T // self.max_tokens)
                 launches = (1 if kind == B.K_LM_HEAD else m.layers) * (N if phase == 0 else passes)
                 rows = self.max_tokens // T if phase == 1 else 1
@@ -388,6 +399,7 @@ def main():
     kv = {"f32": B.F32, "bf16": B.BF16, None: None}[args.kv]
     s = torch.cuda.Stream(device=torch.device("cuda:0"))
     peaks = measure_peaks(s)
+    progress(f"peaks {peaks}")
 
     r = Run(w, prec, kv, s)
     pre, dec, ms, wall = r.timed(args.steps, args.warmup)
@@ -444,6 +456,7 @@ def main():
         line["extra"] = {"llama1b": extra_1b(s, peaks),
                          "longctx_bf16kv": extra_longctx_bf16kv(s, peaks)}
     if not args.no_cpu_baseline:
+        progress("cpu baseline (oracle on the host cores)")
         line["cpu_baseline"] = cpu_baseline(w, r.ck, r.prompt)
     print(json.dumps(line), flush=True)
 

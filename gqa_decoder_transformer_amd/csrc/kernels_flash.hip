@@ -414,7 +414,14 @@ __global__ void __launch_bounds__((TiledCfg<HD, SPLIT>::NT)) k_flash_tiled(Flash
   // second half in increasing position, so blocks half a grid apart (dispatched into
   // the same slots) carry complementary amounts of work.
   const int nq = gridDim.x, HR = gridDim.y * gridDim.z, total = nq * HR;
-  const int L = blockIdx.x + nq * (blockIdx.y + gridDim.y * blockIdx.z);
+  int L = blockIdx.x + nq * (blockIdx.y + gridDim.y * blockIdx.z);
+  {
+    // blocks are dealt round-robin to the 8 XCDs: within each run of 8 G dispatched
+    // blocks, XCD x takes G consecutive work items, the G query heads of one kv group at
+    // one query tile, so their K/V tiles are fetched into one L2 at about one time
+    const int G = a.NH / a.NKV, chunk = 8 * G;
+    if (total % chunk == 0) L = L / chunk * chunk + G * (L % 8) + L % chunk / 8;
+  }
   const int half = (total + 1) / 2;
   const int tix = L < half ? L : total - 1 - (L - half);
   const int qt = nq - 1 - tix / HR;

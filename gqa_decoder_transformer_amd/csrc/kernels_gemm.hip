@@ -59,13 +59,20 @@ __global__ void __launch_bounds__(WM * WN * KG * kWave) k_gemm(GemmArgs a) {
   extern __shared__ __align__(16) uint16_t smem[];
 
   // XCD-aware tile order: blocks are dealt round-robin to the 8 XCDs; give each XCD a
-  // contiguous run of logical tiles, M-tiles fastest, so a weight column block stays
-  // within one XCD's L2.
+  // contiguous run of logical tiles. Within the run, tiles go in bands of kBandM M-tiles:
+  // a band's M-tiles fastest, then the next N-tile, so the tiles an XCD runs at one time
+  // form a band-high window that shares both its A rows and its weight columns in the
+  // XCD's L2 (with M-tiles fastest over all of M, as at M = 8192, every N-tile re-read
+  // all of A: 33x the operand bytes fetched from the memory side).
   const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
   const int nblk = mt * nt;
   int lin = blockIdx.x;
   if (nblk % 8 == 0) lin = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
-  const int tm = lin % mt, tn = lin / mt;
+  constexpr int kBandM = 8;
+  const int band = lin / (kBandM * nt), m_first = band * kBandM;
+  const int band_m = min(mt - m_first, kBandM);
+  const int in_band = lin - band * kBandM * nt;
+  const int tm = m_first + in_band % band_m, tn = in_band / band_m;
   const int m0 = tm * BM, n0 = tn * BN;
   const int kg = threadIdx.x / NT, tg = threadIdx.x % NT;  // K group, thread in group
   const int wave = tg / kWave, lane = tg % kWave;
