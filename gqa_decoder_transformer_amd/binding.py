@@ -60,7 +60,8 @@ class EmberTensor(ctypes.Structure):
 class EmberSampler(ctypes.Structure):
     _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32),
                 ("top_p", ctypes.c_float), ("d_uniform", ctypes.c_void_p),
-                ("n_pos", ctypes.c_int32), ("ld", ctypes.c_int32)]
+                ("n_pos", ctypes.c_int32), ("ld", ctypes.c_int32),
+                ("seed", ctypes.c_uint64)]
 
 
 class EmberError(RuntimeError):
@@ -415,19 +416,27 @@ class Engine:
         ember_sync(self.model, self.sp)
 
     def set_sampler(self, temperature: float = 0.0, top_k: int = 0, top_p: float = 1.0,
-                    uniform=None):
+                    uniform=None, seed=None):
         """uniform: device f32 tensor [n_pos, ld] of draws in [0, 1), kept referenced here
-        while the sampler is set. temperature 0 returns to greedy argmax."""
-        if temperature == 0.0 and uniform is None:
+        while the sampler is set; or seed (with uniform None): draws generated on the
+        device (Philox4x32-10). temperature 0 returns to greedy argmax."""
+        if temperature == 0.0 and uniform is None and seed is None:
             self._uniform = None
             ember_set_sampler(self.model, None)
             return
-        if uniform is None or uniform.dim() != 2 or not uniform.is_contiguous():
+        if uniform is None:
+            if seed is None:
+                raise ValueError("draws need a uniform tensor or a seed")
+            s = EmberSampler(temperature, top_k, top_p, None, 0, 0, int(seed))
+            ember_set_sampler(self.model, s)
+            self._uniform = None
+            return
+        if uniform.dim() != 2 or not uniform.is_contiguous():
             raise ValueError("uniform must be a contiguous [n_pos, ld] device tensor")
         if uniform.dtype != self.torch.float32:
             raise ValueError("uniform must be float32")
         s = EmberSampler(temperature, top_k, top_p, uniform.data_ptr(), uniform.shape[0],
-                         uniform.shape[1])
+                         uniform.shape[1], 0)
         ember_set_sampler(self.model, s)
         self._uniform = uniform
 

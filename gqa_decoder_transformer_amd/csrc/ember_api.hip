@@ -352,6 +352,7 @@ void launch_draw(const Ctx& cx, const float* logits, int R, long long ld, int32_
   a.logits = logits; a.ld = ld; a.R = R; a.V = md->cfg.vocab;
   a.temperature = md->samp.temperature; a.top_k = md->samp.top_k; a.top_p = md->samp.top_p;
   a.uniform = md->samp.d_uniform; a.u_rows = md->samp.n_pos; a.u_ld = md->samp.ld;
+  a.seed = md->samp.seed;
   a.col0 = u_col0; a.pos = u_pos < 0 ? 0 : u_pos;
   a.d_pos = u_pos < 0 ? md->at<int>(md->plan.row_pos) : nullptr;
   a.next = next; a.flags = md->at<int>(md->plan.flags);
@@ -362,7 +363,7 @@ void launch_draw(const Ctx& cx, const float* logits, int R, long long ld, int32_
 
 // Whether a call drawing `rows` rows from draw row `u_pos` fits the sampler's draws.
 ember_status check_draws(const ember_model* md, int rows, long long u_pos) {
-  if (!md->sampling) return EMBER_OK;
+  if (!md->sampling || !md->samp.d_uniform) return EMBER_OK;   // on-device draws: no array
   if (u_pos >= md->samp.n_pos)
     return fail(EMBER_E_CAPACITY, "draw row %lld beyond the sampler's %d rows", u_pos,
                 md->samp.n_pos);
@@ -1336,8 +1337,8 @@ ember_status ember_set_sampler(ember_model* md, const ember_sampler* s) {
   if (on) {
     if (!std::isfinite(s->top_p) || s->top_p < 0.f) return fail(EMBER_E_ARG, "top_p must be finite and >= 0");
     if (s->top_k < 0) return fail(EMBER_E_ARG, "top_k must be >= 0");
-    if (!s->d_uniform || s->n_pos < 1 || s->ld < 1)
-      return fail(EMBER_E_ARG, "the sampler needs draws d_uniform [n_pos >= 1, ld >= 1]");
+    if (s->d_uniform && (s->n_pos < 1 || s->ld < 1))
+      return fail(EMBER_E_ARG, "draws d_uniform need n_pos >= 1 and ld >= 1");
     if (md->cfg.head_kind != EMBER_HEAD_TIED_LM)
       return fail(EMBER_E_STATE, "sampling needs the tied LM head");
     if (md->cfg.vocab > kSampleMaxVocab)
@@ -1452,6 +1453,7 @@ ember_status ember_sample_noalloc(ember_model* md, const float* d_logits, int32_
   a.logits = d_logits; a.ld = ld_logits; a.R = rows; a.V = md->cfg.vocab;
   a.temperature = md->samp.temperature; a.top_k = md->samp.top_k; a.top_p = md->samp.top_p;
   a.uniform = md->samp.d_uniform; a.u_rows = md->samp.n_pos; a.u_ld = md->samp.ld;
+  a.seed = md->samp.seed;
   a.col0 = 0; a.pos = pos; a.d_pos = nullptr;
   a.next = d_next; a.flags = md->at<int>(md->plan.flags);
   a.state = state;

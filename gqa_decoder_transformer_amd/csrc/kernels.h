@@ -155,9 +155,11 @@ struct SampleArgs {
   float temperature;
   int top_k;
   float top_p;
-  const float* uniform;
+  const float* uniform;    // null: on-device draws (Philox4x32-10 keyed by seed, see
+                           // kernels_sample.hip)
   int u_rows;
   long long u_ld;
+  unsigned long long seed;
   int col0;
   int pos;
   const int* d_pos;

@@ -510,10 +510,13 @@ __global__ void __launch_bounds__((TiledCfg<HD, SPLIT>::NT)) k_flash_tiled(Flash
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
   float mrun = -INFINITY;
-  // the softmax denominators come from the matrix core: an all-ones A operand against
-  // P^T gives every row of `lsum` the per-query sum of exactly the probabilities the
-  // P V product uses (bf16 in FAST, hi + lo in EXACT)
+  // FAST: the softmax denominators come from the matrix core: an all-ones A operand
+  // against P^T gives every row of `lsum` the per-query sum of exactly the bf16
+  // probabilities the P V product uses. EXACT: each lane sums its f32 probabilities
+  // (lpart; the query's other half is in lane ^ 32), which the hi + lo planes of P carry
+  // to 2^-17, so no MFMA is spent on it
   f32x16_t lsum;
+  float lpart = 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) lsum[e] = 0.f;
   const u32x4_t ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
@@ -607,6 +610,7 @@ __global__ void __launch_bounds__((TiledCfg<HD, SPLIT>::NT)) k_flash_tiled(Flash
         const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);   // mrun = -inf -> 0
 #pragma unroll
         for (int e = 0; e < 16; ++e) lsum[e] *= alpha;
+        lpart *= alpha;
 #pragma unroll
         for (int d = 0; d < NDB; ++d)
 #pragma unroll
@@ -618,6 +622,12 @@ __global__ void __launch_bounds__((TiledCfg<HD, SPLIT>::NT)) k_flash_tiled(Flash
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           sc[kb][e] = __builtin_amdgcn_exp2f(sc[kb][e] - mrun);   // masked (-inf) -> 0
+      if (SPLIT) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) lpart += sc[kb][e];
+      }
 #pragma unroll
       for (int t = 0; t < kTK / 16; ++t) {
         const int kb = t / 2, e0 = 8 * (t % 2);
@@ -629,8 +639,7 @@ __global__ void __launch_bounds__((TiledCfg<HD, SPLIT>::NT)) k_flash_tiled(Flash
           if (SPLIT) pl[i] = cvt_pk_bf16(p0 - bf16_lo(ph[i]), p1 - bf16_hi(ph[i]));
         }
         const bf16x8_t pbh = as_bf16x8(ph), pbl = as_bf16x8(pl);
-        lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pbh, lsum, 0, 0, 0);
-        if (SPLIT) lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pbl, lsum, 0, 0, 0);
+        if (!SPLIT) lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pbh, lsum, 0, 0, 0);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int vo = (db * 32 + lq) * VS + 16 * t + 8 * hl;   // keys stored permuted
@@ -659,7 +668,7 @@ __global__ void __launch_bounds__((TiledCfg<HD, SPLIT>::NT)) k_flash_tiled(Flash
 
   // normalise and stage the wave's 32 output rows (f32, padded) through LDS
   float* ow = (float*)sm + wave * 32 * (HD + 1);
-  const float lrun = lsum[0];
+  const float lrun = SPLIT ? lpart + __shfl_xor(lpart, 32) : lsum[0];
   const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)

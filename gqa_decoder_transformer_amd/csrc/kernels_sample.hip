@@ -97,6 +97,32 @@ EMBER_DEV T block_reduce(T v, T* red, Op op) {
   return r;
 }
 
+// The on-device draw of batch row `row` for the token predicted from position `pos`
+// (when the caller passes no draws): the first output word of Philox4x32-10 (Salmon,
+// Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11) at counter
+// (pos, row, 0, 0) and key (seed mod 2^32, seed div 2^32), as (word >> 8) * 2^-24.
+// Philox4x32-10 rounds: the products M0 c0 and M1 c2 (high and low words) give the next
+// counter (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key moves
+// by the Weyl constants between rounds. Only the first output word is kept.
+EMBER_DEV float sample_philox_u(unsigned long long seed, uint32_t pos, uint32_t row) {
+  uint32_t c0 = pos, c1 = row, c2 = 0u, c3 = 0u;
+  uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+#pragma unroll
+  for (int rnd = 0; rnd < 10; ++rnd) {
+    if (rnd) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const unsigned long long p0 = (unsigned long long)0xD2511F53u * c0;
+    const unsigned long long p1 = (unsigned long long)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1, n3 = (uint32_t)p0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  return (float)(c0 >> 8) * 0x1p-24f;
+}
+
+
 struct Shared {
   union {
     u64 hist[kBins];                                  // digit histogram of the block
@@ -296,8 +322,13 @@ __global__ void __launch_bounds__(kSB) k_sample_phase(SampleArgs a) {
     __syncthreads();
     const float S2 = s.total;
     const int did = a.d_pos ? a.d_pos[r] : a.pos;
-    const int urow = min(max(did, 0), a.u_rows - 1);
-    const float u = a.uniform[(size_t)urow * a.u_ld + a.col0 + r];
+    float u;
+    if (a.uniform) {
+      const int urow = min(max(did, 0), a.u_rows - 1);
+      u = a.uniform[(size_t)urow * a.u_ld + a.col0 + r];
+    } else {
+      u = sample_philox_u(a.seed, (uint32_t)max(did, 0), (uint32_t)(a.col0 + r));
+    }
     const float target = u * S2;
     // the first weighted tile whose running sum at its end exceeds the target
     int first = ntiles;

@@ -255,21 +255,28 @@ ember_status ember_sync(ember_model* model, void* stream);
  * the rest (uniform when every z is -inf); the first index whose running probability sum
  * in index order exceeds the draw u, or the last index of the maximum when rounding
  * leaves none.
- * The draws are inputs: d_uniform is device f32 [n_pos, ld], values in [0, 1), borrowed
- * while the sampler is set. Row q, column b is the draw of batch row b for the token
- * predicted from the logits at position q: a decode step at `pos` reads row pos, a
- * prefill of positions [start_pos, start_pos + n) reads row start_pos + n - 1. */
+ * The draw u of batch row b for the token predicted from the logits at position q (a
+ * decode step at `pos` draws for q = pos, a prefill of positions [start_pos, start_pos +
+ * n) for q = start_pos + n - 1; the page draws it from a seeded generator it does not
+ * name) comes from one of two sources:
+ *  - d_uniform non-null: an input array, device f32 [n_pos, ld] with values in [0, 1),
+ *    borrowed while the sampler is set; u = d_uniform[q * ld + b];
+ *  - d_uniform null: generated on the device by the counter-based generator
+ *    Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1,
+ *    2, 3", SC'11): its first output word at counter (q, b, 0, 0) and key (seed mod 2^32,
+ *    seed div 2^32), u = (word >> 8) * 2^-24. No position or batch capacity applies. */
 typedef struct ember_sampler {
   float temperature;           /* > 0 draws; 0 = greedy argmax (the default) */
   int32_t top_k;               /* 0 or >= vocab: stage off */
   float top_p;                 /* outside (0, 1): stage off */
-  const float* d_uniform;      /* device [n_pos, ld] f32 */
+  const float* d_uniform;      /* device [n_pos, ld] f32, or null: draws from `seed` */
   int32_t n_pos;               /* rows of d_uniform */
   int32_t ld;                  /* row stride of d_uniform in floats */
+  uint64_t seed;               /* key of the on-device draws (d_uniform null) */
 } ember_sampler;
 
 /* Set the sampler of `model` (copied), or with NULL or temperature 0 return to greedy
- * argmax. A negative or non-finite temperature or top_p, top_k < 0, a NULL d_uniform,
+ * argmax. A negative or non-finite temperature or top_p, top_k < 0, or a d_uniform with
  * n_pos < 1 or ld < 1 fail with EMBER_E_ARG, a classification-head model with
  * EMBER_E_STATE, a vocabulary above 1048576 with EMBER_E_CAPACITY. Afterwards a prefill
  * or decode step whose draw row lies beyond n_pos - 1 or whose batch exceeds ld fails

@@ -11,6 +11,7 @@ import pytest
 
 import oracle as O
 import workloads as W
+from oracle import rng as R
 from oracle import sampler as S
 from tests.gpu_util import TOL_EXACT, gpu_generate, say
 from tests.small_models import LLAMA_SMALL, QWEN_SMALL
@@ -111,6 +112,39 @@ def test_sample_full_vocabulary_matches_oracle(bigv, setting):
     say(f"{off} of {4 * rows} draws differ from the f32 oracle, all within the candidates")
 
 
+SEED = 0x9E3779B97F4A7C15              # both 32-bit key words nonzero
+
+
+@pytest.mark.parametrize("setting", [(1.0, 0, 1.0), (0.8, 50, 0.9), (1e4, 0, 1.0)],
+                         ids=["plain", "k50-p0.9", "flat"])
+def test_sample_on_device_draws_match_oracle_generator(bigv, setting):
+    """No draws passed: the sampler generates u on the device (Philox4x32-10 at counter
+    (position, row), key = the seed). The oracle's generator, written independently from
+    the published definition and pinned by its known-answer vectors, supplies the same
+    u to the oracle's sampler. At t = 1e4 the distribution is nearly flat, so the token
+    is a direct function of u (a wrong draw moves it)."""
+    import torch
+    t, k, p = setting
+    V = BIGV.vocab
+    rows = 8
+    logits = W.make_logits(300 + int(t * 10) % 97, rows, V)
+    d_l = torch.from_numpy(logits).cuda()
+    bigv.set_sampler(t, k, p, seed=SEED)
+    off = 0
+    for pos in (0, 7, 4095, 70000):
+        got = bigv.sample(d_l, pos).cpu().numpy()
+        u = R.uniform(SEED, pos, np.arange(rows))
+        want = S.sample_rows(logits, t, k, p, u)
+        for r in range(rows):
+            if got[r] != want[r]:
+                off += 1
+                cand = candidates(logits[r], t, k, p, float(u[r]), 2e-5, 2e-5)
+                assert got[r] in cand, (pos, r, got[r], want[r])
+    bigv.sync()
+    bigv.set_sampler()
+    say(f"on-device draws {setting}: {off} of {4 * rows} differ from the f32 oracle, within the candidates")
+
+
 def test_sample_masked_and_uniform_rows(bigv):
     """A row of -inf only is drawn uniformly; a row with most tokens at -inf never draws
     one of them; temperature 0 is the greedy argmax (lowest index of the maximum)."""
@@ -198,15 +232,21 @@ def _check_forward_draws(g_ids, or_ids, or_logits, t, k, p, U, T, col):
                                                (LLAMA_SMALL, 3, 25.0)],
                          ids=["qwen-b1-init", "qwen-b1-peaked", "llama-b3-peaked"])
 @pytest.mark.parametrize("setting", [(1.0, 0, 1.0), (0.8, 20, 0.9)], ids=["plain", "k20-p0.9"])
-def test_prefill_and_decode_draws_match_oracle(model, batch, scale, setting):
+@pytest.mark.parametrize("draws", ["array", "philox"])
+def test_prefill_and_decode_draws_match_oracle(model, batch, scale, setting, draws):
     """The forward pass with a sampler set: the prefill's draw (row T - 1) and every decode
-    step's draw (row pos), batch row b reading column b; decode steps on a side stream,
-    so that they are replayed from the step graph."""
+    step's draw (row pos), batch row b reading column b (or, with on-device draws, the
+    generator at counter (pos, b)); decode steps on a side stream, so that they are
+    replayed from the step graph."""
     import torch
     t, k, p = setting
     T, N = 13, 10
     prompt = np.random.default_rng(31).integers(0, model.vocab, (batch, T)).astype(np.int32)
-    U = W.make_uniforms(41, T + N, batch + 1)
+    if draws == "array":
+        U = W.make_uniforms(41, T + N, batch + 1)
+    else:
+        pos, col = np.meshgrid(np.arange(T + N), np.arange(batch + 1), indexing="ij")
+        U = R.uniform(SEED, pos, col)
     say(f"forward draws {model.name} B={batch} scale={scale} t={t} k={k} p={p}")
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
@@ -214,7 +254,10 @@ def test_prefill_and_decode_draws_match_oracle(model, batch, scale, setting):
         om = O.OracleModel(model, ck)
         orc = [_oracle_sampled(om, prompt[b], N, t, k, p, U, b) for b in range(batch)]
         feed = np.stack([ids[:N] for ids, _ in orc], 1)      # [N, batch]
-        eng.set_sampler(t, k, p, torch.from_numpy(U).cuda())
+        if draws == "array":
+            eng.set_sampler(t, k, p, torch.from_numpy(U).cuda())
+        else:
+            eng.set_sampler(t, k, p, seed=SEED)
         g_ids, _ = gpu_generate(eng, prompt, N, feed=feed)
         eng.set_sampler()
     torch.cuda.synchronize()
