@@ -371,7 +371,7 @@ __global__ void __launch_bounds__(WM * WN * KG * kWave) k_gemm(GemmArgs a) {
 // Tile configurations: block BM x BN, WM x WN waves, register prefetch depth PF, KG
 // groups of waves over the K range.
 enum GemmCfg { CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x128 = 3, CFG_256x256 = 4, CFG_64x64 = 5,
-               CFG_128x128_K2 = 6 };
+               CFG_128x128_K2 = 6, CFG_128x256_W8 = 7 };
 
 template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI, int KG = 1>
 void set_attr() {
@@ -411,7 +411,9 @@ int tiles_of(const GemmArgs& a, int bm, int bn) {
 // split-K planes and reduce that 128 x 128 tiles need (0.5B prefill GEMMs 10-20 % faster).
 int pick_cfg(const GemmArgs& a) {
   if (a.M <= 128) return CFG_64x64;
-  if (a.a_lo) return tiles_of(a, 128, 256) >= 180 ? CFG_128x256 : CFG_128x128;
+  // two-plane input: 128 x 256 tiles over 8 waves of 64 x 64 (two waves per SIMD; over 4
+  // waves of 64 x 128 the accumulators and fragments held a wave to one per SIMD)
+  if (a.a_lo) return tiles_of(a, 128, 256) >= 180 ? CFG_128x256_W8 : CFG_128x128;
   if (tiles_of(a, 256, 256) >= 256) return CFG_256x256;
   // long K against N (the down projection at M = 2048): 256 x 256 tiles over four K
   // slices, whose partial planes cost less than the halved operand traffic saves there
@@ -429,7 +431,7 @@ int pick_cfg(const GemmArgs& a) {
 void cfg_dims(int cfg, int& bm, int& bn) {
   switch (cfg) {
     case CFG_256x256: bm = 256; bn = 256; break;
-    case CFG_128x256: bm = 128; bn = 256; break;
+    case CFG_128x256: case CFG_128x256_W8: bm = 128; bn = 256; break;
     case CFG_128x128: case CFG_128x128_K2: bm = 128; bn = 128; break;
     case CFG_64x64: bm = 64; bn = 64; break;
     default: bm = 64; bn = 128; break;
@@ -443,6 +445,7 @@ void launch_split(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
       if constexpr (!SPLIT) launch_cfg<256, 256, 2, 4, 1, false, EPI>(a, splits, st);
       break;
     case CFG_128x256: launch_cfg<128, 256, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
+    case CFG_128x256_W8: launch_cfg<128, 256, 2, 4, 2, SPLIT, EPI>(a, splits, st); break;
     case CFG_128x128: launch_cfg<128, 128, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
     case CFG_128x128_K2:
       if constexpr (!SPLIT) launch_cfg<128, 128, 2, 2, 2, false, EPI, 2>(a, splits, st);
@@ -465,6 +468,7 @@ void set_attrs_split() {
     set_attr<128, 128, 2, 2, 2, false, EPI, 2>();
   }
   set_attr<128, 256, 2, 2, 2, SPLIT, EPI>();
+  set_attr<128, 256, 2, 4, 2, SPLIT, EPI>();
   set_attr<128, 128, 2, 2, 2, SPLIT, EPI>();
   set_attr<64, 128, 2, 2, 2, SPLIT, EPI>();
   set_attr<64, 64, 2, 1, 4, SPLIT, EPI>();
