@@ -402,17 +402,20 @@ struct TiledCfg {
 template <int HD, bool SPLIT>
 __global__ void __launch_bounds__((TiledCfg<HD, SPLIT>::NT)) k_flash_tiled(FlashArgs a,
                                                                          const uint16_t* kp,
-                                                                         const uint16_t* vt, int LK) {
+                                                                         const uint16_t* vt, int LK,
+                                                                         int longest_first) {
   using C = TiledCfg<HD, SPLIT>;
   constexpr int NPK = C::NPK, NPV = C::NPV, KS = C::KS, VS = C::VS, NT = C::NT, TQ = C::TQ;
   constexpr int NKS = HD / 16, NDB = HD / 32;
   constexpr int CK = kTK * HD / 8 / NT;                          // 16-byte chunks per thread
   extern __shared__ __align__(16) uint16_t sm[];
 
-  // Dispatch order L (x fastest, then heads, then rows) -> tile: the first half of the
-  // grid takes the tiles in decreasing query position (long causal rows first), the
-  // second half in increasing position, so blocks half a grid apart (dispatched into
-  // the same slots) carry complementary amounts of work.
+  // Dispatch order L (x fastest, then heads, then rows) -> tile. A grid larger than the
+  // CUs hold at once is dispatched as blocks finish: there the tiles go in decreasing
+  // query position (long causal rows first, the short ones fill in at the end).
+  // Otherwise the first half of the grid takes the tiles in decreasing position and the
+  // second half in increasing position, so blocks half a grid apart (dispatched into the
+  // same slots) carry complementary amounts of work.
   const int nq = gridDim.x, HR = gridDim.y * gridDim.z, total = nq * HR;
   int L = blockIdx.x + nq * (blockIdx.y + gridDim.y * blockIdx.z);
   {
@@ -423,7 +426,7 @@ __global__ void __launch_bounds__((TiledCfg<HD, SPLIT>::NT)) k_flash_tiled(Flash
     if (total % chunk == 0) L = L / chunk * chunk + G * (L % 8) + L % chunk / 8;
   }
   const int half = (total + 1) / 2;
-  const int tix = L < half ? L : total - 1 - (L - half);
+  const int tix = longest_first ? L : L < half ? L : total - 1 - (L - half);
   const int qt = nq - 1 - tix / HR;
   const int h = (tix % HR) % gridDim.y, r = (tix % HR) / gridDim.y;
   const int g = h / (a.NH / a.NKV);
@@ -730,20 +733,47 @@ void launch_kv_pack(const KvPackArgs& a, hipStream_t st) {
   else report_unlaunched("K/V packing: head_dim");
 }
 
+namespace {
+// blocks of each tiled-attention form that the device holds at once (CUs x blocks per
+// CU), per device: [device][HD 128][split]
+constexpr int kMaxDevices = 64;
+int g_tiled_resident[kMaxDevices][2][2];
+
+template <int HD, bool SPLIT>
+void tiled_init(int dev, int cus) {
+  using TC = TiledCfg<HD, SPLIT>;
+  (void)hipFuncSetAttribute((const void*)k_flash_tiled<HD, SPLIT>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)TC::LDS);
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_flash_tiled<HD, SPLIT>,
+                                                   TC::NT, TC::LDS) != hipSuccess)
+    per_cu = 0;
+  g_tiled_resident[dev][HD == 128][SPLIT] = per_cu * cus;
+}
+}  // namespace
+
 void flash_init() {
-  (void)hipFuncSetAttribute((const void*)k_flash_tiled<64, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)TiledCfg<64, false>::LDS);
-  (void)hipFuncSetAttribute((const void*)k_flash_tiled<64, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)TiledCfg<64, true>::LDS);
-  (void)hipFuncSetAttribute((const void*)k_flash_tiled<128, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)TiledCfg<128, false>::LDS);
-  (void)hipFuncSetAttribute((const void*)k_flash_tiled<128, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)TiledCfg<128, true>::LDS);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+  tiled_init<64, false>(dev, cus);
+  tiled_init<64, true>(dev, cus);
+  tiled_init<128, false>(dev, cus);
+  tiled_init<128, true>(dev, cus);
 }
 
 void launch_flash_tiled(const FlashArgs& a, const uint16_t* kp, const uint16_t* vt, int LK,
                         bool split, hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
 #define EMBER_TILED(HDV, SP)                                                           \
   {                                                                                    \
     using TC = TiledCfg<HDV, SP>;                                                      \
     const dim3 grid((a.tokens_per_row + TC::TQ - 1) / TC::TQ, a.NH, a.rows);            \
-    hipLaunchKernelGGL((k_flash_tiled<HDV, SP>), grid, dim3(TC::NT), TC::LDS, st, a, kp, vt, LK); \
+    const long long blocks = (long long)grid.x * grid.y * grid.z;                      \
+    const int resident = g_tiled_resident[dev][HDV == 128][SP];                        \
+    const int lf = resident > 0 && blocks > resident;                                  \
+    hipLaunchKernelGGL((k_flash_tiled<HDV, SP>), grid, dim3(TC::NT), TC::LDS, st, a, kp, vt, LK, lf); \
   }
   if (a.HD == 64) {
     if (split) EMBER_TILED(64, true) else EMBER_TILED(64, false)

@@ -6,14 +6,15 @@
 // by both planes, which makes each product f32-accurate to ~2^-17 relative (the weights
 // are exactly bf16, and bf16 x bf16 products are exact in f32); in FAST mode only hi.
 //
-// Tiling: 256 threads (4 waves, 2 x 2), block tile BM x BN, K stage 64. Global loads are
-// 16 bytes per lane, 8 lanes per 128-byte row segment, and run PF stages ahead in
-// registers; the LDS holds two stages (rows padded by 16 bytes, so the 32 rows a
-// fragment read touches fall on distinct banks). Each wave computes (BM/2) x (BN/2) with
-// 32x32x16 MFMAs and reads the fragments of k-step t + 1 while the MFMAs of step t run
-// (scheduling groups pin that interleave, and put the next stage's LDS stores under the
-// last step's MFMAs). Blocks are remapped so that consecutive tiles of one weight column
-// block run on the same XCD (its L2 serves the repeated weight reads).
+// Two main loops share the tiling and the epilogues. k_gemm: global loads of 16 bytes per
+// lane, 8 lanes per 128-byte row segment, PF stages ahead in registers, then stored to an
+// LDS of two stages (rows padded by 16 bytes, so the 32 rows a fragment read touches fall
+// on distinct banks); it serves every K. k_gemm_dl (K a multiple of 64): the tiles go
+// straight from global memory into LDS (below). Block tile BM x BN, K stage 64; each wave
+// computes a WM x WN share of it with 32x32x16 MFMAs and reads the fragments of k-step
+// t + 1 while the MFMAs of step t run (scheduling groups pin that interleave). Blocks are
+// remapped so that the tiles one XCD runs at a time share A rows and weight columns in
+// its L2.
 //
 // Epilogues: store (+bias), residual add (x += C), SiLU*up over the gate/up rows that
 // the weight repack interleaves in blocks of 32 (the lane holding gate column j of
@@ -37,6 +38,136 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 template <int BM, int BN, bool SPLIT>
 constexpr size_t gemm_lds_bytes() {
   return (size_t)2 * ((SPLIT ? 2 : 1) * BM + BN) * LDS_STRIDE * 2;
+}
+
+// Epilogue of one wave's TM x TN fragments: element e of fragment (i, j) is C[row][col]
+// with row = m0 + wm0 + 32 i + 4 (lane / 32) + 8 (e / 4) + e % 4,
+// col = n0 + wn0 + 32 j + lane % 32.
+template <int TM, int TN, int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x16_t (&acc)[TM][TN],
+                                              const float (&biasv)[TN], int m0, int n0,
+                                              int wm0, int wn0, int lane) {
+  const int fr = lane % 32;
+  // One 64-bit base per fragment, 32-bit row offsets after it (fewer live registers
+  // across the whole kernel than a 64-bit product per element).
+  const int rb0 = m0 + wm0 + 4 * (lane / 32);
+  if (a.partial) {                         // split-K: raw f32 tile into this slice's plane
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wn0 + j * 32 + fr;
+        const int row0 = rb0 + i * 32;
+        float* pb = a.partial + ((size_t)blockIdx.y * a.M + row0) * a.N + col;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int dr = 8 * (e / 4) + e % 4;
+          if (col < a.N && row0 + dr < a.M) pb[dr * a.N] = acc[i][j][e];
+        }
+      }
+    return;
+  }
+  if constexpr (EPI == GEMM_QKV) {
+    // head_dim 64: the wave's columns start on a head, so fragment j (even) holds dims
+    // 0..31 of head (n0 + wn0 + 32 j) / 64 in this lane's column and fragment j + 1 dims
+    // 32..63: the rotate-half pair (d, d + 32) of a row sits in one lane, and the 32 lanes
+    // of a half-wave hold one row's 64 dims (the per-head norm is a 5-step lane sum).
+    // Heads run q, then k, then v ("ember scripts/reference_forward.py", rope; q/k norm
+    // before RoPE: "PII-Tracer serving/reference_forward.py", forward); K and V land at the
+    // token's explicit position (ember internals page, "cursor semantics").
+    const QkvPostArgs& qp = a.post;
+    const int start = qp.d_pos ? *qp.d_pos : qp.start_pos;
+#pragma unroll
+    for (int j = 0; j < TN; j += 2) {
+      const int hcol = n0 + wn0 + 32 * j;
+      if (hcol >= a.N) continue;                            // wave-uniform
+      const int h = hcol / 64;
+      const bool is_q = h < qp.NH, is_v = h >= qp.NH + qp.NKV;
+      const float* nw = is_q ? qp.q_norm : qp.k_norm;
+      const bool norm = nw != nullptr && !is_v;             // wave-uniform
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row0 = rb0 + i * 32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = row0 + 8 * (e / 4) + e % 4;
+          float x0 = acc[i][j][e] + biasv[j], x1 = acc[i][j + 1][e] + biasv[j + 1];
+          if (norm) {
+            float ss = x0 * x0 + x1 * x1;
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o);
+            const float rms = sqrtf(ss / 64.f + qp.eps);
+            x0 = x0 / rms * nw[fr];
+            x1 = x1 / rms * nw[fr + 32];
+          }
+          if (row >= a.M) continue;
+          const int p = start + row % qp.tokens_per_row;
+          float y0 = x0, y1 = x1;
+          if (!is_v) {
+            const float cs = qp.cos_t[(size_t)p * 32 + fr], sn = qp.sin_t[(size_t)p * 32 + fr];
+            y0 = x0 * cs - x1 * sn;
+            y1 = x1 * cs + x0 * sn;
+          }
+          if (is_q) {
+            float* dst = qp.q_out + (size_t)row * qp.NH * 64 + h * 64 + fr;
+            dst[0] = y0;
+            dst[32] = y1;
+          } else {
+            const int b = qp.b0 + row / qp.tokens_per_row;
+            const int kvh = is_v ? h - qp.NH - qp.NKV : h - qp.NH;
+            const size_t off = (((size_t)b * qp.NKV + kvh) * qp.max_seq + p) * 64 + fr;
+            void* cache = is_v ? qp.v_cache : qp.k_cache;
+            if (qp.kv_bf16) {
+              ((uint16_t*)cache)[off] = (uint16_t)f32_to_bf16_rne(y0);
+              ((uint16_t*)cache)[off + 32] = (uint16_t)f32_to_bf16_rne(y1);
+            } else {
+              ((float*)cache)[off] = y0;
+              ((float*)cache)[off + 32] = y1;
+            }
+          }
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn0 + j * 32 + fr;
+      const int row0 = rb0 + i * 32;
+      if (EPI == GEMM_SILU) {
+        // fragment j (even) holds gate outputs, fragment j + 1 the matching up outputs
+        if (j % 2) continue;
+        const int ocol = (col / (2 * kGuBlock)) * kGuBlock + col % kGuBlock;
+        const size_t ob = (size_t)row0 * a.ldo + ocol;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int dr = 8 * (e / 4) + e % 4;
+          if (row0 + dr >= a.M || col >= a.N) continue;
+          const float v = silu(acc[i][j][e]) * acc[i][j + 1][e];
+          const size_t o = ob + dr * a.ldo;
+          if (a.o_f32) a.o_f32[o] = v;
+          if (a.o_hi) {
+            uint32_t h, l;
+            split_bf16(v, h, l);
+            a.o_hi[o] = (uint16_t)h;
+            if (a.o_lo) a.o_lo[o] = (uint16_t)l;
+          }
+        }
+      } else {
+        float* cb = a.c + (size_t)row0 * a.ldc + col;
+        const int ld = (int)a.ldc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int dr = 8 * (e / 4) + e % 4;
+          if (col >= a.N || row0 + dr >= a.M) continue;
+          if (EPI == GEMM_RESID) cb[dr * ld] += acc[i][j][e];
+          else cb[dr * ld] = acc[i][j][e] + biasv[j];
+        }
+      }
+    }
+  }
 }
 
 // KG > 1: KG groups of WM x WN waves compute the same tile over consecutive parts of
@@ -244,134 +375,214 @@ __global__ void __launch_bounds__(WM * WN * KG * kWave) k_gemm(GemmArgs a) {
             acc[i][j][e] += red[(((((size_t)(g - 1) * WM * WN + wave) * TM + i) * TN + j) * 16 + e) * kWave + lane];
   }
 
-  // epilogue: element e of fragment (i, j) is C[row][col] with
-  // row = m0 + wm0 + 32 i + 4 (lane / 32) + 8 (e / 4) + e % 4, col = n0 + wn0 + 32 j + lane % 32.
-  // One 64-bit base per fragment, 32-bit row offsets after it (fewer live registers
-  // across the whole kernel than a 64-bit product per element).
-  const int rb0 = m0 + wm0 + 4 * (lane / 32);
-  if (a.partial) {                         // split-K: raw f32 tile into this slice's plane
+  gemm_epilogue<TM, TN, EPI>(a, acc, biasv, m0, n0, wm0, wn0, lane);
+}
+
+// ------------------------------------------------------------------ direct-to-LDS main loop
+// The operand tiles go from global memory straight into LDS with global_load_lds_dwordx4
+// (each lane's 16 bytes land at the wave's LDS address + 16 x lane), NS stages deep: no
+// register staging, no LDS store instructions, and the loads of NS - 1 stages in flight
+// behind the MFMAs. One wave-wide load moves RPI whole rows of a BK-column stage. Rows are
+// unpadded (a wave-wide load is 1 KB of consecutive LDS), so the 16-byte chunks of a row
+// are stored XOR-swizzled: chunk c of stage row r sits in slot c ^ swz(r), which spreads
+// the 32 rows of one fragment read over all bank groups. One barrier per stage: a stage's
+// slot is refilled only after every wave has passed the barrier that follows its use.
+template <int BK>
+EMBER_DEV int dl_swz(int r) { return BK == 64 ? (r & 7) : ((r >> 1) & 3); }
+
+// s_waitcnt immediate: vector-memory count <= n, the other counters unconstrained
+constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+
+template <int BM, int BN, int WM, int WN, int BK, int NS, bool SPLIT, int EPI>
+__global__ void __launch_bounds__(WM * WN * kWave) k_gemm_dl(GemmArgs a) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;     // 32x32 fragments per wave
+  constexpr int NP = SPLIT ? 2 : 1;
+  constexpr int CPR = BK / 8, RPI = kWave / CPR;          // chunks per row, rows per load
+  constexpr int ROWS = NP * BM + BN;                      // stage rows: A planes, then W
+  constexpr int IA = BM / (RPI * NW), NI = ROWS / (RPI * NW);
+  constexpr int STAGE = ROWS * BK;                        // bf16 elements
+  static_assert(BK == 32 || BK == 64, "stage width");
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "a load stays in one operand");
+  static_assert(NS >= 2 && NS <= 4 && (NS - 1) * NI <= 63, "stages in flight within the vmcnt range");
+  static_assert(EPI != GEMM_SILU || TN % 2 == 0, "SiLU pairs gate/up fragments");
+  extern __shared__ __align__(16) uint16_t smem[];
+
+  // XCD-aware band order of the tiles (as in k_gemm)
+  const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
+  const int nblk = mt * nt;
+  int lin = blockIdx.x;
+  if (nblk % 8 == 0) lin = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
+  constexpr int kBandM = 8;
+  const int band = lin / (kBandM * nt), m_first = band * kBandM;
+  const int band_m = min(mt - m_first, kBandM);
+  const int in_band = lin - band * kBandM * nt;
+  const int tm = m_first + in_band % band_m, tn = in_band / band_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wm0 = (wave / WN) * (BM / WM), wn0 = (wave % WN) * (BN / WN);
+  const int fr = lane % 32;
+
+  // K range of this block (split-K slices of k_chunk columns; whole stages)
+  const int kb0 = blockIdx.y * a.k_chunk;
+  const int nk = (min(a.K, kb0 + a.k_chunk) - kb0) / BK;
+
+  // load i of a stage covers stage rows (i NW + wave) RPI .. + RPI; this lane takes row
+  // lr of them and stores its chunk in slot ls, so it loads chunk ls ^ swz(row)
+  const int lr = lane / CPR, ls = lane % CPR;
+  uint32_t off[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int srow = (i * NW + wave) * RPI + lr;
+    const int c = ls ^ dl_swz<BK>(srow);
+    if (i < NP * IA) {
+      const int r = srow - (i < IA ? 0 : BM);
+      off[i] = (uint32_t)min(m0 + r, a.M - 1) * (uint32_t)a.lda + c * 8;
+    } else {
+      const int r = srow - NP * BM;
+      off[i] = (uint32_t)min(n0 + r, a.N - 1) * (uint32_t)a.K + c * 8;
+    }
+  }
+  auto issue = [&](int slot, int t) {
+    const int k0 = kb0 + t * BK;
+    uint16_t* st = smem + slot * STAGE;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint16_t* base = i < IA ? a.a_hi : (SPLIT && i < NP * IA) ? a.a_lo : a.w;
+      __builtin_amdgcn_global_load_lds((const void*)(base + off[i] + k0),
+                                       (__attribute__((address_space(3))) void*)(st + (i * NW + wave) * RPI * BK),
+                                       16, 0, 0);
+    }
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  float biasv[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+    biasv[j] = ((EPI == GEMM_STORE || EPI == GEMM_QKV) && a.bias && !a.partial)
+                   ? a.bias[min(n0 + wn0 + j * 32 + fr, a.N - 1)] : 0.f;
+
+  // fragment reads: A fragment i is stage row wm0 + 32 i + fr, W fragment j stage row
+  // NP BM + wn0 + 32 j + fr; k-step kk reads logical chunk 2 kk + lane / 32 (the swizzle
+  // of these rows depends on fr alone)
+  const int sw = dl_swz<BK>(fr);
+  int cofs[BK / 16];
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) cofs[kk] = ((2 * kk + lane / 32) ^ sw) * 8;
+  const int arow = (wm0 + fr) * BK, wrow = (NP * BM + wn0 + fr) * BK;
+  bf16x8_t fh[2][TM], fl[2][SPLIT ? TM : 1], fw[2][TN];
+  auto rdfrag = [&](int f, const uint16_t* st, int kk) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      fh[f][i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + arow + i * 32 * BK + cofs[kk]));
+      if (SPLIT)
+        fl[f][i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + BM * BK + arow + i * 32 * BK + cofs[kk]));
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      fw[f][j] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + wrow + j * 32 * BK + cofs[kk]));
+  };
+  auto mfmas = [&](int f) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int col = n0 + wn0 + j * 32 + fr;
-        const int row0 = rb0 + i * 32;
-        float* pb = a.partial + ((size_t)blockIdx.y * a.M + row0) * a.N + col;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int dr = 8 * (e / 4) + e % 4;
-          if (col < a.N && row0 + dr < a.M) pb[dr * a.N] = acc[i][j][e];
-        }
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[f][i], fw[f][j], acc[i][j], 0, 0, 0);
+        if (SPLIT)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[f][i], fw[f][j], acc[i][j], 0, 0, 0);
       }
-    return;
-  }
-  if constexpr (EPI == GEMM_QKV) {
-    // head_dim 64: the wave's columns start on a head, so fragment j (even) holds dims
-    // 0..31 of head (n0 + wn0 + 32 j) / 64 in this lane's column and fragment j + 1 dims
-    // 32..63: the rotate-half pair (d, d + 32) of a row sits in one lane, and the 32 lanes
-    // of a half-wave hold one row's 64 dims (the per-head norm is a 5-step lane sum).
-    // Heads run q, then k, then v ("ember scripts/reference_forward.py", rope; q/k norm
-    // before RoPE: "PII-Tracer serving/reference_forward.py", forward); K and V land at the
-    // token's explicit position (ember internals page, "cursor semantics").
-    const QkvPostArgs& qp = a.post;
-    const int start = qp.d_pos ? *qp.d_pos : qp.start_pos;
+  };
+
+  // Stage t sits in slot t % NS. The barrier between stages t and t + 1 comes after every
+  // wave has read all of stage t (lgkmcnt 0) and seen stage t + 1 land (vmcnt); behind it
+  // the wave refills slot t % NS with stage t + NS, reads stage t + 1's first fragments
+  // and only then issues stage t's last MFMAs, so no wave restarts with an empty pipe.
+  constexpr int KS = BK / 16;
+  constexpr int NMF = NP * TM * TN, NRD = NP * TM + TN;   // MFMAs, fragment reads per k-step
+  static_assert(KS % 2 == 0, "stage t + 1 starts in fragment buffer 0");
 #pragma unroll
-    for (int j = 0; j < TN; j += 2) {
-      const int hcol = n0 + wn0 + 32 * j;
-      if (hcol >= a.N) continue;                            // wave-uniform
-      const int h = hcol / 64;
-      const bool is_q = h < qp.NH, is_v = h >= qp.NH + qp.NKV;
-      const float* nw = is_q ? qp.q_norm : qp.k_norm;
-      const bool norm = nw != nullptr && !is_v;             // wave-uniform
+  for (int p = 0; p < NS; ++p)
+    if (p < nk) issue(p, p);
+  int slot = 0;
+  if (nk > 0) {
+    // stage 0 has landed once at most min(NS, nk) - 1 younger stages are in flight
+    const int younger = min(NS, nk) - 1;
+    if (younger <= 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    else if (younger == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));
+    else if (younger == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    rdfrag(0, smem, 0);
+  }
+  for (int t = 0; t < nk; ++t) {
+    const uint16_t* st = smem + slot * STAGE;
+#pragma unroll
+    for (int kk = 0; kk + 1 < KS; ++kk) {
+      rdfrag((kk + 1) & 1, st, kk + 1);
+      mfmas(kk & 1);
+    }
+    // one fragment read of the next k-step after every NMF / NRD MFMAs of this one
+#pragma unroll
+    for (int kk = 0; kk + 1 < KS; ++kk)
+#pragma unroll
+      for (int r = 0; r < NRD; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF / NRD > 0 ? NMF / NRD : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    const int nslot = slot + 1 == NS ? 0 : slot + 1;
+    {
+      // stages t + 2 .. min(t + NS - 1, nk - 1) may stay in flight (after the last stage
+      // nothing is in flight; its barrier and reads are harmless: the reads fetch a slot's
+      // stale data and are never used)
+      const int younger = min(NS - 2, nk - 2 - t);
+      if (younger <= 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & ~(15 << 8));
+      else if (younger == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI) & ~(15 << 8));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI) & ~(15 << 8));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      // the last k-step's fragments pass through an empty asm statement behind the
+      // barrier: its MFMAs cannot be scheduled above it
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int row0 = rb0 + i * 32;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = row0 + 8 * (e / 4) + e % 4;
-          float x0 = acc[i][j][e] + biasv[j], x1 = acc[i][j + 1][e] + biasv[j + 1];
-          if (norm) {
-            float ss = x0 * x0 + x1 * x1;
-#pragma unroll
-            for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o);
-            const float rms = sqrtf(ss / 64.f + qp.eps);
-            x0 = x0 / rms * nw[fr];
-            x1 = x1 / rms * nw[fr + 32];
-          }
-          if (row >= a.M) continue;
-          const int p = start + row % qp.tokens_per_row;
-          float y0 = x0, y1 = x1;
-          if (!is_v) {
-            const float cs = qp.cos_t[(size_t)p * 32 + fr], sn = qp.sin_t[(size_t)p * 32 + fr];
-            y0 = x0 * cs - x1 * sn;
-            y1 = x1 * cs + x0 * sn;
-          }
-          if (is_q) {
-            float* dst = qp.q_out + (size_t)row * qp.NH * 64 + h * 64 + fr;
-            dst[0] = y0;
-            dst[32] = y1;
-          } else {
-            const int b = qp.b0 + row / qp.tokens_per_row;
-            const int kvh = is_v ? h - qp.NH - qp.NKV : h - qp.NH;
-            const size_t off = (((size_t)b * qp.NKV + kvh) * qp.max_seq + p) * 64 + fr;
-            void* cache = is_v ? qp.v_cache : qp.k_cache;
-            if (qp.kv_bf16) {
-              ((uint16_t*)cache)[off] = (uint16_t)f32_to_bf16_rne(y0);
-              ((uint16_t*)cache)[off + 32] = (uint16_t)f32_to_bf16_rne(y1);
-            } else {
-              ((float*)cache)[off] = y0;
-              ((float*)cache)[off + 32] = y1;
-            }
-          }
-        }
+        asm volatile("" : "+v"(fh[(KS - 1) & 1][i]));
+        if (SPLIT) asm volatile("" : "+v"(fl[(KS - 1) & 1][i]));
       }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(fw[(KS - 1) & 1][j]));
+      if (t + NS < nk) issue(slot, t + NS);
+      rdfrag(0, smem + nslot * STAGE, 0);
     }
-    return;
-  }
+    mfmas((KS - 1) & 1);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn0 + j * 32 + fr;
-      const int row0 = rb0 + i * 32;
-      if (EPI == GEMM_SILU) {
-        // fragment j (even) holds gate outputs, fragment j + 1 the matching up outputs
-        if (j % 2) continue;
-        const int ocol = (col / (2 * kGuBlock)) * kGuBlock + col % kGuBlock;
-        const size_t ob = (size_t)row0 * a.ldo + ocol;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int dr = 8 * (e / 4) + e % 4;
-          if (row0 + dr >= a.M || col >= a.N) continue;
-          const float v = silu(acc[i][j][e]) * acc[i][j + 1][e];
-          const size_t o = ob + dr * a.ldo;
-          if (a.o_f32) a.o_f32[o] = v;
-          if (a.o_hi) {
-            uint32_t h, l;
-            split_bf16(v, h, l);
-            a.o_hi[o] = (uint16_t)h;
-            if (a.o_lo) a.o_lo[o] = (uint16_t)l;
-          }
-        }
-      } else {
-        float* cb = a.c + (size_t)row0 * a.ldc + col;
-        const int ld = (int)a.ldc;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int dr = 8 * (e / 4) + e % 4;
-          if (col >= a.N || row0 + dr >= a.M) continue;
-          if (EPI == GEMM_RESID) cb[dr * ld] += acc[i][j][e];
-          else cb[dr * ld] = acc[i][j][e] + biasv[j];
-        }
-      }
+    for (int r = 0; r < NRD; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF / NRD > 0 ? NMF / NRD : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    slot = nslot;
   }
+  gemm_epilogue<TM, TN, EPI>(a, acc, biasv, m0, n0, wm0, wn0, lane);
+}
+
+template <int BM, int BN, int BK, int NS, bool SPLIT>
+constexpr size_t gemm_dl_lds_bytes() {
+  return (size_t)NS * ((SPLIT ? 2 : 1) * BM + BN) * BK * 2;
 }
 
 // Tile configurations: block BM x BN, WM x WN waves, register prefetch depth PF, KG
 // groups of waves over the K range.
 enum GemmCfg { CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x128 = 3, CFG_256x256 = 4, CFG_64x64 = 5,
-               CFG_128x128_K2 = 6, CFG_128x256_W8 = 7 };
+               CFG_128x128_K2 = 6, CFG_128x256_W8 = 7,
+               // direct-to-LDS main loop (k_gemm_dl), BK 64, two stages
+               CFG_DL_256x256 = 8,        // one plane: 8 waves of 128 x 64
+               CFG_DL_S128x256 = 9 };     // two planes: 8 waves of 64 x 64
 
 template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI, int KG = 1>
 void set_attr() {
@@ -397,6 +608,21 @@ void launch_cfg(const GemmArgs& a, int splits, hipStream_t st) {
                        dim3(WM * WN * KG * kWave), lds, st, a);
 }
 
+template <int BM, int BN, int WM, int WN, int BK, int NS, bool SPLIT, int EPI>
+void set_attr_dl() {
+  (void)hipFuncSetAttribute((const void*)k_gemm_dl<BM, BN, WM, WN, BK, NS, SPLIT, EPI>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)gemm_dl_lds_bytes<BM, BN, BK, NS, SPLIT>());
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int NS, bool SPLIT, int EPI>
+void launch_dl(const GemmArgs& a, int splits, hipStream_t st) {
+  const int blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  constexpr size_t lds = gemm_dl_lds_bytes<BM, BN, BK, NS, SPLIT>();
+  hipLaunchKernelGGL((k_gemm_dl<BM, BN, WM, WN, BK, NS, SPLIT, EPI>), dim3(blocks, splits),
+                     dim3(WM * WN * kWave), lds, st, a);
+}
+
 int tiles_of(const GemmArgs& a, int bm, int bn) {
   return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
 }
@@ -411,16 +637,20 @@ int tiles_of(const GemmArgs& a, int bm, int bn) {
 // split-K planes and reduce that 128 x 128 tiles need (0.5B prefill GEMMs 10-20 % faster).
 int pick_cfg(const GemmArgs& a) {
   if (a.M <= 128) return CFG_64x64;
+  // K in whole 64-column stages: the large tile forms load straight from global memory
+  // into LDS (k_gemm_dl; 4-10 % faster than register staging on the 1B-shape GEMMs)
+  const bool dl = a.K % BK == 0;
   // two-plane input: 128 x 256 tiles over 8 waves of 64 x 64 (two waves per SIMD; over 4
   // waves of 64 x 128 the accumulators and fragments held a wave to one per SIMD)
-  if (a.a_lo) return tiles_of(a, 128, 256) >= 180 ? CFG_128x256_W8 : CFG_128x128;
-  if (tiles_of(a, 256, 256) >= 256) return CFG_256x256;
+  if (a.a_lo)
+    return tiles_of(a, 128, 256) >= 180 ? (dl ? CFG_DL_S128x256 : CFG_128x256_W8) : CFG_128x128;
+  if (tiles_of(a, 256, 256) >= 256) return dl ? CFG_DL_256x256 : CFG_256x256;
   // long K against N (the down projection at M = 2048): 256 x 256 tiles over four K
   // slices, whose partial planes cost less than the halved operand traffic saves there
   // (measured slower for K <= N)
   if (a.partial && a.K >= 4 * a.N && a.K >= 4096 && tiles_of(a, 256, 256) >= 64 &&
       (size_t)4 * a.M * a.N <= a.partial_elems)
-    return CFG_256x256;
+    return dl ? CFG_DL_256x256 : CFG_256x256;
   // about one 128 x 128 tile per CU: two K groups per tile (two waves per SIMD) when the
   // stages split evenly
   const int t128 = tiles_of(a, 128, 128);
@@ -431,7 +661,8 @@ int pick_cfg(const GemmArgs& a) {
 void cfg_dims(int cfg, int& bm, int& bn) {
   switch (cfg) {
     case CFG_256x256: bm = 256; bn = 256; break;
-    case CFG_128x256: case CFG_128x256_W8: bm = 128; bn = 256; break;
+    case CFG_128x256: case CFG_128x256_W8: case CFG_DL_S128x256: bm = 128; bn = 256; break;
+    case CFG_DL_256x256: bm = 256; bn = 256; break;
     case CFG_128x128: case CFG_128x128_K2: bm = 128; bn = 128; break;
     case CFG_64x64: bm = 64; bn = 64; break;
     default: bm = 64; bn = 128; break;
@@ -451,6 +682,14 @@ void launch_split(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
       if constexpr (!SPLIT) launch_cfg<128, 128, 2, 2, 2, false, EPI, 2>(a, splits, st);
       break;
     case CFG_64x64: launch_cfg<64, 64, 2, 1, 4, SPLIT, EPI>(a, splits, st); break;
+    case CFG_DL_256x256:
+      if constexpr (!SPLIT) launch_dl<256, 256, 2, 4, 64, 2, false, EPI>(a, splits, st);
+      else report_unlaunched("GEMM: one-plane tile form with two planes");
+      break;
+    case CFG_DL_S128x256:
+      if constexpr (SPLIT) launch_dl<128, 256, 2, 4, 64, 2, true, EPI>(a, splits, st);
+      else report_unlaunched("GEMM: two-plane tile form with one plane");
+      break;
     default: launch_cfg<64, 128, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
   }
 }
@@ -472,6 +711,8 @@ void set_attrs_split() {
   set_attr<128, 128, 2, 2, 2, SPLIT, EPI>();
   set_attr<64, 128, 2, 2, 2, SPLIT, EPI>();
   set_attr<64, 64, 2, 1, 4, SPLIT, EPI>();
+  if constexpr (!SPLIT) set_attr_dl<256, 256, 2, 4, 64, 2, false, EPI>();
+  else set_attr_dl<128, 256, 2, 4, 64, 2, true, EPI>();
 }
 
 template <int EPI>
@@ -577,9 +818,10 @@ int pick_splits(const GemmArgs& a, int cfg) {
   cfg_dims(cfg, bm, bn);
   const int tiles = tiles_of(a, bm, bn);
   if (tiles >= 192) return 1;
-  const int target = (cfg == CFG_64x64 || cfg == CFG_256x256) ? 256 : 512;
+  const bool big = bm == 256 && bn == 256;
+  const int target = (cfg == CFG_64x64 || big) ? 256 : 512;
   int s = (target + tiles - 1) / tiles;
-  const int max_s = a.K / (cfg == CFG_256x256 ? 1024 : 256);
+  const int max_s = a.K / (big ? 1024 : 256);
   if (s > max_s) s = max_s;
   if ((size_t)s * a.M * a.N > a.partial_elems) s = (int)(a.partial_elems / ((size_t)a.M * a.N));
   return s < 2 ? 1 : s;
