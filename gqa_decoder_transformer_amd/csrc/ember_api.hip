@@ -452,13 +452,20 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     g.M = ps.M; g.N = p.qkv_n; g.K = H; g.bias = bqkv; g.c = qkv; g.ldc = p.qkv_n;
     if (exact) {
       // EXACT: the input as three bf16 planes (within ~2^-25), so q and k are f32-level:
-      // planes hi + lo store the projections (+bias), the third plane adds into them;
-      // the post-processing (prefill) or the decode attention then reads them
+      // planes hi + lo store the projections (+bias), the third plane adds into them
+      // (v as well: with peaked attention the output is one value row, and two planes
+      // leave it ~2^-17 sqrt(K) off, 1e-4 in the logits); the post-processing (prefill)
+      // or the decode attention then reads them
       if (want(cx, EMBER_K_QKV)) {
-        launch_gemm(g, GEMM_STORE, st);
         GemmArgs g3 = g;
-        g3.a_hi = pa_x2; g3.a_lo = nullptr; g3.bias = nullptr;
-        launch_gemm(g3, GEMM_RESID, st);
+        g3.a_x2 = pa_x2;
+        if (gemm_three_planes(g3)) {
+          launch_gemm(g3, GEMM_STORE, st);              // all three planes in one pass
+        } else {
+          launch_gemm(g, GEMM_STORE, st);
+          g3.a_hi = pa_x2; g3.a_lo = nullptr; g3.a_x2 = nullptr; g3.bias = nullptr;
+          launch_gemm(g3, GEMM_RESID, st);
+        }
       }
       if (want_aux(cx) && ps.attn == ATTN_FLASH) launch_qkv_post(qa, st);
     } else if (ps.attn == ATTN_FLASH) {

@@ -240,6 +240,9 @@ struct GemmArgs {
   // A: activations as bf16 planes [M, lda] (hi, and lo in EXACT mode; lo == null: one pass)
   const uint16_t* a_hi;
   const uint16_t* a_lo;
+  // optional third plane x2 = bf16(x - hi - lo) in the same layout (EXACT QKV input); only
+  // where gemm_three_planes() holds, and with GEMM_STORE
+  const uint16_t* a_x2;
   int lda;
   // B: weights bf16 [N, K] row-major (K contiguous). With w_lo (same layout) the weights
   // are w + w_lo (a value that bf16 cannot hold, such as a dequantised q8_0 weight, as a
@@ -265,6 +268,9 @@ struct GemmArgs {
   QkvPostArgs post;        // GEMM_QKV only (post.qkv = c)
 };
 void launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
+// true when launch_gemm takes a_x2 as a third activation plane in the same pass (tile forms
+// that load straight into LDS); otherwise the caller adds that plane's product separately
+bool gemm_three_planes(const GemmArgs& a);
 // Sets the dynamic LDS limit of every GEMM kernel (call once before the first launch).
 void gemm_init();
 
@@ -339,7 +345,7 @@ void flash_init();
 // Measurement kernels (kernels_peak.hip): a streaming copy of `bytes` from src to dst, and
 // an MFMA-only loop over kPeakMfmaBlocks blocks of 256 threads that writes one float per
 // thread to `out` and returns the flops of one launch.
-constexpr int kPeakMfmaBlocks = 2048;
+constexpr int kPeakMfmaBlocks = 1024;
 constexpr int kPeakReadBlocks = 256 * 8;
 void launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 // A streaming read of `bytes` at src; one word per thread of kPeakReadBlocks x 256 to out.

@@ -393,18 +393,31 @@ EMBER_DEV int dl_swz(int r) { return BK == 64 ? (r & 7) : ((r >> 1) & 3); }
 // s_waitcnt immediate: vector-memory count <= n, the other counters unconstrained
 constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
 
-template <int BM, int BN, int WM, int WN, int BK, int NS, bool SPLIT, int EPI>
+// wait until at most min(younger, Y) stages of NI loads each are in flight (immediate
+// operands: one s_waitcnt per possible count); LGKM: also every LDS read done
+template <int NI, int Y, bool LGKM>
+EMBER_DEV void wait_stages(int younger) {
+  constexpr int lg = LGKM ? ~(15 << 8) : ~0;
+  if constexpr (Y <= 0) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & lg);
+  } else {
+    if (younger >= Y) __builtin_amdgcn_s_waitcnt(vmcnt_imm(Y * NI) & lg);
+    else wait_stages<NI, Y - 1, LGKM>(younger);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int EPI>
 __global__ void __launch_bounds__(WM * WN * kWave) k_gemm_dl(GemmArgs a) {
+  // NP activation planes: hi (1), + lo (2), + x2 (3: a_x2, the EXACT QKV input)
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;     // 32x32 fragments per wave
-  constexpr int NP = SPLIT ? 2 : 1;
   constexpr int CPR = BK / 8, RPI = kWave / CPR;          // chunks per row, rows per load
   constexpr int ROWS = NP * BM + BN;                      // stage rows: A planes, then W
   constexpr int IA = BM / (RPI * NW), NI = ROWS / (RPI * NW);
   constexpr int STAGE = ROWS * BK;                        // bf16 elements
   static_assert(BK == 32 || BK == 64, "stage width");
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "a load stays in one operand");
-  static_assert(NS >= 2 && NS <= 4 && (NS - 1) * NI <= 63, "stages in flight within the vmcnt range");
+  static_assert(NS >= 2 && (NS - 1) * NI <= 63, "stages in flight within the vmcnt range");
   static_assert(EPI != GEMM_SILU || TN % 2 == 0, "SiLU pairs gate/up fragments");
   extern __shared__ __align__(16) uint16_t smem[];
 
@@ -436,7 +449,7 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm_dl(GemmArgs a) {
     const int srow = (i * NW + wave) * RPI + lr;
     const int c = ls ^ dl_swz<BK>(srow);
     if (i < NP * IA) {
-      const int r = srow - (i < IA ? 0 : BM);
+      const int r = srow - (i / IA) * BM;
       off[i] = (uint32_t)min(m0 + r, a.M - 1) * (uint32_t)a.lda + c * 8;
     } else {
       const int r = srow - NP * BM;
@@ -448,7 +461,8 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm_dl(GemmArgs a) {
     uint16_t* st = smem + slot * STAGE;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const uint16_t* base = i < IA ? a.a_hi : (SPLIT && i < NP * IA) ? a.a_lo : a.w;
+      const uint16_t* base = i < IA ? a.a_hi : (NP > 1 && i < 2 * IA) ? a.a_lo
+                                             : (NP > 2 && i < 3 * IA) ? a.a_x2 : a.w;
       __builtin_amdgcn_global_load_lds((const void*)(base + off[i] + k0),
                                        (__attribute__((address_space(3))) void*)(st + (i * NW + wave) * RPI * BK),
                                        16, 0, 0);
@@ -476,13 +490,15 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm_dl(GemmArgs a) {
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) cofs[kk] = ((2 * kk + lane / 32) ^ sw) * 8;
   const int arow = (wm0 + fr) * BK, wrow = (NP * BM + wn0 + fr) * BK;
-  bf16x8_t fh[2][TM], fl[2][SPLIT ? TM : 1], fw[2][TN];
+  bf16x8_t fh[2][TM], fl[2][NP > 1 ? TM : 1], fx[2][NP > 2 ? TM : 1], fw[2][TN];
   auto rdfrag = [&](int f, const uint16_t* st, int kk) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       fh[f][i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + arow + i * 32 * BK + cofs[kk]));
-      if (SPLIT)
+      if (NP > 1)
         fl[f][i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + BM * BK + arow + i * 32 * BK + cofs[kk]));
+      if (NP > 2)
+        fx[f][i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(st + 2 * BM * BK + arow + i * 32 * BK + cofs[kk]));
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j)
@@ -494,8 +510,10 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm_dl(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[f][i], fw[f][j], acc[i][j], 0, 0, 0);
-        if (SPLIT)
+        if (NP > 1)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[f][i], fw[f][j], acc[i][j], 0, 0, 0);
+        if (NP > 2)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx[f][i], fw[f][j], acc[i][j], 0, 0, 0);
       }
   };
 
@@ -512,11 +530,7 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm_dl(GemmArgs a) {
   int slot = 0;
   if (nk > 0) {
     // stage 0 has landed once at most min(NS, nk) - 1 younger stages are in flight
-    const int younger = min(NS, nk) - 1;
-    if (younger <= 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    else if (younger == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));
-    else if (younger == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));
+    wait_stages<NI, NS - 1, false>(min(NS, nk) - 1);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     rdfrag(0, smem, 0);
@@ -541,10 +555,7 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm_dl(GemmArgs a) {
       // stages t + 2 .. min(t + NS - 1, nk - 1) may stay in flight (after the last stage
       // nothing is in flight; its barrier and reads are harmless: the reads fetch a slot's
       // stale data and are never used)
-      const int younger = min(NS - 2, nk - 2 - t);
-      if (younger <= 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & ~(15 << 8));
-      else if (younger == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI) & ~(15 << 8));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI) & ~(15 << 8));
+      wait_stages<NI, NS - 2, true>(min(NS - 2, nk - 2 - t));
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
@@ -553,7 +564,8 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm_dl(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         asm volatile("" : "+v"(fh[(KS - 1) & 1][i]));
-        if (SPLIT) asm volatile("" : "+v"(fl[(KS - 1) & 1][i]));
+        if (NP > 1) asm volatile("" : "+v"(fl[(KS - 1) & 1][i]));
+        if (NP > 2) asm volatile("" : "+v"(fx[(KS - 1) & 1][i]));
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(fw[(KS - 1) & 1][j]));
@@ -571,9 +583,9 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm_dl(GemmArgs a) {
   gemm_epilogue<TM, TN, EPI>(a, acc, biasv, m0, n0, wm0, wn0, lane);
 }
 
-template <int BM, int BN, int BK, int NS, bool SPLIT>
+template <int BM, int BN, int BK, int NS, int NP>
 constexpr size_t gemm_dl_lds_bytes() {
-  return (size_t)NS * ((SPLIT ? 2 : 1) * BM + BN) * BK * 2;
+  return (size_t)NS * (NP * BM + BN) * BK * 2;
 }
 
 // Tile configurations: block BM x BN, WM x WN waves, register prefetch depth PF, KG
@@ -582,7 +594,8 @@ enum GemmCfg { CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x128 = 3, CFG_256x256 = 4
                CFG_128x128_K2 = 6, CFG_128x256_W8 = 7,
                // direct-to-LDS main loop (k_gemm_dl), BK 64, two stages
                CFG_DL_256x256 = 8,        // one plane: 8 waves of 128 x 64
-               CFG_DL_S128x256 = 9 };     // two planes: 8 waves of 64 x 64
+               CFG_DL_S128x256 = 9,       // two planes: 8 waves of 64 x 64
+               CFG_DL_64x64 = 10 };       // 2 waves of 32 x 64, 8 (one plane) / 6 stages
 
 template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI, int KG = 1>
 void set_attr() {
@@ -608,18 +621,19 @@ void launch_cfg(const GemmArgs& a, int splits, hipStream_t st) {
                        dim3(WM * WN * KG * kWave), lds, st, a);
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NS, bool SPLIT, int EPI>
+template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int EPI>
 void set_attr_dl() {
-  (void)hipFuncSetAttribute((const void*)k_gemm_dl<BM, BN, WM, WN, BK, NS, SPLIT, EPI>,
+  static_assert(gemm_dl_lds_bytes<BM, BN, BK, NS, NP>() <= 160 * 1024, "LDS of one CU");
+  (void)hipFuncSetAttribute((const void*)k_gemm_dl<BM, BN, WM, WN, BK, NS, NP, EPI>,
                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)gemm_dl_lds_bytes<BM, BN, BK, NS, SPLIT>());
+                            (int)gemm_dl_lds_bytes<BM, BN, BK, NS, NP>());
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NS, bool SPLIT, int EPI>
+template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int EPI>
 void launch_dl(const GemmArgs& a, int splits, hipStream_t st) {
   const int blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  constexpr size_t lds = gemm_dl_lds_bytes<BM, BN, BK, NS, SPLIT>();
-  hipLaunchKernelGGL((k_gemm_dl<BM, BN, WM, WN, BK, NS, SPLIT, EPI>), dim3(blocks, splits),
+  constexpr size_t lds = gemm_dl_lds_bytes<BM, BN, BK, NS, NP>();
+  hipLaunchKernelGGL((k_gemm_dl<BM, BN, WM, WN, BK, NS, NP, EPI>), dim3(blocks, splits),
                      dim3(WM * WN * kWave), lds, st, a);
 }
 
@@ -636,10 +650,14 @@ int tiles_of(const GemmArgs& a, int bm, int bn) {
 // waves, four stages of weight loads in flight: at M = 128 they fill the GPU without the
 // split-K planes and reduce that 128 x 128 tiles need (0.5B prefill GEMMs 10-20 % faster).
 int pick_cfg(const GemmArgs& a) {
-  if (a.M <= 128) return CFG_64x64;
-  // K in whole 64-column stages: the large tile forms load straight from global memory
-  // into LDS (k_gemm_dl; 4-10 % faster than register staging on the 1B-shape GEMMs)
+  // K in whole 64-column stages: the tile forms load straight from global memory into
+  // LDS (k_gemm_dl; 4-10 % faster than register staging on the 1B-shape GEMMs), the
+  // 64 x 64 form with six or eight stages in flight (the weights of a few-row GEMM stream
+  // from HBM, and only the loads in flight hide that latency)
   const bool dl = a.K % BK == 0;
+  // (the LM head's thousands of 64 x 64 tiles run faster two blocks per CU, register
+  // staged)
+  if (a.M <= 128) return dl && tiles_of(a, 64, 64) < 512 ? CFG_DL_64x64 : CFG_64x64;
   // two-plane input: 128 x 256 tiles over 8 waves of 64 x 64 (two waves per SIMD; over 4
   // waves of 64 x 128 the accumulators and fragments held a wave to one per SIMD)
   if (a.a_lo)
@@ -664,7 +682,7 @@ void cfg_dims(int cfg, int& bm, int& bn) {
     case CFG_128x256: case CFG_128x256_W8: case CFG_DL_S128x256: bm = 128; bn = 256; break;
     case CFG_DL_256x256: bm = 256; bn = 256; break;
     case CFG_128x128: case CFG_128x128_K2: bm = 128; bn = 128; break;
-    case CFG_64x64: bm = 64; bn = 64; break;
+    case CFG_64x64: case CFG_DL_64x64: bm = 64; bn = 64; break;
     default: bm = 64; bn = 128; break;
   }
 }
@@ -683,20 +701,41 @@ void launch_split(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
       break;
     case CFG_64x64: launch_cfg<64, 64, 2, 1, 4, SPLIT, EPI>(a, splits, st); break;
     case CFG_DL_256x256:
-      if constexpr (!SPLIT) launch_dl<256, 256, 2, 4, 64, 2, false, EPI>(a, splits, st);
+      if constexpr (!SPLIT) launch_dl<256, 256, 2, 4, 64, 2, 1, EPI>(a, splits, st);
       else report_unlaunched("GEMM: one-plane tile form with two planes");
       break;
     case CFG_DL_S128x256:
-      if constexpr (SPLIT) launch_dl<128, 256, 2, 4, 64, 2, true, EPI>(a, splits, st);
+      if constexpr (SPLIT) launch_dl<128, 256, 2, 4, 64, 2, 2, EPI>(a, splits, st);
       else report_unlaunched("GEMM: two-plane tile form with one plane");
+      break;
+    case CFG_DL_64x64:
+      if constexpr (SPLIT) launch_dl<64, 64, 2, 1, 64, 6, 2, EPI>(a, splits, st);
+      else launch_dl<64, 64, 2, 1, 64, 8, 1, EPI>(a, splits, st);
       break;
     default: launch_cfg<64, 128, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
   }
 }
 
+// three activation planes (EXACT QKV input): the direct-to-LDS forms only, store epilogue
+template <int EPI>
+void launch_three(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
+  if constexpr (EPI == GEMM_STORE) {
+    if (cfg == CFG_DL_S128x256) {
+      launch_dl<128, 256, 2, 4, 64, 2, 3, EPI>(a, splits, st);
+      return;
+    }
+    if (cfg == CFG_DL_64x64) {
+      launch_dl<64, 64, 2, 1, 64, 4, 3, EPI>(a, splits, st);
+      return;
+    }
+  }
+  report_unlaunched("GEMM: three activation planes in this tile form or epilogue");
+}
+
 template <int EPI>
 void launch_epi(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
-  if (a.a_lo) launch_split<true, EPI>(a, cfg, splits, st);
+  if (a.a_x2) launch_three<EPI>(a, cfg, splits, st);
+  else if (a.a_lo) launch_split<true, EPI>(a, cfg, splits, st);
   else launch_split<false, EPI>(a, cfg, splits, st);
 }
 
@@ -711,8 +750,13 @@ void set_attrs_split() {
   set_attr<128, 128, 2, 2, 2, SPLIT, EPI>();
   set_attr<64, 128, 2, 2, 2, SPLIT, EPI>();
   set_attr<64, 64, 2, 1, 4, SPLIT, EPI>();
-  if constexpr (!SPLIT) set_attr_dl<256, 256, 2, 4, 64, 2, false, EPI>();
-  else set_attr_dl<128, 256, 2, 4, 64, 2, true, EPI>();
+  if constexpr (!SPLIT) {
+    set_attr_dl<256, 256, 2, 4, 64, 2, 1, EPI>();
+    set_attr_dl<64, 64, 2, 1, 64, 8, 1, EPI>();
+  } else {
+    set_attr_dl<128, 256, 2, 4, 64, 2, 2, EPI>();
+    set_attr_dl<64, 64, 2, 1, 64, 6, 2, EPI>();
+  }
 }
 
 template <int EPI>
@@ -819,7 +863,7 @@ int pick_splits(const GemmArgs& a, int cfg) {
   const int tiles = tiles_of(a, bm, bn);
   if (tiles >= 192) return 1;
   const bool big = bm == 256 && bn == 256;
-  const int target = (cfg == CFG_64x64 || big) ? 256 : 512;
+  const int target = (bm == 64 && bn == 64) || big ? 256 : 512;
   int s = (target + tiles - 1) / tiles;
   const int max_s = a.K / (big ? 1024 : 256);
   if (s > max_s) s = max_s;
@@ -883,7 +927,17 @@ void launch_reduce(const GemmArgs& a, int epi, int used, hipStream_t st) {
 
 }  // namespace
 
+bool gemm_three_planes(const GemmArgs& a) {
+  // a second weight plane (dequantised q8_0) adds its pass with the residual epilogue,
+  // which has no three-plane form: such weights keep the separate third-plane pass
+  if (!a.a_lo || !a.a_x2 || a.w_lo) return false;
+  const int cfg = pick_cfg(a);
+  return cfg == CFG_DL_S128x256 || cfg == CFG_DL_64x64;
+}
+
 void gemm_init() {
+  set_attr_dl<128, 256, 2, 4, 64, 2, 3, GEMM_STORE>();
+  set_attr_dl<64, 64, 2, 1, 64, 4, 3, GEMM_STORE>();
   set_attrs_epi<GEMM_STORE>();
   set_attrs_epi<GEMM_RESID>();
   set_attrs_epi<GEMM_SILU>();
