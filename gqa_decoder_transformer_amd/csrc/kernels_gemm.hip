@@ -384,11 +384,15 @@ __global__ void __launch_bounds__(WM * WN * KG * kWave) k_gemm(GemmArgs a) {
 // register staging, no LDS store instructions, and the loads of NS - 1 stages in flight
 // behind the MFMAs. One wave-wide load moves RPI whole rows of a BK-column stage. Rows are
 // unpadded (a wave-wide load is 1 KB of consecutive LDS), so the 16-byte chunks of a row
-// are stored XOR-swizzled: chunk c of stage row r sits in slot c ^ swz(r), which spreads
-// the 32 rows of one fragment read over all bank groups. One barrier per stage: a stage's
-// slot is refilled only after every wave has passed the barrier that follows its use.
+// are stored XOR-swizzled: chunk c of stage row r sits in slot c ^ swz(r). A 16-byte LDS
+// read is served in four passes of 16 lanes over 64 four-byte banks (256 bytes), and a
+// fragment read has 16 consecutive rows in a pass at one logical chunk: with 128-byte
+// rows, rows r and r + 1 differ in the bank half and swz(r) = (r / 2) mod 8 gives the
+// eight row pairs distinct slots (r mod 8 put rows r and r + 8 on the same banks: 4.0
+// conflict cycles per LDS instruction, measured). One barrier per stage: a stage's slot is
+// refilled only after every wave has passed the barrier that follows its use.
 template <int BK>
-EMBER_DEV int dl_swz(int r) { return BK == 64 ? (r & 7) : ((r >> 1) & 3); }
+EMBER_DEV int dl_swz(int r) { return BK == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 
 // s_waitcnt immediate: vector-memory count <= n, the other counters unconstrained
 constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
@@ -483,8 +487,8 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm_dl(GemmArgs a) {
                    ? a.bias[min(n0 + wn0 + j * 32 + fr, a.N - 1)] : 0.f;
 
   // fragment reads: A fragment i is stage row wm0 + 32 i + fr, W fragment j stage row
-  // NP BM + wn0 + 32 j + fr; k-step kk reads logical chunk 2 kk + lane / 32 (the swizzle
-  // of these rows depends on fr alone)
+  // NP BM + wn0 + 32 j + fr; k-step kk reads logical chunk 2 kk + lane / 32 (these rows
+  // start on multiples of 32, so their swizzle depends on fr alone)
   const int sw = dl_swz<BK>(fr);
   int cofs[BK / 16];
 #pragma unroll
