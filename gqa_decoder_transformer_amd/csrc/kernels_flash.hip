@@ -381,12 +381,14 @@ constexpr int kTK = 64;
 
 // EXACT keeps three K planes and two V planes per stage (k_kv_pack). At head_dim 64 two
 // such stages take 92 KB, one block per CU: the block has 8 waves (256 queries) so every
-// SIMD still runs two. At head_dim 128 two stages exceed the LDS, so that form runs one
-// stage (tile j + 1 waits in registers while tile j is consumed, then one more barrier
-// per tile) with 4 waves.
-template <int HD, bool SPLIT>
+// SIMD still runs two, except on grids too small to give every CU a block (short
+// prompts), which take 4 waves (an 8-wave block over 128 tokens ran half its waves on
+// no queries, 9.2 -> 12.6 us). At head_dim 128 two stages exceed the LDS, so that form
+// runs one stage (tile j + 1 waits in registers while tile j is consumed, then one more
+// barrier per tile) with 4 waves.
+template <int HD, bool SPLIT, int W = 4>
 struct TiledCfg {
-  static constexpr int NW = (SPLIT && HD == 64) ? 8 : 4;       // waves of 32 queries
+  static constexpr int NW = W;                                  // waves of 32 queries
   static constexpr int NT = NW * kWave, TQ = NW * 32;
   static constexpr int NPK = SPLIT ? 3 : 1, NPV = SPLIT ? 2 : 1;
   static constexpr int KS = HD + 8, VS = kTK + 8;
@@ -399,12 +401,12 @@ struct TiledCfg {
   static_assert(kTK * HD / 8 % NT == 0, "tile chunks per thread");
 };
 
-template <int HD, bool SPLIT>
-__global__ void __launch_bounds__((TiledCfg<HD, SPLIT>::NT)) k_flash_tiled(FlashArgs a,
-                                                                         const uint16_t* kp,
-                                                                         const uint16_t* vt, int LK,
-                                                                         int longest_first) {
-  using C = TiledCfg<HD, SPLIT>;
+template <int HD, bool SPLIT, int W>
+__global__ void __launch_bounds__((TiledCfg<HD, SPLIT, W>::NT)) k_flash_tiled(FlashArgs a,
+                                                                            const uint16_t* kp,
+                                                                            const uint16_t* vt, int LK,
+                                                                            int longest_first) {
+  using C = TiledCfg<HD, SPLIT, W>;
   constexpr int NPK = C::NPK, NPV = C::NPV, KS = C::KS, VS = C::VS, NT = C::NT, TQ = C::TQ;
   constexpr int NKS = HD / 16, NDB = HD / 32;
   constexpr int CK = kTK * HD / 8 / NT;                          // 16-byte chunks per thread
@@ -735,20 +737,21 @@ void launch_kv_pack(const KvPackArgs& a, hipStream_t st) {
 
 namespace {
 // blocks of each tiled-attention form that the device holds at once (CUs x blocks per
-// CU), per device: [device][HD 128][split]
+// CU), and its CU count, per device: [device][HD 128][split][8 waves]
 constexpr int kMaxDevices = 64;
-int g_tiled_resident[kMaxDevices][2][2];
+int g_tiled_resident[kMaxDevices][2][2][2];
+int g_cus[kMaxDevices];
 
-template <int HD, bool SPLIT>
+template <int HD, bool SPLIT, int W>
 void tiled_init(int dev, int cus) {
-  using TC = TiledCfg<HD, SPLIT>;
-  (void)hipFuncSetAttribute((const void*)k_flash_tiled<HD, SPLIT>,
+  using TC = TiledCfg<HD, SPLIT, W>;
+  (void)hipFuncSetAttribute((const void*)k_flash_tiled<HD, SPLIT, W>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)TC::LDS);
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_flash_tiled<HD, SPLIT>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_flash_tiled<HD, SPLIT, W>,
                                                    TC::NT, TC::LDS) != hipSuccess)
     per_cu = 0;
-  g_tiled_resident[dev][HD == 128][SPLIT] = per_cu * cus;
+  g_tiled_resident[dev][HD == 128][SPLIT][W == 8] = per_cu * cus;
 }
 }  // namespace
 
@@ -756,29 +759,35 @@ void flash_init() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
-  tiled_init<64, false>(dev, cus);
-  tiled_init<64, true>(dev, cus);
-  tiled_init<128, false>(dev, cus);
-  tiled_init<128, true>(dev, cus);
+  g_cus[dev] = cus;
+  tiled_init<64, false, 4>(dev, cus);
+  tiled_init<64, true, 4>(dev, cus);
+  tiled_init<64, true, 8>(dev, cus);
+  tiled_init<128, false, 4>(dev, cus);
+  tiled_init<128, true, 4>(dev, cus);
 }
 
 void launch_flash_tiled(const FlashArgs& a, const uint16_t* kp, const uint16_t* vt, int LK,
                         bool split, hipStream_t st) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-#define EMBER_TILED(HDV, SP)                                                           \
+#define EMBER_TILED(HDV, SP, WV)                                                       \
   {                                                                                    \
-    using TC = TiledCfg<HDV, SP>;                                                      \
+    using TC = TiledCfg<HDV, SP, WV>;                                                  \
     const dim3 grid((a.tokens_per_row + TC::TQ - 1) / TC::TQ, a.NH, a.rows);            \
     const long long blocks = (long long)grid.x * grid.y * grid.z;                      \
-    const int resident = g_tiled_resident[dev][HDV == 128][SP];                        \
+    const int resident = g_tiled_resident[dev][HDV == 128][SP][WV == 8];               \
     const int lf = resident > 0 && blocks > resident;                                  \
-    hipLaunchKernelGGL((k_flash_tiled<HDV, SP>), grid, dim3(TC::NT), TC::LDS, st, a, kp, vt, LK, lf); \
+    hipLaunchKernelGGL((k_flash_tiled<HDV, SP, WV>), grid, dim3(TC::NT), TC::LDS, st, a, kp, vt, LK, lf); \
   }
   if (a.HD == 64) {
-    if (split) EMBER_TILED(64, true) else EMBER_TILED(64, false)
+    // EXACT: 8-wave blocks unless that grid leaves CUs without a block
+    const long long b8 = (long long)((a.tokens_per_row + 255) / 256) * a.NH * a.rows;
+    if (!split) EMBER_TILED(64, false, 4)
+    else if (b8 >= g_cus[dev]) EMBER_TILED(64, true, 8)
+    else EMBER_TILED(64, true, 4)
   } else if (a.HD == 128) {
-    if (split) EMBER_TILED(128, true) else EMBER_TILED(128, false)
+    if (split) EMBER_TILED(128, true, 4) else EMBER_TILED(128, false, 4)
   } else {
     report_unlaunched("tiled attention: head_dim");
   }

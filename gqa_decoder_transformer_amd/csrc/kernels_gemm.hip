@@ -659,9 +659,9 @@ int pick_cfg(const GemmArgs& a) {
   // 64 x 64 form with six or eight stages in flight (the weights of a few-row GEMM stream
   // from HBM, and only the loads in flight hide that latency)
   const bool dl = a.K % BK == 0;
-  // (the LM head's thousands of 64 x 64 tiles run faster two blocks per CU, register
-  // staged)
-  if (a.M <= 128) return dl && tiles_of(a, 64, 64) < 512 ? CFG_DL_64x64 : CFG_64x64;
+  // when its blocks fit the CUs at one per CU (144 KB of LDS each; more tiles, as in the
+  // LM head or a 128-row gate/up, run faster register staged at two blocks per CU)
+  if (a.M <= 128) return dl && tiles_of(a, 64, 64) <= 256 ? CFG_DL_64x64 : CFG_64x64;
   // two-plane input: 128 x 256 tiles over 8 waves of 64 x 64 (two waves per SIMD; over 4
   // waves of 64 x 128 the accumulators and fragments held a wave to one per SIMD)
   if (a.a_lo)
