@@ -455,11 +455,18 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
       // planes hi + lo store the projections (+bias), the third plane adds into them
       // (v as well: with peaked attention the output is one value row, and two planes
       // leave it ~2^-17 sqrt(K) off, 1e-4 in the logits); the post-processing (prefill)
-      // or the decode attention then reads them
+      // or the decode attention then reads them. Where one pass takes all three planes,
+      // a prefill with head_dim 64 does the post-processing in that GEMM's epilogue
+      // (the f32 projections never reach memory)
+      GemmArgs g3 = g;
+      g3.a_x2 = pa_x2;
+      const bool three = gemm_three_planes(g3);
+      const bool fused = three && ps.attn == ATTN_FLASH && HD == 64;
       if (want(cx, EMBER_K_QKV)) {
-        GemmArgs g3 = g;
-        g3.a_x2 = pa_x2;
-        if (gemm_three_planes(g3)) {
+        if (fused) {
+          g3.post = qa;
+          launch_gemm(g3, GEMM_QKV, st);
+        } else if (three) {
           launch_gemm(g3, GEMM_STORE, st);              // all three planes in one pass
         } else {
           launch_gemm(g, GEMM_STORE, st);
@@ -467,7 +474,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
           launch_gemm(g3, GEMM_RESID, st);
         }
       }
-      if (want_aux(cx) && ps.attn == ATTN_FLASH) launch_qkv_post(qa, st);
+      if (want_aux(cx) && ps.attn == ATTN_FLASH && !fused) launch_qkv_post(qa, st);
     } else if (ps.attn == ATTN_FLASH) {
       g.post = qa;
       if (want(cx, EMBER_K_QKV)) launch_gemm(g, GEMM_QKV, st);

@@ -720,10 +720,11 @@ void launch_split(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
   }
 }
 
-// three activation planes (EXACT QKV input): the direct-to-LDS forms only, store epilogue
+// three activation planes (EXACT QKV input): the direct-to-LDS forms only, with the store
+// or the QKV post-processing epilogue
 template <int EPI>
 void launch_three(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
-  if constexpr (EPI == GEMM_STORE) {
+  if constexpr (EPI == GEMM_STORE || EPI == GEMM_QKV) {
     if (cfg == CFG_DL_S128x256) {
       launch_dl<128, 256, 2, 4, 64, 2, 3, EPI>(a, splits, st);
       return;
@@ -942,6 +943,8 @@ bool gemm_three_planes(const GemmArgs& a) {
 void gemm_init() {
   set_attr_dl<128, 256, 2, 4, 64, 2, 3, GEMM_STORE>();
   set_attr_dl<64, 64, 2, 1, 64, 4, 3, GEMM_STORE>();
+  set_attr_dl<128, 256, 2, 4, 64, 2, 3, GEMM_QKV>();
+  set_attr_dl<64, 64, 2, 1, 64, 4, 3, GEMM_QKV>();
   set_attrs_epi<GEMM_STORE>();
   set_attrs_epi<GEMM_RESID>();
   set_attrs_epi<GEMM_SILU>();
