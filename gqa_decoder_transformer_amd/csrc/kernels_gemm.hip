@@ -696,12 +696,14 @@ void launch_split(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
   switch (cfg) {
     case CFG_256x256:
       if constexpr (!SPLIT) launch_cfg<256, 256, 2, 4, 1, false, EPI>(a, splits, st);
+      else report_unlaunched("GEMM: one-plane tile form with two planes");
       break;
     case CFG_128x256: launch_cfg<128, 256, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
     case CFG_128x256_W8: launch_cfg<128, 256, 2, 4, 2, SPLIT, EPI>(a, splits, st); break;
     case CFG_128x128: launch_cfg<128, 128, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
     case CFG_128x128_K2:
       if constexpr (!SPLIT) launch_cfg<128, 128, 2, 2, 2, false, EPI, 2>(a, splits, st);
+      else report_unlaunched("GEMM: one-plane tile form with two planes");
       break;
     case CFG_64x64: launch_cfg<64, 64, 2, 1, 4, SPLIT, EPI>(a, splits, st); break;
     case CFG_DL_256x256:
