@@ -164,11 +164,11 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
       const int key = max(0, min(s0 + grp + NGRP * (batch * KI + i), s_hi - 1));
       const size_t off = base + (size_t)key * HD + sub * DPL;
       if (KV_BF16) {
-        kb[i] = *(const u32x4_t*)((const uint16_t*)a.k_cache + off);
-        vb[i] = *(const u32x4_t*)((const uint16_t*)a.v_cache + off);
+        kb[i] = ld_stream((const uint16_t*)a.k_cache + off);
+        vb[i] = ld_stream((const uint16_t*)a.v_cache + off);
       } else {
-        kb[i] = *(const u32x4_t*)((const float*)a.k_cache + off);
-        vb[i] = *(const u32x4_t*)((const float*)a.v_cache + off);
+        kb[i] = ld_stream((const float*)a.k_cache + off);
+        vb[i] = ld_stream((const float*)a.v_cache + off);
       }
     }
   };

@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_wave(GemvArgs a) {
 #pragma unroll
         for (int t = 0; t < U; ++t) {
           const int c = min(lane + kWave * t, nch - 1);   // clamped chunk: x is 0 there
-          w[t][u * RU + r] = *(const u32x4_t*)(row + (size_t)c * E);
+          w[t][u * RU + r] = ld_stream(row + (size_t)c * E);
           sc[t][u * RU + r] = chunk_scale<WT>(a, wr, c);
         }
       }
@@ -310,7 +310,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_block(GemvArgs a) {
 #pragma unroll
         for (int t = 0; t < U; ++t) {
           const int c = min((int)threadIdx.x + kThreads * t, nch - 1);
-          w[t][u * RU + r] = *(const u32x4_t*)(row + (size_t)c * E);
+          w[t][u * RU + r] = ld_stream(row + (size_t)c * E);
           sc[t][u * RU + r] = chunk_scale<WT>(a, wr, c);
         }
       }
@@ -478,7 +478,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_long(GemvArgs a) {
       for (int r = 0; r < RU; ++r) {
         const int wr = weight_row<EPI>(n, r);
         const auto* row = (const typename WTraits<WT>::Elem*)a.W + (size_t)wr * K;
-        acc[r] = chunk_dot<WT>(*(const u32x4_t*)(row + (size_t)c * E), xv, sx,
+        acc[r] = chunk_dot<WT>(ld_stream(row + (size_t)c * E), xv, sx,
                                chunk_scale<WT>(a, wr, c), acc[r]);
       }
     }

@@ -2,8 +2,9 @@
 // the kernels' roofline fractions are also reported against.
 //   k_peak_copy: a plain streaming copy, 16-byte loads and stores, grid-stride (bytes
 //                read plus bytes written per second);
-//   k_peak_read: a streaming read, 16-byte loads, sixteen in flight per thread (the
-//                reference for kernels that mostly read: weights and KV cache);
+//   k_peak_read: a streaming read, 16-byte non-temporal loads, sixteen in flight per
+//                thread (the reference for kernels that mostly read: weights and KV
+//                cache);
 //   k_peak_mfma: independent chains of v_mfma_f32_32x32x16_bf16 on register operands, no
 //                memory traffic (the matrix-core reference for bf16 work).
 #include "common.h"
@@ -34,7 +35,7 @@ __global__ void __launch_bounds__(256) k_peak_read(const u32x4_t* __restrict__ s
     const u32x4_t* p = src + sg * 256 * U + threadIdx.x;
     u32x4_t v[U];
 #pragma unroll
-    for (int j = 0; j < U; ++j) v[j] = p[256 * j];
+    for (int j = 0; j < U; ++j) v[j] = ld_stream(p + 256 * j);
 #pragma unroll
     for (int j = 0; j < U; ++j) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
   }

@@ -356,7 +356,7 @@ ember_status ember_time_kernel(ember_model* model, ember_cache* cache, int32_t k
  * kernels' roofline fractions are also reported against, beside the published ones.
  *   EMBER_PEAK_COPY: a plain streaming copy from the first half of d_buf to the second
  *     (16-byte loads and stores); *out = GB/s, counting bytes read plus bytes written.
- *   EMBER_PEAK_READ: a streaming read of d_buf past its first 2 MiB (16-byte loads,
+ *   EMBER_PEAK_READ: a streaming read of d_buf past its first 2 MiB (16-byte non-temporal loads,
  *     sixteen in flight per thread), which receive one word per thread; *out = GB/s read.
  *   EMBER_PEAK_MFMA: chains of v_mfma_f32_32x32x16_bf16 on register operands with no
  *     memory traffic, 2048 blocks of 256 threads; *out = TFLOP/s (dense bf16); d_buf (at
