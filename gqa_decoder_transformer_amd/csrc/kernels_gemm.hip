@@ -467,9 +467,13 @@ __global__ void __launch_bounds__(WM * WN * kWave) k_gemm_dl(GemmArgs a) {
     for (int i = 0; i < NI; ++i) {
       const uint16_t* base = i < IA ? a.a_hi : (NP > 1 && i < 2 * IA) ? a.a_lo
                                              : (NP > 2 && i < 3 * IA) ? a.a_x2 : a.w;
-      __builtin_amdgcn_global_load_lds((const void*)(base + off[i] + k0),
-                                       (__attribute__((address_space(3))) void*)(st + (i * NW + wave) * RPI * BK),
-                                       16, 0, 0);
+      auto* dst = (__attribute__((address_space(3))) void*)(st + (i * NW + wave) * RPI * BK);
+      // the 64 x 64 form serves GEMMs of at most 128 rows, whose weights are read once:
+      // their loads carry the non-temporal hint
+      if (BM == 64 && i >= NP * IA)
+        __builtin_amdgcn_global_load_lds((const void*)(base + off[i] + k0), dst, 16, 0, 2);
+      else
+        __builtin_amdgcn_global_load_lds((const void*)(base + off[i] + k0), dst, 16, 0, 0);
     }
   };
 
