@@ -20,6 +20,7 @@ constexpr int kWave = 64;
 // cache in decode attention), marked non-temporal: streaming reads with the hint measured
 // 6.6-6.8 TB/s against 5.8-6.2 without it
 EMBER_DEV u32x4_t ld_stream(const void* p) { return __builtin_nontemporal_load((const u32x4_t*)p); }
+EMBER_DEV float4 ld_stream_f4(const void* p) { return __builtin_bit_cast(float4, ld_stream(p)); }
 EMBER_DEV float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 EMBER_DEV float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
 EMBER_DEV float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }

@@ -293,8 +293,8 @@ __global__ void __launch_bounds__(256) k_kv_pack(KvPackArgs a) {
     if (pos < a.key_end) {
       const size_t off = cbase + (size_t)pos * HD + d8;
       if (a.kv_bf16) {
-        const u32x4_t kr = *(const u32x4_t*)((const uint16_t*)a.k_cache + off);
-        const u32x4_t vr = *(const u32x4_t*)((const uint16_t*)a.v_cache + off);
+        const u32x4_t kr = ld_stream((const uint16_t*)a.k_cache + off);   // read once
+        const u32x4_t vr = ld_stream((const uint16_t*)a.v_cache + off);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           kv[2 * j] = bf16_lo(kr[j]); kv[2 * j + 1] = bf16_hi(kr[j]);
@@ -303,8 +303,8 @@ __global__ void __launch_bounds__(256) k_kv_pack(KvPackArgs a) {
       } else {
         const float* kf = (const float*)a.k_cache + off;
         const float* vf = (const float*)a.v_cache + off;
-        const float4 k0v = *(const float4*)kf, k1v = *(const float4*)(kf + 4);
-        const float4 v0v = *(const float4*)vf, v1v = *(const float4*)(vf + 4);
+        const float4 k0v = ld_stream_f4(kf), k1v = ld_stream_f4(kf + 4);   // read once
+        const float4 v0v = ld_stream_f4(vf), v1v = ld_stream_f4(vf + 4);
         kv[0] = k0v.x; kv[1] = k0v.y; kv[2] = k0v.z; kv[3] = k0v.w;
         kv[4] = k1v.x; kv[5] = k1v.y; kv[6] = k1v.z; kv[7] = k1v.w;
         vv[0] = v0v.x; vv[1] = v0v.y; vv[2] = v0v.z; vv[3] = v0v.w;

@@ -826,9 +826,9 @@ __global__ void __launch_bounds__(256) k_splitk_reduce4(GemmArgs a, int splits) 
       // four outputs of one block of 32 read four consecutive gate and up columns
       const float* pg = a.partial + (size_t)row * a.N + gu_row(col, 0);
       const float* pu = a.partial + (size_t)row * a.N + gu_row(col, 1);
-      float4 g = *(const float4*)pg, u = *(const float4*)pu;
+      float4 g = ld_stream_f4(pg), u = ld_stream_f4(pu);   // partial planes: read once
       for (int s = 1; s < splits; ++s) {
-        const float4 gs = *(const float4*)(pg + s * plane), us = *(const float4*)(pu + s * plane);
+        const float4 gs = ld_stream_f4(pg + s * plane), us = ld_stream_f4(pu + s * plane);
         g.x += gs.x; g.y += gs.y; g.z += gs.z; g.w += gs.w;
         u.x += us.x; u.y += us.y; u.z += us.z; u.w += us.w;
       }
@@ -844,9 +844,9 @@ __global__ void __launch_bounds__(256) k_splitk_reduce4(GemmArgs a, int splits) 
       }
     } else {
       const float* pp = a.partial + (size_t)row * a.N + col;
-      float4 acc = *(const float4*)pp;
+      float4 acc = ld_stream_f4(pp);                     // partial planes: read once
       for (int s = 1; s < splits; ++s) {
-        const float4 ps = *(const float4*)(pp + s * plane);
+        const float4 ps = ld_stream_f4(pp + s * plane);
         acc.x += ps.x; acc.y += ps.y; acc.z += ps.z; acc.w += ps.w;
       }
       float4* cp = (float4*)(a.c + (size_t)row * a.ldc + col);

@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(256) k_rmsnorm_v(const float* x, const float* 
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int i = threadIdx.x + 256 * j;
-    v[j] = i < H4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[j] = i < H4 ? ld_stream_f4(xr + i) : make_float4(0.f, 0.f, 0.f, 0.f);   // read once
     ss += v[j].x * v[j].x;
     ss += v[j].y * v[j].y;
     ss += v[j].z * v[j].z;
