@@ -603,7 +603,8 @@ enum GemmCfg { CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x128 = 3, CFG_256x256 = 4
                // direct-to-LDS main loop (k_gemm_dl), BK 64, two stages
                CFG_DL_256x256 = 8,        // one plane: 8 waves of 128 x 64
                CFG_DL_S128x256 = 9,       // two planes: 8 waves of 64 x 64
-               CFG_DL_64x64 = 10 };       // 2 waves of 32 x 64, 8 (one plane) / 6 stages
+               CFG_DL_64x64 = 10,         // 2 waves of 32 x 64, three stages (two: three planes)
+               CFG_DL_64x256 = 11 };      // two planes, M <= 64: 4 waves of 64 x 64, three stages
 
 template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI, int KG = 1>
 void set_attr() {
@@ -655,16 +656,21 @@ int tiles_of(const GemmArgs& a, int bm, int bn) {
 // least one tile per CU (measured faster there at every K), else 128 x 128; the
 // two-plane (EXACT) input (a third LDS plane) takes 128 x 256 when that leaves ~0.7
 // tiles per CU. M <= 128 (batched decode, short prompts) takes 64 x 64 tiles over 2
-// waves, four stages of weight loads in flight: at M = 128 they fill the GPU without the
-// split-K planes and reduce that 128 x 128 tiles need (0.5B prefill GEMMs 10-20 % faster).
+// waves: at M = 128 they fill the GPU without the split-K planes and reduce that
+// 128 x 128 tiles need (0.5B prefill GEMMs 10-20 % faster).
 int pick_cfg(const GemmArgs& a) {
   // K in whole 64-column stages: the tile forms load straight from global memory into
-  // LDS (k_gemm_dl; 4-10 % faster than register staging on the 1B-shape GEMMs), the
-  // 64 x 64 form with six or eight stages in flight (the weights of a few-row GEMM stream
-  // from HBM, and only the loads in flight hide that latency)
+  // LDS (k_gemm_dl; 4-10 % faster than register staging on the 1B-shape GEMMs)
   const bool dl = a.K % BK == 0;
-  // when its blocks fit the CUs at one per CU (144 KB of LDS each; more tiles, as in the
-  // LM head or a 128-row gate/up, run faster register staged at two blocks per CU)
+  // a wide two-plane GEMM of at most 64 rows (the EXACT LM head of a decode batch): a
+  // 64 x 64 tile reads its two activation planes from L2 at twice its weight bytes, a
+  // 64 x 256 tile at half (64-row LM head 155 -> 138 us; with one plane, or with 64 x 128
+  // tiles on the 16384-column gate/up, no faster)
+  if (a.M <= 64 && dl && a.a_lo && !a.a_x2 && tiles_of(a, 64, 64) >= 1024) return CFG_DL_64x256;
+  // the 64 x 64 direct-to-LDS form when its blocks fit the CUs (more tiles, as in the
+  // one-plane LM head or a 128-row gate/up, run faster register staged); three stages
+  // (72 KB of LDS, 48 KB with one plane) run as fast as six or eight and leave room for
+  // a second block per CU (64-row EXACT decode layer 91.2 -> 87.8 us, FAST 80.0 -> 76.8)
   if (a.M <= 128) return dl && tiles_of(a, 64, 64) <= 256 ? CFG_DL_64x64 : CFG_64x64;
   // two-plane input: 128 x 256 tiles over 8 waves of 64 x 64 (two waves per SIMD; over 4
   // waves of 64 x 128 the accumulators and fragments held a wave to one per SIMD)
@@ -691,6 +697,7 @@ void cfg_dims(int cfg, int& bm, int& bn) {
     case CFG_DL_256x256: bm = 256; bn = 256; break;
     case CFG_128x128: case CFG_128x128_K2: bm = 128; bn = 128; break;
     case CFG_64x64: case CFG_DL_64x64: bm = 64; bn = 64; break;
+    case CFG_DL_64x256: bm = 64; bn = 256; break;
     default: bm = 64; bn = 128; break;
   }
 }
@@ -719,8 +726,12 @@ void launch_split(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
       else report_unlaunched("GEMM: two-plane tile form with one plane");
       break;
     case CFG_DL_64x64:
-      if constexpr (SPLIT) launch_dl<64, 64, 2, 1, 64, 6, 2, EPI>(a, splits, st);
-      else launch_dl<64, 64, 2, 1, 64, 8, 1, EPI>(a, splits, st);
+      if constexpr (SPLIT) launch_dl<64, 64, 2, 1, 64, 3, 2, EPI>(a, splits, st);
+      else launch_dl<64, 64, 2, 1, 64, 3, 1, EPI>(a, splits, st);
+      break;
+    case CFG_DL_64x256:
+      if constexpr (SPLIT) launch_dl<64, 256, 1, 4, 64, 3, 2, EPI>(a, splits, st);
+      else report_unlaunched("GEMM: two-plane tile form with one plane");
       break;
     default: launch_cfg<64, 128, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
   }
@@ -736,7 +747,7 @@ void launch_three(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
       return;
     }
     if (cfg == CFG_DL_64x64) {
-      launch_dl<64, 64, 2, 1, 64, 4, 3, EPI>(a, splits, st);
+      launch_dl<64, 64, 2, 1, 64, 2, 3, EPI>(a, splits, st);
       return;
     }
   }
@@ -763,10 +774,11 @@ void set_attrs_split() {
   set_attr<64, 64, 2, 1, 4, SPLIT, EPI>();
   if constexpr (!SPLIT) {
     set_attr_dl<256, 256, 2, 4, 64, 2, 1, EPI>();
-    set_attr_dl<64, 64, 2, 1, 64, 8, 1, EPI>();
+    set_attr_dl<64, 64, 2, 1, 64, 3, 1, EPI>();
   } else {
     set_attr_dl<128, 256, 2, 4, 64, 2, 2, EPI>();
-    set_attr_dl<64, 64, 2, 1, 64, 6, 2, EPI>();
+    set_attr_dl<64, 64, 2, 1, 64, 3, 2, EPI>();
+    set_attr_dl<64, 256, 1, 4, 64, 3, 2, EPI>();
   }
 }
 
@@ -864,7 +876,7 @@ __global__ void __launch_bounds__(256) k_splitk_reduce4(GemmArgs a, int splits) 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // Split K when the tiles cannot fill the GPU: slices of >= 256 columns, about 512 blocks
-// (256 for the 64 x 64 tiles of small M, which stream four stages ahead, and for 256 x 256
+// (256 for the 64 x 64 tiles of small M, whose blocks each stream their weights, and for 256 x 256
 // tiles, whose slices keep >= 1024 columns: every split adds an f32 partial plane to write
 // and reduce).
 int pick_splits(const GemmArgs& a, int cfg) {
@@ -948,9 +960,9 @@ bool gemm_three_planes(const GemmArgs& a) {
 
 void gemm_init() {
   set_attr_dl<128, 256, 2, 4, 64, 2, 3, GEMM_STORE>();
-  set_attr_dl<64, 64, 2, 1, 64, 4, 3, GEMM_STORE>();
+  set_attr_dl<64, 64, 2, 1, 64, 2, 3, GEMM_STORE>();
   set_attr_dl<128, 256, 2, 4, 64, 2, 3, GEMM_QKV>();
-  set_attr_dl<64, 64, 2, 1, 64, 4, 3, GEMM_QKV>();
+  set_attr_dl<64, 64, 2, 1, 64, 2, 3, GEMM_QKV>();
   set_attrs_epi<GEMM_STORE>();
   set_attrs_epi<GEMM_RESID>();
   set_attrs_epi<GEMM_SILU>();
