@@ -390,7 +390,11 @@ struct Pass {
 };
 
 // One decoder block over the pass's tokens: x += attn(norm(x)); x += mlp(norm(x)).
-void run_layer(const Ctx& cx, int li, const Pass& ps) {
+// One layer of a pass. `pending` > 0: the previous layer's down projection left that many
+// split-K partial planes for this layer's first norm to add into x. With `defer_down` (the
+// caller runs the next layer right after this one, with no reader of x in between) this
+// layer's down projection may do the same; returns its plane count (0: x is complete).
+int run_layer(const Ctx& cx, int li, const Pass& ps, int pending = 0, bool defer_down = false) {
   ember_model* md = cx.m;
   const ember_config& c = md->cfg;
   const Plan& p = md->plan;
@@ -435,6 +439,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   qa.kv_bf16 = c.kv_dtype == EMBER_BF16; qa.max_seq = c.max_seq;
 
   // ---- attention block
+  int qkv_deferred = 0;
   if (ps.path == PATH_GEMV) {
     GemvArgs g{};
     gemv_weights(md, g, L.wqkv, L.wqkv_s);
@@ -443,8 +448,12 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     if (want(cx, EMBER_K_QKV)) launch_gemv(g, GEMV_STORE, st);
   } else if (ps.path == PATH_MFMA) {
     uint16_t* pa_x2 = exact ? md->at<uint16_t>(p.pa_x2) : nullptr;
+    // one-token decode: a split-K QKV GEMM leaves its partial planes to the attention
+    // kernel, which sums the few projections it reads (no reduce launch)
+    const bool defer_qkv = want_aux(cx) && ps.attn == ATTN_DECODE;
     if (want_aux(cx))
-      launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st, pa_x2);
+      launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st, pa_x2,
+                     md->splitk(), pending);
     GemmArgs g{};
     g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
     g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka;
@@ -467,7 +476,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
           g3.post = qa;
           launch_gemm(g3, GEMM_QKV, st);
         } else if (three) {
-          launch_gemm(g3, GEMM_STORE, st);              // all three planes in one pass
+          qkv_deferred = launch_gemm(g3, GEMM_STORE, st, defer_qkv);   // all three planes, one pass
         } else {
           launch_gemm(g, GEMM_STORE, st);
           g3.a_hi = pa_x2; g3.a_lo = nullptr; g3.a_x2 = nullptr; g3.bias = nullptr;
@@ -479,7 +488,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
       g.post = qa;
       if (want(cx, EMBER_K_QKV)) launch_gemm(g, GEMM_QKV, st);
     } else if (want(cx, EMBER_K_QKV)) {
-      launch_gemm(g, GEMM_STORE, st);
+      qkv_deferred = launch_gemm(g, GEMM_STORE, st, defer_qkv);
     }
   } else {
     if (want_aux(cx)) launch_rmsnorm(x, ln1, c.rms_eps, ps.M, H, 1, 0, xb, nullptr, nullptr, 0, st);
@@ -531,6 +540,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     da.B = ps.M; da.NH = NH; da.NKV = NKV; da.HD = HD; da.max_seq = c.max_seq;
     da.d_pos = ps.d_pos; da.nsplit = dp.nsplit; da.chunk_min = dp.chunk_min; da.scale = scale;
     da.part = part; da.heads_per_block = dp.heads_per_block;
+    da.qkv_part = md->splitk(); da.qkv_splits = qkv_deferred; da.qkv_bias = bqkv;
     da.out_f32 = planes_out ? nullptr : att;
     da.out_hi = planes_out ? pa_hi : nullptr;
     da.out_lo = planes_out ? pa_lo : nullptr;
@@ -540,6 +550,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
                           da.out_f32, da.out_hi, da.out_lo, st);
   }
 
+  int o_deferred = 0;
   if (ps.path == PATH_GEMV) {
     GemvArgs g{};
     gemv_weights(md, g, L.wo, L.wo_s);
@@ -557,7 +568,9 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka;
     g.w = (const uint16_t*)gemm_weights(cx, L.wo, L.wo_s, H, NH * HD, &g.w_lo);
     g.M = ps.M; g.N = H; g.K = NH * HD; g.c = x; g.ldc = H;
-    if (want(cx, EMBER_K_O)) launch_gemm(g, GEMM_RESID, st);
+    // a split-K residual add is left to the norm that follows (it reads x anyway)
+    if (want(cx, EMBER_K_O))
+      o_deferred = launch_gemm(g, GEMM_RESID, st, want_aux(cx) && rmsnorm_adds_partials(H, p.ka));
   } else {
     GemmF32Args g{};
     g.a = att; g.lda = NH * HD; g.w = (const float*)gemm_weights(cx, L.wo, L.wo_s, H, NH * HD);
@@ -567,6 +580,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
   }
 
   // ---- MLP block
+  int down_deferred = 0;
   if (ps.path == PATH_GEMV) {
     GemvArgs g{};
     gemv_weights(md, g, L.wgu, L.wgu_s);
@@ -578,7 +592,9 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     d.N = H; d.K = FF; d.M = ps.M; d.x = act; d.y = x; d.ldy = H;
     if (want(cx, EMBER_K_DOWN)) launch_gemv(d, GEMV_RESID, st);
   } else if (ps.path == PATH_MFMA) {
-    if (want_aux(cx)) launch_rmsnorm(x, ln2, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st);
+    if (want_aux(cx))
+      launch_rmsnorm(x, ln2, c.rms_eps, ps.M, H, 1, 0, nullptr, pa_hi, pa_lo, p.ka, st, nullptr,
+                     md->splitk(), o_deferred);
     GemmArgs g{};
     g.partial = md->splitk(); g.partial_elems = p.splitk_elems;
     g.a_hi = pa_hi; g.a_lo = pa_lo; g.lda = p.ka;
@@ -590,7 +606,9 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     d.M = ps.M; d.N = H; d.K = FF; d.c = x; d.ldc = H;
     if (want(cx, EMBER_K_GATE_UP)) launch_gemm(g, GEMM_SILU, st);
     d.w = (const uint16_t*)gemm_weights(cx, L.wd, L.wd_s, H, FF, &d.w_lo);   // after the gate/up GEMM
-    if (want(cx, EMBER_K_DOWN)) launch_gemm(d, GEMM_RESID, st);
+    if (want(cx, EMBER_K_DOWN))
+      down_deferred = launch_gemm(d, GEMM_RESID, st,
+                                  defer_down && want_aux(cx) && rmsnorm_adds_partials(H, p.ka));
   } else {
     if (want_aux(cx)) launch_rmsnorm(x, ln2, c.rms_eps, ps.M, H, 1, 0, xb, nullptr, nullptr, 0, st);
     GemmF32Args g{};
@@ -604,6 +622,7 @@ void run_layer(const Ctx& cx, int li, const Pass& ps) {
     d.c = x; d.ldc = H;
     if (want(cx, EMBER_K_DOWN)) launch_gemm_f32w(d, GEMM_RESID, st);
   }
+  return down_deferred;
 }
 
 // Tied LM head over R rows of x (row r = x[r * row_step + row_off]): final RMSNorm, then
@@ -700,8 +719,11 @@ void decode_body(const Ctx& cx, int B, int32_t* next, int only_layer = -1) {
   ps.M = B; ps.rows = B; ps.tpr = 1; ps.b0 = 0; ps.start = 0; ps.d_pos = md->at<int>(p.row_pos);
   ps.path = B == 1 ? PATH_GEMV : (md->mfma ? PATH_MFMA : PATH_F32W);
   ps.attn = ATTN_DECODE;
+  // layer l's down projection may leave its split-K planes to layer l + 1's first norm
+  int pending = 0;
   for (int l = 0; l < c.layers; ++l)
-    if (only_layer < 0 || l == only_layer) run_layer(cx, l, ps);
+    if (only_layer < 0 || l == only_layer)
+      pending = run_layer(cx, l, ps, pending, only_layer < 0 && l + 1 < c.layers);
   if ((want(cx, EMBER_K_LM_HEAD) || cx.only == EMBER_K_SAMPLE) && (cx.only >= 0 || only_layer < 0))
     run_lm_head(cx, B, 1, 0, md->at<float>(p.logits), c.vocab, next);
 }
@@ -987,9 +1009,11 @@ ember_status prefill_impl(ember_model* md, ember_cache* cache, const int32_t* h_
       ps.path = M == 1 ? PATH_GEMV : (md->mfma ? PATH_MFMA : PATH_F32W);
       ps.attn = ATTN_FLASH;
       const bool last_chunk = t0 + tpr == T;
+      const bool taps = d_acts && last_chunk;      // x is read after every layer
+      int pending = 0;
       for (int l = 0; l < c.layers; ++l) {
-        run_layer(cx, l, ps);
-        if (d_acts && last_chunk)
+        pending = run_layer(cx, l, ps, pending, !taps && l + 1 < c.layers);
+        if (taps)
           launch_copy_rows(md->at<float>(p.x), rows, tpr, tpr - 1, c.hidden,
                            d_acts + ((size_t)bi * c.layers + l) * c.hidden,
                            (long long)c.layers * c.hidden, st);

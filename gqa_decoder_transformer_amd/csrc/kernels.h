@@ -49,10 +49,15 @@ void launch_q8_dequant(const uint8_t* q, const uint16_t* s, int N, int K, void* 
 // Row-wise RMSNorm of rows src_row(r) = r * row_step + row_off, r < R, of x [*, H]:
 // y = x / sqrt(mean(x^2) + eps) * w. Writes any of: out_f32 [R, H], planes hi/lo
 // [R, ld_plane] bf16 (lo may be null: single plane); with x2 (needs lo) the three planes
-// y = hi + lo + x2 of split3_bf16 instead of the pair.
+// y = hi + lo + x2 of split3_bf16 instead of the pair. With nsplit > 0 (row_step 1,
+// row_off 0, and rmsnorm_adds_partials(H, ld_plane)) it first completes a deferred
+// split-K residual GEMM: x += the sum of the partial planes part [nsplit][R][H], in plane
+// order, written back to x.
 void launch_rmsnorm(const float* x, const float* w, float eps, int R, int H, int row_step,
                     int row_off, float* out_f32, uint16_t* hi, uint16_t* lo, int ld_plane,
-                    hipStream_t st, uint16_t* x2 = nullptr);
+                    hipStream_t st, uint16_t* x2 = nullptr, const float* part = nullptr,
+                    int nsplit = 0);
+bool rmsnorm_adds_partials(int H, int ld_plane);
 
 struct QkvPostArgs {
   const float* qkv;        // [M, (NH + 2 NKV) HD] raw projections (bias included)
@@ -267,7 +272,12 @@ struct GemmArgs {
   int k_chunk;             // set by launch_gemm
   QkvPostArgs post;        // GEMM_QKV only (post.qkv = c)
 };
-void launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
+// Returns 0 when the output is complete. With `defer`, a store or residual GEMM that
+// splits K into at most kMaxDeferredPlanes slices leaves its f32 partial planes
+// ([n][M][N] at a.partial) for the caller's next kernel to sum (planes 0..n-1 in order,
+// then + bias or into the residual) and returns n.
+constexpr int kMaxDeferredPlanes = 8;
+int launch_gemm(const GemmArgs& a, int epi, hipStream_t st, bool defer = false);
 // true when launch_gemm takes a_x2 as a third activation plane in the same pass (tile forms
 // that load straight into LDS); otherwise the caller adds that plane's product separately
 bool gemm_three_planes(const GemmArgs& a);
@@ -366,6 +376,12 @@ struct DecodeAttnArgs {
   int nsplit, chunk_min;   // nsplit == 1 or chunk_min >= ceil(max_seq / nsplit)
   float scale;
   float* part;             // [B][NH][nsplit][HD + 2] split partials (m, l, acc)
+  // qkv_splits > 0: qkv is not written; the current token's projections are the sum of
+  // the deferred split-K planes qkv_part [qkv_splits][B][(NH + 2 NKV) HD] (in plane
+  // order) plus qkv_bias (may be null)
+  const float* qkv_part;
+  int qkv_splits;
+  const float* qkv_bias;
   float* out_f32;          // nsplit == 1: the normalised output [B, NH*HD] (f32 and/or
   uint16_t* out_hi;        // bf16 planes) is written directly and no combine follows
   uint16_t* out_lo;

@@ -177,8 +177,23 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
   // current token: raw q (G heads), this step's RoPE row and, in the split that holds
   // the position, raw k/v of head kvh
   const int qkv_n = (a.NH + 2 * a.NKV) * HD;
-  const float* row = a.qkv + (size_t)b * qkv_n;
-  for (int e = threadIdx.x; e < G * HD; e += blockDim.x) qs[e] = row[h0 * HD + e];
+  // projection column c of this row: stored by the QKV GEMM, or the sum of its deferred
+  // split-K planes in plane order plus the bias (what the split-K reduce would have stored)
+  // (every plane's load issued before the first add)
+  auto proj = [&](int c) -> float {
+    if (a.qkv_splits <= 0) return a.qkv[(size_t)b * qkv_n + c];
+    const float* pp = a.qkv_part + (size_t)b * qkv_n + c;
+    const size_t plane = (size_t)a.B * qkv_n;
+    float pv[kMaxDeferredPlanes];
+#pragma unroll
+    for (int s = 0; s < kMaxDeferredPlanes; ++s) pv[s] = pp[min(s, a.qkv_splits - 1) * plane];
+    float acc = pv[0];
+#pragma unroll
+    for (int s = 1; s < kMaxDeferredPlanes; ++s)
+      if (s < a.qkv_splits) acc += pv[s];
+    return acc + (a.qkv_bias ? a.qkv_bias[c] : 0.f);
+  };
+  for (int e = threadIdx.x; e < G * HD; e += blockDim.x) qs[e] = proj(h0 * HD + e);
   for (int e = threadIdx.x; e < HALF; e += blockDim.x) {
     cs[e] = a.rope_cur[(size_t)b * HD + e];
     sn[e] = a.rope_cur[(size_t)b * HD + HALF + e];
@@ -191,8 +206,8 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
   const int nb = batches(s1);
   if (has_cur)
     for (int e = threadIdx.x; e < HD; e += blockDim.x) {
-      kc[e] = row[(a.NH + kvh) * HD + e];
-      vc[e] = row[(a.NH + a.NKV + kvh) * HD + e];
+      kc[e] = proj((a.NH + kvh) * HD + e);
+      vc[e] = proj((a.NH + a.NKV + kvh) * HD + e);
     }
   __syncthreads();
   // RoPE (and q/k norm) in place: pair e (thread e + 256 j) is pair e % HALF of head

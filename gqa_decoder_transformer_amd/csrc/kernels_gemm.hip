@@ -969,8 +969,8 @@ void gemm_init() {
   set_attrs_epi<GEMM_QKV>();
 }
 
-void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
-  if (a0.M <= 0 || a0.N <= 0) return;
+int launch_gemm(const GemmArgs& a0, int epi, hipStream_t st, bool defer) {
+  if (a0.M <= 0 || a0.N <= 0) return 0;
   if (epi == GEMM_QKV) {
     GemmArgs a = a0;
     const int cfg = pick_cfg(a);
@@ -985,19 +985,19 @@ void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
       pa.splits = used;
       pa.bias = a0.bias;
       launch_qkv_post(pa, st);
-      return;
+      return 0;
     }
     if (a0.post.HD != 64 || a0.w_lo) {
       QkvPostArgs pa = a0.post;
       pa.qkv = a0.c;
       launch_gemm(a, GEMM_STORE, st);                // raw projections into c, then
       launch_qkv_post(pa, st);                       // the separate post-processing
-      return;
+      return 0;
     }
     a.partial = nullptr;
     a.k_chunk = a.K;
     launch_epi<GEMM_QKV>(a, cfg, 1, st);
-    return;
+    return 0;
   }
   GemmArgs a = a0;
   a.w_lo = nullptr;
@@ -1008,7 +1008,7 @@ void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
   int splits = pick_splits(a, cfg);
   if (two && !a.partial && epi == GEMM_SILU) {          // needs the split-K planes
     report_unlaunched("two-plane SiLU GEMM without split-K planes");
-    return;
+    return 0;
   }
   if (two && (splits <= 1 || !a.partial) && epi != GEMM_SILU) {
     // tiles that fill the GPU: the second plane's pass adds into the output
@@ -1020,7 +1020,7 @@ void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
     b.w = a0.w_lo;
     b.bias = nullptr;
     launch_epi<GEMM_RESID>(b, cfg, 1, st);
-    return;
+    return 0;
   }
   if (!two && splits <= 1) {
     a.partial = nullptr;
@@ -1031,7 +1031,7 @@ void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
       case GEMM_SILU: launch_epi<GEMM_SILU>(a, cfg, 1, st); break;
       default: report_unlaunched("GEMM: epilogue"); break;
     }
-    return;
+    return 0;
   }
   if (splits < 1) splits = 1;
   // K slices are whole 64-column stages
@@ -1044,7 +1044,12 @@ void launch_gemm(const GemmArgs& a0, int epi, hipStream_t st) {
     b.partial = a.partial + (size_t)used * a.M * a.N;
     launch_epi<GEMM_STORE>(b, cfg, used, st);
   }
+  // deferred: the caller's next kernel sums the partial planes itself (the same fixed
+  // order as the reduce: planes 0, 1, ... then the residual or the bias)
+  if (defer && !two && (epi == GEMM_STORE || epi == GEMM_RESID) && used <= kMaxDeferredPlanes)
+    return used;
   launch_reduce(a, epi, two ? 2 * used : used, st);
+  return 0;
 }
 
 void launch_gemm_f32w(const GemmF32Args& a, int epi, hipStream_t st) {

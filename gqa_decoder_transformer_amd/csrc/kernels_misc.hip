@@ -150,26 +150,44 @@ __global__ void __launch_bounds__(256) k_rmsnorm(const float* x, const float* w,
 
 // Vector form for H a multiple of 4 and at most 4096: each thread keeps its NV groups of
 // four elements in registers (one read of the row), 16-byte loads and stores, 8-byte
-// stores of the bf16 planes.
+// stores of the bf16 planes. With nsplit > 0 (rows 0..R-1 in order) the residual add of a
+// split-K GEMM comes first: x += sum of its partial planes [nsplit][R][H], summed in plane
+// order as the split-K reduce sums them, and the new row is written back to x.
 template <int NV>
-__global__ void __launch_bounds__(256) k_rmsnorm_v(const float* x, const float* w, float eps, int H,
+__global__ void __launch_bounds__(256) k_rmsnorm_v(float* x, const float* w, float eps, int H,
                                                    int row_step, int row_off, float* out_f32,
                                                    uint16_t* hi, uint16_t* lo, uint16_t* x2,
-                                                   int ld_plane) {
+                                                   int ld_plane, const float* part, int nsplit) {
   __shared__ float red[16];
   const int r = blockIdx.x;
   const int H4 = H / 4;
-  const float4* xr = (const float4*)(x + ((size_t)r * row_step + row_off) * H);
+  float4* xr = (float4*)(x + ((size_t)r * row_step + row_off) * H);
   float4 v[NV];
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int i = threadIdx.x + 256 * j;
     v[j] = i < H4 ? ld_stream_f4(xr + i) : make_float4(0.f, 0.f, 0.f, 0.f);   // read once
-    ss += v[j].x * v[j].x;
-    ss += v[j].y * v[j].y;
-    ss += v[j].z * v[j].z;
-    ss += v[j].w * v[j].w;
+    if (nsplit > 0 && i < H4) {
+      // every plane's load issued before the first add (one latency, not nsplit)
+      const size_t plane = (size_t)gridDim.x * H4;
+      const float4* pp = (const float4*)part + (size_t)r * H4 + i;
+      float4 pv[kMaxDeferredPlanes];
+#pragma unroll
+      for (int s = 0; s < kMaxDeferredPlanes; ++s) pv[s] = ld_stream_f4(pp + min(s, nsplit - 1) * plane);
+      float4 acc = pv[0];
+#pragma unroll
+      for (int s = 1; s < kMaxDeferredPlanes; ++s)
+        if (s < nsplit) { acc.x += pv[s].x; acc.y += pv[s].y; acc.z += pv[s].z; acc.w += pv[s].w; }
+      v[j] = make_float4(v[j].x + acc.x, v[j].y + acc.y, v[j].z + acc.z, v[j].w + acc.w);
+      xr[i] = v[j];
+    }
+    // explicit FMAs: the order of the sum of squares does not depend on how the
+    // compiler chooses to contract x*x + y*y
+    ss = fmaf(v[j].x, v[j].x, ss);
+    ss = fmaf(v[j].y, v[j].y, ss);
+    ss = fmaf(v[j].z, v[j].z, ss);
+    ss = fmaf(v[j].w, v[j].w, ss);
   }
   ss = block_sum(ss, red);
   const float rms = sqrtf(ss / (float)H + eps);
@@ -198,17 +216,28 @@ __global__ void __launch_bounds__(256) k_rmsnorm_v(const float* x, const float* 
   }
 }
 
+bool rmsnorm_adds_partials(int H, int ld_plane) {
+  return H % 4 == 0 && ld_plane % 4 == 0 && (H / 4 + 255) / 256 <= 4;
+}
+
 void launch_rmsnorm(const float* x, const float* w, float eps, int R, int H, int row_step,
                     int row_off, float* out_f32, uint16_t* hi, uint16_t* lo, int ld_plane,
-                    hipStream_t st, uint16_t* x2) {
+                    hipStream_t st, uint16_t* x2, const float* part, int nsplit) {
   if (R <= 0) return;
   const int nv = (H / 4 + 255) / 256;
+  if (nsplit > 0 && (!part || row_step != 1 || row_off != 0 || nsplit > kMaxDeferredPlanes ||
+                     !rmsnorm_adds_partials(H, ld_plane))) {
+    report_unlaunched("RMSNorm: residual partial planes in a form that cannot add them");
+    return;
+  }
+  // the residual add writes x (only with nsplit > 0)
+  float* xm = const_cast<float*>(x);
   if (H % 4 == 0 && (!hi || ld_plane % 4 == 0) && nv <= 4) {
     switch (nv) {
-      case 1: hipLaunchKernelGGL(k_rmsnorm_v<1>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, x2, ld_plane); return;
-      case 2: hipLaunchKernelGGL(k_rmsnorm_v<2>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, x2, ld_plane); return;
-      case 3: hipLaunchKernelGGL(k_rmsnorm_v<3>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, x2, ld_plane); return;
-      default: hipLaunchKernelGGL(k_rmsnorm_v<4>, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off, out_f32, hi, lo, x2, ld_plane); return;
+      case 1: hipLaunchKernelGGL(k_rmsnorm_v<1>, dim3(R), dim3(256), 0, st, xm, w, eps, H, row_step, row_off, out_f32, hi, lo, x2, ld_plane, part, nsplit); return;
+      case 2: hipLaunchKernelGGL(k_rmsnorm_v<2>, dim3(R), dim3(256), 0, st, xm, w, eps, H, row_step, row_off, out_f32, hi, lo, x2, ld_plane, part, nsplit); return;
+      case 3: hipLaunchKernelGGL(k_rmsnorm_v<3>, dim3(R), dim3(256), 0, st, xm, w, eps, H, row_step, row_off, out_f32, hi, lo, x2, ld_plane, part, nsplit); return;
+      default: hipLaunchKernelGGL(k_rmsnorm_v<4>, dim3(R), dim3(256), 0, st, xm, w, eps, H, row_step, row_off, out_f32, hi, lo, x2, ld_plane, part, nsplit); return;
     }
   }
   hipLaunchKernelGGL(k_rmsnorm, dim3(R), dim3(256), 0, st, x, w, eps, H, row_step, row_off,
