@@ -179,7 +179,8 @@ __global__ void __launch_bounds__(256) k_decode_attn(DecodeAttnArgs a) {
   const int qkv_n = (a.NH + 2 * a.NKV) * HD;
   // projection column c of this row: stored by the QKV GEMM, or the sum of its deferred
   // split-K planes in plane order plus the bias (what the split-K reduce would have stored)
-  // (every plane's load issued before the first add)
+  // (every plane's load issued before the first add; past the last plane the loads repeat
+  // it, unused: 1.4 us per layer faster than branching around them)
   auto proj = [&](int c) -> float {
     if (a.qkv_splits <= 0) return a.qkv[(size_t)b * qkv_n + c];
     const float* pp = a.qkv_part + (size_t)b * qkv_n + c;

@@ -163,22 +163,31 @@ __global__ void __launch_bounds__(256) k_rmsnorm_v(float* x, const float* w, flo
   const int H4 = H / 4;
   float4* xr = (float4*)(x + ((size_t)r * row_step + row_off) * H);
   float4 v[NV];
-  float ss = 0.f;
+  // the residual add of a deferred split-K GEMM: every load of the row and of its planes
+  // issued before the first add (one latency, not one per plane or per group; the plane
+  // count is uniform, so the guards are scalar branches)
+  float4 pv[NV][kMaxDeferredPlanes];
+  const size_t plane = (size_t)gridDim.x * H4;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int i = threadIdx.x + 256 * j;
     v[j] = i < H4 ? ld_stream_f4(xr + i) : make_float4(0.f, 0.f, 0.f, 0.f);   // read once
     if (nsplit > 0 && i < H4) {
-      // every plane's load issued before the first add (one latency, not nsplit)
-      const size_t plane = (size_t)gridDim.x * H4;
       const float4* pp = (const float4*)part + (size_t)r * H4 + i;
-      float4 pv[kMaxDeferredPlanes];
 #pragma unroll
-      for (int s = 0; s < kMaxDeferredPlanes; ++s) pv[s] = ld_stream_f4(pp + min(s, nsplit - 1) * plane);
-      float4 acc = pv[0];
+      for (int s = 0; s < kMaxDeferredPlanes; ++s)
+        if (s < nsplit) pv[j][s] = ld_stream_f4(pp + s * plane);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    if (nsplit > 0 && i < H4) {
+      float4 acc = pv[j][0];
 #pragma unroll
       for (int s = 1; s < kMaxDeferredPlanes; ++s)
-        if (s < nsplit) { acc.x += pv[s].x; acc.y += pv[s].y; acc.z += pv[s].z; acc.w += pv[s].w; }
+        if (s < nsplit) { acc.x += pv[j][s].x; acc.y += pv[j][s].y; acc.z += pv[j][s].z; acc.w += pv[j][s].w; }
       v[j] = make_float4(v[j].x + acc.x, v[j].y + acc.y, v[j].z + acc.z, v[j].w + acc.w);
       xr[i] = v[j];
     }
