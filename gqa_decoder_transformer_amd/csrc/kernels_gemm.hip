@@ -604,7 +604,8 @@ enum GemmCfg { CFG_128x256 = 1, CFG_128x128 = 2, CFG_64x128 = 3, CFG_256x256 = 4
                CFG_DL_256x256 = 8,        // one plane: 8 waves of 128 x 64
                CFG_DL_S128x256 = 9,       // two planes: 8 waves of 64 x 64
                CFG_DL_64x64 = 10,         // 2 waves of 32 x 64, three stages (two: three planes)
-               CFG_DL_64x256 = 11 };      // two planes, M <= 64: 4 waves of 64 x 64, three stages
+               CFG_DL_64x256 = 11,        // two planes, M <= 64: 4 waves of 64 x 64, three stages
+               CFG_DL_128x128 = 12 };     // two planes: 4 waves of 64 x 64, three stages
 
 template <int BM, int BN, int WM, int WN, int PF, bool SPLIT, int EPI, int KG = 1>
 void set_attr() {
@@ -673,9 +674,14 @@ int pick_cfg(const GemmArgs& a) {
   // a second block per CU (64-row EXACT decode layer 91.2 -> 87.8 us, FAST 80.0 -> 76.8)
   if (a.M <= 128) return dl && tiles_of(a, 64, 64) <= 256 ? CFG_DL_64x64 : CFG_64x64;
   // two-plane input: 128 x 256 tiles over 8 waves of 64 x 64 (two waves per SIMD; over 4
-  // waves of 64 x 128 the accumulators and fragments held a wave to one per SIMD)
-  if (a.a_lo)
-    return tiles_of(a, 128, 256) >= 180 ? (dl ? CFG_DL_S128x256 : CFG_128x256_W8) : CFG_128x128;
+  // waves of 64 x 128 the accumulators and fragments held a wave to one per SIMD); with
+  // fewer such tiles, 128 x 128 straight into LDS over three stages (the 1B shape's output
+  // and down projections at M = 2048: 53.5 -> 51 us and 152-160 -> 142 us against register
+  // staging; with one plane the same form was slower, the QKV projection 50 -> 69 us)
+  if (a.a_lo) {
+    if (tiles_of(a, 128, 256) >= 180) return dl ? CFG_DL_S128x256 : CFG_128x256_W8;
+    return dl ? CFG_DL_128x128 : CFG_128x128;
+  }
   if (tiles_of(a, 256, 256) >= 256) return dl ? CFG_DL_256x256 : CFG_256x256;
   // long K against N (the down projection at M = 2048): 256 x 256 tiles over four K
   // slices, whose partial planes cost less than the halved operand traffic saves there
@@ -698,6 +704,7 @@ void cfg_dims(int cfg, int& bm, int& bn) {
     case CFG_128x128: case CFG_128x128_K2: bm = 128; bn = 128; break;
     case CFG_64x64: case CFG_DL_64x64: bm = 64; bn = 64; break;
     case CFG_DL_64x256: bm = 64; bn = 256; break;
+    case CFG_DL_128x128: bm = 128; bn = 128; break;
     default: bm = 64; bn = 128; break;
   }
 }
@@ -731,6 +738,10 @@ void launch_split(const GemmArgs& a, int cfg, int splits, hipStream_t st) {
       break;
     case CFG_DL_64x256:
       if constexpr (SPLIT) launch_dl<64, 256, 1, 4, 64, 3, 2, EPI>(a, splits, st);
+      else report_unlaunched("GEMM: two-plane tile form with one plane");
+      break;
+    case CFG_DL_128x128:
+      if constexpr (SPLIT) launch_dl<128, 128, 2, 2, 64, 3, 2, EPI>(a, splits, st);
       else report_unlaunched("GEMM: two-plane tile form with one plane");
       break;
     default: launch_cfg<64, 128, 2, 2, 2, SPLIT, EPI>(a, splits, st); break;
@@ -779,6 +790,7 @@ void set_attrs_split() {
     set_attr_dl<128, 256, 2, 4, 64, 2, 2, EPI>();
     set_attr_dl<64, 64, 2, 1, 64, 3, 2, EPI>();
     set_attr_dl<64, 256, 1, 4, 64, 3, 2, EPI>();
+    set_attr_dl<128, 128, 2, 2, 64, 3, 2, EPI>();
   }
 }
 
