@@ -444,3 +444,35 @@ def test_kv_cache_contents_match_the_oracle(model, prec_name):
             assert err < tol
     raw = eng.kv.view(2, L, 1, NKV, S, HD * (4 if prec == B.EXACT else 2))
     assert bool((raw[:, :, :, :, n:] == 255).all())
+
+
+@pytest.mark.parametrize("model", [LLAMA_SPLITK, LLAMA_SMALL], ids=lambda m: m.name)
+@pytest.mark.parametrize("prec_name", ["exact", "fast"])
+def test_mid_length_prompts_between_the_tile_forms(model, prec_name):
+    """Two rows of 300 tokens (600 rows per pass): more than the 64-row forms take, too few
+    for the large tiles. EXACT's two-plane projections take 128 x 128 tiles straight into
+    LDS, and a down projection with K >= 4 x 256 splits K into partial planes that the next
+    layer's norm adds into x (llama-splitk: K = 1024); the two-row decode steps split their
+    projections and leave those sums to the next norm and to the decode attention.
+    Teacher-forced with the oracle's ids: logits at every step within the tier, and the
+    GPU's argmax against the oracle's under the near-tie rule."""
+    from gqa_decoder_transformer_amd import binding as B
+    prec = B.EXACT if prec_name == "exact" else B.FAST
+    tol = TOL_EXACT if prec == B.EXACT else TOL_FAST
+    ck = W.make_weights(model, 13)
+    Bn, T, N = 2, 300, 6
+    prompt = np.random.default_rng(17).integers(0, model.vocab, (Bn, T)).astype(np.int32)
+    say(f"mid-length prompts {model.name} B={Bn} T={T} N={N} {prec_name}")
+    om = O.OracleModel(model, ck)
+    runs = [O.generate(om, prompt[b], N) for b in range(Bn)]
+    feed = np.stack([runs[b][0][:N] for b in range(Bn)], axis=1)          # [N, B]
+    eng = _engine(model, ck, prec, max_batch=Bn, max_seq=320)
+    g_ids, g_logits = gpu_generate(eng, prompt, N, feed=feed,
+                                   logits_dtype=B.F32 if prec == B.EXACT else B.BF16)
+    for b in range(Bn):
+        or_ids, or_logits = runs[b]
+        err = rel_maxabs(g_logits[:, b], or_logits)
+        say(f"row {b}: max rel err {err.max():.3g}")
+        assert err.max() < tol, (b, err)
+        if prec == B.EXACT:
+            check_greedy(g_ids[:, b], or_ids, or_logits, tol)
