@@ -476,3 +476,32 @@ def test_mid_length_prompts_between_the_tile_forms(model, prec_name):
         assert err.max() < tol, (b, err)
         if prec == B.EXACT:
             check_greedy(g_ids[:, b], or_ids, or_logits, tol)
+
+
+@pytest.mark.parametrize("prec_name", ["exact", "fast"])
+def test_decode_batch_past_64_rows(prec_name):
+    """A 100-row decode batch: the batched-decode projections take two 64-row tiles, the
+    LM head the register-staged form (the 64 x 256 one is for at most 64 rows), and the
+    split-K planes of the residual projections are summed by the next norm over 100 rows.
+    Teacher-forced with random ids; rows 0, 63, 64 and 99 against the oracle at every
+    step (llama-splitk)."""
+    from gqa_decoder_transformer_amd import binding as B
+    prec = B.EXACT if prec_name == "exact" else B.FAST
+    tol = TOL_EXACT if prec == B.EXACT else TOL_FAST
+    model = LLAMA_SPLITK
+    ck = W.make_weights(model, 31)
+    Bn, T, N = 100, 24, 5
+    rng = np.random.default_rng(37)
+    prompt = rng.integers(0, model.vocab, (Bn, T)).astype(np.int32)
+    # the oracle picks after every step, the last one included (its id is not fed back)
+    feed = rng.integers(0, model.vocab, (N + 1, Bn)).astype(np.int32)
+    say(f"decode batch {model.name} B={Bn} T={T} N={N} {prec_name}")
+    eng = _engine(model, ck, prec, max_batch=Bn, max_seq=32, max_tokens=Bn * T)
+    _, g_logits = gpu_generate(eng, prompt, N, feed=feed,
+                               logits_dtype=B.F32 if prec == B.EXACT else B.BF16)
+    om = O.OracleModel(model, ck)
+    for b in (0, 63, 64, 99):
+        _, or_logits = O.generate(om, prompt[b], N, pick=lambda k, lg, b=b: int(feed[k, b]))
+        err = rel_maxabs(g_logits[:, b], or_logits)
+        say(f"row {b}: max rel err {err.max():.3g}")
+        assert err.max() < tol, (b, err)
