@@ -505,3 +505,28 @@ def test_decode_batch_past_64_rows(prec_name):
         err = rel_maxabs(g_logits[:, b], or_logits)
         say(f"row {b}: max rel err {err.max():.3g}")
         assert err.max() < tol, (b, err)
+
+
+def test_few_rows_wide_vocabulary_lm_head():
+    """EXACT decode of 5 rows over a 70 000-token vocabulary: the two-plane LM head of at
+    most 64 rows with at least 1024 64-column tiles takes the 64 x 256 form (rows past the
+    batch are clamped loads, never stored). Free-running greedy ids with the near-tie rule
+    and the logits of every step against the oracle, per row."""
+    from gqa_decoder_transformer_amd import binding as B
+    import workloads.configs as WC
+    model = WC.shrink_model(WC.LLAMA1B, name="llama-wide-vocab", vocab=70000, hidden=128,
+                            layers=1, heads=2, kv_heads=1, head_dim=64, ffn=256)
+    ck = W.make_weights(model, 41)
+    Bn, T, N = 5, 20, 4
+    prompt = np.random.default_rng(43).integers(0, model.vocab, (Bn, T)).astype(np.int32)
+    say(f"wide vocabulary {model.name} B={Bn} T={T} N={N} EXACT")
+    eng = _engine(model, ck, B.EXACT, max_batch=Bn, max_seq=32, max_tokens=Bn * T)
+    g_ids, g_logits = gpu_generate(eng, prompt, N)
+    om = O.OracleModel(model, ck)
+    for b in range(Bn):
+        or_ids, or_logits = O.generate(om, prompt[b], N)
+        upto = check_greedy(g_ids[:, b], or_ids, or_logits, TOL_EXACT)
+        k = N + 1 if upto is None else upto + 1     # steps fed the same ids
+        err = rel_maxabs(g_logits[:k, b], or_logits[:k])
+        say(f"row {b}: max rel err {err.max():.3g}")
+        assert err.max() < TOL_EXACT, (b, err)
